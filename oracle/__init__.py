@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for the joint sCM target.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the product path.
+"""
+from .scm_oracle import (  # noqa: F401
+    Dual, attention, attention_fwd_jvp, attention_lse, boost_factor, joint_block,
+    l2_normalise, scm_direction, scm_sample, scm_target, student_field, time_embedding,
+    trigflow_field, trigflow_noise,
+)
