@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Throughput of the joint sCM target on one MI355X.
+
+One step = one call of t2va_scm_target over one batch of synthetic input
+already resident in HBM: TrigFlow noising, the teacher block, teacher fields,
+the student block with its forward-mode JVP, the sCM direction, per-sample
+per-modality L2 normalisation, residual and loss.  The default workload is the
+high-resolution shape (B=1, 28,672 video + 256 audio + 256 text tokens with
+102 valid, d=2048, 16 heads of 128).
+
+Prints one JSON line.  The roofline object covers the dominant kernel, the
+student attention forward+JVP, timed with HIP events recorded by the library
+around each of its launches on the launch stream during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sCM-target samples/s + attn fwd+JVP TFLOP/s (% MFMA bf16 peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def workload_name(cfg) -> str:
+    return (f"{cfg.name} joint sCM target: B={cfg.B}, video {cfg.Nv}x{cfg.Cv}, audio {cfg.Na}x{cfg.Ca}, "
+            f"text {cfg.Nt} ({cfg.Ntv} valid), d={cfg.d}, {cfg.H}x{cfg.dh} heads, bf16 storage, "
+            f"teacher + student fwd+JVP")
+
+
+def attention_flops(cfg, nk_per_sample) -> float:
+    """Algorithmic flops of one student attention fwd+JVP launch: 12 d Nq Nk per sample."""
+    return float(sum(12.0 * cfg.d * cfg.Nq * nk for nk in nk_per_sample))
+
+
+def cpu_baseline(cfg, budget_s: float) -> dict:
+    """Time the fp64 oracle on a bounded sample of the workload and extrapolate.
+
+    The oracle runs every block through dual numbers (teacher with zero
+    tangents), so its cost is two blocks of: the QKV projection of every token
+    and, per head, the chunked dual attention of every query row over all
+    valid keys.  We time whole 512-row chunks of both on operands of the real
+    shapes and scale linearly in rows and heads.
+    """
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    dh, d = cfg.dh, cfg.d
+    nk = cfg.Nq + cfg.Ntv
+    chunk = 512
+    mk = lambda *s: oracle.Dual(rng.standard_normal(s), rng.standard_normal(s))
+    K, V = mk(nk, dh), mk(nk, dh)
+    Q = mk(chunk, dh)
+    X = mk(chunk, d)
+    W = rng.standard_normal((3 * d, d)) / math.sqrt(d)
+    n_att = n_proj = 0
+    t_att = t_proj = 0.0
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.attention(Q, K, V, chunk=chunk)
+        t_att += time.perf_counter() - t0
+        n_att += 1
+        t0 = time.perf_counter()
+        oracle.scm_oracle.d_linear(X, W)
+        t_proj += time.perf_counter() - t0
+        n_proj += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    per_att = t_att / n_att
+    per_proj = t_proj / n_proj
+    q_chunks = math.ceil(cfg.Nq / chunk)
+    proj_chunks = math.ceil(cfg.N_all / chunk)
+    per_sample = 2 * (cfg.H * q_chunks * per_att + proj_chunks * per_proj)
+    return {
+        "value": 1.0 / per_sample, "unit": "samples/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"{n_att} x oracle.attention (fp64 dual) of {chunk} query rows x {nk} keys x dh {dh}, "
+                   f"{n_proj} x dual QKV projection of {chunk} rows ({d}->{3 * d}); extrapolated to "
+                   f"2 blocks x {cfg.H} heads x {q_chunks} query chunks + {proj_chunks} projection "
+                   f"chunks per sample ({per_sample:.0f} s/sample)"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="high-res")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from joint_video_audio_trigflow_amd import _lib, inputs
+
+    _lib.load()
+    cfg = inputs.CONFIGS[args.config]
+    problem = inputs.make_problem(cfg)
+    dev = _lib.to_device_problem(problem)
+    dt = _lib.DTYPE_BF16 if cfg.in_dtype == "bf16" else _lib.DTYPE_FP32
+    op = _lib.ScmTarget(cfg, in_dtype=dt, weight_dtype=dt)
+    call = lambda: op(dev["teacher"], dev["student"], dev["z0_v"], dev["z0_a"], dev["eps_v"],
+                      dev["eps_a"], dev["text"], dev["text_mask"], dev["t"])
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: warmup done", file=sys.stderr, flush=True)
+
+    _lib.profile_enable(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phases, ncalls = _lib.profile_read()
+    _lib.profile_enable(0)
+    assert ncalls == args.steps, (ncalls, args.steps)
+    loss = op.out["loss"].cpu().numpy()
+    if not np.all(np.isfinite(loss)):
+        raise RuntimeError(f"non-finite loss {loss}")
+
+    ms_step = 1000.0 * elapsed / args.steps
+    nk = [cfg.Nq + int(m.sum()) for m in problem["data"]["text_mask"]]
+    flops = attention_flops(cfg, nk)
+    attn_ms = phases["student_attn"] / ncalls
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    teacher_ms = phases["teacher_attn"] / ncalls
+    teacher_tf = flops / 3.0 / (teacher_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": cfg.B * args.steps / elapsed,
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latents/noise/text, N(0,1/fan_in) weights)",
+        "config": {"workload": workload_name(cfg), "global_batch": cfg.B,
+                   "tokens": cfg.N_all, "valid_keys": nk, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": f"attn_fwd_jvp_kernel<{cfg.dh},true>", "flops_per_launch": flops,
+                     "avg_launch_ms": attn_ms},
+        "phases_ms_per_step": {k: v / ncalls for k, v in phases.items()},
+        "teacher_attn_tflops": teacher_tf,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

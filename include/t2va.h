@@ -1,0 +1,244 @@
+/*
+ * t2va.h - C ABI of the MI355X (gfx950) joint sCM target library (libt2va.so).
+ *
+ * The library computes the training target of TurboT2VA's joint
+ * continuous-time consistency (sCM) stage for paired video and audio latents
+ * (arXiv 2608.24674; "TurboT2VA：分数正则化一致性蒸馏加速 19B 视频音频联合生成",
+ * robotworld.top deep read, sections 3 and 3.1).  All GPU work is hand-written
+ * HIP for gfx950 and is enqueued on the caller's stream.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are plain HIP device addresses; host pointers are named
+ *     *_host.  Nothing is allocated on the hot path: the caller owns every
+ *     buffer, including the workspace.  Inputs are never written; outputs are
+ *     fully overwritten (never accumulated into).
+ *   - Matrices are row-major.  "bf16" is bfloat16 (1-8-7), "fp32" IEEE single.
+ *   - Weights follow the nn.Linear convention [out_features, in_features]:
+ *     y = x W^T.
+ *   - All host-side validation happens before the first launch.  A failing
+ *     call returns a non-zero status, launches nothing and records a message
+ *     that t2va_last_error() returns (thread-local).  No exception or abort
+ *     crosses the ABI.  A failure reported by the HIP runtime at launch maps to
+ *     T2VA_HIP_ERROR; work already enqueued by that call may have run.
+ *   - Work is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Outputs are valid once the caller synchronises that stream.
+ *   - Results are deterministic: no floating-point atomics; reductions run in
+ *     a fixed order, so identical inputs give bitwise-identical outputs.
+ *   - Calls on the same stream are ordered; calls on different streams that
+ *     share a workspace race.
+ */
+#ifndef T2VA_H
+#define T2VA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define T2VA_ABI_VERSION 1
+
+typedef int t2va_status;
+#define T2VA_OK 0
+#define T2VA_INVALID_ARG 1
+#define T2VA_UNSUPPORTED_SHAPE 2
+#define T2VA_WORKSPACE_TOO_SMALL 3
+#define T2VA_HIP_ERROR 4
+
+#define T2VA_DTYPE_BF16 0
+#define T2VA_DTYPE_FP32 1
+
+/* Largest batch one call accepts (per-sample coefficients travel as kernel
+ * arguments). */
+#define T2VA_MAX_BATCH 64
+
+typedef void *t2va_stream; /* hipStream_t */
+
+/* Returns T2VA_ABI_VERSION of the loaded library. */
+int t2va_abi_version(void);
+
+/* Message describing the last failing call on this thread ("" if none).
+ * The pointer stays valid until the next call on this thread. */
+const char *t2va_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Elementwise TrigFlow maps                                                 */
+/* ------------------------------------------------------------------------ */
+#define T2VA_NOISE 0 /* out = cos(t) a + sin(t) b          (a = z0,  b = eps)     */
+#define T2VA_FIELD 1 /* out = (cos(t) a - b) / sin(t)      (a = z_t, b = x0_hat)  */
+
+/*
+ * t2va_trigflow_field - TrigFlow noising z_t = cos t z0 + sin t eps (deep read,
+ * section 3, noising equation) or the TrigFlow field
+ * F = (cos t z_t - x0_hat)/sin t (section 3.1, field equation), per sample.
+ *
+ *   mode            T2VA_NOISE or T2VA_FIELD.
+ *   B               samples, 1..T2VA_MAX_BATCH.
+ *   n_per_sample    elements per sample (>= 0); a, b, out are [B, n_per_sample],
+ *                   contiguous, 16-byte aligned device buffers.
+ *   a_dtype, b_dtype, out_dtype   T2VA_DTYPE_BF16 or T2VA_DTYPE_FP32.
+ *   t_host          host array of B timesteps, each finite with 0 < t < pi/2.
+ * Arithmetic is fp32 with coefficients rounded once from fp64.
+ * Errors: T2VA_INVALID_ARG (null pointer, bad mode/dtype, t out of range,
+ * misalignment), T2VA_UNSUPPORTED_SHAPE (B out of range).
+ */
+t2va_status t2va_trigflow_field(int mode, int B, int64_t n_per_sample, int a_dtype, int b_dtype,
+                                int out_dtype, const double *t_host, const void *a, const void *b,
+                                void *out, t2va_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Joint attention forward + forward-mode JVP                                */
+/* ------------------------------------------------------------------------ */
+/*
+ * Operand layouts (all strides in elements, all bf16):
+ *   q, qd   element (b, i, h, c) at  b*q_batch_stride + i*q_row_stride + h*dh + c
+ *           (sequence-major; the projection's [B, N, H*dh] output works as is)
+ *   k, kd   element (b, j, h, c) at  b*k_batch_stride + j*k_row_stride + h*dh + c
+ *   vt, vdt V stored dh-major per head ("V transposed"):
+ *           element (b, j, h, c) at  b*vt_batch_stride + h*vt_head_stride + c*vt_row_stride + j
+ *           vt_row_stride must be a multiple of 8 and >= round_up(Nk, 8).
+ *   o, od   element (b, i, h, c) at  b*o_batch_stride + i*o_row_stride + h*dh + c,
+ *           dtype out_dtype.
+ *   lse     fp32 [B, H, Nq] (nullable): natural-log log-sum-exp of the scaled
+ *           logits of each query row.
+ * Tangent operands use the same strides as their primal operands.
+ */
+typedef struct {
+  int B, H, dh;  /* dh in {64, 128} */
+  int Nq;        /* query rows per sample (>= 1) */
+  int Nk;        /* key rows present per sample (>= 1); nk_valid[b] <= Nk */
+  int64_t q_batch_stride, q_row_stride;
+  int64_t k_batch_stride, k_row_stride;
+  int64_t vt_batch_stride, vt_head_stride, vt_row_stride;
+  int64_t o_batch_stride, o_row_stride;
+  int has_tangent; /* 0: forward only (qd, kd, vdt, od must be NULL) */
+  int out_dtype;   /* T2VA_DTYPE_BF16 or T2VA_DTYPE_FP32 */
+  float scale;     /* logit scale; 0 selects 1/sqrt(dh) */
+} t2va_attn_desc;
+
+/*
+ * t2va_joint_attn_fwd_jvp - O = softmax(scale Q K^T + mask) V and its tangent
+ * dO along (dQ, dK, dV) for every (sample, head):
+ *   dO = P (dS - mu) V + P dV,  dS = scale (dQ K^T + Q dK^T),  mu = rowsum(P * dS),
+ * where keys j >= nk_valid[b] are excluded (logit -inf).  This is the attention
+ * step of the joint block through which the joint JVP of the sCM stage passes
+ * (deep read, section 3.1, J_theta equation; section 4.2: the JVP passes
+ * through the cross-modal transformer; section 6.3: padded text positions are
+ * removed from the keys).  Softmax state and accumulators are fp32; P and
+ * P*dS enter the matrix cores as bf16.
+ *   nk_valid  device int32 [B], each in [1, Nk].  Values outside that range
+ *             are clamped to it by the kernel.
+ * Errors: T2VA_INVALID_ARG (null/misaligned pointers, strides not multiples
+ * of 8, tangent pointers inconsistent with has_tangent),
+ * T2VA_UNSUPPORTED_SHAPE (dh not 64/128, B/H/Nq/Nk < 1).
+ */
+t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, const void *k,
+                                    const void *vt, const void *qd, const void *kd,
+                                    const void *vdt, const int32_t *nk_valid, void *o, void *od,
+                                    float *lse, t2va_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* The joint sCM target                                                      */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int B;        /* samples, 1..T2VA_MAX_BATCH */
+  int Nv, Na;   /* video and audio tokens per sample (>= 1 each) */
+  int Nt;       /* text positions per sample (>= 0) */
+  int Cv, Ca;   /* latent channels, multiples of 64 */
+  int d, H;     /* block width and heads; d = H*dh with dh in {64, 128} */
+  int in_dtype; /* dtype of z0, eps and text: T2VA_DTYPE_BF16 or T2VA_DTYPE_FP32 */
+  int weight_dtype; /* dtype of all weights: T2VA_DTYPE_BF16 or T2VA_DTYPE_FP32
+                       (fp32 weights are rounded to bf16 into the workspace) */
+  double beta;  /* consistency boost (section 3.1) */
+  double gamma; /* tangent warm-up ratio, 0 <= gamma <= 1 */
+  double eps_scm; /* > 0, added to the L2 norm */
+  double w_v, w_a; /* modality weights of the joint loss */
+} t2va_scm_desc;
+
+/* One copy of the joint block (teacher or student); device pointers. */
+typedef struct {
+  const void *w_in_v;  /* [d, Cv] */
+  const void *w_in_a;  /* [d, Ca] */
+  const void *w_t;     /* [d, d]  linear layer after the sinusoidal time embedding */
+  const void *w_qkv;   /* [3d, d] rows 0..d-1: W_q, d..2d-1: W_k, 2d..3d-1: W_v */
+  const void *w_out_v; /* [Cv, d] */
+  const void *w_out_a; /* [Ca, d] */
+} t2va_block_weights;
+
+/* Exact workspace size in bytes for t2va_scm_target with this descriptor
+ * (0 if the descriptor is invalid; t2va_last_error() says why). */
+size_t t2va_scm_workspace_bytes(const t2va_scm_desc *desc);
+
+/*
+ * t2va_scm_target - the joint sCM target (deep read, section 3 and 3.1):
+ *   z_t^m  = cos t z0^m + sin t eps^m                         (shared t, m in {v, a})
+ *   x0_T   = G_T(z_t^v, z_t^a, t, c),  F_T^m = (cos t z_t^m - x0_T^m)/sin t
+ *   x0_S, dG = G_S and its JVP along (dt = 1, dz^v = F_T^v, dz^a = F_T^a, dc = 0)
+ *   F_S^m  = (cos t z_t^m - x0_S^m)/sin t
+ *   J^m    = cos t sin t * d/ds F_S^m along that tangent
+ *   g^m    = -beta cos t/sqrt(1 - gamma^2 sin^2 t) (F_S^m - F_T^m) - gamma cos t sin t z_t^m - J^m
+ *   n^m    = ||g^m||_2 over all Nm*Cm elements of one sample's modality
+ *   gbar^m = g^m/(n^m + eps_scm),  r^m = F_S - sg(F_S) - gbar^m = -gbar^m (value)
+ *   loss_b = w_v ||r^v||^2 + w_a ||r^a||^2
+ * G is the joint block: per-modality input projection plus a sinusoidal
+ * time embedding (base 10000, [cos | sin]) through w_t; one multi-head
+ * self-attention whose queries are the video and audio tokens and whose keys
+ * are video, audio and the valid text tokens; per-modality output projection.
+ *
+ * Inputs (device):
+ *   z0_v, eps_v  [B, Nv, Cv] in_dtype     z0_a, eps_a [B, Na, Ca] in_dtype
+ *   text         [B, Nt, d]  in_dtype     text_mask   uint8 [B, Nt], nonzero = valid
+ *   t_host       host double [B], each finite with 0 < t < pi/2
+ * Outputs (device, fp32):
+ *   J_v [B, Nv, Cv], J_a [B, Na, Ca]           nullable
+ *   gbar_v, gbar_a  same shapes                 required
+ *   r_v, r_a        same shapes                 nullable
+ *   norms [B, 2]  (n^v, n^a)                    nullable
+ *   loss  [B]                                   required
+ * workspace: device buffer of at least t2va_scm_workspace_bytes(desc) bytes,
+ * 256-byte aligned; its contents on entry are irrelevant.
+ * Errors: T2VA_INVALID_ARG (null required pointers, misalignment, t out of
+ * range, gamma outside [0, 1], eps_scm <= 0, bad dtypes),
+ * T2VA_UNSUPPORTED_SHAPE (d != H*dh, dh not 64/128, Cv/Ca not multiples of 64,
+ * B out of range), T2VA_WORKSPACE_TOO_SMALL.
+ */
+t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights *teacher,
+                            const t2va_block_weights *student, const void *z0_v, const void *z0_a,
+                            const void *eps_v, const void *eps_a, const void *text,
+                            const uint8_t *text_mask, const double *t_host, float *J_v, float *J_a,
+                            float *gbar_v, float *gbar_a, float *r_v, float *r_a, float *norms,
+                            float *loss, void *workspace, size_t workspace_bytes,
+                            t2va_stream stream);
+
+/* ------------------------------------------------------------------------ */
+/* Phase timing (instrumentation for benchmarks)                             */
+/* ------------------------------------------------------------------------ */
+#define T2VA_PHASE_TOTAL 0        /* whole t2va_scm_target call            */
+#define T2VA_PHASE_TEACHER_ATTN 1 /* teacher attention (forward only)      */
+#define T2VA_PHASE_STUDENT_ATTN 2 /* student attention forward + JVP       */
+#define T2VA_PHASE_GEMM 3         /* all projection GEMMs                  */
+#define T2VA_PHASE_OTHER 4        /* embedding, compaction, elementwise    */
+#define T2VA_NUM_PHASES 5
+
+/*
+ * t2va_profile_enable - with max_calls > 0, the next up to max_calls calls of
+ * t2va_scm_target record HIP events around each phase on their stream (the
+ * events are created here, outside the timed calls); with 0, recording stops
+ * and the events are destroyed.  Not thread-safe: enable, run, read from one
+ * thread.
+ */
+t2va_status t2va_profile_enable(int max_calls);
+
+/*
+ * t2va_profile_read - waits for the recorded events, writes per-phase sums of
+ * milliseconds over the recorded calls into ms_out[T2VA_NUM_PHASES], the
+ * number of recorded calls into *n_calls, and starts a new recording window.
+ */
+t2va_status t2va_profile_read(double *ms_out, int *n_calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* T2VA_H */

@@ -1,0 +1,263 @@
+"""ctypes binding of libt2va.so (argument marshalling only).
+
+Every step of the joint sCM target runs in the library's HIP kernels; this
+module only turns torch tensors into device pointers, provides output and
+workspace buffers, and passes torch's current HIP stream.  It raises if the
+library has not been built: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libt2va.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "t2va.h")
+
+T2VA_OK = 0
+DTYPE_BF16, DTYPE_FP32 = 0, 1
+NOISE, FIELD = 0, 1
+MAX_BATCH = 64
+NUM_PHASES = 5
+PHASES = ("total", "teacher_attn", "student_attn", "gemm", "other")
+
+
+class T2VAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"t2va status {status}: {msg}")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("dh", ctypes.c_int), ("Nq", ctypes.c_int),
+                ("Nk", ctypes.c_int),
+                ("q_batch_stride", ctypes.c_int64), ("q_row_stride", ctypes.c_int64),
+                ("k_batch_stride", ctypes.c_int64), ("k_row_stride", ctypes.c_int64),
+                ("vt_batch_stride", ctypes.c_int64), ("vt_head_stride", ctypes.c_int64),
+                ("vt_row_stride", ctypes.c_int64),
+                ("o_batch_stride", ctypes.c_int64), ("o_row_stride", ctypes.c_int64),
+                ("has_tangent", ctypes.c_int), ("out_dtype", ctypes.c_int), ("scale", ctypes.c_float)]
+
+
+class ScmDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("Nv", ctypes.c_int), ("Na", ctypes.c_int), ("Nt", ctypes.c_int),
+                ("Cv", ctypes.c_int), ("Ca", ctypes.c_int), ("d", ctypes.c_int), ("H", ctypes.c_int),
+                ("in_dtype", ctypes.c_int), ("weight_dtype", ctypes.c_int),
+                ("beta", ctypes.c_double), ("gamma", ctypes.c_double), ("eps_scm", ctypes.c_double),
+                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_in_v", "w_in_a", "w_t", "w_qkv", "w_out_v", "w_out_a")]
+
+
+WEIGHT_NAMES = ("w_in_v", "w_in_a", "w_t", "w_qkv", "w_out_v", "w_out_a")
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libt2va.so, raising if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m joint_video_audio_trigflow_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32p, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+    lib.t2va_abi_version.restype = i32
+    lib.t2va_last_error.restype = ctypes.c_char_p
+    lib.t2va_trigflow_field.restype = i32
+    lib.t2va_trigflow_field.argtypes = [i32, i32, i64, i32, i32, i32, dp, vp, vp, vp, vp]
+    lib.t2va_joint_attn_fwd_jvp.restype = i32
+    lib.t2va_joint_attn_fwd_jvp.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 10 + [vp]
+    lib.t2va_scm_workspace_bytes.restype = ctypes.c_size_t
+    lib.t2va_scm_workspace_bytes.argtypes = [ctypes.POINTER(ScmDesc)]
+    lib.t2va_scm_target.restype = i32
+    lib.t2va_scm_target.argtypes = ([ctypes.POINTER(ScmDesc), ctypes.POINTER(BlockWeights),
+                                     ctypes.POINTER(BlockWeights)] + [vp] * 5 + [vp, dp]
+                                    + [f32p] * 8 + [vp, ctypes.c_size_t, vp])
+    lib.t2va_profile_enable.restype = i32
+    lib.t2va_profile_enable.argtypes = [i32]
+    lib.t2va_profile_read.restype = i32
+    lib.t2va_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != T2VA_OK:
+        raise T2VAError(status, load().t2va_last_error().decode())
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _t_host(t):
+    arr = (ctypes.c_double * len(t))(*[float(x) for x in t])
+    return arr
+
+
+def trigflow_field(mode: int, a: torch.Tensor, b: torch.Tensor, t, out_dtype=torch.float32,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """mode NOISE: cos t a + sin t b; mode FIELD: (cos t a - b)/sin t, per sample (leading dim)."""
+    lib = load()
+    assert a.is_contiguous() and b.is_contiguous() and a.shape == b.shape
+    B = a.shape[0]
+    n = a.numel() // B
+    if out is None:
+        out = torch.empty(a.shape, dtype=out_dtype, device=a.device)
+    th = _t_host(t)
+    _check(lib.t2va_trigflow_field(mode, B, n, _dt(a), _dt(b), _dt(out), th, _ptr(a), _ptr(b),
+                                   _ptr(out), _stream(a.device)))
+    return out
+
+
+def attn_desc(q, k, vt, has_tangent: bool, out_dtype: int, scale: float = 0.0) -> AttnDesc:
+    """Descriptor for q [B, Nq, H, dh], k [B, Nk, H, dh] and vt [B, H, dh, ldv] tensors."""
+    B, Nq, H, dh = q.shape
+    Nk = k.shape[1]
+    d = AttnDesc()
+    d.B, d.H, d.dh, d.Nq, d.Nk = B, H, dh, Nq, Nk
+    d.q_batch_stride, d.q_row_stride = q.stride(0), q.stride(1)
+    d.k_batch_stride, d.k_row_stride = k.stride(0), k.stride(1)
+    d.vt_batch_stride, d.vt_head_stride, d.vt_row_stride = vt.stride(0), vt.stride(1), vt.stride(2)
+    d.o_batch_stride, d.o_row_stride = Nq * H * dh, H * dh
+    d.has_tangent = 1 if has_tangent else 0
+    d.out_dtype = out_dtype
+    d.scale = scale
+    return d
+
+
+def joint_attn_fwd_jvp(q, k, vt, nk, qd=None, kd=None, vdt=None, out_dtype=torch.float32,
+                       want_lse=False, scale: float = 0.0, desc: AttnDesc | None = None, out=None):
+    """Attention forward (+ JVP when tangents are given).
+
+    q, qd: [B, Nq, H, dh] bf16 (any strides whose last two dims are dense);
+    k, kd: [B, Nk, H, dh]; vt, vdt: [B, H, dh, ldv] bf16 (V stored dh-major);
+    nk: int32 [B] on the device.  Returns (o, od, lse).
+    """
+    lib = load()
+    tan = qd is not None
+    B, Nq, H, dh = q.shape
+    odt = torch.bfloat16 if out_dtype == torch.bfloat16 else torch.float32
+    if desc is None:
+        desc = attn_desc(q, k, vt, tan, _dt(torch.empty(0, dtype=odt)), scale)
+    if out is None:
+        o = torch.empty((B, Nq, H, dh), dtype=odt, device=q.device)
+        od = torch.empty_like(o) if tan else None
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if want_lse else None
+    else:
+        o, od, lse = out
+    _check(lib.t2va_joint_attn_fwd_jvp(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(vt), _ptr(qd),
+                                       _ptr(kd), _ptr(vdt), _ptr(nk), _ptr(o), _ptr(od), _ptr(lse),
+                                       _stream(q.device)))
+    return o, od, lse
+
+
+def scm_desc(cfg, in_dtype: int, weight_dtype: int) -> ScmDesc:
+    d = ScmDesc()
+    d.B, d.Nv, d.Na, d.Nt = cfg.B, cfg.Nv, cfg.Na, cfg.Nt
+    d.Cv, d.Ca, d.d, d.H = cfg.Cv, cfg.Ca, cfg.d, cfg.H
+    d.in_dtype, d.weight_dtype = in_dtype, weight_dtype
+    d.beta, d.gamma, d.eps_scm, d.w_v, d.w_a = cfg.beta, cfg.gamma, cfg.eps_scm, cfg.w_v, cfg.w_a
+    return d
+
+
+def workspace_bytes(desc: ScmDesc) -> int:
+    n = load().t2va_scm_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        raise T2VAError(1, load().t2va_last_error().decode())
+    return n
+
+
+class ScmTarget:
+    """Holds device buffers for repeated calls of t2va_scm_target on one shape."""
+
+    def __init__(self, cfg, device="cuda", in_dtype=DTYPE_BF16, weight_dtype=DTYPE_BF16,
+                 want_J=True, want_r=True):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.desc = scm_desc(cfg, in_dtype, weight_dtype)
+        self.ws_bytes = workspace_bytes(self.desc)
+        self.workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.workspace.data_ptr()
+        self.ws_ptr = ctypes.c_void_p((base + 255) // 256 * 256)
+        B = cfg.B
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.out = {
+            "J_v": torch.empty((B, cfg.Nv, cfg.Cv), **f32) if want_J else None,
+            "J_a": torch.empty((B, cfg.Na, cfg.Ca), **f32) if want_J else None,
+            "gbar_v": torch.empty((B, cfg.Nv, cfg.Cv), **f32),
+            "gbar_a": torch.empty((B, cfg.Na, cfg.Ca), **f32),
+            "r_v": torch.empty((B, cfg.Nv, cfg.Cv), **f32) if want_r else None,
+            "r_a": torch.empty((B, cfg.Na, cfg.Ca), **f32) if want_r else None,
+            "norms": torch.empty((B, 2), **f32),
+            "loss": torch.empty((B,), **f32),
+        }
+
+    @staticmethod
+    def weights_struct(w: dict) -> BlockWeights:
+        s = BlockWeights()
+        for n in WEIGHT_NAMES:
+            setattr(s, n, w[n].data_ptr())
+        return s
+
+    def __call__(self, teacher: dict, student: dict, z0_v, z0_a, eps_v, eps_a, text, text_mask, t):
+        lib = load()
+        tw, sw = self.weights_struct(teacher), self.weights_struct(student)
+        o = self.out
+        th = _t_host(t)
+        _check(lib.t2va_scm_target(
+            ctypes.byref(self.desc), ctypes.byref(tw), ctypes.byref(sw), _ptr(z0_v), _ptr(z0_a),
+            _ptr(eps_v), _ptr(eps_a), _ptr(text), _ptr(text_mask), th,
+            _ptr(o["J_v"]), _ptr(o["J_a"]), _ptr(o["gbar_v"]), _ptr(o["gbar_a"]), _ptr(o["r_v"]),
+            _ptr(o["r_a"]), _ptr(o["norms"]), _ptr(o["loss"]), self.ws_ptr, self.ws_bytes,
+            _stream(self.device)))
+        return o
+
+
+def profile_enable(max_calls: int):
+    _check(load().t2va_profile_enable(max_calls))
+
+
+def profile_read() -> tuple[dict, int]:
+    ms = (ctypes.c_double * NUM_PHASES)()
+    n = ctypes.c_int(0)
+    _check(load().t2va_profile_read(ms, ctypes.byref(n)))
+    return {PHASES[i]: ms[i] for i in range(NUM_PHASES)}, n.value
+
+
+def to_device_problem(problem: dict, device="cuda"):
+    """Seeded numpy problem -> device tensors in the dtypes the library consumes."""
+    cfg, data = problem["cfg"], problem["data"]
+    tdt = torch.bfloat16 if cfg.in_dtype == "bf16" else torch.float32
+
+    def dev(x, dt):
+        return torch.from_numpy(x.astype("float32")).to(device=device, dtype=dt).contiguous()
+
+    out = {k: dev(data[k], tdt) for k in ("z0_v", "z0_a", "eps_v", "eps_a", "text")}
+    out["text_mask"] = torch.from_numpy(data["text_mask"]).to(device)
+    out["t"] = [float(x) for x in data["t"]]
+    for which in ("teacher", "student"):
+        out[which] = {k: dev(v, tdt) for k, v in problem[which].items()}
+    return out

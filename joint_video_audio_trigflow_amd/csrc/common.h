@@ -1,0 +1,154 @@
+// Shared device helpers and the internal launch interface of libt2va.
+// gfx950 (CDNA4) only: 64-lane wavefronts, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace t2va {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxBatch = 64;
+constexpr int kWave = 64;
+
+// fp32 <-> bf16.  The fp32 -> bf16 conversion compiles to gfx950's
+// v_cvt_pk_bf16_f32 (round to nearest even).
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+
+template <typename T> struct Store;
+template <> struct Store<float> {
+  __device__ __forceinline__ static float cvt(float x) { return x; }
+};
+template <> struct Store<bf16> {
+  __device__ __forceinline__ static bf16 cvt(float x) { return (bf16)x; }
+};
+
+// 8 consecutive elements <-> 8 floats.
+__device__ __forceinline__ void load8(const bf16 *p, float *f) {
+  uint4 u = *reinterpret_cast<const uint4 *>(p);
+  const bf16x8 v = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
+}
+__device__ __forceinline__ void load8(const float *p, float *f) {
+  const float4 a = reinterpret_cast<const float4 *>(p)[0];
+  const float4 b = reinterpret_cast<const float4 *>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16 *p, const float *f) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (bf16)f[i];
+  *reinterpret_cast<uint4 *>(p) = __builtin_bit_cast(uint4, v);
+}
+__device__ __forceinline__ void store8(float *p, const float *f) {
+  reinterpret_cast<float4 *>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+  reinterpret_cast<float4 *>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+// Per-sample coefficients, rounded once from fp64 on the host; travels as a
+// kernel argument so no host-to-device copy is needed.
+struct Coef {
+  float cos_t, sin_t, inv_sin, ct_st, cos2, boost, gamma_ct_st, t;
+};
+struct CoefTable {
+  int B;
+  Coef c[kMaxBatch];
+};
+
+// ---------------------------------------------------------------------------
+// Internal launchers (implemented in the .hip files).
+// ---------------------------------------------------------------------------
+
+// Elementwise TrigFlow maps.  op: 0 noise (a=z0,b=eps), 1 field (a=z_t,b=x0),
+// 2 field from noise inputs (a=z0, b=eps, x=x0 fp32): (cos(c a + s b) - x)/s.
+hipError_t launch_trigflow(int op, const CoefTable &coef, int64_t n, int a_dt, int b_dt, int out_dt,
+                           const void *a, const void *b, const float *x, void *out,
+                           int64_t a_bs, int64_t b_bs, int64_t x_bs, int64_t out_bs,
+                           hipStream_t s);
+
+// Sinusoidal time embedding e(t_b) (rows 0..B-1) and de/dt (rows B..2B-1), fp32 [2B, d].
+hipError_t launch_time_embedding(const CoefTable &coef, int d, float *E, hipStream_t s);
+
+// tau[r] = W_t e_r for r in [0, rows): fp32 [rows, d] from bf16 W_t [d, d].
+hipError_t launch_time_linear(const float *E, int rows, int d, const bf16 *w_t, float *tau,
+                              hipStream_t s);
+
+// Text rows of X: for each sample, the valid text positions (mask != 0) in
+// order, converted to bf16, at rows [Nq, Nq + count); rows up to Nq + Nt are
+// zero.  With zero_only, every text row is zero (tangent of the text).
+// nk[b] = Nq + count (written when nk != nullptr).
+hipError_t launch_text_rows(int B, int Nq, int Nt, int d, const void *text, int text_dt,
+                            const uint8_t *mask, bf16 *X, int64_t x_batch_stride, int zero_only,
+                            int32_t *nk, hipStream_t s);
+
+// nk[b] = value for every sample (used when there is no text).
+hipError_t launch_fill_nk(int32_t *nk, int B, int value, hipStream_t s);
+
+// Blocks the per-sample elementwise kernels use for n elements.
+int elementwise_blocks(int64_t n);
+
+// fp32 -> bf16 copy.
+hipError_t launch_cast_bf16(const float *src, bf16 *dst, int64_t n, hipStream_t s);
+
+// g, J and per-block partial sums of g^2 for both modalities.
+struct GParams {
+  const void *z0[2], *eps[2];
+  const float *x0T[2], *x0S[2], *Gd[2];
+  int64_t x_bs[2];   // batch stride (elements) of x0T/x0S/Gd
+  float *J[2];       // nullable
+  float *g[2];       // g (later normalised in place)
+  float *partial[2]; // [B, nblk[m]]
+  int64_t n[2];      // elements per sample per modality
+  int nblk[2];
+  int in_dt;
+};
+hipError_t launch_scm_direction(const CoefTable &coef, const GParams &p, hipStream_t s);
+
+// gbar = g/(n + eps) in place, r = -gbar, norms, loss.
+struct NormParams {
+  float *g[2];
+  float *r[2];        // nullable
+  const float *partial[2];
+  int64_t n[2];
+  int nblk[2];
+  float *norms;       // nullable [B, 2]
+  float *loss;        // [B]
+  double eps, w[2];
+};
+hipError_t launch_normalise(int B, const NormParams &p, hipStream_t s);
+
+// C = A W^T (+ bias) for `batch` independent problems.
+struct GemmParams {
+  const bf16 *A; int64_t lda, a_bs;
+  const bf16 *W; int64_t ldw;             // W [N, K], shared by all batches
+  void *C; int64_t ldc, c_bs; int c_dt;   // columns [0, n_split) go to C
+  const float *bias; int64_t bias_bs;     // nullable, fp32 [batch][N]
+  bf16 *VT; int64_t vt_bs, vt_hs, vt_rs;  // columns >= n_split: V^T[b][h][c][row]
+  int n_split, dh;
+  int M, N, K, batch;
+};
+hipError_t launch_gemm(const GemmParams &p, hipStream_t s);
+
+// Attention forward (+JVP).
+struct AttnParams {
+  const bf16 *q, *k, *vt, *qd, *kd, *vdt;
+  const int32_t *nk;
+  void *o, *od;
+  float *lse;
+  int64_t q_bs, q_rs, k_bs, k_rs, vt_bs, vt_hs, vt_rs, o_bs, o_rs;
+  int B, H, Nq, Nk;
+  int out_dt;
+  float scale;
+};
+hipError_t launch_attention(int dh, bool tangent, const AttnParams &p, hipStream_t s);
+
+}  // namespace t2va

@@ -1,0 +1,495 @@
+// Host side of libt2va: argument validation, workspace layout, the launch
+// sequence of the joint sCM target, and phase timing.
+//
+// Method: TurboT2VA deep read (robotworld.top, arXiv 2608.24674), sections 3
+// and 3.1; the block G and its JVP as described in t2va.h.
+#include "../../include/t2va.h"
+#include "common.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+using namespace t2va;
+
+namespace {
+
+thread_local std::string g_err;
+
+t2va_status fail(t2va_status code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+t2va_status hip_fail(hipError_t e, const char *what) {
+  return fail(T2VA_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                     \
+  do {                                          \
+    hipError_t _e = (expr);                     \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool valid_dtype(int dt) { return dt == T2VA_DTYPE_BF16 || dt == T2VA_DTYPE_FP32; }
+
+int dt_size(int dt) { return dt == T2VA_DTYPE_BF16 ? 2 : 4; }
+
+t2va_status check_t(int B, const double *t_host) {
+  if (!t_host) return fail(T2VA_INVALID_ARG, "t_host is NULL");
+  for (int b = 0; b < B; ++b) {
+    const double t = t_host[b];
+    if (!(t > 0.0 && t < M_PI / 2) || !isfinite(t))
+      return fail(T2VA_INVALID_ARG, "t[%d] = %g is outside the open interval (0, pi/2)", b, t);
+  }
+  return T2VA_OK;
+}
+
+// Coefficients of the sCM target in fp64, rounded once to fp32.
+CoefTable make_coef(int B, const double *t_host, double beta, double gamma) {
+  CoefTable c;
+  memset(&c, 0, sizeof(c));
+  c.B = B;
+  for (int b = 0; b < B; ++b) {
+    const double t = t_host[b];
+    const double ct = cos(t), st = sin(t);
+    // beta cos t / sqrt(1 - gamma^2 sin^2 t), with the root written as
+    // sqrt(cos^2 t + (1 - gamma^2) sin^2 t) to avoid cancellation near pi/2.
+    const double root = sqrt(ct * ct + (1.0 - gamma * gamma) * st * st);
+    c.c[b].cos_t = (float)ct;
+    c.c[b].sin_t = (float)st;
+    c.c[b].inv_sin = (float)(1.0 / st);
+    c.c[b].ct_st = (float)(ct * st);
+    c.c[b].cos2 = (float)(ct * ct);
+    c.c[b].boost = (float)(beta * ct / root);
+    c.c[b].gamma_ct_st = (float)(gamma * ct * st);
+    c.c[b].t = (float)t;
+  }
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout of t2va_scm_target.
+// ---------------------------------------------------------------------------
+struct Layout {
+  int Nq, N_all, dh, ldv, nblk_v, nblk_a;
+  size_t wts, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v, x0S_a, part_v, part_a;
+  size_t total;
+  size_t w_elems[6];  // per-block weight element counts
+};
+
+Layout make_layout(const t2va_scm_desc &d) {
+  Layout L;
+  L.Nq = d.Nv + d.Na;
+  L.N_all = L.Nq + d.Nt;
+  L.dh = d.d / d.H;
+  L.ldv = (int)align_up((size_t)L.N_all, 64);
+  L.nblk_v = elementwise_blocks((int64_t)d.Nv * d.Cv);
+  L.nblk_a = elementwise_blocks((int64_t)d.Na * d.Ca);
+  const size_t B = d.B, D = d.d;
+  L.w_elems[0] = D * d.Cv;
+  L.w_elems[1] = D * d.Ca;
+  L.w_elems[2] = D * D;
+  L.w_elems[3] = 3 * D * D;
+  L.w_elems[4] = (size_t)d.Cv * D;
+  L.w_elems[5] = (size_t)d.Ca * D;
+  size_t wcount = 0;
+  for (int i = 0; i < 6; ++i) wcount += align_up(L.w_elems[i], 128);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
+  L.zv = take(2 * B * d.Nv * d.Cv * sizeof(bf16));
+  L.za = take(2 * B * d.Na * d.Ca * sizeof(bf16));
+  L.E = take(2 * B * D * sizeof(float));
+  L.tau = take(2 * B * D * sizeof(float));
+  L.X = take(2 * B * L.N_all * D * sizeof(bf16));
+  L.QK = take(2 * B * L.N_all * 2 * D * sizeof(bf16));
+  L.VT = take(2 * B * D * (size_t)L.ldv * sizeof(bf16));
+  L.nk = take(B * sizeof(int32_t));
+  L.O = take(2 * B * L.Nq * D * sizeof(bf16));
+  L.x0T_v = take(B * d.Nv * d.Cv * sizeof(float));
+  L.x0T_a = take(B * d.Na * d.Ca * sizeof(float));
+  L.x0S_v = take(2 * B * d.Nv * d.Cv * sizeof(float));
+  L.x0S_a = take(2 * B * d.Na * d.Ca * sizeof(float));
+  L.part_v = take(B * L.nblk_v * sizeof(float));
+  L.part_a = take(B * L.nblk_a * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+t2va_status check_desc(const t2va_scm_desc *d) {
+  if (!d) return fail(T2VA_INVALID_ARG, "desc is NULL");
+  if (d->B < 1 || d->B > T2VA_MAX_BATCH)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "B = %d outside [1, %d]", d->B, T2VA_MAX_BATCH);
+  if (d->Nv < 1 || d->Na < 1 || d->Nt < 0)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "need Nv >= 1, Na >= 1, Nt >= 0 (got %d, %d, %d)", d->Nv,
+                d->Na, d->Nt);
+  if (d->Cv < 64 || d->Cv % 64 || d->Ca < 64 || d->Ca % 64)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "Cv = %d and Ca = %d must be positive multiples of 64",
+                d->Cv, d->Ca);
+  if (d->H < 1 || d->d < 1 || d->d % d->H)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "d = %d is not a multiple of H = %d", d->d, d->H);
+  const int dh = d->d / d->H;
+  if (dh != 64 && dh != 128)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "head dim d/H = %d must be 64 or 128", dh);
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->weight_dtype))
+    return fail(T2VA_INVALID_ARG, "in_dtype / weight_dtype must be T2VA_DTYPE_BF16 or _FP32");
+  if (!(d->gamma >= 0.0 && d->gamma <= 1.0))
+    return fail(T2VA_INVALID_ARG, "gamma = %g outside [0, 1]", d->gamma);
+  if (!(d->eps_scm > 0.0) || !isfinite(d->eps_scm))
+    return fail(T2VA_INVALID_ARG, "eps_scm = %g must be positive and finite", d->eps_scm);
+  if (!isfinite(d->beta) || !isfinite(d->w_v) || !isfinite(d->w_a))
+    return fail(T2VA_INVALID_ARG, "beta, w_v and w_a must be finite");
+  return T2VA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Phase timing.
+// ---------------------------------------------------------------------------
+struct Profiler {
+  int max_calls = 0, calls = 0;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  struct Rec { int phase; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+  bool active() const { return max_calls > 0 && calls < max_calls; }
+  hipEvent_t next() { return used < pool.size() ? pool[used++] : nullptr; }
+};
+Profiler g_prof;
+
+struct PhaseScope {
+  hipStream_t s;
+  int phase;
+  hipEvent_t a = nullptr, b = nullptr;
+  bool on;
+  PhaseScope(hipStream_t s_, int ph, bool on_) : s(s_), phase(ph), on(on_) {
+    if (on) {
+      a = g_prof.next();
+      b = g_prof.next();
+      if (a && b) hipEventRecord(a, s);
+    }
+  }
+  ~PhaseScope() {
+    if (on && a && b) {
+      hipEventRecord(b, s);
+      g_prof.recs.push_back({phase, a, b});
+    }
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int t2va_abi_version(void) { return T2VA_ABI_VERSION; }
+
+const char *t2va_last_error(void) { return g_err.c_str(); }
+
+t2va_status t2va_trigflow_field(int mode, int B, int64_t n_per_sample, int a_dtype, int b_dtype,
+                                int out_dtype, const double *t_host, const void *a, const void *b,
+                                void *out, t2va_stream stream) {
+  g_err.clear();
+  if (mode != T2VA_NOISE && mode != T2VA_FIELD) return fail(T2VA_INVALID_ARG, "bad mode %d", mode);
+  if (B < 1 || B > T2VA_MAX_BATCH)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "B = %d outside [1, %d]", B, T2VA_MAX_BATCH);
+  if (n_per_sample < 0) return fail(T2VA_INVALID_ARG, "n_per_sample < 0");
+  if (!valid_dtype(a_dtype) || !valid_dtype(b_dtype) || !valid_dtype(out_dtype))
+    return fail(T2VA_INVALID_ARG, "dtypes must be T2VA_DTYPE_BF16 or T2VA_DTYPE_FP32");
+  if (t2va_status st = check_t(B, t_host)) return st;
+  if (n_per_sample == 0) return T2VA_OK;
+  if (!a || !b || !out) return fail(T2VA_INVALID_ARG, "a, b and out must be non-NULL");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+    return fail(T2VA_INVALID_ARG, "a, b and out must be 16-byte aligned");
+  const CoefTable coef = make_coef(B, t_host, 0.0, 0.0);
+  HIP_TRY(launch_trigflow(mode, coef, n_per_sample, a_dtype, b_dtype, out_dtype, a, b, nullptr,
+                          out, n_per_sample, n_per_sample, 0, n_per_sample, (hipStream_t)stream),
+          "trigflow kernel launch");
+  return T2VA_OK;
+}
+
+t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, const void *k,
+                                    const void *vt, const void *qd, const void *kd,
+                                    const void *vdt, const int32_t *nk_valid, void *o, void *od,
+                                    float *lse, t2va_stream stream) {
+  g_err.clear();
+  if (!desc) return fail(T2VA_INVALID_ARG, "desc is NULL");
+  const t2va_attn_desc &d = *desc;
+  if (d.dh != 64 && d.dh != 128) return fail(T2VA_UNSUPPORTED_SHAPE, "dh = %d must be 64 or 128", d.dh);
+  if (d.B < 1 || d.H < 1 || d.Nq < 1 || d.Nk < 1)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "B, H, Nq and Nk must be >= 1");
+  if (!q || !k || !vt || !nk_valid || !o) return fail(T2VA_INVALID_ARG, "q, k, vt, nk_valid and o are required");
+  const bool tan = d.has_tangent != 0;
+  if (tan && (!qd || !kd || !vdt || !od))
+    return fail(T2VA_INVALID_ARG, "has_tangent needs qd, kd, vdt and od");
+  if (!tan && (qd || kd || vdt || od))
+    return fail(T2VA_INVALID_ARG, "tangent pointers given with has_tangent = 0");
+  if (!valid_dtype(d.out_dtype)) return fail(T2VA_INVALID_ARG, "bad out_dtype");
+  const void *ptrs[] = {q, k, vt, qd, kd, vdt, nk_valid, o, od};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(T2VA_INVALID_ARG, "operands must be 16-byte aligned");
+  const int64_t strides[] = {d.q_batch_stride, d.q_row_stride, d.k_batch_stride, d.k_row_stride,
+                             d.vt_batch_stride, d.vt_head_stride, d.vt_row_stride,
+                             d.o_batch_stride, d.o_row_stride};
+  for (int64_t s : strides)
+    if (s < 0 || s % 8) return fail(T2VA_INVALID_ARG, "strides must be non-negative multiples of 8");
+  if (d.vt_row_stride < ((d.Nk + 7) / 8) * 8)
+    return fail(T2VA_INVALID_ARG, "vt_row_stride %lld < round_up(Nk, 8)", (long long)d.vt_row_stride);
+  if (d.q_row_stride < (int64_t)d.H * d.dh || d.k_row_stride < (int64_t)d.H * d.dh ||
+      d.o_row_stride < (int64_t)d.H * d.dh)
+    return fail(T2VA_INVALID_ARG, "row strides must cover H*dh elements");
+  AttnParams p;
+  p.q = (const bf16 *)q; p.k = (const bf16 *)k; p.vt = (const bf16 *)vt;
+  p.qd = (const bf16 *)qd; p.kd = (const bf16 *)kd; p.vdt = (const bf16 *)vdt;
+  p.nk = nk_valid; p.o = o; p.od = od; p.lse = lse;
+  p.q_bs = d.q_batch_stride; p.q_rs = d.q_row_stride;
+  p.k_bs = d.k_batch_stride; p.k_rs = d.k_row_stride;
+  p.vt_bs = d.vt_batch_stride; p.vt_hs = d.vt_head_stride; p.vt_rs = d.vt_row_stride;
+  p.o_bs = d.o_batch_stride; p.o_rs = d.o_row_stride;
+  p.B = d.B; p.H = d.H; p.Nq = d.Nq; p.Nk = d.Nk;
+  p.out_dt = d.out_dtype;
+  p.scale = d.scale != 0.f ? d.scale : (float)(1.0 / sqrt((double)d.dh));
+  HIP_TRY(launch_attention(d.dh, tan, p, (hipStream_t)stream), "attention kernel launch");
+  return T2VA_OK;
+}
+
+size_t t2va_scm_workspace_bytes(const t2va_scm_desc *desc) {
+  g_err.clear();
+  if (check_desc(desc) != T2VA_OK) return 0;
+  return make_layout(*desc).total;
+}
+
+t2va_status t2va_profile_enable(int max_calls) {
+  g_err.clear();
+  if (max_calls < 0) return fail(T2VA_INVALID_ARG, "max_calls < 0");
+  for (hipEvent_t e : g_prof.pool) hipEventDestroy(e);
+  g_prof = Profiler();
+  if (max_calls == 0) return T2VA_OK;
+  const size_t n = (size_t)max_calls * 32;
+  g_prof.pool.resize(n, nullptr);
+  for (size_t i = 0; i < n; ++i) HIP_TRY(hipEventCreate(&g_prof.pool[i]), "hipEventCreate");
+  g_prof.max_calls = max_calls;
+  return T2VA_OK;
+}
+
+t2va_status t2va_profile_read(double *ms_out, int *n_calls) {
+  g_err.clear();
+  if (!ms_out || !n_calls) return fail(T2VA_INVALID_ARG, "NULL output");
+  for (int i = 0; i < T2VA_NUM_PHASES; ++i) ms_out[i] = 0.0;
+  double other = 0.0;
+  for (const auto &r : g_prof.recs) {
+    HIP_TRY(hipEventSynchronize(r.b), "hipEventSynchronize");
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b), "hipEventElapsedTime");
+    ms_out[r.phase] += ms;
+    (void)other;
+  }
+  double parts = ms_out[T2VA_PHASE_TEACHER_ATTN] + ms_out[T2VA_PHASE_STUDENT_ATTN] + ms_out[T2VA_PHASE_GEMM];
+  ms_out[T2VA_PHASE_OTHER] = ms_out[T2VA_PHASE_TOTAL] - parts;
+  *n_calls = g_prof.calls;
+  g_prof.recs.clear();
+  g_prof.used = 0;
+  g_prof.calls = 0;
+  return T2VA_OK;
+}
+
+t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights *teacher,
+                            const t2va_block_weights *student, const void *z0_v, const void *z0_a,
+                            const void *eps_v, const void *eps_a, const void *text,
+                            const uint8_t *text_mask, const double *t_host, float *J_v, float *J_a,
+                            float *gbar_v, float *gbar_a, float *r_v, float *r_a, float *norms,
+                            float *loss, void *workspace, size_t workspace_bytes,
+                            t2va_stream stream) {
+  g_err.clear();
+  // ---------------- validation (before any HIP call) ----------------
+  if (t2va_status st = check_desc(desc)) return st;
+  const t2va_scm_desc &d = *desc;
+  if (t2va_status st = check_t(d.B, t_host)) return st;
+  if (!teacher || !student) return fail(T2VA_INVALID_ARG, "weights are NULL");
+  const t2va_block_weights *wb[2] = {teacher, student};
+  for (int i = 0; i < 2; ++i) {
+    const void *w[6] = {wb[i]->w_in_v, wb[i]->w_in_a, wb[i]->w_t, wb[i]->w_qkv, wb[i]->w_out_v, wb[i]->w_out_a};
+    for (const void *p : w) {
+      if (!p) return fail(T2VA_INVALID_ARG, "%s weight pointer is NULL", i ? "student" : "teacher");
+      if (!aligned16(p)) return fail(T2VA_INVALID_ARG, "weights must be 16-byte aligned");
+    }
+  }
+  const void *req[] = {z0_v, z0_a, eps_v, eps_a, gbar_v, gbar_a, loss};
+  for (const void *p : req)
+    if (!p) return fail(T2VA_INVALID_ARG, "z0, eps, gbar and loss pointers are required");
+  if (d.Nt > 0 && (!text || !text_mask))
+    return fail(T2VA_INVALID_ARG, "text and text_mask are required when Nt > 0");
+  const void *al[] = {z0_v, z0_a, eps_v, eps_a, text, J_v, J_a, gbar_v, gbar_a, r_v, r_a};
+  for (const void *p : al)
+    if (p && !aligned16(p)) return fail(T2VA_INVALID_ARG, "tensor operands must be 16-byte aligned");
+  const Layout L = make_layout(d);
+  if (!workspace) return fail(T2VA_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(T2VA_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(T2VA_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+
+  // ---------------- launch sequence ----------------
+  hipStream_t s = (hipStream_t)stream;
+  const bool prof = g_prof.active();
+  if (prof) g_prof.calls++;
+  PhaseScope total(s, T2VA_PHASE_TOTAL, prof);
+
+  char *ws = (char *)workspace;
+  const int B = d.B, D = d.d, H = d.H, dh = L.dh, Nq = L.Nq, NA = L.N_all;
+  const int64_t nv = (int64_t)d.Nv * d.Cv, na = (int64_t)d.Na * d.Ca;
+  const CoefTable coef = make_coef(B, t_host, d.beta, d.gamma);
+
+  // Weights as bf16.
+  const bf16 *W[2][6];
+  {
+    bf16 *wdst = (bf16 *)(ws + L.wts);
+    for (int i = 0; i < 2; ++i) {
+      const void *src[6] = {wb[i]->w_in_v, wb[i]->w_in_a, wb[i]->w_t, wb[i]->w_qkv, wb[i]->w_out_v, wb[i]->w_out_a};
+      for (int j = 0; j < 6; ++j) {
+        if (d.weight_dtype == T2VA_DTYPE_FP32) {
+          HIP_TRY(launch_cast_bf16((const float *)src[j], wdst, (int64_t)L.w_elems[j], s), "cast");
+          W[i][j] = wdst;
+          wdst += align_up(L.w_elems[j], 128);
+        } else {
+          W[i][j] = (const bf16 *)src[j];
+        }
+      }
+    }
+  }
+
+  bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
+  float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
+  bf16 *X = (bf16 *)(ws + L.X), *QK = (bf16 *)(ws + L.QK), *VT = (bf16 *)(ws + L.VT);
+  bf16 *O = (bf16 *)(ws + L.O);
+  int32_t *nk = (int32_t *)(ws + L.nk);
+  float *x0T_v = (float *)(ws + L.x0T_v), *x0T_a = (float *)(ws + L.x0T_a);
+  float *x0S_v = (float *)(ws + L.x0S_v), *x0S_a = (float *)(ws + L.x0S_a);
+  float *part_v = (float *)(ws + L.part_v), *part_a = (float *)(ws + L.part_a);
+
+  const int64_t x_bs = (int64_t)NA * D;       // X rows per sample
+  const int64_t qk_bs = (int64_t)NA * 2 * D;  // fused Q|K rows per sample
+  const int64_t vt_hs = (int64_t)dh * L.ldv, vt_bs = (int64_t)H * vt_hs;
+  const int64_t o_bs = (int64_t)Nq * D;
+
+  // z_t = cos t z0 + sin t eps (bf16 GEMM input), half 0 of zv / za.
+  {
+    PhaseScope ps(s, T2VA_PHASE_OTHER, false);
+    HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v,
+                            nullptr, zv, nv, nv, 0, nv, s), "noise");
+    HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a,
+                            nullptr, za, na, na, 0, na, s), "noise");
+    HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
+    HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
+    if (d.Nt > 0)
+      HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, x_bs, 0, nk, s), "text rows");
+    else
+      HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
+  }
+
+  auto gemm = [&](const bf16 *A, int64_t lda, int64_t a_bs, const bf16 *Wt, int64_t ldw, void *Cp,
+                  int64_t ldc, int64_t c_bs, int c_dt, const float *bias, int64_t bias_bs, int M,
+                  int N, int K, int batch, bf16 *vt, int n_split) -> t2va_status {
+    GemmParams g;
+    g.A = A; g.lda = lda; g.a_bs = a_bs;
+    g.W = Wt; g.ldw = ldw;
+    g.C = Cp; g.ldc = ldc; g.c_bs = c_bs; g.c_dt = c_dt;
+    g.bias = bias; g.bias_bs = bias_bs;
+    g.VT = vt; g.vt_bs = vt_bs; g.vt_hs = vt_hs; g.vt_rs = L.ldv;
+    g.n_split = n_split; g.dh = dh;
+    g.M = M; g.N = N; g.K = K; g.batch = batch;
+    PhaseScope ps(s, T2VA_PHASE_GEMM, prof);
+    HIP_TRY(launch_gemm(g, s), "gemm");
+    return T2VA_OK;
+  };
+  auto attention = [&](bool tan, int phase) -> t2va_status {
+    AttnParams p;
+    p.q = QK; p.k = QK + D; p.vt = VT;
+    p.qd = tan ? QK + (int64_t)B * qk_bs : nullptr;
+    p.kd = tan ? QK + (int64_t)B * qk_bs + D : nullptr;
+    p.vdt = tan ? VT + (int64_t)B * vt_bs : nullptr;
+    p.nk = nk; p.o = O; p.od = tan ? O + (int64_t)B * o_bs : nullptr; p.lse = nullptr;
+    p.q_bs = qk_bs; p.q_rs = 2 * D; p.k_bs = qk_bs; p.k_rs = 2 * D;
+    p.vt_bs = vt_bs; p.vt_hs = vt_hs; p.vt_rs = L.ldv;
+    p.o_bs = o_bs; p.o_rs = D;
+    p.B = B; p.H = H; p.Nq = Nq; p.Nk = NA;
+    p.out_dt = T2VA_DTYPE_BF16;
+    p.scale = (float)(1.0 / sqrt((double)dh));
+    PhaseScope ps(s, phase, prof);
+    HIP_TRY(launch_attention(dh, tan, p, s), "attention");
+    return T2VA_OK;
+  };
+#define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
+
+  // ---------------- teacher: x0_T = G_T(z_t, t, c) ----------------
+  T2VA_CALL(gemm(zv, d.Cv, nv, W[0][0], d.Cv, X, D, x_bs, 0, tau, D, d.Nv, D, d.Cv, B, nullptr, D));
+  T2VA_CALL(gemm(za, d.Ca, na, W[0][1], d.Ca, X + (int64_t)d.Nv * D, D, x_bs, 0, tau, D, d.Na, D,
+                 d.Ca, B, nullptr, D));
+  T2VA_CALL(gemm(X, D, x_bs, W[0][3], D, QK, 2 * D, qk_bs, 0, nullptr, 0, NA, 3 * D, D, B, VT, 2 * D));
+  T2VA_CALL(attention(false, T2VA_PHASE_TEACHER_ATTN));
+  T2VA_CALL(gemm(O, D, o_bs, W[0][4], D, x0T_v, d.Cv, nv, 1, nullptr, 0, d.Nv, d.Cv, D, B, nullptr, d.Cv));
+  T2VA_CALL(gemm(O + (int64_t)d.Nv * D, D, o_bs, W[0][5], D, x0T_a, d.Ca, na, 1, nullptr, 0, d.Na,
+                 d.Ca, D, B, nullptr, d.Ca));
+
+  // ---------------- F_T (tangent of the student's latent inputs) ----------------
+  HIP_TRY(launch_trigflow(2, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v, x0T_v,
+                          zv + (int64_t)B * nv, nv, nv, nv, nv, s), "teacher field");
+  HIP_TRY(launch_trigflow(2, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a, x0T_a,
+                          za + (int64_t)B * na, na, na, na, na, s), "teacher field");
+
+  // ---------------- student: G_S and its JVP ----------------
+  HIP_TRY(launch_time_linear(E, 2 * B, D, W[1][2], tau, s), "student time linear");
+  if (d.Nt > 0)
+    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X + (int64_t)B * x_bs, x_bs,
+                             1, nullptr, s), "tangent text rows");
+  T2VA_CALL(gemm(zv, d.Cv, nv, W[1][0], d.Cv, X, D, x_bs, 0, tau, D, d.Nv, D, d.Cv, 2 * B, nullptr, D));
+  T2VA_CALL(gemm(za, d.Ca, na, W[1][1], d.Ca, X + (int64_t)d.Nv * D, D, x_bs, 0, tau, D, d.Na, D,
+                 d.Ca, 2 * B, nullptr, D));
+  T2VA_CALL(gemm(X, D, x_bs, W[1][3], D, QK, 2 * D, qk_bs, 0, nullptr, 0, NA, 3 * D, D, 2 * B, VT, 2 * D));
+  T2VA_CALL(attention(true, T2VA_PHASE_STUDENT_ATTN));
+  T2VA_CALL(gemm(O, D, o_bs, W[1][4], D, x0S_v, d.Cv, nv, 1, nullptr, 0, d.Nv, d.Cv, D, 2 * B, nullptr, d.Cv));
+  T2VA_CALL(gemm(O + (int64_t)d.Nv * D, D, o_bs, W[1][5], D, x0S_a, d.Ca, na, 1, nullptr, 0, d.Na,
+                 d.Ca, D, 2 * B, nullptr, d.Ca));
+
+  // ---------------- g, norms, gbar, r, loss ----------------
+  GParams gp;
+  gp.z0[0] = z0_v; gp.z0[1] = z0_a; gp.eps[0] = eps_v; gp.eps[1] = eps_a;
+  gp.x0T[0] = x0T_v; gp.x0T[1] = x0T_a;
+  gp.x0S[0] = x0S_v; gp.x0S[1] = x0S_a;
+  gp.Gd[0] = x0S_v + (int64_t)B * nv; gp.Gd[1] = x0S_a + (int64_t)B * na;
+  gp.x_bs[0] = nv; gp.x_bs[1] = na;
+  gp.J[0] = J_v; gp.J[1] = J_a;
+  gp.g[0] = gbar_v; gp.g[1] = gbar_a;
+  gp.partial[0] = part_v; gp.partial[1] = part_a;
+  gp.n[0] = nv; gp.n[1] = na;
+  gp.nblk[0] = L.nblk_v; gp.nblk[1] = L.nblk_a;
+  gp.in_dt = d.in_dtype;
+  HIP_TRY(launch_scm_direction(coef, gp, s), "sCM direction");
+  NormParams np;
+  np.g[0] = gbar_v; np.g[1] = gbar_a; np.r[0] = r_v; np.r[1] = r_a;
+  np.partial[0] = part_v; np.partial[1] = part_a;
+  np.n[0] = nv; np.n[1] = na;
+  np.nblk[0] = L.nblk_v; np.nblk[1] = L.nblk_a;
+  np.norms = norms; np.loss = loss;
+  np.eps = d.eps_scm; np.w[0] = d.w_v; np.w[1] = d.w_a;
+  HIP_TRY(launch_normalise(B, np, s), "normalise");
+#undef T2VA_CALL
+  return T2VA_OK;
+}
+
+}  // extern "C"

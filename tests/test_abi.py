@@ -1,0 +1,141 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/t2va.h, and rejects bad arguments on the host before
+launching anything."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from joint_video_audio_trigflow_amd import _lib, inputs
+
+HEADER = _lib.HEADER_PATH
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(t2va_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libt2va.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"t2va_scm_target", "t2va_joint_attn_fwd_jvp", "t2va_trigflow_field",
+            "t2va_scm_workspace_bytes", "t2va_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.t2va_abi_version() == 1
+
+
+def test_struct_sizes_match_header(lib):
+    # the binding's structs mirror the header: field counts and natural packing
+    assert ctypes.sizeof(_lib.AttnDesc) == 5 * 4 + 4 + 9 * 8 + 3 * 4 + 4
+    assert ctypes.sizeof(_lib.ScmDesc) == 10 * 4 + 5 * 8
+    assert ctypes.sizeof(_lib.BlockWeights) == 6 * 8
+
+
+def err(lib):
+    return lib.t2va_last_error().decode()
+
+
+def test_workspace_bytes_validation(lib):
+    cfg = inputs.CONFIGS["high-res"]
+    d = _lib.scm_desc(cfg, _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    n = lib.t2va_scm_workspace_bytes(ctypes.byref(d))
+    assert n > 0 and n % 256 == 0
+    # the big buffers: X, fused QK, V^T and O for primal and tangent
+    assert n > 2 * cfg.N_all * cfg.d * 2 * 4
+    assert n < 8 * 2**30
+    bad = _lib.scm_desc(cfg.replace(H=5), _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) == 0
+    assert "multiple" in err(lib)
+    bad = _lib.scm_desc(cfg.replace(H=32), _lib.DTYPE_BF16, _lib.DTYPE_BF16)  # dh = 64 ok
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) > 0
+    bad = _lib.scm_desc(cfg.replace(H=64), _lib.DTYPE_BF16, _lib.DTYPE_BF16)  # dh = 32
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) == 0
+    bad = _lib.scm_desc(cfg.replace(B=65), _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) == 0
+    bad = _lib.scm_desc(cfg.replace(Cv=100), _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) == 0
+    bad = _lib.scm_desc(cfg.replace(gamma=1.5), _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) == 0
+    assert "gamma" in err(lib)
+
+
+def fake_ptr(i=1):
+    return ctypes.c_void_p(0x10000 * i)
+
+
+def test_scm_target_rejects_before_launch(lib):
+    cfg = inputs.CONFIGS["tiny"]
+    d = _lib.scm_desc(cfg, _lib.DTYPE_FP32, _lib.DTYPE_FP32)
+    w = _lib.BlockWeights(*[0x10000 * (i + 1) for i in range(6)])
+    t = (ctypes.c_double * 1)(0.5)
+    ptrs = [fake_ptr(i + 10) for i in range(6)]
+    outs = [fake_ptr(i + 20) for i in range(8)]
+    ws_bytes = lib.t2va_scm_workspace_bytes(ctypes.byref(d))
+
+    def call(t_arr=t, ws=fake_ptr(100), nbytes=ws_bytes, weights=w, o=outs):
+        return lib.t2va_scm_target(ctypes.byref(d), ctypes.byref(weights), ctypes.byref(w), *ptrs,
+                                   t_arr, *o, ws, nbytes, None)
+
+    assert call(t_arr=(ctypes.c_double * 1)(0.0)) == 1 and "t[0]" in err(lib)
+    assert call(t_arr=(ctypes.c_double * 1)(math.pi / 2)) == 1
+    assert call(t_arr=(ctypes.c_double * 1)(float("nan"))) == 1
+    assert call(nbytes=ws_bytes - 1) == 3 and "workspace" in err(lib)
+    assert call(ws=ctypes.c_void_p(0x10010)) == 1 and "aligned" in err(lib)
+    o2 = list(outs)
+    o2[7] = None  # loss is required
+    assert call(o=o2) == 1
+    w2 = _lib.BlockWeights(*([0] + [0x10000 * (i + 1) for i in range(5)]))
+    assert call(weights=w2) == 1 and "teacher" in err(lib)
+    w3 = _lib.BlockWeights(*[0x10008 * (i + 1) for i in range(6)])
+    assert call(weights=w3) == 1 and "aligned" in err(lib)
+
+
+def test_attention_rejects_before_launch(lib):
+    d = _lib.AttnDesc()
+    d.B, d.H, d.dh, d.Nq, d.Nk = 1, 2, 128, 10, 20
+    d.q_batch_stride = d.k_batch_stride = 20 * 256
+    d.q_row_stride = d.k_row_stride = d.o_row_stride = 256
+    d.o_batch_stride = 10 * 256
+    d.vt_row_stride, d.vt_head_stride, d.vt_batch_stride = 24, 24 * 128, 2 * 24 * 128
+    d.has_tangent, d.out_dtype = 0, 1
+    p = [fake_ptr(i + 1) for i in range(10)]
+
+    def call(desc=d, tangents=(None, None, None), od=None):
+        return lib.t2va_joint_attn_fwd_jvp(ctypes.byref(desc), p[0], p[1], p[2], *tangents, p[6], p[7],
+                                           od, None, None)
+
+    d.dh = 96
+    assert call() == 2
+    d.dh = 128
+    assert call(tangents=(p[3], p[4], p[5])) == 1          # tangents with has_tangent = 0
+    d.has_tangent = 1
+    assert call() == 1                                      # has_tangent without tangents
+    d.has_tangent = 0
+    d.vt_row_stride = 16                                    # < round_up(Nk, 8)
+    assert call() == 1 and "vt_row_stride" in err(lib)
+    d.vt_row_stride = 24
+    d.q_row_stride = 250                                    # not a multiple of 8
+    assert call() == 1
+
+
+def test_trigflow_rejects_before_launch(lib):
+    t = (ctypes.c_double * 2)(0.3, 2.0)
+    assert lib.t2va_trigflow_field(0, 2, 16, 0, 0, 1, t, fake_ptr(1), fake_ptr(2), fake_ptr(3), None) == 1
+    t = (ctypes.c_double * 2)(0.3, 0.4)
+    assert lib.t2va_trigflow_field(5, 2, 16, 0, 0, 1, t, fake_ptr(1), fake_ptr(2), fake_ptr(3), None) == 1
+    assert lib.t2va_trigflow_field(0, 0, 16, 0, 0, 1, t, fake_ptr(1), fake_ptr(2), fake_ptr(3), None) == 2
+    assert lib.t2va_trigflow_field(0, 2, 16, 0, 0, 1, t, ctypes.c_void_p(0x10004), fake_ptr(2),
+                                   fake_ptr(3), None) == 1
+    # zero elements: nothing to launch, success
+    assert lib.t2va_trigflow_field(0, 2, 0, 0, 0, 1, t, None, None, None, None) == 0
