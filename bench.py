@@ -101,6 +101,8 @@ def main() -> int:
     ap.add_argument("--config", default="high-res")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -111,6 +113,16 @@ def main() -> int:
     import numpy as np
     import torch
     from joint_video_audio_trigflow_amd import _lib, inputs
+
+    if args.copy_calibration:
+        n = args.copy_calibration * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": args.steps}), flush=True)
+        return 0
 
     _lib.load()
     cfg = inputs.CONFIGS[args.config]

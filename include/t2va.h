@@ -97,7 +97,9 @@ t2va_status t2va_trigflow_field(int mode, int B, int64_t n_per_sample, int a_dty
  *   k, kd   element (b, j, h, c) at  b*k_batch_stride + j*k_row_stride + h*dh + c
  *   vt, vdt V stored dh-major per head ("V transposed"):
  *           element (b, j, h, c) at  b*vt_batch_stride + h*vt_head_stride + c*vt_row_stride + j
- *           vt_row_stride must be a multiple of 8 and >= round_up(Nk, 8).
+ *           vt_row_stride must be a multiple of 8 and >= round_up(Nk, 64).  Keys
+ *           are read in blocks of 64: columns j in [nk_valid[b], round_up(nk_valid[b], 64))
+ *           must hold finite values (zeros, say); they get zero weight.
  *   o, od   element (b, i, h, c) at  b*o_batch_stride + i*o_row_stride + h*dh + c,
  *           dtype out_dtype.
  *   lse     fp32 [B, H, Nq] (nullable): natural-log log-sum-exp of the scaled
@@ -130,8 +132,9 @@ typedef struct {
  *   nk_valid  device int32 [B], each in [1, Nk].  Values outside that range
  *             are clamped to it by the kernel.
  * Errors: T2VA_INVALID_ARG (null/misaligned pointers, strides not multiples
- * of 8, tangent pointers inconsistent with has_tangent),
- * T2VA_UNSUPPORTED_SHAPE (dh not 64/128, B/H/Nq/Nk < 1).
+ * of 8, vt_row_stride too small, tangent pointers inconsistent with
+ * has_tangent), T2VA_UNSUPPORTED_SHAPE (dh not 64/128, B/H/Nq/Nk < 1, or the
+ * K or V^T extent of one (sample, head) at or above 2 GiB).
  */
 t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, const void *k,
                                     const void *vt, const void *qd, const void *kd,

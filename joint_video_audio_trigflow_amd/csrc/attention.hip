@@ -7,27 +7,29 @@
 //   s_j  = scale q_i.k_j            ds_j = scale (dq_i.k_j + q_i.dk_j)
 //   p_j  = softmax_j(s)             mu   = sum_j p_j ds_j
 //   o_i  = sum_j p_j v_j            do_i = sum_j p_j (ds_j - mu) v_j + p_j dv_j
-// streamed over key tiles with fp32 online-softmax state.  With running max
-// m, alpha = exp(m_old - m_new) rescales l = sum p, mu~ = sum p ds,
-// A = sum p v and dA = sum (p ds) v + p dv; at the end o = A/l,
+// streamed over key tiles with fp32 softmax state: with a reference max m,
+// l = sum 2^(s'-m), mu~ = sum 2^(s'-m) ds, A = sum 2^(s'-m) v and
+// dA = sum 2^(s'-m) (ds v + dv) (s' = s log2 e); at the end o = A/l,
 // do = dA/l - (mu~/l) o.  Keys j >= nk[b] (padded text, section 6.3 of the
 // deep read) get logit -inf.
 //
-// Layout of the work: one workgroup = 4 waves = 128 query rows of one
-// (sample, head); each wave owns 32 query rows.  Every product is computed
-// transposed so that one lane owns one query row throughout:
-//   S^T  = K Q^T           A operand: K rows from LDS, B operand: Q^T in registers
-//   dS^T = dK Q^T + K dQ^T
-//   O^T += V^T P^T         A operand: V^T rows from LDS, B operand: P^T in registers
-//   dO^T += V^T (P*dS)^T + dV^T P^T
-// With v_mfma_f32_32x32x16_bf16 a lane l holds output column l%32 and rows
-// 8*(v/4) + 4*(l/32) + v%4.  Reading the K rows in the permuted order
-// sigma(r) (bits 2 and 3 of r swapped) makes register v of lane l hold key
-// 8*(l/32) + v (v < 8) or 16 + 8*(l/32) + (v-8), which is exactly the B
-// operand layout the P^T V^T product needs: no shuffles between the two MFMAs.
-// The key-tile (K, dK, V^T, dV^T) is staged through LDS with padded rows
-// (conflict-free 16-byte reads); the next tile is fetched into registers while
-// the current one is consumed.
+// Work decomposition: a workgroup of 8 waves (two per SIMD) owns 128 query
+// rows of one (sample, head); a wave owns 16 rows.  Products are computed
+// transposed so that one lane column owns one query row throughout, using
+// v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8(l/16)..+7;
+// B: k = 8(l/16)..+7, column l%16; C: column l%16, rows 4(l/16)+r):
+//   S^T  = K Q^T, dS^T = dK Q^T + K dQ^T    (A: K rows from LDS, B: Q^T in registers)
+//   O^T += V^T P^T, dO^T += V^T (P dS)^T + dV^T P^T   (A: V^T rows from LDS, B: P^T)
+// For 32-key sub-tile half t the K rows are read in the order
+// 8(i/4) + 4t + i%4, which makes register r of half t of a lane with g = l/16
+// hold key 8g + 4t + r: the 8 values a lane owns are then exactly the
+// B-operand keys 8g..8g+7 of the P^T V^T product, with no lane exchange.
+//
+// Key tiles (K, dK, V^T, dV^T) go from global memory straight into LDS with
+// buffer_load_dwordx4 ... lds (no staging registers; SGPR descriptors and
+// 32-bit lane offsets), double-buffered in 64-key stages.  16-byte slots are
+// XOR-swizzled so that every 16-lane group of an operand read hits 16
+// different bank groups.
 #include "common.h"
 
 #include <math.h>
@@ -36,33 +38,53 @@ namespace t2va {
 
 namespace {
 
-constexpr int BM = 128;     // query rows per workgroup
-constexpr int BN = 64;      // keys per tile
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;             // two waves per SIMD
+constexpr int kThreads = kWaves * 64;
+constexpr int BM = 16 * kWaves;       // query rows per workgroup
+constexpr int BN = 64;                // keys per LDS stage
 
 template <int DH, bool TAN>
 struct AttnCfg {
-  static constexpr int KSTEPS = DH / 16;     // MFMA k-steps over the head dimension
-  static constexpr int DT = DH / 32;         // 32-wide tiles of the head dimension
-  static constexpr int KROW = DH + 8;        // LDS row (elements) of K / dK
-  static constexpr int VROW = BN + 8;        // LDS row (elements) of V^T / dV^T
-  static constexpr int K_ELEMS = BN * KROW;
-  static constexpr int V_ELEMS = DH * VROW;
+  static constexpr int KSTEPS = DH / 32;   // MFMA k-steps over the head dimension
+  static constexpr int DT = DH / 16;       // 16-row tiles of the head dimension
+  static constexpr int CPR = DH / 8;       // 16-byte chunks per K row
+  static constexpr int K_ELEMS = BN * DH;  // K tile [BN][DH], swizzled slots
+  static constexpr int V_ELEMS = DH * BN;  // V^T tile [DH][BN], swizzled slots
   static constexpr int NSTREAM = TAN ? 2 : 1;
-  static constexpr size_t LDS_BYTES = (size_t)NSTREAM * (K_ELEMS + V_ELEMS) * sizeof(bf16);
-  // 16-byte chunks per thread per operand tile
-  static constexpr int KCH = BN * DH / 8 / kThreads;
-  static constexpr int VCH = DH * BN / 8 / kThreads;
+  static constexpr int BUF_ELEMS = NSTREAM * (K_ELEMS + V_ELEMS);          // one stage
+  static constexpr size_t LDS_BYTES = (size_t)2 * BUF_ELEMS * sizeof(bf16);  // two stages
+  // one direct load instruction moves 64 lanes x 16 B = 1 KB = 512 elements
+  static constexpr int KCH = K_ELEMS / 512 / kWaves;   // per wave, per operand tile
+  static constexpr int VCH = V_ELEMS / 512 / kWaves;
+  static constexpr int K_ROWS_PER_CHUNK = 512 / DH;
 };
 
-__device__ __forceinline__ int sigma(int r) {
-  // swap bits 2 and 3
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+// 16-byte slot of chunk c of K row `row`.  The rows one 16-lane group reads
+// together differ in bits 0, 1, 3, 4 (bit 2 is the sub-tile half); the XOR key
+// spreads them over 16 bank groups.
+template <int CPR>
+__device__ __forceinline__ int kslot(int row, int c) {
+  if constexpr (CPR == 16) return c ^ ((row & 3) | ((row >> 1) & 12));
+  else return c ^ (((row >> 1) & 1) | ((row >> 2) & 6));   // 8 slots; row parity picks the half
+}
+// 16-byte slot of key chunk kc (8 keys) of V^T row e (64 keys = 8 chunks per row)
+__device__ __forceinline__ int vslot(int e, int kc) { return kc ^ ((e >> 1) & 7); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over [base, base + bytes): loads past the end return zeros.
+// Word 3 selects a 32-bit data format, as raw dword loads need on gfx9 parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from rsrc + voffset straight into LDS; lane i writes LDS
+// bytes [dst + 16 i, dst + 16 i + 16) of a wave-uniform destination.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, bf16 *dst_wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst_wave, 16, voffset, 0, 0, 0);
 }
 
-// key offset (within a 32-key sub-tile) held in register v of a lane with half hi
-__device__ __forceinline__ int key_of(int v, int hi) {
-  return (v < 8) ? (8 * hi + v) : (16 + 8 * hi + (v - 8));
+__device__ __forceinline__ floatx4 mfma16(const bf16x8 &a, const bf16x8 &b, const floatx4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 template <int DH, bool TAN>
@@ -70,10 +92,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
                                                                    int per_xcd, int total) {
   using C = AttnCfg<DH, TAN>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16 *sK = reinterpret_cast<bf16 *>(smem_raw);
-  bf16 *sVT = sK + C::K_ELEMS;
-  bf16 *sKd = sVT + C::V_ELEMS;            // valid when TAN
-  bf16 *sVdT = sKd + C::K_ELEMS;
+  bf16 *const lds = reinterpret_cast<bf16 *>(smem_raw);
+  // per stage: [K | V^T | dK | dV^T]
+  auto sK = [&](int buf) { return lds + buf * C::BUF_ELEMS; };
+  auto sVT = [&](int buf) { return lds + buf * C::BUF_ELEMS + C::K_ELEMS; };
+  auto sKd = [&](int buf) { return lds + buf * C::BUF_ELEMS + C::K_ELEMS + C::V_ELEMS; };
+  auto sVdT = [&](int buf) { return lds + buf * C::BUF_ELEMS + 2 * C::K_ELEMS + C::V_ELEMS; };
 
   // XCD-aware order: hardware places workgroup w on XCD w % 8; give each XCD a
   // contiguous range of logical tiles so one head's K/V stay in that XCD's L2.
@@ -86,232 +110,269 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int q_row = qb * BM + wave * 32 + l32;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int q_row = qb * BM + wave * 16 + l16;
   const int q_ld = min(q_row, p.Nq - 1);
   const int nk = min(max(p.nk[b], 1), p.Nk);
 
   const float scale = p.scale;
   const float c_log2 = scale * 1.4426950408889634f;
 
-  // Q^T (and dQ^T) as B operands: lane holds Q[q_row][16 s + 8 hi .. +7].
+  // Q^T (and dQ^T) as B operands: lane holds Q[q_row][32 s + 8 g .. +7].
   bf16x8 qf[C::KSTEPS], qdf[TAN ? C::KSTEPS : 1];
   {
-    const bf16 *qp = p.q + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * hi;
+    const bf16 *qp = p.q + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * g;
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
+    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
     if constexpr (TAN) {
-      const bf16 *qdp = p.qd + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * hi;
+      const bf16 *qdp = p.qd + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * g;
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) qdf[s] = *reinterpret_cast<const bf16x8 *>(qdp + 16 * s);
+      for (int s = 0; s < C::KSTEPS; ++s) qdf[s] = *reinterpret_cast<const bf16x8 *>(qdp + 32 * s);
     }
   }
 
-  const bf16 *kbase = p.k + (int64_t)b * p.k_bs + h * DH;
-  const bf16 *vtbase = p.vt + (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs;
-  const bf16 *kdbase = TAN ? p.kd + (int64_t)b * p.k_bs + h * DH : nullptr;
-  const bf16 *vdtbase = TAN ? p.vdt + (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs : nullptr;
-
-  uint4 rk[C::KCH], rv[C::VCH], rkd[TAN ? C::KCH : 1], rvd[TAN ? C::VCH : 1];
-
-  auto fetch = [&](int k0) {
+  // ---- global -> LDS staging of one 64-key stage ----
+  // The K descriptors end after key row nk-1, so rows >= nk load as zeros
+  // (their logits are masked).  V^T columns in [nk, round_up(nk, 64)) are read
+  // as stored; the caller keeps them finite, and their weights are zero.
+  const uint32_t k_bytes = (uint32_t)(((int64_t)(nk - 1) * p.k_rs + DH) * 2);
+  const uint32_t v_bytes = (uint32_t)((int64_t)DH * p.vt_rs * 2);
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.k + (int64_t)b * p.k_bs + h * DH, k_bytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.vt + (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs, v_bytes);
+  __amdgpu_buffer_rsrc_t rKd = rK, rVd = rV;
+  if constexpr (TAN) {
+    rKd = make_rsrc(p.kd + (int64_t)b * p.k_bs + h * DH, k_bytes);
+    rVd = make_rsrc(p.vdt + (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs, v_bytes);
+  }
+  // loop-invariant byte offsets of this lane's 16-byte chunks (at key 0)
+  uint32_t kvo[C::KCH], vvo[C::VCH];
+#pragma unroll
+  for (int r = 0; r < C::KCH; ++r) {
+    const int chunk = wave + kWaves * r;
+    const int row = chunk * C::K_ROWS_PER_CHUNK + lane / C::CPR;
+    const int c = kslot<C::CPR>(row, lane % C::CPR);   // the XOR swizzle is an involution
+    kvo[r] = (uint32_t)((row * p.k_rs + 8 * c) * 2);
+  }
+#pragma unroll
+  for (int r = 0; r < C::VCH; ++r) {
+    const int chunk = wave + kWaves * r;
+    const int e = chunk * 8 + lane / 8;
+    vvo[r] = (uint32_t)((e * p.vt_rs + 8 * vslot(e, lane % 8)) * 2);
+  }
+  auto issue = [&](int buf, int k0) {
+    const uint32_t kstep = (uint32_t)(k0 * p.k_rs * 2), vstep = (uint32_t)(k0 * 2);
 #pragma unroll
     for (int r = 0; r < C::KCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int key = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      const bool ok = (k0 + key) < nk;
-      const int64_t off = (int64_t)(k0 + key) * p.k_rs + col;
-      rk[r] = ok ? *reinterpret_cast<const uint4 *>(kbase + off) : make_uint4(0, 0, 0, 0);
-      if constexpr (TAN)
-        rkd[r] = ok ? *reinterpret_cast<const uint4 *>(kdbase + off) : make_uint4(0, 0, 0, 0);
+      const int chunk = wave + kWaves * r;
+      load_lds16(rK, kvo[r] + kstep, sK(buf) + chunk * 512);
+      if constexpr (TAN) load_lds16(rKd, kvo[r] + kstep, sKd(buf) + chunk * 512);
     }
 #pragma unroll
     for (int r = 0; r < C::VCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int e = c / (BN / 8), kc = (c % (BN / 8)) * 8;
-      const int j0 = k0 + kc;
-      const int64_t off = (int64_t)e * p.vt_rs + j0;
-      uint4 x = make_uint4(0, 0, 0, 0), xd = make_uint4(0, 0, 0, 0);
-      if (j0 < nk) {
-        x = *reinterpret_cast<const uint4 *>(vtbase + off);
-        if constexpr (TAN) xd = *reinterpret_cast<const uint4 *>(vdtbase + off);
-        if (j0 + 8 > nk) {  // partial chunk: zero the keys past nk
-          bf16x8 a = __builtin_bit_cast(bf16x8, x), ad = __builtin_bit_cast(bf16x8, xd);
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (j0 + u >= nk) { a[u] = (bf16)0.f; ad[u] = (bf16)0.f; }
-          x = __builtin_bit_cast(uint4, a);
-          xd = __builtin_bit_cast(uint4, ad);
-        }
-      }
-      rv[r] = x;
-      if constexpr (TAN) rvd[r] = xd;
+      const int chunk = wave + kWaves * r;
+      load_lds16(rV, vvo[r] + vstep, sVT(buf) + chunk * 512);
+      if constexpr (TAN) load_lds16(rVd, vvo[r] + vstep, sVdT(buf) + chunk * 512);
     }
   };
-  auto stage = [&]() {
-#pragma unroll
-    for (int r = 0; r < C::KCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int key = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      *reinterpret_cast<uint4 *>(sK + key * C::KROW + col) = rk[r];
-      if constexpr (TAN) *reinterpret_cast<uint4 *>(sKd + key * C::KROW + col) = rkd[r];
-    }
-#pragma unroll
-    for (int r = 0; r < C::VCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int e = c / (BN / 8), kc = (c % (BN / 8)) * 8;
-      *reinterpret_cast<uint4 *>(sVT + e * C::VROW + kc) = rv[r];
-      if constexpr (TAN) *reinterpret_cast<uint4 *>(sVdT + e * C::VROW + kc) = rvd[r];
-    }
-  };
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0); };
 
-  floatx16 O[C::DT], Od[TAN ? C::DT : 1];
+  // Per-lane swizzled read offsets (elements).  K: half t, k-step s, within a
+  // 32-key sub-tile (add 32 * DH per sub-tile).  V^T: rows l16 (+16 per d-tile),
+  // key chunk g of sub-tile u (add 16 * BN per d-tile).
+  int koff[2][C::KSTEPS];
 #pragma unroll
-  for (int e = 0; e < C::DT; ++e)
+  for (int t = 0; t < 2; ++t) {
+    const int row = 8 * (l16 >> 2) + 4 * t + (l16 & 3);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      O[e][v] = 0.f;
-      if constexpr (TAN) Od[e][v] = 0.f;
-    }
-  float m_run = -INFINITY, l_part = 0.f, mu_part = 0.f;
+    for (int s = 0; s < C::KSTEPS; ++s) koff[t][s] = row * DH + 8 * kslot<C::CPR>(row, 4 * s + g);
+  }
+  int voff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) voff[u] = l16 * BN + 8 * vslot(l16, 4 * u + g);
 
-  const int ntiles = (nk + BN - 1) / BN;
-  fetch(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int k0 = tile * BN;
-    stage();
-    __syncthreads();
-    if (tile + 1 < ntiles) fetch(k0 + BN);
-
-    // ---- S^T (and dS^T) for two 32-key sub-tiles ----
-    floatx16 S[2], Sd[2];
+  // ---- logits of one 32-key sub-tile u of a stage buffer ----
+  // S[t][r] holds key 32 u + 8 g + 4 t + r.
+  auto compute_s = [&](int buf, int u, floatx4 (&S)[2], floatx4 (&Sd)[2]) {
+    const bf16 *kt = sK(buf) + 32 * u * DH;
+    const bf16 *kdt = sKd(buf) + 32 * u * DH;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        S[t][v] = 0.f;
-        Sd[t][v] = 0.f;
+      for (int r = 0; r < 4; ++r) {
+        S[t][r] = 0.f;
+        if constexpr (TAN) Sd[t][r] = 0.f;
       }
-      const bf16 *krow = sK + (32 * t + sigma(l32)) * C::KROW + 8 * hi;
-      const bf16 *kdrow = sKd + (32 * t + sigma(l32)) * C::KROW + 8 * hi;
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(krow + 16 * s);
-        S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], S[t], 0, 0, 0);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + koff[t][s]);
+        S[t] = mfma16(ka, qf[s], S[t]);
         if constexpr (TAN) {
-          const bf16x8 kda = *reinterpret_cast<const bf16x8 *>(kdrow + 16 * s);
-          Sd[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kda, qf[s], Sd[t], 0, 0, 0);
-          Sd[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qdf[s], Sd[t], 0, 0, 0);
+          const bf16x8 kda = *reinterpret_cast<const bf16x8 *>(kdt + koff[t][s]);
+          Sd[t] = mfma16(kda, qf[s], Sd[t]);
+          Sd[t] = mfma16(ka, qdf[s], Sd[t]);
         }
       }
     }
-
-    // ---- mask, online softmax ----
-    if (k0 + BN > nk) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (k0 + 32 * t + key_of(v, hi) >= nk) {
-            S[t][v] = -INFINITY;
-            Sd[t][v] = 0.f;
-          }
-    }
-    float mx = -INFINITY;
+  };
+  auto mask_s = [&](int kb, floatx4 (&S)[2], floatx4 (&Sd)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[t][v]);
+      for (int r = 0; r < 4; ++r)
+        if (kb + 8 * g + 4 * t + r >= nk) {
+          S[t][r] = -INFINITY;
+          if constexpr (TAN) Sd[t][r] = 0.f;
+        }
+  };
+  // row max over the sub-tile, in log2 units of the scaled logits
+  auto row_max = [&](const floatx4 (&S)[2]) {
+    float mx = fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3]));
+    mx = fmaxf(mx, fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    return mx * c_log2;
+  };
 
-    bf16x8 P[2][2], PS[2][2];
+  floatx4 O[C::DT], Od[TAN ? C::DT : 1];
+#pragma unroll
+  for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      O[e][r] = 0.f;
+      if constexpr (TAN) Od[e][r] = 0.f;
+    }
+  // m_run is a reference max (log2 units), not the exact running max: it is
+  // raised only when a row's logits exceed it by more than kLazy, so every p is
+  // at most 2^kLazy.  Raising it (and rescaling the accumulators) happens
+  // outside the inner loop, which therefore never touches O/dO with the VALU.
+  constexpr float kLazy = 16.f;
+  float m_run, l_part = 0.f, mu_part = 0.f;
+
+  // p = 2^(s c - m_run) and p ds as bf16 B operands (keys 8g..8g+7), row sums
+  auto softmax = [&](const floatx4 (&S)[2], const floatx4 (&Sd)[2], bf16x8 &P, bf16x8 &PS) {
     float lsum = 0.f, musum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int v = 8 * u + j;
-          const float pv = __builtin_amdgcn_exp2f(S[t][v] * c_log2 - m_new);
-          lsum += pv;
-          P[t][u][j] = (bf16)pv;
-          if constexpr (TAN) {
-            const float ps = pv * (Sd[t][v] * scale);
-            musum += ps;
-            PS[t][u][j] = (bf16)ps;
-          }
-        }
-    l_part = alpha * l_part + lsum;
-    if constexpr (TAN) mu_part = alpha * mu_part + musum;
-
-    // ---- O^T = alpha O^T + V^T P^T (and the tangent) ----
+    for (int m = 0; m < 8; ++m) {
+      const int t = m >> 2, r = m & 3;
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][r], c_log2, -m_run));
+      lsum += pv;
+      P[m] = (bf16)pv;
+      if constexpr (TAN) {
+        const float ps = pv * (Sd[t][r] * scale);
+        musum += ps;
+        PS[m] = (bf16)ps;
+      }
+    }
+    l_part += lsum;
+    if constexpr (TAN) mu_part += musum;
+  };
+  auto pv_accum = [&](int buf, int u, const bf16x8 &P, const bf16x8 &PS) {
+    const bf16 *vt = sVT(buf) + voff[u];
+    const bf16 *vdt = sVdT(buf) + voff[u];
 #pragma unroll
     for (int e = 0; e < C::DT; ++e) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        O[e][v] *= alpha;
-        if constexpr (TAN) Od[e][v] *= alpha;
+      const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vt + 16 * e * BN);
+      O[e] = mfma16(va, P, O[e]);
+      if constexpr (TAN) {
+        const bf16x8 vda = *reinterpret_cast<const bf16x8 *>(vdt + 16 * e * BN);
+        Od[e] = mfma16(va, PS, Od[e]);
+        Od[e] = mfma16(vda, P, Od[e]);
       }
-      const bf16 *vrow = sVT + (32 * e + l32) * C::VROW + 8 * hi;
-      const bf16 *vdrow = sVdT + (32 * e + l32) * C::VROW + 8 * hi;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vrow + 32 * t + 16 * u);
-          O[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[t][u], O[e], 0, 0, 0);
-          if constexpr (TAN) {
-            const bf16x8 vda = *reinterpret_cast<const bf16x8 *>(vdrow + 32 * t + 16 * u);
-            Od[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, PS[t][u], Od[e], 0, 0, 0);
-            Od[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vda, P[t][u], Od[e], 0, 0, 0);
-          }
-        }
     }
-    __syncthreads();
-  }
+  };
 
-  // ---- epilogue ----
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const float inv_l = 1.f / l_tot;
-  float mu = 0.f;
-  if constexpr (TAN) mu = (mu_part + __shfl_xor(mu_part, 32)) * inv_l;
-  if (q_row < p.Nq) {
-    if (p.lse && hi == 0)
-      p.lse[((int64_t)b * p.H + h) * p.Nq + q_row] = m_run * 0.6931471805599453f + logf(l_tot);
-    const int64_t obase = (int64_t)b * p.o_bs + (int64_t)q_row * p.o_rs + h * DH;
+  // ---- main loop over 32-key sub-tiles; 64-key stages in two LDS buffers ----
+  // The logits of sub-tile j+1 are computed in the same basic block as the
+  // softmax of sub-tile j, so the matrix cores work while the VALU exponentiates.
+  const int nst = (nk + BN - 1) / BN;
+  const int nsub = 2 * nst;
+  issue(0, 0);
+  wait_loads();
+  __syncthreads();
+  if (nst > 1) issue(1, BN);
+  floatx4 S[2], Sd[2], Sn[2], Sdn[2];
+  bf16x8 P, PS;
+  compute_s(0, 0, S, Sd);
+  if (nst == 1) mask_s(0, S, Sd);
+  m_run = row_max(S);   // key 0 is always valid, so this is finite
+  int j = 0;
+  for (;;) {
+    for (; j < nsub; ++j) {
+      const int u = j & 1, st = j >> 1, cur = st & 1;
+      if (__any(row_max(S) > m_run + kLazy)) break;   // rare: raise m_run outside
+      if (u == 1 && j + 1 < nsub) {                     // the next stage landed: publish it
+        wait_loads();
+        __syncthreads();
+      }
+      compute_s(u == 0 ? cur : cur ^ 1, u ^ 1, Sn, Sdn);   // (unused past the end)
+      softmax(S, Sd, P, PS);
+      pv_accum(cur, u, P, PS);
+      if (u == 1) {                                     // stage consumed: refill its buffer
+        __syncthreads();
+        if (st + 2 < nst) issue(cur, (st + 2) * BN);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        S[t] = Sn[t];
+        if constexpr (TAN) Sd[t] = Sdn[t];
+      }
+      if (j + 1 < nsub && ((j + 1) >> 1) == nst - 1) mask_s(32 * (j + 1), S, Sd);
+    }
+    if (j >= nsub) break;
+    // raise the reference max of the rows that outgrew it; rescale accumulators
+    const float m_new = fmaxf(m_run, row_max(S));
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_part *= alpha;
+    mu_part *= alpha;
 #pragma unroll
     for (int e = 0; e < C::DT; ++e)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * e + 8 * g + 4 * hi;
-        float o4[4], od4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          o4[u] = O[e][4 * g + u] * inv_l;
-          if constexpr (TAN) od4[u] = Od[e][4 * g + u] * inv_l - mu * o4[u];
-        }
-        if (p.out_dt == 0) {
-          bf16x4 a;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) a[u] = (bf16)o4[u];
-          *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(p.o) + obase + col) = a;
-          if constexpr (TAN) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) a[u] = (bf16)od4[u];
-            *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(p.od) + obase + col) = a;
-          }
-        } else {
-          *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.o) + obase + col) =
-              make_float4(o4[0], o4[1], o4[2], o4[3]);
-          if constexpr (TAN)
-            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.od) + obase + col) =
-                make_float4(od4[0], od4[1], od4[2], od4[3]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        O[e][r] *= alpha;
+        if constexpr (TAN) Od[e][r] *= alpha;
       }
+  }
+
+  // ---- epilogue: combine the four lanes of a row, normalise, store ----
+  float l_tot = l_part + __shfl_xor(l_part, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const float inv_l = 1.f / l_tot;
+  float mu = 0.f;
+  if constexpr (TAN) {
+    mu = mu_part + __shfl_xor(mu_part, 16);
+    mu = (mu + __shfl_xor(mu, 32)) * inv_l;
+  }
+  if (q_row < p.Nq) {
+    if (p.lse && g == 0)
+      p.lse[((int64_t)b * p.H + h) * p.Nq + q_row] = m_run * 0.6931471805599453f + logf(l_tot);
+    const int64_t obase = (int64_t)b * p.o_bs + (int64_t)q_row * p.o_rs + h * DH + 4 * g;
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) {
+      float o4[4], od4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        o4[r] = O[e][r] * inv_l;
+        if constexpr (TAN) od4[r] = Od[e][r] * inv_l - mu * o4[r];
+      }
+      if (p.out_dt == 0) {
+        bf16x4 a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = (bf16)o4[r];
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(p.o) + obase + 16 * e) = a;
+        if constexpr (TAN) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a[r] = (bf16)od4[r];
+          *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(p.od) + obase + 16 * e) = a;
+        }
+      } else {
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.o) + obase + 16 * e) =
+            make_float4(o4[0], o4[1], o4[2], o4[3]);
+        if constexpr (TAN)
+          *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.od) + obase + 16 * e) =
+              make_float4(od4[0], od4[1], od4[2], od4[3]);
+      }
+    }
   }
 }
 

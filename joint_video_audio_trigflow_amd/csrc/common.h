@@ -133,6 +133,7 @@ struct GemmParams {
   void *C; int64_t ldc, c_bs; int c_dt;   // columns [0, n_split) go to C
   const float *bias; int64_t bias_bs;     // nullable, fp32 [batch][N]
   bf16 *VT; int64_t vt_bs, vt_hs, vt_rs;  // columns >= n_split: V^T[b][h][c][row]
+  int vt_rows;                            // V^T rows [M, vt_rows) are written as zeros
   int n_split, dh;
   int M, N, K, batch;
 };

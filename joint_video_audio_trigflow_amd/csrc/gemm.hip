@@ -134,7 +134,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int row = m0 + wm * 64 + i * 32 + 8 * g + 4 * hi;
-          if (row + 3 < p.M) {
+          // rows in [M, vt_rows) read zero A rows: they store the zero padding
+          if (row + 3 < p.vt_rows) {
             bf16x4 pk;
 #pragma unroll
             for (int u = 0; u < 4; ++u) pk[u] = (bf16)(acc[i][j][4 * g + u] + bcol);
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
           } else {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-              if (row + u < p.M) vt[row + u] = (bf16)(acc[i][j][4 * g + u] + bcol);
+              if (row + u < p.vt_rows) vt[row + u] = (bf16)(acc[i][j][4 * g + u] + bcol);
           }
         }
       }
@@ -163,7 +164,7 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
     g_attr_set = true;
   }
   const int tiles_n = (p.N + BN - 1) / BN;
-  const int tiles_m = (p.M + BM - 1) / BM;
+  const int tiles_m = (max(p.M, p.VT ? p.vt_rows : 0) + BM - 1) / BM;
   dim3 grid(tiles_n * tiles_m, p.batch);
   hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(kThreads), kLdsBytes, s, p, tiles_n);
   return hipGetLastError();

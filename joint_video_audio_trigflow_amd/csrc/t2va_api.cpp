@@ -249,8 +249,12 @@ t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, c
                              d.o_batch_stride, d.o_row_stride};
   for (int64_t s : strides)
     if (s < 0 || s % 8) return fail(T2VA_INVALID_ARG, "strides must be non-negative multiples of 8");
-  if (d.vt_row_stride < ((d.Nk + 7) / 8) * 8)
-    return fail(T2VA_INVALID_ARG, "vt_row_stride %lld < round_up(Nk, 8)", (long long)d.vt_row_stride);
+  if (d.vt_row_stride < ((d.Nk + 63) / 64) * 64)
+    return fail(T2VA_INVALID_ARG, "vt_row_stride %lld < round_up(Nk, 64)", (long long)d.vt_row_stride);
+  // per-(sample, head) byte offsets must fit the 32-bit buffer addressing
+  if ((int64_t)(d.Nk + 64) * d.k_row_stride * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)d.dh * d.vt_row_stride * 2 >= ((int64_t)1 << 31))
+    return fail(T2VA_UNSUPPORTED_SHAPE, "K or V^T extent per (sample, head) exceeds 2 GiB");
   if (d.q_row_stride < (int64_t)d.H * d.dh || d.k_row_stride < (int64_t)d.H * d.dh ||
       d.o_row_stride < (int64_t)d.H * d.dh)
     return fail(T2VA_INVALID_ARG, "row strides must cover H*dh elements");
@@ -410,7 +414,7 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
     g.W = Wt; g.ldw = ldw;
     g.C = Cp; g.ldc = ldc; g.c_bs = c_bs; g.c_dt = c_dt;
     g.bias = bias; g.bias_bs = bias_bs;
-    g.VT = vt; g.vt_bs = vt_bs; g.vt_hs = vt_hs; g.vt_rs = L.ldv;
+    g.VT = vt; g.vt_bs = vt_bs; g.vt_hs = vt_hs; g.vt_rs = L.ldv; g.vt_rows = L.ldv;
     g.n_split = n_split; g.dh = dh;
     g.M = M; g.N = N; g.K = K; g.batch = batch;
     PhaseScope ps(s, T2VA_PHASE_GEMM, prof);

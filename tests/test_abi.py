@@ -107,7 +107,7 @@ def test_attention_rejects_before_launch(lib):
     d.q_batch_stride = d.k_batch_stride = 20 * 256
     d.q_row_stride = d.k_row_stride = d.o_row_stride = 256
     d.o_batch_stride = 10 * 256
-    d.vt_row_stride, d.vt_head_stride, d.vt_batch_stride = 24, 24 * 128, 2 * 24 * 128
+    d.vt_row_stride, d.vt_head_stride, d.vt_batch_stride = 64, 64 * 128, 2 * 64 * 128
     d.has_tangent, d.out_dtype = 0, 1
     p = [fake_ptr(i + 1) for i in range(10)]
 
@@ -122,9 +122,9 @@ def test_attention_rejects_before_launch(lib):
     d.has_tangent = 1
     assert call() == 1                                      # has_tangent without tangents
     d.has_tangent = 0
-    d.vt_row_stride = 16                                    # < round_up(Nk, 8)
+    d.vt_row_stride = 24                                    # < round_up(Nk, 64)
     assert call() == 1 and "vt_row_stride" in err(lib)
-    d.vt_row_stride = 24
+    d.vt_row_stride = 64
     d.q_row_stride = 250                                    # not a multiple of 8
     assert call() == 1
 

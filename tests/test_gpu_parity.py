@@ -71,7 +71,7 @@ def run_attention(ops, H, dh, tangent=True, out_dtype=torch.float32, ldv_pad=0):
     L = lib()
     B, Nq = ops["q"].shape[:2]
     Nk = ops["k"].shape[1]
-    ldv = (Nk + 7) // 8 * 8 + ldv_pad
+    ldv = (Nk + 63) // 64 * 64 + ldv_pad
 
     def dev(x):
         return torch.from_numpy(x.astype(np.float32)).to("cuda", torch.bfloat16).contiguous()
