@@ -13,7 +13,7 @@
 // do = dA/l - (mu~/l) o.  Keys j >= nk[b] (padded text, section 6.3 of the
 // deep read) get logit -inf.
 //
-// Work decomposition: a workgroup of 8 waves (two per SIMD) owns 128 query
+// Work decomposition: a workgroup of 12 waves (three per SIMD) owns 192 query
 // rows of one (sample, head); a wave owns 16 rows.  Products are computed
 // transposed so that one lane column owns one query row throughout, using
 // v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8(l/16)..+7;
@@ -38,13 +38,28 @@ namespace t2va {
 
 namespace {
 
-constexpr int kWaves = 8;             // two waves per SIMD
-constexpr int kThreads = kWaves * 64;
-constexpr int BM = 16 * kWaves;       // query rows per workgroup
+#ifndef T2VA_ATTN_WAVES_JVP
+#define T2VA_ATTN_WAVES_JVP 12
+#endif
+#ifndef T2VA_ATTN_WAVES_FWD
+#define T2VA_ATTN_WAVES_FWD 12
+#endif
+#ifndef T2VA_ATTN_PIPE_JVP
+#define T2VA_ATTN_PIPE_JVP 1
+#endif
+#ifndef T2VA_ATTN_PIPE_FWD
+#define T2VA_ATTN_PIPE_FWD 0
+#endif
+constexpr int kLoadWaves = 8;         // waves that issue the LDS loads
 constexpr int BN = 64;                // keys per LDS stage
 
 template <int DH, bool TAN>
 struct AttnCfg {
+  // waves per workgroup: 12 (three per SIMD) by default; 16 query rows per wave
+  static constexpr int NW = TAN ? T2VA_ATTN_WAVES_JVP : T2VA_ATTN_WAVES_FWD;
+  static constexpr bool PIPE = TAN ? T2VA_ATTN_PIPE_JVP : T2VA_ATTN_PIPE_FWD;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BM = 16 * NW;       // query rows per workgroup
   static constexpr int KSTEPS = DH / 32;   // MFMA k-steps over the head dimension
   static constexpr int DT = DH / 16;       // 16-row tiles of the head dimension
   static constexpr int CPR = DH / 8;       // 16-byte chunks per K row
@@ -54,8 +69,8 @@ struct AttnCfg {
   static constexpr int BUF_ELEMS = NSTREAM * (K_ELEMS + V_ELEMS);          // one stage
   static constexpr size_t LDS_BYTES = (size_t)2 * BUF_ELEMS * sizeof(bf16);  // two stages
   // one direct load instruction moves 64 lanes x 16 B = 1 KB = 512 elements
-  static constexpr int KCH = K_ELEMS / 512 / kWaves;   // per wave, per operand tile
-  static constexpr int VCH = V_ELEMS / 512 / kWaves;
+  static constexpr int KCH = K_ELEMS / 512 / kLoadWaves;   // per loading wave, per operand tile
+  static constexpr int VCH = V_ELEMS / 512 / kLoadWaves;
   static constexpr int K_ROWS_PER_CHUNK = 512 / DH;
 };
 
@@ -88,7 +103,7 @@ __device__ __forceinline__ floatx4 mfma16(const bf16x8 &a, const bf16x8 &b, cons
 }
 
 template <int DH, bool TAN>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p, int nqb,
+__global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_kernel(AttnParams p, int nqb,
                                                                    int per_xcd, int total) {
   using C = AttnCfg<DH, TAN>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -111,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int q_row = qb * BM + wave * 16 + l16;
+  const int q_row = qb * C::BM + wave * 16 + l16;
   const int q_ld = min(q_row, p.Nq - 1);
   const int nk = min(max(p.nk[b], 1), p.Nk);
 
@@ -145,31 +160,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
     rVd = make_rsrc(p.vdt + (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs, v_bytes);
   }
   // loop-invariant byte offsets of this lane's 16-byte chunks (at key 0)
+  const int lw = wave % kLoadWaves;
+  const bool loader = wave < kLoadWaves;
   uint32_t kvo[C::KCH], vvo[C::VCH];
 #pragma unroll
   for (int r = 0; r < C::KCH; ++r) {
-    const int chunk = wave + kWaves * r;
+    const int chunk = lw + kLoadWaves * r;
     const int row = chunk * C::K_ROWS_PER_CHUNK + lane / C::CPR;
     const int c = kslot<C::CPR>(row, lane % C::CPR);   // the XOR swizzle is an involution
     kvo[r] = (uint32_t)((row * p.k_rs + 8 * c) * 2);
   }
 #pragma unroll
   for (int r = 0; r < C::VCH; ++r) {
-    const int chunk = wave + kWaves * r;
+    const int chunk = lw + kLoadWaves * r;
     const int e = chunk * 8 + lane / 8;
     vvo[r] = (uint32_t)((e * p.vt_rs + 8 * vslot(e, lane % 8)) * 2);
   }
   auto issue = [&](int buf, int k0) {
+    if (!loader) return;
     const uint32_t kstep = (uint32_t)(k0 * p.k_rs * 2), vstep = (uint32_t)(k0 * 2);
 #pragma unroll
     for (int r = 0; r < C::KCH; ++r) {
-      const int chunk = wave + kWaves * r;
+      const int chunk = lw + kLoadWaves * r;
       load_lds16(rK, kvo[r] + kstep, sK(buf) + chunk * 512);
       if constexpr (TAN) load_lds16(rKd, kvo[r] + kstep, sKd(buf) + chunk * 512);
     }
 #pragma unroll
     for (int r = 0; r < C::VCH; ++r) {
-      const int chunk = wave + kWaves * r;
+      const int chunk = lw + kLoadWaves * r;
       load_lds16(rV, vvo[r] + vstep, sVT(buf) + chunk * 512);
       if constexpr (TAN) load_lds16(rVd, vvo[r] + vstep, sVdT(buf) + chunk * 512);
     }
@@ -179,13 +197,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
   // Per-lane swizzled read offsets (elements).  K: half t, k-step s, within a
   // 32-key sub-tile (add 32 * DH per sub-tile).  V^T: rows l16 (+16 per d-tile),
   // key chunk g of sub-tile u (add 16 * BN per d-tile).
-  int koff[2][C::KSTEPS];
+  // K slot of k-step s is 4 s + g; with the XOR key x of the row it is
+  // (4 s + g) ^ x = 4 (s ^ (x >> 2)) + (g ^ (x & 3)), so one XOR per read.
+  int kbase_off[2], kxs[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int row = 8 * (l16 >> 2) + 4 * t + (l16 & 3);
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) koff[t][s] = row * DH + 8 * kslot<C::CPR>(row, 4 * s + g);
+    const int x = kslot<C::CPR>(row, 0);                 // the row's XOR key
+    kbase_off[t] = row * DH + 8 * (g ^ (x & 3));
+    kxs[t] = x >> 2;
   }
+  auto koff = [&](int t, int s) { return kbase_off[t] + 32 * (s ^ kxs[t]); };
   int voff[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) voff[u] = l16 * BN + 8 * vslot(l16, 4 * u + g);
@@ -204,10 +226,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
       }
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + koff[t][s]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + koff(t, s));
         S[t] = mfma16(ka, qf[s], S[t]);
         if constexpr (TAN) {
-          const bf16x8 kda = *reinterpret_cast<const bf16x8 *>(kdt + koff[t][s]);
+          const bf16x8 kda = *reinterpret_cast<const bf16x8 *>(kdt + koff(t, s));
           Sd[t] = mfma16(kda, qf[s], Sd[t]);
           Sd[t] = mfma16(ka, qdf[s], Sd[t]);
         }
@@ -233,6 +255,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
     return mx * c_log2;
   };
 
+  // row max (log2 units) and the tangent logit of the key attaining it; ties
+  // go to the larger tangent so the four lanes of a row agree
+  auto row_max_arg = [&](const floatx4 (&S)[2], const floatx4 (&Sd)[2], float &sd_at_max) {
+    float mx = S[0][0], sd = Sd[0][0];
+#pragma unroll
+    for (int m = 1; m < 8; ++m) {
+      const float v = S[m >> 2][m & 3], vd = Sd[m >> 2][m & 3];
+      const bool gt = v > mx || (v == mx && vd > sd);
+      mx = gt ? v : mx;
+      sd = gt ? vd : sd;
+    }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float om = __shfl_xor(mx, off), od = __shfl_xor(sd, off);
+      const bool gt = om > mx || (om == mx && od > sd);
+      mx = gt ? om : mx;
+      sd = gt ? od : sd;
+    }
+    sd_at_max = sd * scale;
+    return mx * c_log2;
+  };
+
   floatx4 O[C::DT], Od[TAN ? C::DT : 1];
 #pragma unroll
   for (int e = 0; e < C::DT; ++e)
@@ -245,8 +289,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
   // raised only when a row's logits exceed it by more than kLazy, so every p is
   // at most 2^kLazy.  Raising it (and rescaling the accumulators) happens
   // outside the inner loop, which therefore never touches O/dO with the VALU.
-  constexpr float kLazy = 16.f;
-  float m_run, l_part = 0.f, mu_part = 0.f;
+  //
+  // The tangent weights are centred: the kernel accumulates p (ds - c) with c
+  // the tangent logit of the row's max key at the last raise, and
+  // mu~ = sum p (ds - c).  Then do = dA/l - (mu~/l) o still holds, and when
+  // softmax is nearly one-hot (large logits) the dominant key contributes
+  // p (ds - c) ~ 0 instead of a large p ds that the final subtraction would
+  // have to cancel after bf16 rounding.  For that the JVP kernel raises (and
+  // re-centres) once a row's max grows by more than 4 (a factor of 16).
+#ifndef T2VA_ATTN_LAZY_JVP
+#define T2VA_ATTN_LAZY_JVP 4.f
+#endif
+#ifndef T2VA_ATTN_CENTRE
+#define T2VA_ATTN_CENTRE 1
+#endif
+  constexpr float kLazy = TAN ? T2VA_ATTN_LAZY_JVP : 16.f;
+  float m_run, l_part = 0.f, mu_part = 0.f, c_ref = 0.f;
 
   // p = 2^(s c - m_run) and p ds as bf16 B operands (keys 8g..8g+7), row sums
   auto softmax = [&](const floatx4 (&S)[2], const floatx4 (&Sd)[2], bf16x8 &P, bf16x8 &PS) {
@@ -258,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
       lsum += pv;
       P[m] = (bf16)pv;
       if constexpr (TAN) {
-        const float ps = pv * (Sd[t][r] * scale);
+        const float ps = pv * __builtin_fmaf(Sd[t][r], scale, -c_ref);   // p (ds - c)
         musum += ps;
         PS[m] = (bf16)ps;
       }
@@ -290,16 +348,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
   wait_loads();
   __syncthreads();
   if (nst > 1) issue(1, BN);
-  floatx4 S[2], Sd[2], Sn[2], Sdn[2];
+  floatx4 S[2], Sd[2];
   bf16x8 P, PS;
   compute_s(0, 0, S, Sd);
   if (nst == 1) mask_s(0, S, Sd);
-  m_run = row_max(S);   // key 0 is always valid, so this is finite
+  // key 0 is always valid, so this is finite
+  if constexpr (TAN) { m_run = row_max_arg(S, Sd, c_ref); if (!T2VA_ATTN_CENTRE) c_ref = 0.f; }
+  else m_run = row_max(S);
   int j = 0;
+  floatx4 Sn[2], Sdn[2];
   for (;;) {
     for (; j < nsub; ++j) {
       const int u = j & 1, st = j >> 1, cur = st & 1;
       if (__any(row_max(S) > m_run + kLazy)) break;   // rare: raise m_run outside
+      if constexpr (C::PIPE) {
       if (u == 1 && j + 1 < nsub) {                     // the next stage landed: publish it
         wait_loads();
         __syncthreads();
@@ -317,20 +379,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_jvp_kernel(AttnParams p,
         if constexpr (TAN) Sd[t] = Sdn[t];
       }
       if (j + 1 < nsub && ((j + 1) >> 1) == nst - 1) mask_s(32 * (j + 1), S, Sd);
+      } else {
+      softmax(S, Sd, P, PS);
+      pv_accum(cur, u, P, PS);
+      if (j + 1 < nsub) {
+        if (u == 1) {
+          // one barrier: every wave is done with this stage's buffer and the
+          // next stage (whose loads this wave waited for) is visible
+          wait_loads();
+          __syncthreads();
+          if (st + 2 < nst) issue(cur, (st + 2) * BN);
+        }
+        compute_s(u == 0 ? cur : cur ^ 1, u ^ 1, S, Sd);
+        if (((j + 1) >> 1) == nst - 1) mask_s(32 * (j + 1), S, Sd);
+      }
+      }
     }
     if (j >= nsub) break;
-    // raise the reference max of the rows that outgrew it; rescale accumulators
-    const float m_new = fmaxf(m_run, row_max(S));
+    // raise the reference max of the rows that outgrew it; rescale the
+    // accumulators and re-centre the tangent weights on the new max key
+    float sd_max = 0.f;
+    const float mx = TAN ? row_max_arg(S, Sd, sd_max) : row_max(S);
+    const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float c_new = (TAN && T2VA_ATTN_CENTRE && mx > m_run) ? sd_max : c_ref;
+    const float delta = c_ref - c_new;   // dA += delta A, mu~ += delta l
     m_run = m_new;
+    c_ref = c_new;
+    if constexpr (TAN) mu_part = alpha * (mu_part + delta * l_part);
     l_part *= alpha;
-    mu_part *= alpha;
 #pragma unroll
     for (int e = 0; e < C::DT; ++e)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        if constexpr (TAN) Od[e][r] = alpha * __builtin_fmaf(delta, O[e][r], Od[e][r]);
         O[e][r] *= alpha;
-        if constexpr (TAN) Od[e][r] *= alpha;
       }
   }
 
@@ -387,10 +470,10 @@ hipError_t launch_impl(const AttnParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int nqb = (p.Nq + BM - 1) / BM;
+  const int nqb = (p.Nq + C::BM - 1) / C::BM;
   const int total = nqb * p.H * p.B;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((attn_fwd_jvp_kernel<DH, TAN>), dim3(per_xcd * 8), dim3(kThreads),
+  hipLaunchKernelGGL((attn_fwd_jvp_kernel<DH, TAN>), dim3(per_xcd * 8), dim3(C::THREADS),
                      C::LDS_BYTES, s, p, nqb, per_xcd, total);
   return hipGetLastError();
 }

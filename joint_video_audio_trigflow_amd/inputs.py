@@ -175,7 +175,8 @@ def make_problem(cfg: Config) -> dict:
 
 
 def make_attention_operands(B: int, H: int, dh: int, Nq: int, Nk: int, seed: int,
-                            nk_valid=None, q_scale: float = 1.0) -> dict:
+                            nk_valid=None, q_scale: float = 1.0, dtype=np.float64,
+                            k_scale: float = 1.0, tangent_scale: float = 1.0) -> dict:
     """Random bf16-valued attention operands in sequence-major layout [B, N, H, dh].
 
     Queries are the first Nq rows of the same token sequence the keys span
@@ -185,12 +186,17 @@ def make_attention_operands(B: int, H: int, dh: int, Nq: int, Nk: int, seed: int
     rng = np.random.default_rng(seed)
     sh_q = (B, Nq, H, dh)
     sh_k = (B, Nk, H, dh)
-    q = round_bf16(rng.standard_normal(sh_q) * q_scale)
-    k = round_bf16(rng.standard_normal(sh_k))
-    v = round_bf16(rng.standard_normal(sh_k))
-    qd = round_bf16(rng.standard_normal(sh_q))
-    kd = round_bf16(rng.standard_normal(sh_k))
-    vd = round_bf16(rng.standard_normal(sh_k))
+
+    def draw(shape, s=1.0):
+        x = rng.standard_normal(shape, dtype=np.float32 if dtype == np.float32 else np.float64)
+        return round_bf16(x * s).astype(dtype)
+
+    q = draw(sh_q, q_scale)
+    k = draw(sh_k, k_scale)
+    v = draw(sh_k)
+    qd = draw(sh_q, tangent_scale)
+    kd = draw(sh_k, tangent_scale)
+    vd = draw(sh_k, tangent_scale)
     if nk_valid is None:
         nk_valid = np.full(B, Nk, dtype=np.int32)
     return dict(q=q, k=k, v=v, qd=qd, kd=kd, vd=vd, nk=np.asarray(nk_valid, dtype=np.int32))

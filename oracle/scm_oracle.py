@@ -41,6 +41,33 @@ import numpy as np
 
 
 # ---------------------------------------------------------------------------
+# Optional storage rounding.  With STORAGE = "bf16" the values the GPU path
+# stores in bfloat16 between its kernels (noised latents and their tangents,
+# the block's token rows, Q/K/V and their tangents, the attention outputs) are
+# rounded to bfloat16 here too, so that decisions a near-one-hot softmax takes
+# on those values are taken in the same precision on both sides.  The default
+# (None) is the exact fp64 oracle.
+# ---------------------------------------------------------------------------
+STORAGE = None
+
+
+def _bf16(x):
+    """Round float64 values to the nearest bfloat16 (ties to even) via fp32 bits."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _store(x):
+    if STORAGE is None:
+        return x
+    if isinstance(x, Dual):
+        return Dual(_bf16(x.p), _bf16(x.t))
+    return _bf16(x)
+
+
+# ---------------------------------------------------------------------------
 # Dual numbers: value p and tangent t, pushed forward by the chain rule.
 # ---------------------------------------------------------------------------
 class Dual:
@@ -213,6 +240,7 @@ def joint_block(zv: Dual, za: Dual, t: Dual, text: np.ndarray, mask: np.ndarray,
     tau = d_linear(time_embedding(t, d), W["w_t"])
     hv = d_add(d_linear(zv, W["w_in_v"]), Dual(tau.p[None, :], tau.t[None, :]))
     ha = d_add(d_linear(za, W["w_in_a"]), Dual(tau.p[None, :], tau.t[None, :]))
+    hv, ha = _store(hv), _store(ha)
     hc = const(text[mask.astype(bool)])
     X = d_concat([hv, ha, hc])
     if query_rows is None:
@@ -223,15 +251,15 @@ def joint_block(zv: Dual, za: Dual, t: Dual, text: np.ndarray, mask: np.ndarray,
         Xq = d_concat([d_rows(hv, rv), d_rows(ha, ra)])
         nqv = len(rv)
     w_q, w_k, w_v = W["w_qkv"][:d], W["w_qkv"][d:2 * d], W["w_qkv"][2 * d:]
-    Q = d_linear(Xq, w_q)
-    K = d_linear(X, w_k)
-    V = d_linear(X, w_v)
+    Q = _store(d_linear(Xq, w_q))
+    K = _store(d_linear(X, w_k))
+    V = _store(d_linear(X, w_v))
     heads = []
     for h in range(H):
         sl = slice(h * dh, (h + 1) * dh)
         heads.append(attention(Dual(Q.p[:, sl], Q.t[:, sl]), Dual(K.p[:, sl], K.t[:, sl]),
                                Dual(V.p[:, sl], V.t[:, sl])))
-    Y = d_concat(heads, axis=1)
+    Y = _store(d_concat(heads, axis=1))
     Gv = d_linear(d_rows(Y, slice(0, nqv)), W["w_out_v"])
     Ga = d_linear(d_rows(Y, slice(nqv, None)), W["w_out_a"])
     return Gv, Ga
@@ -257,14 +285,16 @@ def scm_sample(cfg, data: dict, teacher: dict, student: dict, b: int, beta=None,
            "a": trigflow_noise(t, data["z0_a"][b], data["eps_a"][b])}
 
     # Teacher: primal forward only.
-    gT_v, gT_a = joint_block(const(z_t["v"]), const(z_t["a"]), const(t), text, mask, teacher, cfg.H)
+    zin = {m: _store(z_t[m]) for m in "va"}
+    gT_v, gT_a = joint_block(const(zin["v"]), const(zin["a"]), const(t), text, mask, teacher, cfg.H)
     x0_T = {"v": gT_v.p, "a": gT_a.p}
     F_T = {m: trigflow_field(t, z_t[m], x0_T[m]) for m in "va"}
 
     # Student: dual forward along (dt = 1, dz^v = F_T^v, dz^a = F_T^a, dc = 0).
     td = Dual(np.float64(t), np.float64(1.0))
     zd = {m: Dual(z_t[m], F_T[m]) for m in "va"}
-    gS_v, gS_a = joint_block(zd["v"], zd["a"], td, text, mask, student, cfg.H, query_rows=query_rows)
+    zb = {m: Dual(zin[m], _store(F_T[m])) for m in "va"}   # the block's (stored) inputs
+    gS_v, gS_a = joint_block(zb["v"], zb["a"], td, text, mask, student, cfg.H, query_rows=query_rows)
     G_S = {"v": gS_v, "a": gS_a}
 
     if query_rows is not None:

@@ -3,7 +3,10 @@
 For each of the standard, stress and high-resolution workloads this runs the
 fp64 oracle on the whole target and stores, per sample, the per-modality L2
 norms, the loss, and J and gbar on a fixed random sample of rows (48 video
-and 24 audio rows).  Usage: python tests/golden/make_full_size_expected.py [names...]
+and 24 audio rows).  With --storage it also runs the oracle with bf16 rounding
+at the points where the GPU path stores bf16 (keys prefixed "st_"), which
+measures how sensitive each sample is to that storage precision.
+Usage: python tests/golden/make_full_size_expected.py [--storage] [names...]
 """
 import os
 import sys
@@ -28,22 +31,40 @@ def sample_rows(cfg):
     return rv, ra
 
 
-def main(names):
+def rows_of(res, cfg, prefix=""):
+    rv, ra = sample_rows(cfg)
+    b = np.arange(cfg.B)[:, None]
+    return {prefix + "J_v": res["J_v"][b, rv].astype(np.float32),
+            prefix + "J_a": res["J_a"][b, ra].astype(np.float32),
+            prefix + "gbar_v": res["gbar_v"][b, rv].astype(np.float32),
+            prefix + "gbar_a": res["gbar_a"][b, ra].astype(np.float32),
+            prefix + "norms": res["norms"], prefix + "loss": res["loss"]}
+
+
+def main(names, storage):
+    from oracle import scm_oracle
     for name in names:
         cfg = inputs.CONFIGS[name]
         t0 = time.time()
         p = inputs.make_problem(cfg)
-        res = oracle.scm_target(p)
-        rv, ra = sample_rows(cfg)
-        b = np.arange(cfg.B)[:, None]
-        np.savez_compressed(
-            os.path.join(OUT, f"expected_{name}.npz"),
-            rows_v=rv, rows_a=ra,
-            J_v=res["J_v"][b, rv].astype(np.float32), J_a=res["J_a"][b, ra].astype(np.float32),
-            gbar_v=res["gbar_v"][b, rv].astype(np.float32), gbar_a=res["gbar_a"][b, ra].astype(np.float32),
-            norms=res["norms"], loss=res["loss"], t=res["t"])
+        path = os.path.join(OUT, f"expected_{name}.npz")
+        if os.path.exists(path):
+            out = dict(np.load(path))
+        else:
+            scm_oracle.STORAGE = None
+            res = oracle.scm_target(p)
+            rv, ra = sample_rows(cfg)
+            out = dict(rows_v=rv, rows_a=ra, t=res["t"], **rows_of(res, cfg))
+        if storage:
+            scm_oracle.STORAGE = "bf16"
+            out.update(rows_of(oracle.scm_target(p), cfg, "st_"))
+            scm_oracle.STORAGE = None
+        np.savez_compressed(path, **out)
         print(f"{name}: {time.time() - t0:.0f} s", flush=True)
 
 
 if __name__ == "__main__":
-    main(sys.argv[1:] or ["standard", "stress", "high-res"])
+    args = sys.argv[1:]
+    storage = "--storage" in args
+    names = [a for a in args if not a.startswith("--")]
+    main(names or ["standard", "stress", "high-res"], storage)

@@ -1,0 +1,127 @@
+"""Full-size GPU parity for the three large workloads, in the launch
+configuration bench.py times.
+
+The fp64 oracle takes minutes on these shapes, so its results were written
+once by tests/golden/make_full_size_expected.py (which calls only the oracle
+and the seeded input generator): per-sample norms and losses, and J and gbar
+on a fixed random sample of rows.  The GPU run recomputes the same seeded
+inputs.  Properties that hold at any size are checked on all elements.
+
+Where stored, the oracle was also run with bf16 rounding at the points where
+the GPU path stores bf16; the gap between the two oracle runs measures how
+sensitive a sample is to that storage precision.  Wherever it is below half
+the tolerance, the GPU must match both oracle runs within the tolerance.  For
+more sensitive samples (the stress workload's small-t samples, whose
+attention is nearly one-hot because the block has no normalisation and the
+latents are scaled by 10) the GPU's gaps to both runs must stay within that
+sensitivity plus the tolerance, and are reported.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from joint_video_audio_trigflow_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TOL_FIELD = 2e-2
+TOL_LOSS = 1e-3
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+@pytest.mark.parametrize("name", ["standard", "stress", "high-res"])
+def test_full_size_target_against_stored_oracle(name):
+    from joint_video_audio_trigflow_amd import _lib
+    print(f"full-size scm_target {name}", flush=True)
+    exp = np.load(os.path.join(GOLDEN, f"expected_{name}.npz"))
+    cfg = inputs.CONFIGS[name]
+    p = inputs.make_problem(cfg)
+    assert np.array_equal(p["data"]["t"], exp["t"]), "seeded inputs differ from the stored run"
+    dev = _lib.to_device_problem(p)
+    op = _lib.ScmTarget(cfg)
+    out = op(dev["teacher"], dev["student"], dev["z0_v"], dev["z0_a"], dev["eps_v"], dev["eps_a"],
+             dev["text"], dev["text_mask"], dev["t"])
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
+    worst = {}
+    for b in range(cfg.B):
+        for m, i in (("v", 0), ("a", 1)):
+            rows = exp[f"rows_{m}"][b]
+            for key in ("J", "gbar"):
+                g = got[f"{key}_{m}"][b, rows]
+                e = rel_l2(g, exp[f"{key}_{m}"][b])
+                cond, e_st = 0.0, None
+                if f"st_{key}_{m}" in exp:
+                    # the oracle run with bf16 storage where the GPU stores bf16:
+                    # how far bf16 storage alone moves the exact result
+                    e_st = rel_l2(g, exp[f"st_{key}_{m}"][b])
+                    cond = rel_l2(exp[f"st_{key}_{m}"][b], exp[f"{key}_{m}"][b])
+                if cond <= 0.5 * TOL_FIELD:
+                    # well conditioned: bf16 storage moves the exact result by < 1e-2
+                    assert e <= TOL_FIELD, (name, b, m, key, e)
+                    if e_st is not None:
+                        assert e_st <= TOL_FIELD, (name, b, m, key, "storage oracle", e_st)
+                    worst[f"{key}_{m}"] = max(worst.get(f"{key}_{m}", 0.0), e)
+                else:
+                    # ill conditioned (near one-hot attention): one bf16 ulp can flip
+                    # the dominant key of a row, so neither oracle is reproducible to
+                    # the tolerance; the GPU must stay within the measured sensitivity
+                    assert e <= cond + TOL_FIELD, (name, b, m, key, e, cond)
+                    assert e_st <= cond + TOL_FIELD, (name, b, m, key, "storage oracle", e_st, cond)
+                    print(f"  {name} b={b} {key}_{m}: ill-conditioned: gap to exact oracle {e:.3f}, "
+                          f"to bf16-storage oracle {e_st:.3f}; storage sensitivity {cond:.3f}", flush=True)
+            n = got["norms"][b, i]
+            n_cond = abs(exp["st_norms"][b, i] / exp["norms"][b, i] - 1) if "st_norms" in exp else 0.0
+            assert abs(n - exp["norms"][b, i]) <= (TOL_FIELD + n_cond) * exp["norms"][b, i]
+            # at any size: ||gbar|| = n/(n + eps), r = -gbar, everything finite
+            gb = got[f"gbar_{m}"][b].astype(np.float64)
+            assert np.all(np.isfinite(gb)) and np.all(np.isfinite(got[f"J_{m}"][b]))
+            assert abs(np.linalg.norm(gb) - n / (n + cfg.eps_scm)) <= 1e-4
+            assert np.array_equal(got[f"r_{m}"][b], -got[f"gbar_{m}"][b])
+        assert abs(got["loss"][b] - exp["loss"][b]) <= TOL_LOSS * abs(exp["loss"][b])
+    print(name, "worst sampled rel-L2:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
+
+
+def test_attention_full_high_res_shape_sampled_queries():
+    """The standalone entry point at the high-resolution shape (16 heads, 28,928
+    queries, 29,030 valid of 29,184 keys), checked on sampled query rows."""
+    from joint_video_audio_trigflow_amd import _lib
+    print("attention high-res shape", flush=True)
+    cfg = inputs.CONFIGS["high-res"]
+    B, H, dh, Nq, Nk = 1, cfg.H, cfg.dh, cfg.Nq, cfg.N_all
+    nk = Nq + cfg.Ntv
+    ops = inputs.make_attention_operands(B, H, dh, Nq, Nk, seed=31, nk_valid=[nk], dtype=np.float32)
+    ldv = (Nk + 63) // 64 * 64
+
+    def dev(x):
+        return torch.from_numpy(x).to("cuda", torch.bfloat16).contiguous()
+
+    def devT(x):
+        vt = torch.zeros((B, H, dh, ldv), dtype=torch.bfloat16, device="cuda")
+        vt[..., :Nk] = torch.from_numpy(x).to("cuda", torch.bfloat16).permute(0, 2, 3, 1)
+        return vt
+
+    o, od, lse = _lib.joint_attn_fwd_jvp(dev(ops["q"]), dev(ops["k"]), devT(ops["v"]),
+                                        torch.tensor([nk], dtype=torch.int32, device="cuda"),
+                                        dev(ops["qd"]), dev(ops["kd"]), devT(ops["vd"]),
+                                        out_dtype=torch.bfloat16, want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(Nq, 48, replace=False))
+    rows[-1] = Nq - 1
+    eo, eod, else_ = oracle.attention_fwd_jvp(ops["q"], ops["k"], ops["v"], ops["qd"], ops["kd"],
+                                              ops["vd"], ops["nk"], query_rows=rows)
+    o = o.float().cpu().numpy()[:, rows]
+    od = od.float().cpu().numpy()[:, rows]
+    for h in range(H):
+        assert rel_l2(o[0, :, h], eo[0, :, h]) < 1e-2, h
+        assert rel_l2(od[0, :, h], eod[0, :, h]) < 1e-2, h
+    assert np.max(np.abs(lse.cpu().numpy()[:, :, rows] - else_)) < 2e-2

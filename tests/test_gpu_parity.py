@@ -120,6 +120,22 @@ def test_attention_matches_oracle(case, tangent):
     assert np.max(np.abs(lse - else_)) < 2e-2
 
 
+@pytest.mark.parametrize("qk_scale,tan_scale", [(10.0, 20.0), (4.0, 1.0)])
+def test_attention_peaked_softmax(qk_scale, tan_scale):
+    """Large logits make softmax nearly one-hot; with large tangents the JVP
+    must not lose the small result to the subtraction mu * o."""
+    B, H, dh, Nq, Nk = 1, 2, 128, 150, 700
+    say(f"attention peaked qk_scale={qk_scale} tan_scale={tan_scale}")
+    ops = inputs.make_attention_operands(B, H, dh, Nq, Nk, seed=13, nk_valid=[650], q_scale=qk_scale,
+                                         k_scale=qk_scale, tangent_scale=tan_scale)
+    o, od, lse = run_attention(ops, H, dh, True)
+    eo, eod, else_ = oracle.attention_fwd_jvp(ops["q"], ops["k"], ops["v"], ops["qd"], ops["kd"],
+                                              ops["vd"], ops["nk"])
+    for h in range(H):
+        assert rel_l2(o[0, :, h], eo[0, :, h]) < 1e-2, h
+        assert rel_l2(od[0, :, h], eod[0, :, h]) < 1e-2, (h, rel_l2(od[0, :, h], eod[0, :, h]))
+
+
 def test_attention_bf16_output_and_padding_garbage():
     """bf16 outputs; V^T columns past nk hold huge values that must not leak."""
     L = lib()
