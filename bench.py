@@ -35,6 +35,21 @@ def workload_name(cfg) -> str:
             f"teacher + student fwd+JVP")
 
 
+def counted_traffic(cfg):
+    """HBM bytes per launch of the student attention kernel, from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE runs (copy-calibrated), or None if those
+    counters were taken on another workload or on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_jvp_high_res_counters.json")
+    if cfg.name != "high-res" or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["source_files"])
+    if hashlib.sha256(src).hexdigest() != rec["kernel_source_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def attention_flops(cfg, nk_per_sample) -> float:
     """Algorithmic flops of one student attention fwd+JVP launch: 12 d Nq Nk per sample."""
     return float(sum(12.0 * cfg.d * cfg.Nq * nk for nk in nk_per_sample))
@@ -174,7 +189,7 @@ def main() -> int:
         "config": {"workload": workload_name(cfg), "global_batch": cfg.B,
                    "tokens": cfg.N_all, "valid_keys": nk, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": counted_traffic(cfg),
                      "kernel": f"attn_fwd_jvp_kernel<{cfg.dh},true>", "flops_per_launch": flops,
                      "avg_launch_ms": attn_ms},
         "phases_ms_per_step": {k: v / ncalls for k, v in phases.items()},

@@ -1,0 +1,69 @@
+"""Summarise rocprofv3 CSV output into the short text kept under profiles/.
+
+Reads a --kernel-trace --stats directory and two --pmc runs (FETCH_SIZE,
+WRITE_SIZE) of bench.py, plus the same counters for bench.py
+--copy-calibration (a plain device-to-device copy of known size), and prints
+a markdown summary with per-kernel average durations, counter values per
+dispatch, the calibration factors and the resulting HBM traffic per launch.
+Usage: python -m joint_video_audio_trigflow_amd.profile_summary <rocprof output dir>
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import json
+import os
+import sys
+
+
+def short(name: str) -> str:
+    for key, label in (("attn_fwd_jvp_kernel<128, true>", "attn_fwd_jvp<128,true> (student fwd+JVP)"),
+                       ("attn_fwd_jvp_kernel<128, false>", "attn_fwd_jvp<128,false> (teacher fwd)"),
+                       ("gemm_bf16_kernel", "gemm_bf16"),
+                       ("copyBuffer", "copyBuffer"),
+                       ("elementwise_kernel", "torch copy")):
+        if key in name:
+            return label
+    for key in ("trigflow_kernel", "text_rows_kernel", "scm_direction_kernel", "normalise_kernel",
+                "time_linear_kernel", "time_embedding_kernel", "cast_kernel"):
+        if key in name:
+            return key
+    return name[:60]
+
+
+def counters(path):
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        agg[short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def main(d):
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "trace", "*kernel_stats.csv"))[0])))
+    print("| kernel | calls | avg ms | total % |\n|---|---|---|---|")
+    for r in stats:
+        print(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | {float(r['Percentage']):.2f} |")
+    fetch = counters(glob.glob(os.path.join(d, "FETCH_SIZE", "*counter_collection.csv"))[0])
+    write = counters(glob.glob(os.path.join(d, "WRITE_SIZE", "*counter_collection.csv"))[0])
+    cf = counters(glob.glob(os.path.join(d, "copy_FETCH_SIZE", "*counter_collection.csv"))[0])
+    cw = counters(glob.glob(os.path.join(d, "copy_WRITE_SIZE", "*counter_collection.csv"))[0])
+    copy_kib = 1024 * 1024  # --copy-calibration 1024: 1 GiB read and 1 GiB written per launch
+    copy_name = next(k for k in cf if "copy" in k.lower() and cf[k] > 1000)
+    f_fac, w_fac = copy_kib / cf[copy_name], copy_kib / cw[copy_name]
+    print(f"\nCopy calibration ({copy_name}, 1 GiB): FETCH_SIZE {cf[copy_name]:.0f} KiB, "
+          f"WRITE_SIZE {cw[copy_name]:.0f} KiB per launch -> factors {f_fac:.3f} (fetch), {w_fac:.3f} (write)\n")
+    print("| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/dispatch (scaled) |\n|---|---|---|---|")
+    out = {}
+    for k in fetch:
+        if k in write:
+            b = (fetch[k] * f_fac + write[k] * w_fac) * 1024
+            out[k] = b
+            print(f"| {k} | {fetch[k]:.0f} | {write[k]:.0f} | {b / 1e9:.3f} GB |")
+    return dict(fetch_factor=f_fac, write_factor=w_fac, bytes=out, fetch=fetch, write=write)
+
+
+if __name__ == "__main__":
+    res = main(sys.argv[1])
+    if len(sys.argv) > 2:
+        json.dump(res, open(sys.argv[2], "w"), indent=1)

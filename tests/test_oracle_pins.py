@@ -315,3 +315,25 @@ def test_video_tangent_depends_on_audio(tiny_problem):
     data2["z0_a"] = data2["z0_a"] + 0.25
     r2 = oracle.scm_target(dict(p, data=data2))
     assert rel_l2(r2["J_v"], r1["J_v"]) > 1e-4
+
+
+def test_storage_rounding_mode_is_a_small_perturbation(tiny_problem):
+    """STORAGE = "bf16" only rounds stored intermediates: on a well-conditioned
+    workload it moves J by about the bf16 unit roundoff, and the default mode is
+    untouched by it."""
+    from oracle import scm_oracle
+    cfg, data = tiny_problem["cfg"], tiny_problem["data"]
+    exact = oracle.scm_sample(cfg, data, tiny_problem["teacher"], tiny_problem["student"], 0)
+    scm_oracle.STORAGE = "bf16"
+    try:
+        st = oracle.scm_sample(cfg, data, tiny_problem["teacher"], tiny_problem["student"], 0)
+    finally:
+        scm_oracle.STORAGE = None
+    again = oracle.scm_sample(cfg, data, tiny_problem["teacher"], tiny_problem["student"], 0)
+    for m in "va":
+        e = rel_l2(st[f"J_{m}"], exact[f"J_{m}"])
+        assert 1e-5 < e < 1e-2, (m, e)
+        assert np.array_equal(again[f"J_{m}"], exact[f"J_{m}"])
+    # the rounding helper is round-to-nearest-even bfloat16
+    x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -2.5])
+    assert np.array_equal(scm_oracle._bf16(x), np.array([1.0, 1 + 2 * 2.0 ** -7, -2.5]))
