@@ -51,6 +51,14 @@ class Config:
     z0_scale_a: float = 1.0
     mask_mode: str = "prefix"  # "prefix" or "scatter" (valid positions spread over the sequence)
     index: int = 0           # seed offset: data 100+index, teacher 200+index, student 300+index
+    # The joint DMD term and the stage-3 mix: guidance scales of the teacher
+    # prediction per modality (3.0 video, 5.0 audio, and equal sCM/DMD weights
+    # in the pages' training setup), the residual-scale normaliser's epsilon.
+    cfg_v: float = 3.0
+    cfg_a: float = 5.0
+    eps_dmd: float = 1e-6
+    lam_scm: float = 1.0
+    lam_dmd: float = 1.0
 
     @property
     def dh(self) -> int:
@@ -152,11 +160,12 @@ def make_data(cfg: Config) -> dict:
 
 
 def make_weights(cfg: Config, which: str) -> dict:
-    """One seeded copy of the joint block (teacher: seed 200+index, student: 300+index).
+    """One seeded copy of the joint block (teacher: seed 200+index, student:
+    300+index, the DMD fake-score block: 400+index).
 
     Draw order: w_in_v, w_in_a, w_t, w_qkv, w_out_v, w_out_a; each ~ N(0, 1/fan_in).
     """
-    seed = {"teacher": 200, "student": 300}[which] + cfg.index
+    seed = {"teacher": 200, "student": 300, "fake": 400}[which] + cfg.index
     rng = np.random.default_rng(seed)
     d = cfg.d
 
@@ -172,6 +181,37 @@ def make_problem(cfg: Config) -> dict:
     """Everything one call of the sCM target consumes."""
     return dict(cfg=cfg, data=make_data(cfg), teacher=make_weights(cfg, "teacher"),
                 student=make_weights(cfg, "student"))
+
+
+def make_dmd_data(cfg: Config) -> dict:
+    """Inputs of the joint DMD term (seed 500+index).
+
+    The student's generated paired sample x0_hat (drawn like the data latents,
+    with the same per-modality scales), fresh noise, and timesteps drawn like
+    the sCM ones.  Draw order: x0_v, x0_a, eps_v, eps_a, t.  The text and its
+    mask are the sCM batch's own (``make_data``): both terms share the batch's
+    condition.
+    """
+    rng = np.random.default_rng(500 + cfg.index)
+    x0_v = rng.standard_normal((cfg.B, cfg.Nv, cfg.Cv)) * cfg.z0_scale_v
+    x0_a = rng.standard_normal((cfg.B, cfg.Na, cfg.Ca)) * cfg.z0_scale_a
+    eps_v = rng.standard_normal((cfg.B, cfg.Nv, cfg.Cv))
+    eps_a = rng.standard_normal((cfg.B, cfg.Na, cfg.Ca))
+    t = draw_t(cfg, rng)
+    dt = cfg.in_dtype
+    return dict(x0_v=round_to(x0_v, dt), x0_a=round_to(x0_a, dt), eps_v=round_to(eps_v, dt),
+                eps_a=round_to(eps_a, dt), t=t)
+
+
+def make_dmd_problem(cfg: Config, data: dict | None = None) -> dict:
+    """Everything one call of the DMD term consumes: its own sample, noise and
+    timesteps, the sCM batch's text and mask, the teacher and the fake-score block."""
+    data = make_data(cfg) if data is None else data
+    dmd = make_dmd_data(cfg)
+    dmd["text"] = data["text"]
+    dmd["text_mask"] = data["text_mask"]
+    return dict(cfg=cfg, data=dmd, teacher=make_weights(cfg, "teacher"),
+                fake=make_weights(cfg, "fake"))
 
 
 def make_attention_operands(B: int, H: int, dh: int, Nq: int, Nk: int, seed: int,

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the joint sCM target.
+"""fp64 CPU oracle for the joint sCM target, the joint DMD term and the stage-3 mix.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py, never by the product path.
@@ -7,4 +7,7 @@ from .scm_oracle import (  # noqa: F401
     Dual, attention, attention_fwd_jvp, attention_lse, boost_factor, joint_block,
     l2_normalise, scm_direction, scm_sample, scm_target, student_field, time_embedding,
     trigflow_field, trigflow_noise,
+)
+from .dmd_oracle import (  # noqa: F401
+    dmd_sample, dmd_target, guided, residual_scale, stage3_loss, teacher_prediction,
 )
