@@ -35,17 +35,29 @@ def workload_name(cfg) -> str:
             f"teacher + student fwd+JVP")
 
 
+def attention_kernel_digest() -> str:
+    """SHA-256 of the source text the attention kernel is compiled from:
+    attention.hip, the shared types and helpers at the top of common.h, and
+    the AttnParams declaration (other kernels' declarations do not count)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "joint_video_audio_trigflow_amd", "csrc")
+    common = open(os.path.join(csrc, "common.h")).read()
+    head = common[:common.index("// Internal launchers")]
+    a = common.index("struct AttnParams")
+    params = common[a:common.index("};", a) + 2]
+    attn = open(os.path.join(csrc, "attention.hip")).read()
+    return hashlib.sha256((attn + head + params).encode()).hexdigest()
+
+
 def counted_traffic(cfg):
     """HBM bytes per launch of the student attention kernel, from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE runs (copy-calibrated), or None if those
     counters were taken on another workload or on a different kernel source."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "attn_fwd_jvp_high_res_counters.json")
     if cfg.name != "high-res" or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["source_files"])
-    if hashlib.sha256(src).hexdigest() != rec["kernel_source_sha256"]:
+    if attention_kernel_digest() != rec["kernel_source_digest"]:
         return None
     return rec["traffic_bytes_per_launch"]
 

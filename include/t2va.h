@@ -215,10 +215,74 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
                             t2va_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* Joint DMD term and the stage-3 objective                                  */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int B;        /* samples, 1..T2VA_MAX_BATCH */
+  int Nv, Na;   /* video and audio tokens per sample (>= 1) */
+  int Nt;       /* text positions per sample (>= 0) */
+  int Cv, Ca;   /* latent channels, multiples of 64 */
+  int d, H;     /* block width and heads; d = H*dh with dh in {64, 128} */
+  int in_dtype; /* dtype of x0, eps and text: T2VA_DTYPE_BF16 or T2VA_DTYPE_FP32 */
+  int weight_dtype; /* dtype of all weights (fp32 is rounded to bf16 in the workspace) */
+  double cfg_v, cfg_a; /* guidance scales of the teacher prediction per modality
+                          (finite; 1 for both skips the unconditional pass) */
+  double eps_dmd;      /* > 0, added to the residual scale */
+  double w_v, w_a;     /* modality weights of the joint loss */
+} t2va_dmd_desc;
+
+/* Exact workspace size in bytes for t2va_dmd_target (0 if the descriptor is invalid). */
+size_t t2va_dmd_workspace_bytes(const t2va_dmd_desc *desc);
+
+/*
+ * t2va_dmd_target - the joint DMD term (deep read, section 4):
+ *   z_t^m   = cos t x0^m + sin t eps^m        (x0 = the student's paired sample)
+ *   x0_T^m  = u^m + s_m (c^m - u^m)           guided teacher prediction: c = G_T(z_t, t, text),
+ *                                             u = G_T(z_t, t, no text) (every text key masked),
+ *                                             s_v = cfg_v, s_a = cfg_a
+ *   x0_F^m  = G_F(z_t, t, text)               the fake-score block
+ *   g^m     = x0_F^m - x0_T^m
+ *   c^m     = (1/(Nm*Cm)) sum_i |x0_i^m - x0_T,i^m|          residual scale
+ *   gbar^m  = g^m/(c^m + eps_dmd),  Delta^m = x0^m - sg(x0^m - gbar^m) = gbar^m (value)
+ *   loss_b  = w_v sum_i (Delta_i^v)^2 + w_a sum_i (Delta_i^a)^2   (summed, not averaged)
+ * The unconditional pass shares the conditional pass's Q, K and V (in this
+ * one-block model the video and audio rows do not depend on the text); only
+ * its attention runs again over the video and audio keys.
+ *
+ * Inputs (device):
+ *   x0_v, eps_v [B, Nv, Cv] in_dtype     x0_a, eps_a [B, Na, Ca] in_dtype
+ *   text        [B, Nt, d]  in_dtype     text_mask   uint8 [B, Nt], nonzero = valid
+ *   t_host      host double [B], each finite with 0 < t < pi/2
+ *   teacher, fake: block weights as for t2va_scm_target
+ * Outputs (device, fp32):
+ *   delta_v [B, Nv, Cv], delta_a [B, Na, Ca]    required (Delta = gbar in value)
+ *   scales  [B, 2]  (c^v, c^a)                   nullable
+ *   loss    [B]                                  required
+ * workspace: at least t2va_dmd_workspace_bytes(desc) bytes, 256-byte aligned.
+ * Errors: as t2va_scm_target, plus T2VA_INVALID_ARG for non-finite guidance
+ * scales or eps_dmd <= 0.
+ */
+t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights *teacher,
+                            const t2va_block_weights *fake, const void *x0_v, const void *x0_a,
+                            const void *eps_v, const void *eps_a, const void *text,
+                            const uint8_t *text_mask, const double *t_host, float *delta_v,
+                            float *delta_a, float *scales, float *loss, void *workspace,
+                            size_t workspace_bytes, t2va_stream stream);
+
+/*
+ * t2va_stage3_mix - out[b] = lam_scm * loss_scm[b] + lam_dmd * loss_dmd[b]
+ * (deep read, section 4.1), fp32 device arrays of B elements (in place on
+ * either input is allowed).  B in 1..T2VA_MAX_BATCH, lam finite.
+ */
+t2va_status t2va_stage3_mix(int B, double lam_scm, double lam_dmd, const float *loss_scm,
+                            const float *loss_dmd, float *out, t2va_stream stream);
+
+/* ------------------------------------------------------------------------ */
 /* Phase timing (instrumentation for benchmarks)                             */
 /* ------------------------------------------------------------------------ */
-#define T2VA_PHASE_TOTAL 0        /* whole t2va_scm_target call            */
-#define T2VA_PHASE_TEACHER_ATTN 1 /* teacher attention (forward only)      */
+#define T2VA_PHASE_TOTAL 0        /* whole t2va_scm_target / _dmd_target call */
+#define T2VA_PHASE_TEACHER_ATTN 1 /* forward-only attention (teacher, fake)   */
 #define T2VA_PHASE_STUDENT_ATTN 2 /* student attention forward + JVP       */
 #define T2VA_PHASE_GEMM 3         /* all projection GEMMs                  */
 #define T2VA_PHASE_OTHER 4        /* embedding, compaction, elementwise    */
@@ -226,7 +290,7 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
 
 /*
  * t2va_profile_enable - with max_calls > 0, the next up to max_calls calls of
- * t2va_scm_target record HIP events around each phase on their stream (the
+ * t2va_scm_target or t2va_dmd_target record HIP events around each phase on their stream (the
  * events are created here, outside the timed calls); with 0, recording stops
  * and the events are destroyed.  Not thread-safe: enable, run, read from one
  * thread.

@@ -1,6 +1,7 @@
 """ctypes binding of libt2va.so (argument marshalling only).
 
-Every step of the joint sCM target runs in the library's HIP kernels; this
+Every step of the joint sCM target and the joint DMD term runs in the
+library's HIP kernels; this
 module only turns torch tensors into device pointers, provides output and
 workspace buffers, and passes torch's current HIP stream.  It raises if the
 library has not been built: there is no fallback implementation.
@@ -50,6 +51,14 @@ class ScmDesc(ctypes.Structure):
                 ("w_v", ctypes.c_double), ("w_a", ctypes.c_double)]
 
 
+class DmdDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("Nv", ctypes.c_int), ("Na", ctypes.c_int), ("Nt", ctypes.c_int),
+                ("Cv", ctypes.c_int), ("Ca", ctypes.c_int), ("d", ctypes.c_int), ("H", ctypes.c_int),
+                ("in_dtype", ctypes.c_int), ("weight_dtype", ctypes.c_int),
+                ("cfg_v", ctypes.c_double), ("cfg_a", ctypes.c_double), ("eps_dmd", ctypes.c_double),
+                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double)]
+
+
 class BlockWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_in_v", "w_in_a", "w_t", "w_qkv", "w_out_v", "w_out_a")]
 
@@ -81,6 +90,14 @@ def load() -> ctypes.CDLL:
     lib.t2va_scm_target.argtypes = ([ctypes.POINTER(ScmDesc), ctypes.POINTER(BlockWeights),
                                      ctypes.POINTER(BlockWeights)] + [vp] * 5 + [vp, dp]
                                     + [f32p] * 8 + [vp, ctypes.c_size_t, vp])
+    lib.t2va_dmd_workspace_bytes.restype = ctypes.c_size_t
+    lib.t2va_dmd_workspace_bytes.argtypes = [ctypes.POINTER(DmdDesc)]
+    lib.t2va_dmd_target.restype = i32
+    lib.t2va_dmd_target.argtypes = ([ctypes.POINTER(DmdDesc), ctypes.POINTER(BlockWeights),
+                                     ctypes.POINTER(BlockWeights)] + [vp] * 5 + [vp, dp]
+                                    + [f32p] * 4 + [vp, ctypes.c_size_t, vp])
+    lib.t2va_stage3_mix.restype = i32
+    lib.t2va_stage3_mix.argtypes = [i32, ctypes.c_double, ctypes.c_double, f32p, f32p, f32p, vp]
     lib.t2va_profile_enable.restype = i32
     lib.t2va_profile_enable.argtypes = [i32]
     lib.t2va_profile_read.restype = i32
@@ -236,6 +253,68 @@ class ScmTarget:
         return o
 
 
+def dmd_desc(cfg, in_dtype: int, weight_dtype: int, cfg_v=None, cfg_a=None) -> DmdDesc:
+    d = DmdDesc()
+    d.B, d.Nv, d.Na, d.Nt = cfg.B, cfg.Nv, cfg.Na, cfg.Nt
+    d.Cv, d.Ca, d.d, d.H = cfg.Cv, cfg.Ca, cfg.d, cfg.H
+    d.in_dtype, d.weight_dtype = in_dtype, weight_dtype
+    d.cfg_v = cfg.cfg_v if cfg_v is None else cfg_v
+    d.cfg_a = cfg.cfg_a if cfg_a is None else cfg_a
+    d.eps_dmd, d.w_v, d.w_a = cfg.eps_dmd, cfg.w_v, cfg.w_a
+    return d
+
+
+def dmd_workspace_bytes(desc: DmdDesc) -> int:
+    n = load().t2va_dmd_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        raise T2VAError(1, load().t2va_last_error().decode())
+    return n
+
+
+class DmdTarget:
+    """Holds device buffers for repeated calls of t2va_dmd_target on one shape."""
+
+    def __init__(self, cfg, device="cuda", in_dtype=DTYPE_BF16, weight_dtype=DTYPE_BF16,
+                 cfg_v=None, cfg_a=None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.desc = dmd_desc(cfg, in_dtype, weight_dtype, cfg_v, cfg_a)
+        self.ws_bytes = dmd_workspace_bytes(self.desc)
+        self.workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.workspace.data_ptr()
+        self.ws_ptr = ctypes.c_void_p((base + 255) // 256 * 256)
+        B = cfg.B
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.out = {
+            "delta_v": torch.empty((B, cfg.Nv, cfg.Cv), **f32),
+            "delta_a": torch.empty((B, cfg.Na, cfg.Ca), **f32),
+            "scales": torch.empty((B, 2), **f32),
+            "loss": torch.empty((B,), **f32),
+        }
+
+    def __call__(self, teacher: dict, fake: dict, x0_v, x0_a, eps_v, eps_a, text, text_mask, t):
+        lib = load()
+        tw, fw = ScmTarget.weights_struct(teacher), ScmTarget.weights_struct(fake)
+        o = self.out
+        th = _t_host(t)
+        _check(lib.t2va_dmd_target(
+            ctypes.byref(self.desc), ctypes.byref(tw), ctypes.byref(fw), _ptr(x0_v), _ptr(x0_a),
+            _ptr(eps_v), _ptr(eps_a), _ptr(text), _ptr(text_mask), th,
+            _ptr(o["delta_v"]), _ptr(o["delta_a"]), _ptr(o["scales"]), _ptr(o["loss"]),
+            self.ws_ptr, self.ws_bytes, _stream(self.device)))
+        return o
+
+
+def stage3_mix(loss_scm: torch.Tensor, loss_dmd: torch.Tensor, lam_scm: float, lam_dmd: float,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """lam_scm * loss_scm + lam_dmd * loss_dmd per sample (fp32 device vectors)."""
+    if out is None:
+        out = torch.empty_like(loss_scm)
+    _check(load().t2va_stage3_mix(loss_scm.numel(), lam_scm, lam_dmd, _ptr(loss_scm), _ptr(loss_dmd),
+                                  _ptr(out), _stream(loss_scm.device)))
+    return out
+
+
 def profile_enable(max_calls: int):
     _check(load().t2va_profile_enable(max_calls))
 
@@ -259,5 +338,21 @@ def to_device_problem(problem: dict, device="cuda"):
     out["text_mask"] = torch.from_numpy(data["text_mask"]).to(device)
     out["t"] = [float(x) for x in data["t"]]
     for which in ("teacher", "student"):
+        out[which] = {k: dev(v, tdt) for k, v in problem[which].items()}
+    return out
+
+
+def to_device_dmd_problem(problem: dict, device="cuda"):
+    """Seeded numpy DMD problem -> device tensors in the dtypes the library consumes."""
+    cfg, data = problem["cfg"], problem["data"]
+    tdt = torch.bfloat16 if cfg.in_dtype == "bf16" else torch.float32
+
+    def dev(x, dt):
+        return torch.from_numpy(x.astype("float32")).to(device=device, dtype=dt).contiguous()
+
+    out = {k: dev(data[k], tdt) for k in ("x0_v", "x0_a", "eps_v", "eps_a", "text")}
+    out["text_mask"] = torch.from_numpy(data["text_mask"]).to(device)
+    out["t"] = [float(x) for x in data["t"]]
+    for which in ("teacher", "fake"):
         out[which] = {k: dev(v, tdt) for k, v in problem[which].items()}
     return out

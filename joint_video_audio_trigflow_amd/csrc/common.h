@@ -113,11 +113,34 @@ struct GParams {
 };
 hipError_t launch_scm_direction(const CoefTable &coef, const GParams &p, hipStream_t s);
 
-// gbar = g/(n + eps) in place, r = -gbar, norms, loss.
+// DMD direction g = x0_F - x0_T with the guided teacher prediction
+// x0_T = u + s (c - u) (c only when u is null), and per-block partial sums of
+// |x0 - x0_T| and of g^2 for both modalities.
+struct DmdParams {
+  const void *x0[2];
+  const float *tc[2], *tu[2], *fk[2];  // conditional / unconditional teacher, fake; tu nullable
+  int64_t x_bs[2];     // batch stride (elements) of tc/tu/fk
+  float scale[2];      // guidance scale per modality
+  float *g[2];         // g (later normalised in place)
+  float *part_abs[2];  // [B, nblk[m]]
+  float *part_sq[2];   // [B, nblk[m]]
+  int64_t n[2];
+  int nblk[2];
+  int in_dt;
+};
+hipError_t launch_dmd_direction(int B, const DmdParams &p, hipStream_t s);
+
+// Normalisation in place with the loss.
+//   mode 0 (sCM): n = sqrt(sum partial), g /= n + eps, r = -g, norms = n,
+//                 loss = sum_m w_m n_m^2/(n_m + eps)^2
+//   mode 1 (DMD): c = (sum partial)/n_elems, g /= c + eps, norms = c,
+//                 loss = sum_m w_m (sum partial2)/(c_m + eps)^2
 struct NormParams {
+  int mode;
   float *g[2];
   float *r[2];        // nullable
   const float *partial[2];
+  const float *partial2[2];  // mode 1: partial sums of g^2
   int64_t n[2];
   int nblk[2];
   float *norms;       // nullable [B, 2]
@@ -125,6 +148,10 @@ struct NormParams {
   double eps, w[2];
 };
 hipError_t launch_normalise(int B, const NormParams &p, hipStream_t s);
+
+// out[b] = a * x[b] + c * y[b] for b < B.
+hipError_t launch_mix(int B, float a, const float *x, float c, const float *y, float *out,
+                      hipStream_t s);
 
 // C = A W^T (+ bias) for `batch` independent problems.
 struct GemmParams {

@@ -1,11 +1,14 @@
-// HBM-bound kernels of the joint sCM target: TrigFlow noising and fields,
-// the sinusoidal time embedding, text-key compaction, the sCM direction with
-// its per-block sums of squares, and the L2 normalisation with the loss.
+// HBM-bound kernels of the joint sCM target and the joint DMD term: TrigFlow
+// noising and fields, the sinusoidal time embedding, text-key compaction, the
+// sCM direction with its per-block sums of squares, the guided DMD direction
+// with its per-block sums, and the normalisations with the losses.
 //
 // Method: TurboT2VA deep read (robotworld.top, arXiv 2608.24674), section 3
 // (noising) and section 3.1 (fields, joint JVP, sCM direction, per-sample
-// per-modality L2 normalisation, residual, joint loss); section 6.3 (padded
-// text positions are removed before attention).
+// per-modality L2 normalisation, residual, joint loss); section 4 (DMD
+// direction with a guided teacher, residual-scale normaliser, summed loss),
+// 4.1 (stage-3 mix); section 6.3 (padded text positions are removed before
+// attention).
 #include "common.h"
 
 namespace t2va {
@@ -253,30 +256,78 @@ __global__ __launch_bounds__(kThreads) void scm_direction_kernel(CoefTable coef,
   if (threadIdx.x == 0) p.partial[m][(int64_t)bi * p.nblk[m] + cb] = tot;
 }
 
+// Guided teacher prediction, DMD direction g = x0_F - x0_T, and per-block sums
+// of |x0 - x0_T| (the residual scale's numerator) and of g^2.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dmd_direction_kernel(int B, DmdParams p) {
+  __shared__ float red[kThreads / 64];
+  int blk = blockIdx.x;
+  const int m = (blk >= B * p.nblk[0]) ? 1 : 0;
+  if (m) blk -= B * p.nblk[0];
+  const int bi = blk / p.nblk[m], cb = blk % p.nblk[m];
+  const int64_t n = p.n[m];
+  const int64_t off = (int64_t)bi * n;
+  const int64_t xo = (int64_t)bi * p.x_bs[m];
+  const int64_t i0 = (int64_t)cb * kChunk + threadIdx.x * kPerThread;
+  float sa = 0.f, ss = 0.f;
+  if (i0 < n) {  // n is a multiple of 64: whole 8-element groups
+    float x0[8], tc[8], tu[8], fk[8], g[8];
+    load8((const T *)p.x0[m] + off + i0, x0);
+    load8(p.tc[m] + xo + i0, tc);
+    load8(p.fk[m] + xo + i0, fk);
+    if (p.tu[m]) {
+      load8(p.tu[m] + xo + i0, tu);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tc[j] = tu[j] + p.scale[m] * (tc[j] - tu[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      g[j] = fk[j] - tc[j];
+      sa += fabsf(x0[j] - tc[j]);
+      ss += g[j] * g[j];
+    }
+    store8(p.g[m] + off + i0, g);
+  }
+  const float ta = block_sum(sa, red);
+  const float ts = block_sum(ss, red);
+  if (threadIdx.x == 0) {
+    p.part_abs[m][(int64_t)bi * p.nblk[m] + cb] = ta;
+    p.part_sq[m][(int64_t)bi * p.nblk[m] + cb] = ts;
+  }
+}
+
+__device__ __forceinline__ double sum_partials(const float *pp, int nblk, double *red) {
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < nblk; i += kThreads) acc += (double)pp[i];
+  return block_sum(acc, red);
+}
+
 __global__ __launch_bounds__(kThreads) void normalise_kernel(int B, NormParams p) {
   __shared__ double red[kThreads / 64];
   int blk = blockIdx.x;
   const int m = (blk >= B * p.nblk[0]) ? 1 : 0;
   if (m) blk -= B * p.nblk[0];
   const int bi = blk / p.nblk[m], cb = blk % p.nblk[m];
-  double S[2];
+  double S[2], Q[2], scl[2];
 #pragma unroll
   for (int mm = 0; mm < 2; ++mm) {
-    double acc = 0.0;
-    const float *pp = p.partial[mm] + (int64_t)bi * p.nblk[mm];
-    for (int i = threadIdx.x; i < p.nblk[mm]; i += kThreads) acc += (double)pp[i];
-    S[mm] = block_sum(acc, red);
-  }
-  const double nrm = sqrt(S[m]);
-  const float inv = (float)(1.0 / (nrm + p.eps));
-  if (m == 0 && cb == 0 && threadIdx.x == 0) {
-    const double n0 = sqrt(S[0]), n1 = sqrt(S[1]);
-    if (p.norms) {
-      p.norms[2 * bi] = (float)n0;
-      p.norms[2 * bi + 1] = (float)n1;
+    S[mm] = sum_partials(p.partial[mm] + (int64_t)bi * p.nblk[mm], p.nblk[mm], red);
+    if (p.mode == 0) {
+      Q[mm] = S[mm];
+      scl[mm] = sqrt(S[mm]);
+    } else {
+      Q[mm] = sum_partials(p.partial2[mm] + (int64_t)bi * p.nblk[mm], p.nblk[mm], red);
+      scl[mm] = S[mm] / (double)p.n[mm];
     }
-    p.loss[bi] = (float)(p.w[0] * S[0] / ((n0 + p.eps) * (n0 + p.eps)) +
-                         p.w[1] * S[1] / ((n1 + p.eps) * (n1 + p.eps)));
+  }
+  const float inv = (float)(1.0 / (scl[m] + p.eps));
+  if (m == 0 && cb == 0 && threadIdx.x == 0) {
+    if (p.norms) {
+      p.norms[2 * bi] = (float)scl[0];
+      p.norms[2 * bi + 1] = (float)scl[1];
+    }
+    p.loss[bi] = (float)(p.w[0] * Q[0] / ((scl[0] + p.eps) * (scl[0] + p.eps)) +
+                         p.w[1] * Q[1] / ((scl[1] + p.eps) * (scl[1] + p.eps)));
   }
   const int64_t n = p.n[m];
   const int64_t i0 = (int64_t)cb * kChunk + threadIdx.x * kPerThread;
@@ -359,6 +410,28 @@ hipError_t launch_scm_direction(const CoefTable &coef, const GParams &p, hipStre
     hipLaunchKernelGGL(scm_direction_kernel<bf16>, dim3(blocks), dim3(kThreads), 0, s, coef, p);
   else
     hipLaunchKernelGGL(scm_direction_kernel<float>, dim3(blocks), dim3(kThreads), 0, s, coef, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dmd_direction(int B, const DmdParams &p, hipStream_t s) {
+  const unsigned blocks = (unsigned)(B * (p.nblk[0] + p.nblk[1]));
+  if (p.in_dt == 0)
+    hipLaunchKernelGGL(dmd_direction_kernel<bf16>, dim3(blocks), dim3(kThreads), 0, s, B, p);
+  else
+    hipLaunchKernelGGL(dmd_direction_kernel<float>, dim3(blocks), dim3(kThreads), 0, s, B, p);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ void mix_kernel(int B, float a, const float *x, float c, const float *y, float *out) {
+  const int i = threadIdx.x;
+  if (i < B) out[i] = a * x[i] + c * y[i];
+}
+}  // namespace
+
+hipError_t launch_mix(int B, float a, const float *x, float c, const float *y, float *out,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(mix_kernel, dim3(1), dim3(64), 0, s, B, a, x, c, y, out);
   return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
-// Host side of libt2va: argument validation, workspace layout, the launch
-// sequence of the joint sCM target, and phase timing.
+// Host side of libt2va: argument validation, workspace layouts, the launch
+// sequences of the joint sCM target and the joint DMD term, and phase timing.
 //
 // Method: TurboT2VA deep read (robotworld.top, arXiv 2608.24674), sections 3
-// and 3.1; the block G and its JVP as described in t2va.h.
+// and 3.1 (sCM), 4 and 4.1 (DMD, stage-3 mix); the block G and its JVP as
+// described in t2va.h.
 #include "../../include/t2va.h"
 #include "common.h"
 
@@ -81,6 +82,55 @@ CoefTable make_coef(int B, const double *t_host, double beta, double gamma) {
   return c;
 }
 
+t2va_status check_shape(int B, int Nv, int Na, int Nt, int Cv, int Ca, int d, int H, int in_dt,
+                        int w_dt) {
+  if (B < 1 || B > T2VA_MAX_BATCH)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "B = %d outside [1, %d]", B, T2VA_MAX_BATCH);
+  if (Nv < 1 || Na < 1 || Nt < 0)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "need Nv >= 1, Na >= 1, Nt >= 0 (got %d, %d, %d)", Nv, Na, Nt);
+  if (Cv < 64 || Cv % 64 || Ca < 64 || Ca % 64)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "Cv = %d and Ca = %d must be positive multiples of 64", Cv, Ca);
+  if (H < 1 || d < 1 || d % H)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "d = %d is not a multiple of H = %d", d, H);
+  const int dh = d / H;
+  if (dh != 64 && dh != 128)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "head dim d/H = %d must be 64 or 128", dh);
+  if (!valid_dtype(in_dt) || !valid_dtype(w_dt))
+    return fail(T2VA_INVALID_ARG, "in_dtype / weight_dtype must be T2VA_DTYPE_BF16 or _FP32");
+  return T2VA_OK;
+}
+
+// Element counts of the six weights of one block, in t2va_block_weights order.
+void block_weight_elems(int Cv, int Ca, int d, size_t *n) {
+  const size_t D = d;
+  n[0] = D * Cv;
+  n[1] = D * Ca;
+  n[2] = D * D;
+  n[3] = 3 * D * D;
+  n[4] = (size_t)Cv * D;
+  n[5] = (size_t)Ca * D;
+}
+
+// bf16 views of `count` blocks' weights: fp32 weights are rounded into dst
+// (one after another, 128-element aligned), bf16 weights are used in place.
+hipError_t prepare_weights(const t2va_block_weights *const *wb, int count, int weight_dtype,
+                           const size_t *elems, bf16 *dst, const bf16 *W[][6], hipStream_t s) {
+  for (int i = 0; i < count; ++i) {
+    const void *src[6] = {wb[i]->w_in_v, wb[i]->w_in_a, wb[i]->w_t, wb[i]->w_qkv, wb[i]->w_out_v, wb[i]->w_out_a};
+    for (int j = 0; j < 6; ++j) {
+      if (weight_dtype == T2VA_DTYPE_FP32) {
+        hipError_t e = launch_cast_bf16((const float *)src[j], dst, (int64_t)elems[j], s);
+        if (e != hipSuccess) return e;
+        W[i][j] = dst;
+        dst += align_up(elems[j], 128);
+      } else {
+        W[i][j] = (const bf16 *)src[j];
+      }
+    }
+  }
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------------------------
 // Workspace layout of t2va_scm_target.
 // ---------------------------------------------------------------------------
@@ -100,12 +150,7 @@ Layout make_layout(const t2va_scm_desc &d) {
   L.nblk_v = elementwise_blocks((int64_t)d.Nv * d.Cv);
   L.nblk_a = elementwise_blocks((int64_t)d.Na * d.Ca);
   const size_t B = d.B, D = d.d;
-  L.w_elems[0] = D * d.Cv;
-  L.w_elems[1] = D * d.Ca;
-  L.w_elems[2] = D * D;
-  L.w_elems[3] = 3 * D * D;
-  L.w_elems[4] = (size_t)d.Cv * D;
-  L.w_elems[5] = (size_t)d.Ca * D;
+  block_weight_elems(d.Cv, d.Ca, d.d, L.w_elems);
   size_t wcount = 0;
   for (int i = 0; i < 6; ++i) wcount += align_up(L.w_elems[i], 128);
   size_t off = 0;
@@ -136,27 +181,90 @@ Layout make_layout(const t2va_scm_desc &d) {
 
 t2va_status check_desc(const t2va_scm_desc *d) {
   if (!d) return fail(T2VA_INVALID_ARG, "desc is NULL");
-  if (d->B < 1 || d->B > T2VA_MAX_BATCH)
-    return fail(T2VA_UNSUPPORTED_SHAPE, "B = %d outside [1, %d]", d->B, T2VA_MAX_BATCH);
-  if (d->Nv < 1 || d->Na < 1 || d->Nt < 0)
-    return fail(T2VA_UNSUPPORTED_SHAPE, "need Nv >= 1, Na >= 1, Nt >= 0 (got %d, %d, %d)", d->Nv,
-                d->Na, d->Nt);
-  if (d->Cv < 64 || d->Cv % 64 || d->Ca < 64 || d->Ca % 64)
-    return fail(T2VA_UNSUPPORTED_SHAPE, "Cv = %d and Ca = %d must be positive multiples of 64",
-                d->Cv, d->Ca);
-  if (d->H < 1 || d->d < 1 || d->d % d->H)
-    return fail(T2VA_UNSUPPORTED_SHAPE, "d = %d is not a multiple of H = %d", d->d, d->H);
-  const int dh = d->d / d->H;
-  if (dh != 64 && dh != 128)
-    return fail(T2VA_UNSUPPORTED_SHAPE, "head dim d/H = %d must be 64 or 128", dh);
-  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->weight_dtype))
-    return fail(T2VA_INVALID_ARG, "in_dtype / weight_dtype must be T2VA_DTYPE_BF16 or _FP32");
+  if (t2va_status st = check_shape(d->B, d->Nv, d->Na, d->Nt, d->Cv, d->Ca, d->d, d->H,
+                                   d->in_dtype, d->weight_dtype))
+    return st;
   if (!(d->gamma >= 0.0 && d->gamma <= 1.0))
     return fail(T2VA_INVALID_ARG, "gamma = %g outside [0, 1]", d->gamma);
   if (!(d->eps_scm > 0.0) || !isfinite(d->eps_scm))
     return fail(T2VA_INVALID_ARG, "eps_scm = %g must be positive and finite", d->eps_scm);
   if (!isfinite(d->beta) || !isfinite(d->w_v) || !isfinite(d->w_a))
     return fail(T2VA_INVALID_ARG, "beta, w_v and w_a must be finite");
+  return T2VA_OK;
+}
+
+t2va_status check_weights(const t2va_block_weights *const *wb, int n, const char *name0,
+                          const char *name1) {
+  for (int i = 0; i < n; ++i) {
+    const char *name = i ? name1 : name0;
+    if (!wb[i]) return fail(T2VA_INVALID_ARG, "%s weights are NULL", name);
+    const void *w[6] = {wb[i]->w_in_v, wb[i]->w_in_a, wb[i]->w_t, wb[i]->w_qkv, wb[i]->w_out_v, wb[i]->w_out_a};
+    for (const void *p : w) {
+      if (!p) return fail(T2VA_INVALID_ARG, "%s weight pointer is NULL", name);
+      if (!aligned16(p)) return fail(T2VA_INVALID_ARG, "weights must be 16-byte aligned");
+    }
+  }
+  return T2VA_OK;
+}
+
+// Workspace layout of t2va_dmd_target.
+struct DmdLayout {
+  int ldv, nblk_v, nblk_a;
+  size_t wts, zv, za, E, tau, X, QK, VT, nk, nk_null, O, xT_v, xT_a, xF_v, xF_a, pa_v, pa_a, ps_v, ps_a;
+  size_t total;
+  size_t w_elems[6];
+};
+
+DmdLayout make_dmd_layout(const t2va_dmd_desc &d) {
+  DmdLayout L;
+  const int Nq = d.Nv + d.Na, N_all = Nq + d.Nt;
+  L.ldv = (int)align_up((size_t)N_all, 64);
+  L.nblk_v = elementwise_blocks((int64_t)d.Nv * d.Cv);
+  L.nblk_a = elementwise_blocks((int64_t)d.Na * d.Ca);
+  const size_t B = d.B, D = d.d;
+  const size_t nv = (size_t)d.Nv * d.Cv, na = (size_t)d.Na * d.Ca;
+  block_weight_elems(d.Cv, d.Ca, d.d, L.w_elems);
+  size_t wcount = 0;
+  for (int i = 0; i < 6; ++i) wcount += align_up(L.w_elems[i], 128);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
+  L.zv = take(B * nv * sizeof(bf16));
+  L.za = take(B * na * sizeof(bf16));
+  L.E = take(2 * B * D * sizeof(float));
+  L.tau = take(B * D * sizeof(float));
+  L.X = take(B * N_all * D * sizeof(bf16));
+  L.QK = take(B * N_all * 2 * D * sizeof(bf16));
+  L.VT = take(B * D * (size_t)L.ldv * sizeof(bf16));
+  L.nk = take(B * sizeof(int32_t));
+  L.nk_null = take(B * sizeof(int32_t));
+  L.O = take(2 * B * Nq * D * sizeof(bf16));
+  L.xT_v = take(2 * B * nv * sizeof(float));
+  L.xT_a = take(2 * B * na * sizeof(float));
+  L.xF_v = take(B * nv * sizeof(float));
+  L.xF_a = take(B * na * sizeof(float));
+  L.pa_v = take(B * L.nblk_v * sizeof(float));
+  L.pa_a = take(B * L.nblk_a * sizeof(float));
+  L.ps_v = take(B * L.nblk_v * sizeof(float));
+  L.ps_a = take(B * L.nblk_a * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+t2va_status check_dmd_desc(const t2va_dmd_desc *d) {
+  if (!d) return fail(T2VA_INVALID_ARG, "desc is NULL");
+  if (t2va_status st = check_shape(d->B, d->Nv, d->Na, d->Nt, d->Cv, d->Ca, d->d, d->H,
+                                   d->in_dtype, d->weight_dtype))
+    return st;
+  if (!isfinite(d->cfg_v) || !isfinite(d->cfg_a))
+    return fail(T2VA_INVALID_ARG, "guidance scales must be finite");
+  if (!(d->eps_dmd > 0.0) || !isfinite(d->eps_dmd))
+    return fail(T2VA_INVALID_ARG, "eps_dmd = %g must be positive and finite", d->eps_dmd);
+  if (!isfinite(d->w_v) || !isfinite(d->w_a)) return fail(T2VA_INVALID_ARG, "w_v and w_a must be finite");
   return T2VA_OK;
 }
 
@@ -191,6 +299,89 @@ struct PhaseScope {
       hipEventRecord(b, s);
       g_prof.recs.push_back({phase, a, b});
     }
+  }
+};
+
+// The steps of one joint block on the caller's stream: the per-modality input
+// projections (+ tau) and the fused QKV projection, attention, and the
+// per-modality output projections.  `batch` stacks independent problems that
+// share the weights (primal and tangent rows, or conditional and
+// unconditional outputs).
+struct Block {
+  int B, Nv, Na, Cv, Ca, D, H, dh, Nq, NA, ldv;
+  int64_t nv, na, x_bs, qk_bs, vt_hs, vt_bs, o_bs;
+  hipStream_t s;
+  bool prof;
+
+  Block(int B_, int Nv_, int Na_, int Nt, int Cv_, int Ca_, int d, int H_, int ldv_, hipStream_t s_,
+        bool prof_)
+      : B(B_), Nv(Nv_), Na(Na_), Cv(Cv_), Ca(Ca_), D(d), H(H_), dh(d / H_), Nq(Nv_ + Na_),
+        NA(Nv_ + Na_ + Nt), ldv(ldv_), s(s_), prof(prof_) {
+    nv = (int64_t)Nv * Cv;
+    na = (int64_t)Na * Ca;
+    x_bs = (int64_t)NA * D;
+    qk_bs = (int64_t)NA * 2 * D;
+    vt_hs = (int64_t)dh * ldv;
+    vt_bs = (int64_t)H * vt_hs;
+    o_bs = (int64_t)Nq * D;
+  }
+
+  t2va_status gemm(const bf16 *A, int64_t lda, int64_t a_bs, const bf16 *Wt, int64_t ldw, void *Cp,
+                   int64_t ldc, int64_t c_bs, int c_dt, const float *bias, int64_t bias_bs, int M,
+                   int N, int K, int batch, bf16 *vt, int n_split) const {
+    GemmParams g;
+    g.A = A; g.lda = lda; g.a_bs = a_bs;
+    g.W = Wt; g.ldw = ldw;
+    g.C = Cp; g.ldc = ldc; g.c_bs = c_bs; g.c_dt = c_dt;
+    g.bias = bias; g.bias_bs = bias_bs;
+    g.VT = vt; g.vt_bs = vt_bs; g.vt_hs = vt_hs; g.vt_rs = ldv; g.vt_rows = ldv;
+    g.n_split = n_split; g.dh = dh;
+    g.M = M; g.N = N; g.K = K; g.batch = batch;
+    PhaseScope ps(s, T2VA_PHASE_GEMM, prof);
+    HIP_TRY(launch_gemm(g, s), "gemm");
+    return T2VA_OK;
+  }
+
+  // X rows [0, Nq) = [z^v W_in_v^T; z^a W_in_a^T] + tau[b]; then Q|K row-major
+  // into QK and V dh-major into VT, for `batch` problems.
+  t2va_status project_in(const bf16 *const *W, const bf16 *zv, const bf16 *za, const float *tau,
+                         bf16 *X, bf16 *QK, bf16 *VT, int batch) const {
+    if (t2va_status st = gemm(zv, Cv, nv, W[0], Cv, X, D, x_bs, 0, tau, D, Nv, D, Cv, batch, nullptr, D))
+      return st;
+    if (t2va_status st = gemm(za, Ca, na, W[1], Ca, X + (int64_t)Nv * D, D, x_bs, 0, tau, D, Na, D,
+                              Ca, batch, nullptr, D))
+      return st;
+    return gemm(X, D, x_bs, W[3], D, QK, 2 * D, qk_bs, 0, nullptr, 0, NA, 3 * D, D, batch, VT, 2 * D);
+  }
+
+  // O [batch, Nq, D] -> fp32 x0^v [batch, Nv, Cv] and x0^a [batch, Na, Ca].
+  t2va_status project_out(const bf16 *const *W, const bf16 *O, float *xv, float *xa, int batch) const {
+    if (t2va_status st = gemm(O, D, o_bs, W[4], D, xv, Cv, nv, 1, nullptr, 0, Nv, Cv, D, batch, nullptr, Cv))
+      return st;
+    return gemm(O + (int64_t)Nv * D, D, o_bs, W[5], D, xa, Ca, na, 1, nullptr, 0, Na, Ca, D, batch,
+                nullptr, Ca);
+  }
+
+  // Attention of the B problems in QK/VT over nk[b] keys into O; with `tan`,
+  // the tangent operands are the batches that follow (QK + B qk_bs, VT + B
+  // vt_bs) and the tangent output goes to O + B o_bs.
+  t2va_status attention(const bf16 *QK, const bf16 *VT, const int32_t *nk, bf16 *O, bool tan,
+                        int phase) const {
+    AttnParams p;
+    p.q = QK; p.k = QK + D; p.vt = VT;
+    p.qd = tan ? QK + (int64_t)B * qk_bs : nullptr;
+    p.kd = tan ? QK + (int64_t)B * qk_bs + D : nullptr;
+    p.vdt = tan ? VT + (int64_t)B * vt_bs : nullptr;
+    p.nk = nk; p.o = O; p.od = tan ? O + (int64_t)B * o_bs : nullptr; p.lse = nullptr;
+    p.q_bs = qk_bs; p.q_rs = 2 * D; p.k_bs = qk_bs; p.k_rs = 2 * D;
+    p.vt_bs = vt_bs; p.vt_hs = vt_hs; p.vt_rs = ldv;
+    p.o_bs = o_bs; p.o_rs = D;
+    p.B = B; p.H = H; p.Nq = Nq; p.Nk = NA;
+    p.out_dt = T2VA_DTYPE_BF16;
+    p.scale = (float)(1.0 / sqrt((double)dh));
+    PhaseScope ps(s, phase, prof);
+    HIP_TRY(launch_attention(dh, tan, p, s), "attention");
+    return T2VA_OK;
   }
 };
 
@@ -325,15 +516,8 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
   if (t2va_status st = check_desc(desc)) return st;
   const t2va_scm_desc &d = *desc;
   if (t2va_status st = check_t(d.B, t_host)) return st;
-  if (!teacher || !student) return fail(T2VA_INVALID_ARG, "weights are NULL");
   const t2va_block_weights *wb[2] = {teacher, student};
-  for (int i = 0; i < 2; ++i) {
-    const void *w[6] = {wb[i]->w_in_v, wb[i]->w_in_a, wb[i]->w_t, wb[i]->w_qkv, wb[i]->w_out_v, wb[i]->w_out_a};
-    for (const void *p : w) {
-      if (!p) return fail(T2VA_INVALID_ARG, "%s weight pointer is NULL", i ? "student" : "teacher");
-      if (!aligned16(p)) return fail(T2VA_INVALID_ARG, "weights must be 16-byte aligned");
-    }
-  }
+  if (t2va_status st = check_weights(wb, 2, "teacher", "student")) return st;
   const void *req[] = {z0_v, z0_a, eps_v, eps_a, gbar_v, gbar_a, loss};
   for (const void *p : req)
     if (!p) return fail(T2VA_INVALID_ARG, "z0, eps, gbar and loss pointers are required");
@@ -355,27 +539,13 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
   PhaseScope total(s, T2VA_PHASE_TOTAL, prof);
 
   char *ws = (char *)workspace;
-  const int B = d.B, D = d.d, H = d.H, dh = L.dh, Nq = L.Nq, NA = L.N_all;
-  const int64_t nv = (int64_t)d.Nv * d.Cv, na = (int64_t)d.Na * d.Ca;
+  const Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
+  const int B = d.B, D = d.d, Nq = L.Nq;
+  const int64_t nv = blk.nv, na = blk.na;
   const CoefTable coef = make_coef(B, t_host, d.beta, d.gamma);
 
-  // Weights as bf16.
   const bf16 *W[2][6];
-  {
-    bf16 *wdst = (bf16 *)(ws + L.wts);
-    for (int i = 0; i < 2; ++i) {
-      const void *src[6] = {wb[i]->w_in_v, wb[i]->w_in_a, wb[i]->w_t, wb[i]->w_qkv, wb[i]->w_out_v, wb[i]->w_out_a};
-      for (int j = 0; j < 6; ++j) {
-        if (d.weight_dtype == T2VA_DTYPE_FP32) {
-          HIP_TRY(launch_cast_bf16((const float *)src[j], wdst, (int64_t)L.w_elems[j], s), "cast");
-          W[i][j] = wdst;
-          wdst += align_up(L.w_elems[j], 128);
-        } else {
-          W[i][j] = (const bf16 *)src[j];
-        }
-      }
-    }
-  }
+  HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
   float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
@@ -386,69 +556,24 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
   float *x0S_v = (float *)(ws + L.x0S_v), *x0S_a = (float *)(ws + L.x0S_a);
   float *part_v = (float *)(ws + L.part_v), *part_a = (float *)(ws + L.part_a);
 
-  const int64_t x_bs = (int64_t)NA * D;       // X rows per sample
-  const int64_t qk_bs = (int64_t)NA * 2 * D;  // fused Q|K rows per sample
-  const int64_t vt_hs = (int64_t)dh * L.ldv, vt_bs = (int64_t)H * vt_hs;
-  const int64_t o_bs = (int64_t)Nq * D;
-
   // z_t = cos t z0 + sin t eps (bf16 GEMM input), half 0 of zv / za.
-  {
-    PhaseScope ps(s, T2VA_PHASE_OTHER, false);
-    HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v,
-                            nullptr, zv, nv, nv, 0, nv, s), "noise");
-    HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a,
-                            nullptr, za, na, na, 0, na, s), "noise");
-    HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
-    HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
-    if (d.Nt > 0)
-      HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, x_bs, 0, nk, s), "text rows");
-    else
-      HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
-  }
+  HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v,
+                          nullptr, zv, nv, nv, 0, nv, s), "noise");
+  HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a,
+                          nullptr, za, na, na, 0, na, s), "noise");
+  HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
+  HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
+  if (d.Nt > 0)
+    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, 0, nk, s), "text rows");
+  else
+    HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
 
-  auto gemm = [&](const bf16 *A, int64_t lda, int64_t a_bs, const bf16 *Wt, int64_t ldw, void *Cp,
-                  int64_t ldc, int64_t c_bs, int c_dt, const float *bias, int64_t bias_bs, int M,
-                  int N, int K, int batch, bf16 *vt, int n_split) -> t2va_status {
-    GemmParams g;
-    g.A = A; g.lda = lda; g.a_bs = a_bs;
-    g.W = Wt; g.ldw = ldw;
-    g.C = Cp; g.ldc = ldc; g.c_bs = c_bs; g.c_dt = c_dt;
-    g.bias = bias; g.bias_bs = bias_bs;
-    g.VT = vt; g.vt_bs = vt_bs; g.vt_hs = vt_hs; g.vt_rs = L.ldv; g.vt_rows = L.ldv;
-    g.n_split = n_split; g.dh = dh;
-    g.M = M; g.N = N; g.K = K; g.batch = batch;
-    PhaseScope ps(s, T2VA_PHASE_GEMM, prof);
-    HIP_TRY(launch_gemm(g, s), "gemm");
-    return T2VA_OK;
-  };
-  auto attention = [&](bool tan, int phase) -> t2va_status {
-    AttnParams p;
-    p.q = QK; p.k = QK + D; p.vt = VT;
-    p.qd = tan ? QK + (int64_t)B * qk_bs : nullptr;
-    p.kd = tan ? QK + (int64_t)B * qk_bs + D : nullptr;
-    p.vdt = tan ? VT + (int64_t)B * vt_bs : nullptr;
-    p.nk = nk; p.o = O; p.od = tan ? O + (int64_t)B * o_bs : nullptr; p.lse = nullptr;
-    p.q_bs = qk_bs; p.q_rs = 2 * D; p.k_bs = qk_bs; p.k_rs = 2 * D;
-    p.vt_bs = vt_bs; p.vt_hs = vt_hs; p.vt_rs = L.ldv;
-    p.o_bs = o_bs; p.o_rs = D;
-    p.B = B; p.H = H; p.Nq = Nq; p.Nk = NA;
-    p.out_dt = T2VA_DTYPE_BF16;
-    p.scale = (float)(1.0 / sqrt((double)dh));
-    PhaseScope ps(s, phase, prof);
-    HIP_TRY(launch_attention(dh, tan, p, s), "attention");
-    return T2VA_OK;
-  };
 #define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
 
   // ---------------- teacher: x0_T = G_T(z_t, t, c) ----------------
-  T2VA_CALL(gemm(zv, d.Cv, nv, W[0][0], d.Cv, X, D, x_bs, 0, tau, D, d.Nv, D, d.Cv, B, nullptr, D));
-  T2VA_CALL(gemm(za, d.Ca, na, W[0][1], d.Ca, X + (int64_t)d.Nv * D, D, x_bs, 0, tau, D, d.Na, D,
-                 d.Ca, B, nullptr, D));
-  T2VA_CALL(gemm(X, D, x_bs, W[0][3], D, QK, 2 * D, qk_bs, 0, nullptr, 0, NA, 3 * D, D, B, VT, 2 * D));
-  T2VA_CALL(attention(false, T2VA_PHASE_TEACHER_ATTN));
-  T2VA_CALL(gemm(O, D, o_bs, W[0][4], D, x0T_v, d.Cv, nv, 1, nullptr, 0, d.Nv, d.Cv, D, B, nullptr, d.Cv));
-  T2VA_CALL(gemm(O + (int64_t)d.Nv * D, D, o_bs, W[0][5], D, x0T_a, d.Ca, na, 1, nullptr, 0, d.Na,
-                 d.Ca, D, B, nullptr, d.Ca));
+  T2VA_CALL(blk.project_in(W[0], zv, za, tau, X, QK, VT, B));
+  T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
+  T2VA_CALL(blk.project_out(W[0], O, x0T_v, x0T_a, B));
 
   // ---------------- F_T (tangent of the student's latent inputs) ----------------
   HIP_TRY(launch_trigflow(2, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v, x0T_v,
@@ -457,18 +582,15 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
                           za + (int64_t)B * na, na, na, na, na, s), "teacher field");
 
   // ---------------- student: G_S and its JVP ----------------
+  // Batches [0, B) carry the primal rows, [B, 2B) their tangents.
   HIP_TRY(launch_time_linear(E, 2 * B, D, W[1][2], tau, s), "student time linear");
   if (d.Nt > 0)
-    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X + (int64_t)B * x_bs, x_bs,
-                             1, nullptr, s), "tangent text rows");
-  T2VA_CALL(gemm(zv, d.Cv, nv, W[1][0], d.Cv, X, D, x_bs, 0, tau, D, d.Nv, D, d.Cv, 2 * B, nullptr, D));
-  T2VA_CALL(gemm(za, d.Ca, na, W[1][1], d.Ca, X + (int64_t)d.Nv * D, D, x_bs, 0, tau, D, d.Na, D,
-                 d.Ca, 2 * B, nullptr, D));
-  T2VA_CALL(gemm(X, D, x_bs, W[1][3], D, QK, 2 * D, qk_bs, 0, nullptr, 0, NA, 3 * D, D, 2 * B, VT, 2 * D));
-  T2VA_CALL(attention(true, T2VA_PHASE_STUDENT_ATTN));
-  T2VA_CALL(gemm(O, D, o_bs, W[1][4], D, x0S_v, d.Cv, nv, 1, nullptr, 0, d.Nv, d.Cv, D, 2 * B, nullptr, d.Cv));
-  T2VA_CALL(gemm(O + (int64_t)d.Nv * D, D, o_bs, W[1][5], D, x0S_a, d.Ca, na, 1, nullptr, 0, d.Na,
-                 d.Ca, D, 2 * B, nullptr, d.Ca));
+    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X + (int64_t)B * blk.x_bs,
+                             blk.x_bs, 1, nullptr, s), "tangent text rows");
+  T2VA_CALL(blk.project_in(W[1], zv, za, tau, X, QK, VT, 2 * B));
+  T2VA_CALL(blk.attention(QK, VT, nk, O, true, T2VA_PHASE_STUDENT_ATTN));
+  T2VA_CALL(blk.project_out(W[1], O, x0S_v, x0S_a, 2 * B));
+#undef T2VA_CALL
 
   // ---------------- g, norms, gbar, r, loss ----------------
   GParams gp;
@@ -485,14 +607,147 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
   gp.in_dt = d.in_dtype;
   HIP_TRY(launch_scm_direction(coef, gp, s), "sCM direction");
   NormParams np;
+  np.mode = 0;
   np.g[0] = gbar_v; np.g[1] = gbar_a; np.r[0] = r_v; np.r[1] = r_a;
   np.partial[0] = part_v; np.partial[1] = part_a;
+  np.partial2[0] = np.partial2[1] = nullptr;
   np.n[0] = nv; np.n[1] = na;
   np.nblk[0] = L.nblk_v; np.nblk[1] = L.nblk_a;
   np.norms = norms; np.loss = loss;
   np.eps = d.eps_scm; np.w[0] = d.w_v; np.w[1] = d.w_a;
   HIP_TRY(launch_normalise(B, np, s), "normalise");
+  return T2VA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Joint DMD term and the stage-3 mix.
+// ---------------------------------------------------------------------------
+size_t t2va_dmd_workspace_bytes(const t2va_dmd_desc *desc) {
+  g_err.clear();
+  if (check_dmd_desc(desc) != T2VA_OK) return 0;
+  return make_dmd_layout(*desc).total;
+}
+
+t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights *teacher,
+                            const t2va_block_weights *fake, const void *x0_v, const void *x0_a,
+                            const void *eps_v, const void *eps_a, const void *text,
+                            const uint8_t *text_mask, const double *t_host, float *delta_v,
+                            float *delta_a, float *scales, float *loss, void *workspace,
+                            size_t workspace_bytes, t2va_stream stream) {
+  g_err.clear();
+  // ---------------- validation (before any HIP call) ----------------
+  if (t2va_status st = check_dmd_desc(desc)) return st;
+  const t2va_dmd_desc &d = *desc;
+  if (t2va_status st = check_t(d.B, t_host)) return st;
+  const t2va_block_weights *wb[2] = {teacher, fake};
+  if (t2va_status st = check_weights(wb, 2, "teacher", "fake")) return st;
+  const void *req[] = {x0_v, x0_a, eps_v, eps_a, delta_v, delta_a, loss};
+  for (const void *p : req)
+    if (!p) return fail(T2VA_INVALID_ARG, "x0, eps, delta and loss pointers are required");
+  if (d.Nt > 0 && (!text || !text_mask))
+    return fail(T2VA_INVALID_ARG, "text and text_mask are required when Nt > 0");
+  const void *al[] = {x0_v, x0_a, eps_v, eps_a, text, delta_v, delta_a};
+  for (const void *p : al)
+    if (p && !aligned16(p)) return fail(T2VA_INVALID_ARG, "tensor operands must be 16-byte aligned");
+  const DmdLayout L = make_dmd_layout(d);
+  if (!workspace) return fail(T2VA_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(T2VA_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(T2VA_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+
+  // ---------------- launch sequence ----------------
+  hipStream_t s = (hipStream_t)stream;
+  const bool prof = g_prof.active();
+  if (prof) g_prof.calls++;
+  PhaseScope total(s, T2VA_PHASE_TOTAL, prof);
+
+  char *ws = (char *)workspace;
+  const Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
+  const int B = d.B, D = d.d, Nq = d.Nv + d.Na;
+  const int64_t nv = blk.nv, na = blk.na;
+  const CoefTable coef = make_coef(B, t_host, 0.0, 0.0);
+  const bool guided = !(d.cfg_v == 1.0 && d.cfg_a == 1.0);
+
+  const bf16 *W[2][6];
+  HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
+
+  bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
+  float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
+  bf16 *X = (bf16 *)(ws + L.X), *QK = (bf16 *)(ws + L.QK), *VT = (bf16 *)(ws + L.VT);
+  bf16 *O = (bf16 *)(ws + L.O);
+  int32_t *nk = (int32_t *)(ws + L.nk), *nk_null = (int32_t *)(ws + L.nk_null);
+  float *xT_v = (float *)(ws + L.xT_v), *xT_a = (float *)(ws + L.xT_a);
+  float *xF_v = (float *)(ws + L.xF_v), *xF_a = (float *)(ws + L.xF_a);
+
+  // z_t = cos t x0 + sin t eps of the student's sample (bf16 GEMM input).
+  HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, x0_v, eps_v,
+                          nullptr, zv, nv, nv, 0, nv, s), "noise");
+  HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, x0_a, eps_a,
+                          nullptr, za, na, na, 0, na, s), "noise");
+  HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
+  if (d.Nt > 0)
+    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, 0, nk, s), "text rows");
+  else
+    HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
+  if (guided) HIP_TRY(launch_fill_nk(nk_null, B, Nq, s), "fill nk");
+
+#define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
+  // ---------------- teacher: conditional and null-condition passes ----------------
+  // Both passes share Q, K and V; the null condition masks every text key, so
+  // its attention runs over the video and audio keys only.  Outputs: batches
+  // [0, B) conditional, [B, 2B) unconditional.
+  HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
+  T2VA_CALL(blk.project_in(W[0], zv, za, tau, X, QK, VT, B));
+  T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
+  if (guided)
+    T2VA_CALL(blk.attention(QK, VT, nk_null, O + (int64_t)B * blk.o_bs, false, T2VA_PHASE_TEACHER_ATTN));
+  T2VA_CALL(blk.project_out(W[0], O, xT_v, xT_a, guided ? 2 * B : B));
+
+  // ---------------- fake-score block ----------------
+  HIP_TRY(launch_time_linear(E, B, D, W[1][2], tau, s), "fake time linear");
+  T2VA_CALL(blk.project_in(W[1], zv, za, tau, X, QK, VT, B));
+  T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
+  T2VA_CALL(blk.project_out(W[1], O, xF_v, xF_a, B));
 #undef T2VA_CALL
+
+  // ---------------- direction, residual scale, Delta, loss ----------------
+  DmdParams dp;
+  dp.x0[0] = x0_v; dp.x0[1] = x0_a;
+  dp.tc[0] = xT_v; dp.tc[1] = xT_a;
+  dp.tu[0] = guided ? xT_v + (int64_t)B * nv : nullptr;
+  dp.tu[1] = guided ? xT_a + (int64_t)B * na : nullptr;
+  dp.fk[0] = xF_v; dp.fk[1] = xF_a;
+  dp.x_bs[0] = nv; dp.x_bs[1] = na;
+  dp.scale[0] = (float)d.cfg_v; dp.scale[1] = (float)d.cfg_a;
+  dp.g[0] = delta_v; dp.g[1] = delta_a;
+  dp.part_abs[0] = (float *)(ws + L.pa_v); dp.part_abs[1] = (float *)(ws + L.pa_a);
+  dp.part_sq[0] = (float *)(ws + L.ps_v); dp.part_sq[1] = (float *)(ws + L.ps_a);
+  dp.n[0] = nv; dp.n[1] = na;
+  dp.nblk[0] = L.nblk_v; dp.nblk[1] = L.nblk_a;
+  dp.in_dt = d.in_dtype;
+  HIP_TRY(launch_dmd_direction(B, dp, s), "DMD direction");
+  NormParams np;
+  np.mode = 1;
+  np.g[0] = delta_v; np.g[1] = delta_a; np.r[0] = np.r[1] = nullptr;
+  np.partial[0] = dp.part_abs[0]; np.partial[1] = dp.part_abs[1];
+  np.partial2[0] = dp.part_sq[0]; np.partial2[1] = dp.part_sq[1];
+  np.n[0] = nv; np.n[1] = na;
+  np.nblk[0] = L.nblk_v; np.nblk[1] = L.nblk_a;
+  np.norms = scales; np.loss = loss;
+  np.eps = d.eps_dmd; np.w[0] = d.w_v; np.w[1] = d.w_a;
+  HIP_TRY(launch_normalise(B, np, s), "normalise");
+  return T2VA_OK;
+}
+
+t2va_status t2va_stage3_mix(int B, double lam_scm, double lam_dmd, const float *loss_scm,
+                            const float *loss_dmd, float *out, t2va_stream stream) {
+  g_err.clear();
+  if (B < 1 || B > T2VA_MAX_BATCH)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "B = %d outside [1, %d]", B, T2VA_MAX_BATCH);
+  if (!isfinite(lam_scm) || !isfinite(lam_dmd)) return fail(T2VA_INVALID_ARG, "lam must be finite");
+  if (!loss_scm || !loss_dmd || !out) return fail(T2VA_INVALID_ARG, "NULL loss pointer");
+  HIP_TRY(launch_mix(B, (float)lam_scm, loss_scm, (float)lam_dmd, loss_dmd, out, (hipStream_t)stream),
+          "stage-3 mix");
   return T2VA_OK;
 }
 

@@ -16,7 +16,7 @@ HEADER = _lib.HEADER_PATH
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(t2va_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(t2va_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"t2va_scm_target", "t2va_joint_attn_fwd_jvp", "t2va_trigflow_field",
-            "t2va_scm_workspace_bytes", "t2va_last_error"} <= set(names)
+            "t2va_scm_workspace_bytes", "t2va_last_error", "t2va_dmd_target",
+            "t2va_dmd_workspace_bytes", "t2va_stage3_mix"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.t2va_abi_version() == 1
@@ -40,6 +41,7 @@ def test_struct_sizes_match_header(lib):
     assert ctypes.sizeof(_lib.AttnDesc) == 5 * 4 + 4 + 9 * 8 + 3 * 4 + 4
     assert ctypes.sizeof(_lib.ScmDesc) == 10 * 4 + 5 * 8
     assert ctypes.sizeof(_lib.BlockWeights) == 6 * 8
+    assert ctypes.sizeof(_lib.DmdDesc) == 10 * 4 + 5 * 8
 
 
 def err(lib):
@@ -139,3 +141,43 @@ def test_trigflow_rejects_before_launch(lib):
                                    fake_ptr(3), None) == 1
     # zero elements: nothing to launch, success
     assert lib.t2va_trigflow_field(0, 2, 0, 0, 0, 1, t, None, None, None, None) == 0
+
+
+def test_dmd_workspace_and_rejections(lib):
+    cfg = inputs.CONFIGS["high-res"]
+    d = _lib.dmd_desc(cfg, _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    n = lib.t2va_dmd_workspace_bytes(ctypes.byref(d))
+    # forward-only: X, QK and V^T for one batch, O for the two teacher passes
+    assert n > cfg.N_all * cfg.d * 2 * 4 and n < 4 * 2**30 and n % 256 == 0
+    for bad in (dict(eps_dmd=0.0), dict(cfg_v=float("inf")), dict(H=5), dict(Ca=96)):
+        dd = _lib.dmd_desc(cfg.replace(**bad), _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+        assert lib.t2va_dmd_workspace_bytes(ctypes.byref(dd)) == 0, bad
+
+    tiny = inputs.CONFIGS["tiny"]
+    d = _lib.dmd_desc(tiny, _lib.DTYPE_FP32, _lib.DTYPE_FP32)
+    w = _lib.BlockWeights(*[0x10000 * (i + 1) for i in range(6)])
+    t = (ctypes.c_double * 1)(0.5)
+    ptrs = [fake_ptr(i + 10) for i in range(6)]
+    outs = [fake_ptr(i + 20) for i in range(4)]
+    ws_bytes = lib.t2va_dmd_workspace_bytes(ctypes.byref(d))
+
+    def call(t_arr=t, ws=fake_ptr(100), nbytes=ws_bytes, fake=w, o=outs):
+        return lib.t2va_dmd_target(ctypes.byref(d), ctypes.byref(w), ctypes.byref(fake), *ptrs,
+                                   t_arr, *o, ws, nbytes, None)
+
+    assert call(t_arr=(ctypes.c_double * 1)(-0.1)) == 1 and "t[0]" in err(lib)
+    assert call(nbytes=ws_bytes - 1) == 3
+    assert call(ws=ctypes.c_void_p(0x10040)) == 1 and "aligned" in err(lib)
+    o2 = list(outs)
+    o2[3] = None  # loss is required
+    assert call(o=o2) == 1
+    o3 = list(outs)
+    o3[2] = None  # scales are optional: passes validation (not launched: fake pointers)
+    w2 = _lib.BlockWeights(*([0x10000] * 5 + [0]))
+    assert call(fake=w2) == 1 and "fake" in err(lib)
+
+
+def test_stage3_mix_rejections(lib):
+    assert lib.t2va_stage3_mix(0, 1.0, 1.0, fake_ptr(1), fake_ptr(2), fake_ptr(3), None) == 2
+    assert lib.t2va_stage3_mix(2, float("nan"), 1.0, fake_ptr(1), fake_ptr(2), fake_ptr(3), None) == 1
+    assert lib.t2va_stage3_mix(2, 1.0, 1.0, None, fake_ptr(2), fake_ptr(3), None) == 1

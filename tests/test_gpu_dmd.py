@@ -1,0 +1,138 @@
+"""GPU parity of the joint DMD term, the teacher's guidance and the stage-3 mix
+(through the C ABI) against the fp64 oracle.
+
+Tolerances.  Delta (= gbar in value) within 2e-2 relative L2 per (sample,
+modality), the bound the sCM fields use for the same bf16 storage and fp32
+accumulation; the residual scale c within the same relative bound (c is a mean
+of |x0 - x0_T| and moves by at most the mean absolute error of x0_T).  The
+loss is sum_m w_m ||Delta^m||^2, so a relative L2 error e in Delta moves it by
+at most 2e + e^2 relative (Cauchy-Schwarz): 4.04e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from joint_video_audio_trigflow_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_FIELD = 2e-2
+TOL_LOSS = 2 * TOL_FIELD + TOL_FIELD ** 2
+
+RAGGED = inputs.Config("ragged", B=2, Nv=300, Na=45, Nt=20, Ntv=13, Cv=128, Ca=64, d=256, H=2,
+                       in_dtype="bf16", mask_mode="scatter", w_v=0.5, w_a=2.0, index=11)
+RAGGED64 = inputs.Config("ragged64", B=1, Nv=130, Na=70, Nt=0, Ntv=0, Cv=64, Ca=64, d=256, H=4,
+                         in_dtype="bf16", index=12)
+
+
+def lib():
+    from joint_video_audio_trigflow_amd import _lib
+    _lib.load()
+    return _lib
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_dmd(problem, cfg_v=None, cfg_a=None):
+    L = lib()
+    cfg = problem["cfg"]
+    dev = L.to_device_dmd_problem(problem)
+    dt = L.DTYPE_BF16 if cfg.in_dtype == "bf16" else L.DTYPE_FP32
+    op = L.DmdTarget(cfg, in_dtype=dt, weight_dtype=dt, cfg_v=cfg_v, cfg_a=cfg_a)
+    out = op(dev["teacher"], dev["fake"], dev["x0_v"], dev["x0_a"], dev["eps_v"], dev["eps_a"],
+             dev["text"], dev["text_mask"], dev["t"])
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def check(cfg, got, ref):
+    worst = {}
+    for b in range(cfg.B):
+        for i, m in enumerate("va"):
+            e = rel_l2(got[f"delta_{m}"][b], ref[f"delta_{m}"][b])
+            worst[m] = max(worst.get(m, 0.0), e)
+            assert e <= TOL_FIELD, (cfg.name, b, m, e)
+            assert abs(got["scales"][b, i] - ref["scales"][b, i]) <= TOL_FIELD * ref["scales"][b, i]
+            assert np.all(np.isfinite(got[f"delta_{m}"][b]))
+        assert abs(got["loss"][b] - ref["loss"][b]) <= TOL_LOSS * ref["loss"][b], (b, got["loss"][b], ref["loss"][b])
+    say(cfg.name, "worst rel-L2 of Delta:", {k: f"{v:.2e}" for k, v in worst.items()},
+        "loss rel:", [f"{abs(got['loss'][b] / ref['loss'][b] - 1):.1e}" for b in range(cfg.B)])
+
+
+@pytest.mark.parametrize("cfg", [inputs.CONFIGS["tiny"], RAGGED, RAGGED64, inputs.CONFIGS["small"]],
+                         ids=lambda c: c.name)
+def test_dmd_target_matches_oracle(cfg):
+    say(f"dmd_target {cfg.name}")
+    p = inputs.make_dmd_problem(cfg)
+    got = run_dmd(p)
+    ref = oracle.dmd_target(p)
+    check(cfg, got, ref)
+
+
+@pytest.mark.parametrize("scales", [(1.0, 1.0), (0.0, 1.0), (1.0, 0.0), (-2.0, 7.5)])
+def test_dmd_guidance_scales(scales):
+    say(f"dmd_target guidance {scales}")
+    p = inputs.make_dmd_problem(RAGGED)
+    got = run_dmd(p, *scales)
+    ref = oracle.dmd_target(p, *scales)
+    check(RAGGED, got, ref)
+
+
+def test_dmd_target_deterministic_and_mask_invariant():
+    say("dmd_target determinism / mask invariance")
+    p = inputs.make_dmd_problem(RAGGED)
+    a = run_dmd(p)
+    b = run_dmd(p)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    data2 = dict(p["data"])
+    text2 = data2["text"].copy()
+    text2[data2["text_mask"] == 0] = -5.0
+    data2["text"] = text2
+    c = run_dmd(dict(p, data=data2))
+    for k in a:
+        assert np.array_equal(a[k], c[k]), k
+
+
+def test_dmd_target_batch_independence():
+    say("dmd_target batch independence")
+    p = inputs.make_dmd_problem(RAGGED)
+    full = run_dmd(p)
+    one = {k: (v[1:2] if isinstance(v, np.ndarray) else v) for k, v in p["data"].items()}
+    single = run_dmd(dict(p, cfg=RAGGED.replace(B=1), data=one))
+    for k in full:
+        assert np.array_equal(full[k][1:2], single[k]), k
+
+
+def test_stage3_mix_of_both_terms():
+    """Both terms on one batch (same text and mask), mixed on the device."""
+    say("stage-3 mix")
+    L = lib()
+    cfg = RAGGED
+    sp = inputs.make_problem(cfg)
+    dp = inputs.make_dmd_problem(cfg, data=sp["data"])
+    sdev = L.to_device_problem(sp)
+    op = L.ScmTarget(cfg)
+    s_out = op(sdev["teacher"], sdev["student"], sdev["z0_v"], sdev["z0_a"], sdev["eps_v"],
+               sdev["eps_a"], sdev["text"], sdev["text_mask"], sdev["t"])
+    ddev = L.to_device_dmd_problem(dp)
+    dop = L.DmdTarget(cfg)
+    d_out = dop(ddev["teacher"], ddev["fake"], ddev["x0_v"], ddev["x0_a"], ddev["eps_v"],
+                ddev["eps_a"], ddev["text"], ddev["text_mask"], ddev["t"])
+    mixed = L.stage3_mix(s_out["loss"], d_out["loss"], 0.25, 3.0).cpu().numpy()
+    torch.cuda.synchronize()
+    ref = oracle.stage3_loss(oracle.scm_target(sp)["loss"], oracle.dmd_target(dp)["loss"], 0.25, 3.0)
+    for b in range(cfg.B):
+        assert abs(mixed[b] - ref[b]) <= TOL_LOSS * abs(ref[b])
+    # exactly the device arithmetic of the two losses
+    want = (np.float32(0.25) * s_out["loss"].cpu().numpy() + np.float32(3.0) * d_out["loss"].cpu().numpy())
+    assert np.allclose(mixed, want, rtol=1e-6, atol=0)
