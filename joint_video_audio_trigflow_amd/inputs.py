@@ -54,6 +54,9 @@ class Config:
     # The joint DMD term and the stage-3 mix: guidance scales of the teacher
     # prediction per modality (3.0 video, 5.0 audio, and equal sCM/DMD weights
     # in the pages' training setup), the residual-scale normaliser's epsilon.
+    # Parameterisation of the block: "x0" (it predicts x0 at TrigFlow inputs)
+    # or "rf" (a rectified-flow velocity model behind the TrigFlow wrapper).
+    param: str = "x0"
     cfg_v: float = 3.0
     cfg_a: float = 5.0
     eps_dmd: float = 1e-6

@@ -36,7 +36,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .scm_oracle import _store, const, joint_block, trigflow_noise
+from .scm_oracle import block_x0, const, trigflow_noise
 
 
 def guided(x_cond, x_uncond, scale):
@@ -47,14 +47,14 @@ def guided(x_cond, x_uncond, scale):
     return x_uncond + scale * (x_cond - x_uncond)
 
 
-def teacher_prediction(zv, za, t, text, mask, W, H, cfg_v, cfg_a):
-    """The guided teacher x0-prediction for one sample: a conditional pass with
-    the sample's text mask, an unconditional pass with every text key masked,
-    combined with the per-modality scales.  Returns (x0^v, x0^a, parts) where
-    parts holds the two unguided passes."""
-    cv, ca = joint_block(const(zv), const(za), const(t), text, mask, W, H)
+def teacher_prediction(zv, za, t, text, mask, W, H, cfg_v, cfg_a, param="x0"):
+    """The guided teacher x0-prediction for one sample at TrigFlow inputs
+    (z, t): a conditional pass with the sample's text mask, an unconditional
+    pass with every text key masked, combined with the per-modality scales.
+    Returns (x0^v, x0^a, parts) where parts holds the two unguided passes."""
+    cv, ca = block_x0(const(zv), const(za), const(t), text, mask, W, H, param)
     null_mask = np.zeros_like(np.asarray(mask))
-    uv, ua = joint_block(const(zv), const(za), const(t), text, null_mask, W, H)
+    uv, ua = block_x0(const(zv), const(za), const(t), text, null_mask, W, H, param)
     parts = dict(cond_v=cv.p, cond_a=ca.p, uncond_v=uv.p, uncond_a=ua.p)
     return guided(cv.p, uv.p, cfg_v), guided(ca.p, ua.p, cfg_a), parts
 
@@ -76,10 +76,11 @@ def dmd_sample(cfg, data: dict, teacher: dict, fake: dict, b: int, cfg_v=None, c
     text, mask = data["text"][b], data["text_mask"][b]
     x0 = {"v": np.asarray(data["x0_v"][b], np.float64), "a": np.asarray(data["x0_a"][b], np.float64)}
     z_t = {m: trigflow_noise(t, x0[m], data[f"eps_{m}"][b]) for m in "va"}
-    zin = {m: _store(z_t[m]) for m in "va"}      # the blocks' (stored) inputs
+    param = getattr(cfg, "param", "x0")
 
-    tv, ta, parts = teacher_prediction(zin["v"], zin["a"], t, text, mask, teacher, cfg.H, cfg_v, cfg_a)
-    fv, fa = joint_block(const(zin["v"]), const(zin["a"]), const(t), text, mask, fake, cfg.H)
+    tv, ta, parts = teacher_prediction(z_t["v"], z_t["a"], t, text, mask, teacher, cfg.H, cfg_v, cfg_a,
+                                       param)
+    fv, fa = block_x0(const(z_t["v"]), const(z_t["a"]), const(t), text, mask, fake, cfg.H, param)
     x0_T = {"v": tv, "a": ta}
     x0_F = {"v": fv.p, "a": fa.p}
 

@@ -266,6 +266,49 @@ def joint_block(zv: Dual, za: Dual, t: Dual, text: np.ndarray, mask: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# The block's parameterisation: a direct x0-prediction, or a rectified-flow
+# velocity model behind the TrigFlow wrapper.
+# ---------------------------------------------------------------------------
+def rf_wrap(z: Dual, t: Dual):
+    """The TrigFlow -> rectified-flow input map ([deep read] section 4.2):
+    z_rf = z / (cos t + sin t), t_rf = sin t / (cos t + sin t), as duals."""
+    cs = d_add(d_cos(t), d_sin(t))
+    return d_div(z, cs), d_div(d_sin(t), cs)
+
+
+def rf_x0(z_rf: Dual, t_rf: Dual, v: Dual) -> Dual:
+    """x0 from a rectified-flow velocity: with z_rf = (1 - t_rf) x0 + t_rf eps and
+    v = eps - x0, x0 = z_rf - t_rf v.  The pages give only the input map; this
+    output map is the rectified-flow parameterisation solved for x0."""
+    return d_sub(z_rf, d_mul(t_rf, v))
+
+
+def block_x0(zv: Dual, za: Dual, t: Dual, text, mask, W: dict, H: int, param: str = "x0",
+             query_rows=None, block=None):
+    """x0-predictions (x0^v, x0^a) of the joint block at TrigFlow inputs (z, t).
+
+    param "x0": the block predicts x0 directly at (z, t).
+    param "rf": the block is a rectified-flow velocity model; the TrigFlow
+    wrapper feeds it (z_rf, t_rf) and converts its velocity back to x0, so the
+    JVP passes through the wrapper, the time embedding and the block
+    ([deep read] section 4.2).
+    The block's token inputs are what is stored (bf16 in storage mode).
+    ``block`` replaces the joint block (same signature) for checks with a stub.
+    """
+    block = joint_block if block is None else block
+    if param == "x0":
+        return block(_store(zv), _store(za), t, text, mask, W, H, query_rows=query_rows)
+    if param != "rf":
+        raise ValueError(param)
+    zv_rf, t_rf = rf_wrap(zv, t)
+    za_rf, _ = rf_wrap(za, t)
+    vv, va = block(_store(zv_rf), _store(za_rf), t_rf, text, mask, W, H, query_rows=query_rows)
+    if query_rows is not None:
+        zv_rf, za_rf = d_rows(zv_rf, query_rows[0]), d_rows(za_rf, query_rows[1])
+    return rf_x0(zv_rf, t_rf, vv), rf_x0(za_rf, t_rf, va)
+
+
+# ---------------------------------------------------------------------------
 # The full target.
 # ---------------------------------------------------------------------------
 def scm_sample(cfg, data: dict, teacher: dict, student: dict, b: int, beta=None, gamma=None,
@@ -284,17 +327,16 @@ def scm_sample(cfg, data: dict, teacher: dict, student: dict, b: int, beta=None,
     z_t = {"v": trigflow_noise(t, data["z0_v"][b], data["eps_v"][b]),
            "a": trigflow_noise(t, data["z0_a"][b], data["eps_a"][b])}
 
+    param = getattr(cfg, "param", "x0")
     # Teacher: primal forward only.
-    zin = {m: _store(z_t[m]) for m in "va"}
-    gT_v, gT_a = joint_block(const(zin["v"]), const(zin["a"]), const(t), text, mask, teacher, cfg.H)
+    gT_v, gT_a = block_x0(const(z_t["v"]), const(z_t["a"]), const(t), text, mask, teacher, cfg.H, param)
     x0_T = {"v": gT_v.p, "a": gT_a.p}
     F_T = {m: trigflow_field(t, z_t[m], x0_T[m]) for m in "va"}
 
     # Student: dual forward along (dt = 1, dz^v = F_T^v, dz^a = F_T^a, dc = 0).
     td = Dual(np.float64(t), np.float64(1.0))
     zd = {m: Dual(z_t[m], F_T[m]) for m in "va"}
-    zb = {m: Dual(zin[m], _store(F_T[m])) for m in "va"}   # the block's (stored) inputs
-    gS_v, gS_a = joint_block(zb["v"], zb["a"], td, text, mask, student, cfg.H, query_rows=query_rows)
+    gS_v, gS_a = block_x0(zd["v"], zd["a"], td, text, mask, student, cfg.H, param, query_rows=query_rows)
     G_S = {"v": gS_v, "a": gS_a}
 
     if query_rows is not None:
@@ -353,7 +395,8 @@ def scm_target(problem: dict, beta=None, gamma=None) -> dict:
 def student_field(cfg, data, student, b, zv, za, t):
     """Primal student field F_theta(z^v, z^a, t) at an arbitrary point (for derivative checks)."""
     text, mask = data["text"][b], data["text_mask"][b]
-    gv, ga = joint_block(const(zv), const(za), const(t), text, mask, student, cfg.H)
+    gv, ga = block_x0(const(zv), const(za), const(t), text, mask, student, cfg.H,
+                      getattr(cfg, "param", "x0"))
     return trigflow_field(t, zv, gv.p), trigflow_field(t, za, ga.p)
 
 
