@@ -37,12 +37,13 @@ def workload_name(cfg) -> str:
 
 def attention_kernel_digest() -> str:
     """SHA-256 of the source text the attention kernel is compiled from:
-    attention.hip, the shared types and helpers at the top of common.h, and
-    the AttnParams declaration (other kernels' declarations do not count)."""
+    attention.hip, the shared types and load/store helpers at the top of
+    common.h, and the AttnParams declaration (the other kernels' coefficient
+    tables and parameter blocks do not count)."""
     import hashlib
     csrc = os.path.join(ROOT, "joint_video_audio_trigflow_amd", "csrc")
     common = open(os.path.join(csrc, "common.h")).read()
-    head = common[:common.index("// Internal launchers")]
+    head = common[:common.index("// Per-sample coefficients")]
     a = common.index("struct AttnParams")
     params = common[a:common.index("};", a) + 2]
     attn = open(os.path.join(csrc, "attention.hip")).read()
@@ -120,6 +121,36 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
     }
 
 
+def time_dmd(cfg, problem, steps, scm_ms) -> dict:
+    """The joint DMD term (guided teacher: conditional + null-condition passes,
+    fake-score block, residual-scale normaliser) on the same workload, timed
+    after the sCM steps; the stage-3 step is one sCM target plus one DMD term."""
+    import torch
+    from joint_video_audio_trigflow_amd import _lib, inputs
+    dp = inputs.make_dmd_problem(cfg, data=problem["data"])
+    dev = _lib.to_device_dmd_problem(dp)
+    dt = _lib.DTYPE_BF16 if cfg.in_dtype == "bf16" else _lib.DTYPE_FP32
+    op = _lib.DmdTarget(cfg, in_dtype=dt, weight_dtype=dt)
+    call = lambda: op(dev["teacher"], dev["fake"], dev["x0_v"], dev["x0_a"], dev["eps_v"],
+                      dev["eps_a"], dev["text"], dev["text_mask"], dev["t"])
+    call()
+    torch.cuda.synchronize()
+    _lib.profile_enable(steps)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phases, n = _lib.profile_read()
+    _lib.profile_enable(0)
+    ms = 1000.0 * elapsed / steps
+    return {"steps": steps, "ms_per_call": ms, "samples_per_s": cfg.B / (ms * 1e-3),
+            "guidance": [cfg.cfg_v, cfg.cfg_a],
+            "phases_ms_per_call": {"total": phases["total"] / n, "fwd_attention": phases["teacher_attn"] / n,
+                                   "gemm": phases["gemm"] / n, "other": phases["other"] / n},
+            "stage3_ms_per_step": scm_ms + ms}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +159,8 @@ def main() -> int:
     ap.add_argument("--config", default="high-res")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dmd-steps", type=int, default=5,
+                    help="also time the joint DMD term on the same workload (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
@@ -207,6 +240,8 @@ def main() -> int:
         "phases_ms_per_step": {k: v / ncalls for k, v in phases.items()},
         "teacher_attn_tflops": teacher_tf,
     }
+    if args.dmd_steps > 0:
+        rec["dmd_target"] = time_dmd(cfg, problem, args.dmd_steps, ms_step)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

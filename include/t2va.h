@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define T2VA_ABI_VERSION 1
+#define T2VA_ABI_VERSION 2
 
 typedef int t2va_status;
 #define T2VA_OK 0
@@ -48,6 +48,17 @@ typedef int t2va_status;
 
 #define T2VA_DTYPE_BF16 0
 #define T2VA_DTYPE_FP32 1
+
+/* The joint block's parameterisation (deep read, section 4.2).
+ * T2VA_PARAM_X0: the block predicts x0 directly at the TrigFlow inputs (z_t, t).
+ * T2VA_PARAM_RF: the block is a rectified-flow velocity model behind the
+ *   TrigFlow wrapper: it sees z_rf = z_t/(cos t + sin t) and
+ *   t_rf = sin t/(cos t + sin t) (the time embedding takes t_rf), and its
+ *   output v is turned into x0 = z_rf - t_rf v (the rectified-flow relation
+ *   z_rf = (1 - t_rf) x0 + t_rf eps, v = eps - x0, solved for x0).  The JVP
+ *   passes through the wrapper and the time embedding. */
+#define T2VA_PARAM_X0 0
+#define T2VA_PARAM_RF 1
 
 /* Largest batch one call accepts (per-sample coefficients travel as kernel
  * arguments). */
@@ -157,6 +168,7 @@ typedef struct {
   double gamma; /* tangent warm-up ratio, 0 <= gamma <= 1 */
   double eps_scm; /* > 0, added to the L2 norm */
   double w_v, w_a; /* modality weights of the joint loss */
+  int param;       /* T2VA_PARAM_X0 or T2VA_PARAM_RF (the block's parameterisation) */
 } t2va_scm_desc;
 
 /* One copy of the joint block (teacher or student); device pointers. */
@@ -188,6 +200,9 @@ size_t t2va_scm_workspace_bytes(const t2va_scm_desc *desc);
  * time embedding (base 10000, [cos | sin]) through w_t; one multi-head
  * self-attention whose queries are the video and audio tokens and whose keys
  * are video, audio and the valid text tokens; per-modality output projection.
+ * With desc->param == T2VA_PARAM_RF both blocks are rectified-flow velocity
+ * models behind the TrigFlow wrapper (see T2VA_PARAM_RF): G above is then the
+ * wrapped x0-prediction, and the JVP runs through the wrapper.
  *
  * Inputs (device):
  *   z0_v, eps_v  [B, Nv, Cv] in_dtype     z0_a, eps_a [B, Na, Ca] in_dtype
@@ -230,6 +245,7 @@ typedef struct {
                           (finite; 1 for both skips the unconditional pass) */
   double eps_dmd;      /* > 0, added to the residual scale */
   double w_v, w_a;     /* modality weights of the joint loss */
+  int param;           /* T2VA_PARAM_X0 or T2VA_PARAM_RF, as in t2va_scm_desc */
 } t2va_dmd_desc;
 
 /* Exact workspace size in bytes for t2va_dmd_target (0 if the descriptor is invalid). */
@@ -246,6 +262,8 @@ size_t t2va_dmd_workspace_bytes(const t2va_dmd_desc *desc);
  *   c^m     = (1/(Nm*Cm)) sum_i |x0_i^m - x0_T,i^m|          residual scale
  *   gbar^m  = g^m/(c^m + eps_dmd),  Delta^m = x0^m - sg(x0^m - gbar^m) = gbar^m (value)
  *   loss_b  = w_v sum_i (Delta_i^v)^2 + w_a sum_i (Delta_i^a)^2   (summed, not averaged)
+ * With desc->param == T2VA_PARAM_RF all three passes go through the TrigFlow
+ * wrapper and are converted to x0 before the guidance and the differences.
  * The unconditional pass shares the conditional pass's Q, K and V (in this
  * one-block model the video and audio rows do not depend on the text); only
  * its attention runs again over the video and audio keys.

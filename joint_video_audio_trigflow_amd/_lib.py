@@ -21,6 +21,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "t2va.h")
 T2VA_OK = 0
 DTYPE_BF16, DTYPE_FP32 = 0, 1
 NOISE, FIELD = 0, 1
+PARAM_X0, PARAM_RF = 0, 1
+ABI_VERSION = 2
 MAX_BATCH = 64
 NUM_PHASES = 5
 PHASES = ("total", "teacher_attn", "student_attn", "gemm", "other")
@@ -48,7 +50,7 @@ class ScmDesc(ctypes.Structure):
                 ("Cv", ctypes.c_int), ("Ca", ctypes.c_int), ("d", ctypes.c_int), ("H", ctypes.c_int),
                 ("in_dtype", ctypes.c_int), ("weight_dtype", ctypes.c_int),
                 ("beta", ctypes.c_double), ("gamma", ctypes.c_double), ("eps_scm", ctypes.c_double),
-                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double)]
+                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double), ("param", ctypes.c_int)]
 
 
 class DmdDesc(ctypes.Structure):
@@ -56,7 +58,7 @@ class DmdDesc(ctypes.Structure):
                 ("Cv", ctypes.c_int), ("Ca", ctypes.c_int), ("d", ctypes.c_int), ("H", ctypes.c_int),
                 ("in_dtype", ctypes.c_int), ("weight_dtype", ctypes.c_int),
                 ("cfg_v", ctypes.c_double), ("cfg_a", ctypes.c_double), ("eps_dmd", ctypes.c_double),
-                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double)]
+                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double), ("param", ctypes.c_int)]
 
 
 class BlockWeights(ctypes.Structure):
@@ -77,6 +79,10 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m joint_video_audio_trigflow_amd.build` (no fallback exists)")
     lib = ctypes.CDLL(LIB_PATH)
+    lib.t2va_abi_version.restype = ctypes.c_int
+    if lib.t2va_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {lib.t2va_abi_version()}, the binding "
+                           f"expects {ABI_VERSION}: rebuild it")
     vp, i32, i64, f32p, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
     lib.t2va_abi_version.restype = i32
     lib.t2va_last_error.restype = ctypes.c_char_p
@@ -191,12 +197,17 @@ def joint_attn_fwd_jvp(q, k, vt, nk, qd=None, kd=None, vdt=None, out_dtype=torch
     return o, od, lse
 
 
+def _param(cfg) -> int:
+    return {"x0": PARAM_X0, "rf": PARAM_RF}[getattr(cfg, "param", "x0")]
+
+
 def scm_desc(cfg, in_dtype: int, weight_dtype: int) -> ScmDesc:
     d = ScmDesc()
     d.B, d.Nv, d.Na, d.Nt = cfg.B, cfg.Nv, cfg.Na, cfg.Nt
     d.Cv, d.Ca, d.d, d.H = cfg.Cv, cfg.Ca, cfg.d, cfg.H
     d.in_dtype, d.weight_dtype = in_dtype, weight_dtype
     d.beta, d.gamma, d.eps_scm, d.w_v, d.w_a = cfg.beta, cfg.gamma, cfg.eps_scm, cfg.w_v, cfg.w_a
+    d.param = _param(cfg)
     return d
 
 
@@ -261,6 +272,7 @@ def dmd_desc(cfg, in_dtype: int, weight_dtype: int, cfg_v=None, cfg_a=None) -> D
     d.cfg_v = cfg.cfg_v if cfg_v is None else cfg_v
     d.cfg_a = cfg.cfg_a if cfg_a is None else cfg_a
     d.eps_dmd, d.w_v, d.w_a = cfg.eps_dmd, cfg.w_v, cfg.w_a
+    d.param = _param(cfg)
     return d
 
 

@@ -56,11 +56,22 @@ __device__ __forceinline__ void store8(float *p, const float *f) {
 
 // Per-sample coefficients, rounded once from fp64 on the host; travels as a
 // kernel argument so no host-to-device copy is needed.
+//
+// The block's inputs and outputs under its parameterisation:
+//   token input   z_in = r z_t,   its tangent  r F_T + rdot z_t
+//   time input    t_emb,          its tangent  t_emb_dot
+//   x0-prediction x0 = rf ? z_in - t_emb y : y     (y = the block's output)
+//   its tangent   rf ? (r F_T + rdot z_t) - t_emb_dot y - t_emb dy : dy
+// x0-prediction block: r = 1, rdot = 0, t_emb = t, t_emb_dot = 1.
+// Rectified-flow velocity block behind the TrigFlow wrapper: r = 1/(cos t + sin t),
+// rdot = dr/dt, t_emb = t_rf = sin t/(cos t + sin t), t_emb_dot = r^2.
 struct Coef {
-  float cos_t, sin_t, inv_sin, ct_st, cos2, boost, gamma_ct_st, t;
+  float cos_t, sin_t, inv_sin, ct_st, cos2, boost, gamma_ct_st;
+  float r, rdot, t_emb, t_emb_dot;
 };
 struct CoefTable {
   int B;
+  int rf;  // 1: rectified-flow velocity block behind the wrapper
   Coef c[kMaxBatch];
 };
 
@@ -68,8 +79,10 @@ struct CoefTable {
 // Internal launchers (implemented in the .hip files).
 // ---------------------------------------------------------------------------
 
-// Elementwise TrigFlow maps.  op: 0 noise (a=z0,b=eps), 1 field (a=z_t,b=x0),
-// 2 field from noise inputs (a=z0, b=eps, x=x0 fp32): (cos(c a + s b) - x)/s.
+// Elementwise TrigFlow maps.  op: 0 the block's token input r (cos a + sin b)
+// (a=z0, b=eps; r = 1 for an x0-prediction block), 1 field (cos a - b)/sin
+// (a=z_t, b=x0), 2 the tangent of the block's token input from the teacher's
+// output x: with z = cos a + sin b, F_T = (cos z - x0(x))/sin, out = r F_T + rdot z.
 hipError_t launch_trigflow(int op, const CoefTable &coef, int64_t n, int a_dt, int b_dt, int out_dt,
                            const void *a, const void *b, const float *x, void *out,
                            int64_t a_bs, int64_t b_bs, int64_t x_bs, int64_t out_bs,
@@ -117,7 +130,7 @@ hipError_t launch_scm_direction(const CoefTable &coef, const GParams &p, hipStre
 // x0_T = u + s (c - u) (c only when u is null), and per-block partial sums of
 // |x0 - x0_T| and of g^2 for both modalities.
 struct DmdParams {
-  const void *x0[2];
+  const void *x0[2], *eps[2];  // eps is read only for a rectified-flow block
   const float *tc[2], *tu[2], *fk[2];  // conditional / unconditional teacher, fake; tu nullable
   int64_t x_bs[2];     // batch stride (elements) of tc/tu/fk
   float scale[2];      // guidance scale per modality
@@ -128,7 +141,7 @@ struct DmdParams {
   int nblk[2];
   int in_dt;
 };
-hipError_t launch_dmd_direction(int B, const DmdParams &p, hipStream_t s);
+hipError_t launch_dmd_direction(const CoefTable &coef, const DmdParams &p, hipStream_t s);
 
 // Normalisation in place with the loss.
 //   mode 0 (sCM): n = sqrt(sum partial), g /= n + eps, r = -g, norms = n,

@@ -40,7 +40,9 @@ __device__ __forceinline__ void store_n(T *p, int64_t i0, int64_t n, bool vec, c
   }
 }
 
-// out = cos a + sin b (op 0); (cos a - b)/sin (op 1); (cos(cos a + sin b) - x)/sin (op 2).
+// op 0: r (cos a + sin b); op 1: (cos a - b)/sin; op 2: with z = cos a + sin b and
+// the teacher's x0-prediction x0 = rf ? r z - t_emb x : x, F_T = (cos z - x0)/sin
+// and out = r F_T + rdot z (the tangent of the student's token input).
 template <typename TA, typename TB, typename TO>
 __global__ __launch_bounds__(kThreads) void trigflow_kernel(int op, CoefTable coef, int64_t n,
                                                             const TA *a, const TB *b,
@@ -61,12 +63,14 @@ __global__ __launch_bounds__(kThreads) void trigflow_kernel(int op, CoefTable co
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (op == 0) {
-      fo[j] = c.cos_t * fa[j] + c.sin_t * fb[j];
+      fo[j] = c.r * (c.cos_t * fa[j] + c.sin_t * fb[j]);
     } else if (op == 1) {
       fo[j] = (c.cos_t * fa[j] - fb[j]) * c.inv_sin;
     } else {
       const float z = c.cos_t * fa[j] + c.sin_t * fb[j];
-      fo[j] = (c.cos_t * z - fx[j]) * c.inv_sin;
+      const float x0 = coef.rf ? c.r * z - c.t_emb * fx[j] : fx[j];
+      const float F = (c.cos_t * z - x0) * c.inv_sin;
+      fo[j] = coef.rf ? c.r * F + c.rdot * z : F;
     }
   }
   store_n(out, i0, n, vec, fo);
@@ -104,8 +108,9 @@ hipError_t trigflow_launch1(int op, const CoefTable &coef, int64_t n, int b_dt, 
 }
 
 // ---------------------------------------------------------------------------
-// Time embedding: e_k = cos(t w_k), e_{d/2+k} = sin(t w_k), w_k = 10000^(-k/(d/2)),
-// and its t-derivative.  Rows 0..B-1 hold e(t_b), rows B..2B-1 hold de/dt.
+// Time embedding: e_k = cos(s w_k), e_{d/2+k} = sin(s w_k), w_k = 10000^(-k/(d/2)),
+// at the block's time input s = t_emb, and its derivative along dt = 1
+// (de/ds * t_emb_dot).  Rows 0..B-1 hold e, rows B..2B-1 the derivative.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void time_embedding_kernel(CoefTable coef, int d, float *E) {
   const int half = d / 2;
@@ -113,15 +118,16 @@ __global__ __launch_bounds__(kThreads) void time_embedding_kernel(CoefTable coef
   const int bi = blockIdx.y;
   if (k >= half) return;
   const float w = exp2f(-(float)k / (float)half * 13.287712379549449f);  // log2(10000)
-  const float arg = coef.c[bi].t * w;
+  const float arg = coef.c[bi].t_emb * w;
+  const float wd = w * coef.c[bi].t_emb_dot;
   float sn, cs;
   sincosf(arg, &sn, &cs);
   float *e = E + (int64_t)bi * d;
   float *de = E + (int64_t)(coef.B + bi) * d;
   e[k] = cs;
   e[half + k] = sn;
-  de[k] = -w * sn;
-  de[half + k] = w * cs;
+  de[k] = -wd * sn;
+  de[half + k] = wd * cs;
 }
 
 // One wave per output feature i: tau[r][i] = sum_k W_t[i][k] E[r][k].
@@ -244,6 +250,14 @@ __global__ __launch_bounds__(kThreads) void scm_direction_kernel(CoefTable coef,
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float z = c.cos_t * z0[j] + c.sin_t * ep[j];
+      if (coef.rf) {
+        // velocities -> x0-predictions through the wrapper, and the JVP of x0_S
+        const float zin = c.r * z;
+        xt[j] = zin - c.t_emb * xt[j];
+        const float FT = (c.cos_t * z - xt[j]) * c.inv_sin;
+        gd[j] = (c.r * FT + c.rdot * z) - c.t_emb_dot * xs[j] - c.t_emb * gd[j];
+        xs[j] = zin - c.t_emb * xs[j];
+      }
       const float D = (xs[j] - xt[j]) * c.inv_sin;
       J[j] = -c.ct_st * z + c.cos2 * D - c.cos_t * gd[j];
       g[j] = c.boost * D - c.gamma_ct_st * z - J[j];
@@ -259,8 +273,9 @@ __global__ __launch_bounds__(kThreads) void scm_direction_kernel(CoefTable coef,
 // Guided teacher prediction, DMD direction g = x0_F - x0_T, and per-block sums
 // of |x0 - x0_T| (the residual scale's numerator) and of g^2.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void dmd_direction_kernel(int B, DmdParams p) {
+__global__ __launch_bounds__(kThreads) void dmd_direction_kernel(CoefTable coef, DmdParams p) {
   __shared__ float red[kThreads / 64];
+  const int B = coef.B;
   int blk = blockIdx.x;
   const int m = (blk >= B * p.nblk[0]) ? 1 : 0;
   if (m) blk -= B * p.nblk[0];
@@ -279,6 +294,19 @@ __global__ __launch_bounds__(kThreads) void dmd_direction_kernel(int B, DmdParam
       load8(p.tu[m] + xo + i0, tu);
 #pragma unroll
       for (int j = 0; j < 8; ++j) tc[j] = tu[j] + p.scale[m] * (tc[j] - tu[j]);
+    }
+    if (coef.rf) {
+      // velocities -> x0-predictions through the wrapper (affine, so guidance
+      // commutes with it): x0 = r z_t - t_rf v
+      const Coef c = coef.c[bi];
+      float ep[8];
+      load8((const T *)p.eps[m] + off + i0, ep);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float zin = c.r * (c.cos_t * x0[j] + c.sin_t * ep[j]);
+        tc[j] = zin - c.t_emb * tc[j];
+        fk[j] = zin - c.t_emb * fk[j];
+      }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -413,12 +441,12 @@ hipError_t launch_scm_direction(const CoefTable &coef, const GParams &p, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_dmd_direction(int B, const DmdParams &p, hipStream_t s) {
-  const unsigned blocks = (unsigned)(B * (p.nblk[0] + p.nblk[1]));
+hipError_t launch_dmd_direction(const CoefTable &coef, const DmdParams &p, hipStream_t s) {
+  const unsigned blocks = (unsigned)(coef.B * (p.nblk[0] + p.nblk[1]));
   if (p.in_dt == 0)
-    hipLaunchKernelGGL(dmd_direction_kernel<bf16>, dim3(blocks), dim3(kThreads), 0, s, B, p);
+    hipLaunchKernelGGL(dmd_direction_kernel<bf16>, dim3(blocks), dim3(kThreads), 0, s, coef, p);
   else
-    hipLaunchKernelGGL(dmd_direction_kernel<float>, dim3(blocks), dim3(kThreads), 0, s, B, p);
+    hipLaunchKernelGGL(dmd_direction_kernel<float>, dim3(blocks), dim3(kThreads), 0, s, coef, p);
   return hipGetLastError();
 }
 

@@ -59,11 +59,13 @@ t2va_status check_t(int B, const double *t_host) {
   return T2VA_OK;
 }
 
-// Coefficients of the sCM target in fp64, rounded once to fp32.
-CoefTable make_coef(int B, const double *t_host, double beta, double gamma) {
+// Coefficients of the sCM target and of the block's parameterisation in fp64,
+// rounded once to fp32.
+CoefTable make_coef(int B, const double *t_host, double beta, double gamma, int param) {
   CoefTable c;
   memset(&c, 0, sizeof(c));
   c.B = B;
+  c.rf = param == T2VA_PARAM_RF ? 1 : 0;
   for (int b = 0; b < B; ++b) {
     const double t = t_host[b];
     const double ct = cos(t), st = sin(t);
@@ -77,7 +79,19 @@ CoefTable make_coef(int B, const double *t_host, double beta, double gamma) {
     c.c[b].cos2 = (float)(ct * ct);
     c.c[b].boost = (float)(beta * ct / root);
     c.c[b].gamma_ct_st = (float)(gamma * ct * st);
-    c.c[b].t = (float)t;
+    if (c.rf) {
+      // TrigFlow wrapper: z_rf = z/(cos t + sin t), t_rf = sin t/(cos t + sin t)
+      const double cs = ct + st;
+      c.c[b].r = (float)(1.0 / cs);
+      c.c[b].rdot = (float)((st - ct) / (cs * cs));
+      c.c[b].t_emb = (float)(st / cs);
+      c.c[b].t_emb_dot = (float)(1.0 / (cs * cs));
+    } else {
+      c.c[b].r = 1.f;
+      c.c[b].rdot = 0.f;
+      c.c[b].t_emb = (float)t;
+      c.c[b].t_emb_dot = 1.f;
+    }
   }
   return c;
 }
@@ -184,6 +198,8 @@ t2va_status check_desc(const t2va_scm_desc *d) {
   if (t2va_status st = check_shape(d->B, d->Nv, d->Na, d->Nt, d->Cv, d->Ca, d->d, d->H,
                                    d->in_dtype, d->weight_dtype))
     return st;
+  if (d->param != T2VA_PARAM_X0 && d->param != T2VA_PARAM_RF)
+    return fail(T2VA_INVALID_ARG, "param = %d must be T2VA_PARAM_X0 or T2VA_PARAM_RF", d->param);
   if (!(d->gamma >= 0.0 && d->gamma <= 1.0))
     return fail(T2VA_INVALID_ARG, "gamma = %g outside [0, 1]", d->gamma);
   if (!(d->eps_scm > 0.0) || !isfinite(d->eps_scm))
@@ -260,6 +276,8 @@ t2va_status check_dmd_desc(const t2va_dmd_desc *d) {
   if (t2va_status st = check_shape(d->B, d->Nv, d->Na, d->Nt, d->Cv, d->Ca, d->d, d->H,
                                    d->in_dtype, d->weight_dtype))
     return st;
+  if (d->param != T2VA_PARAM_X0 && d->param != T2VA_PARAM_RF)
+    return fail(T2VA_INVALID_ARG, "param = %d must be T2VA_PARAM_X0 or T2VA_PARAM_RF", d->param);
   if (!isfinite(d->cfg_v) || !isfinite(d->cfg_a))
     return fail(T2VA_INVALID_ARG, "guidance scales must be finite");
   if (!(d->eps_dmd > 0.0) || !isfinite(d->eps_dmd))
@@ -408,7 +426,7 @@ t2va_status t2va_trigflow_field(int mode, int B, int64_t n_per_sample, int a_dty
   if (!a || !b || !out) return fail(T2VA_INVALID_ARG, "a, b and out must be non-NULL");
   if (!aligned16(a) || !aligned16(b) || !aligned16(out))
     return fail(T2VA_INVALID_ARG, "a, b and out must be 16-byte aligned");
-  const CoefTable coef = make_coef(B, t_host, 0.0, 0.0);
+  const CoefTable coef = make_coef(B, t_host, 0.0, 0.0, T2VA_PARAM_X0);
   HIP_TRY(launch_trigflow(mode, coef, n_per_sample, a_dtype, b_dtype, out_dtype, a, b, nullptr,
                           out, n_per_sample, n_per_sample, 0, n_per_sample, (hipStream_t)stream),
           "trigflow kernel launch");
@@ -542,7 +560,7 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
   const Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
   const int B = d.B, D = d.d, Nq = L.Nq;
   const int64_t nv = blk.nv, na = blk.na;
-  const CoefTable coef = make_coef(B, t_host, d.beta, d.gamma);
+  const CoefTable coef = make_coef(B, t_host, d.beta, d.gamma, d.param);
 
   const bf16 *W[2][6];
   HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
@@ -665,7 +683,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   const Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
   const int B = d.B, D = d.d, Nq = d.Nv + d.Na;
   const int64_t nv = blk.nv, na = blk.na;
-  const CoefTable coef = make_coef(B, t_host, 0.0, 0.0);
+  const CoefTable coef = make_coef(B, t_host, 0.0, 0.0, d.param);
   const bool guided = !(d.cfg_v == 1.0 && d.cfg_a == 1.0);
 
   const bf16 *W[2][6];
@@ -713,6 +731,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   // ---------------- direction, residual scale, Delta, loss ----------------
   DmdParams dp;
   dp.x0[0] = x0_v; dp.x0[1] = x0_a;
+  dp.eps[0] = eps_v; dp.eps[1] = eps_a;
   dp.tc[0] = xT_v; dp.tc[1] = xT_a;
   dp.tu[0] = guided ? xT_v + (int64_t)B * nv : nullptr;
   dp.tu[1] = guided ? xT_a + (int64_t)B * na : nullptr;
@@ -725,7 +744,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   dp.n[0] = nv; dp.n[1] = na;
   dp.nblk[0] = L.nblk_v; dp.nblk[1] = L.nblk_a;
   dp.in_dt = d.in_dtype;
-  HIP_TRY(launch_dmd_direction(B, dp, s), "DMD direction");
+  HIP_TRY(launch_dmd_direction(coef, dp, s), "DMD direction");
   NormParams np;
   np.mode = 1;
   np.g[0] = delta_v; np.g[1] = delta_a; np.r[0] = np.r[1] = nullptr;

@@ -6,7 +6,10 @@ norms, the loss, and J and gbar on a fixed random sample of rows (48 video
 and 24 audio rows).  With --storage it also runs the oracle with bf16 rounding
 at the points where the GPU path stores bf16 (keys prefixed "st_"), which
 measures how sensitive each sample is to that storage precision.
-Usage: python tests/golden/make_full_size_expected.py [--storage] [names...]
+With --dmd it does the same for the joint DMD term (guided teacher, fake-score
+block): per sample the residual scales, the loss and Delta on the sampled rows,
+into expected_dmd_<name>.npz.
+Usage: python tests/golden/make_full_size_expected.py [--storage] [--dmd] [names...]
 """
 import os
 import sys
@@ -41,6 +44,36 @@ def rows_of(res, cfg, prefix=""):
             prefix + "norms": res["norms"], prefix + "loss": res["loss"]}
 
 
+def dmd_rows_of(res, cfg, prefix=""):
+    rv, ra = sample_rows(cfg)
+    b = np.arange(cfg.B)[:, None]
+    return {prefix + "delta_v": res["delta_v"][b, rv].astype(np.float32),
+            prefix + "delta_a": res["delta_a"][b, ra].astype(np.float32),
+            prefix + "scales": res["scales"], prefix + "loss": res["loss"]}
+
+
+def main_dmd(names, storage):
+    from oracle import scm_oracle
+    for name in names:
+        cfg = inputs.CONFIGS[name]
+        t0 = time.time()
+        p = inputs.make_dmd_problem(cfg)
+        path = os.path.join(OUT, f"expected_dmd_{name}.npz")
+        if os.path.exists(path):
+            out = dict(np.load(path))
+        else:
+            scm_oracle.STORAGE = None
+            res = oracle.dmd_target(p)
+            rv, ra = sample_rows(cfg)
+            out = dict(rows_v=rv, rows_a=ra, t=res["t"], **dmd_rows_of(res, cfg))
+        if storage:
+            scm_oracle.STORAGE = "bf16"
+            out.update(dmd_rows_of(oracle.dmd_target(p), cfg, "st_"))
+            scm_oracle.STORAGE = None
+        np.savez_compressed(path, **out)
+        print(f"dmd {name}: {time.time() - t0:.0f} s", flush=True)
+
+
 def main(names, storage):
     from oracle import scm_oracle
     for name in names:
@@ -67,4 +100,7 @@ if __name__ == "__main__":
     args = sys.argv[1:]
     storage = "--storage" in args
     names = [a for a in args if not a.startswith("--")]
-    main(names or ["standard", "stress", "high-res"], storage)
+    if "--dmd" in args:
+        main_dmd(names or ["standard", "stress", "high-res"], storage)
+    else:
+        main(names or ["standard", "stress", "high-res"], storage)

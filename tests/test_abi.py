@@ -33,15 +33,15 @@ def test_exports_every_declared_symbol(lib):
             "t2va_dmd_workspace_bytes", "t2va_stage3_mix"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.t2va_abi_version() == 1
+    assert lib.t2va_abi_version() == 2
 
 
 def test_struct_sizes_match_header(lib):
     # the binding's structs mirror the header: field counts and natural packing
     assert ctypes.sizeof(_lib.AttnDesc) == 5 * 4 + 4 + 9 * 8 + 3 * 4 + 4
-    assert ctypes.sizeof(_lib.ScmDesc) == 10 * 4 + 5 * 8
+    assert ctypes.sizeof(_lib.ScmDesc) == 10 * 4 + 5 * 8 + 8   # + int param, padded
     assert ctypes.sizeof(_lib.BlockWeights) == 6 * 8
-    assert ctypes.sizeof(_lib.DmdDesc) == 10 * 4 + 5 * 8
+    assert ctypes.sizeof(_lib.DmdDesc) == 10 * 4 + 5 * 8 + 8
 
 
 def err(lib):
@@ -181,3 +181,15 @@ def test_stage3_mix_rejections(lib):
     assert lib.t2va_stage3_mix(0, 1.0, 1.0, fake_ptr(1), fake_ptr(2), fake_ptr(3), None) == 2
     assert lib.t2va_stage3_mix(2, float("nan"), 1.0, fake_ptr(1), fake_ptr(2), fake_ptr(3), None) == 1
     assert lib.t2va_stage3_mix(2, 1.0, 1.0, None, fake_ptr(2), fake_ptr(3), None) == 1
+
+
+def test_param_validation(lib):
+    cfg = inputs.CONFIGS["standard"]
+    d = _lib.scm_desc(cfg, _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    d.param = 2
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(d)) == 0 and "param" in err(lib)
+    d.param = _lib.PARAM_RF
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(d)) > 0
+    dd = _lib.dmd_desc(cfg, _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    dd.param = -1
+    assert lib.t2va_dmd_workspace_bytes(ctypes.byref(dd)) == 0 and "param" in err(lib)

@@ -136,3 +136,13 @@ def test_stage3_mix_of_both_terms():
     # exactly the device arithmetic of the two losses
     want = (np.float32(0.25) * s_out["loss"].cpu().numpy() + np.float32(3.0) * d_out["loss"].cpu().numpy())
     assert np.allclose(mixed, want, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("cfg", [inputs.CONFIGS["tiny"].replace(param="rf"), RAGGED.replace(param="rf")],
+                         ids=lambda c: c.name + "-rf")
+def test_dmd_target_rf_wrapper_matches_oracle(cfg):
+    say(f"dmd_target {cfg.name} through the TrigFlow wrapper")
+    p = inputs.make_dmd_problem(cfg)
+    got = run_dmd(p)
+    ref = oracle.dmd_target(p)
+    check(cfg, got, ref)

@@ -125,3 +125,46 @@ def test_attention_full_high_res_shape_sampled_queries():
         assert rel_l2(o[0, :, h], eo[0, :, h]) < 1e-2, h
         assert rel_l2(od[0, :, h], eod[0, :, h]) < 1e-2, h
     assert np.max(np.abs(lse.cpu().numpy()[:, :, rows] - else_)) < 2e-2
+
+
+TOL_DMD_LOSS = 2 * TOL_FIELD + TOL_FIELD ** 2   # |dL|/L <= 2e + e^2 for a relative L2 error e in Delta
+
+
+@pytest.mark.parametrize("name", ["standard", "stress"])
+def test_full_size_dmd_against_stored_oracle(name):
+    """The joint DMD term at full size against the stored oracle run, with the
+    same conditioning protocol as the sCM target."""
+    from joint_video_audio_trigflow_amd import _lib
+    path = os.path.join(GOLDEN, f"expected_dmd_{name}.npz")
+    print(f"full-size dmd_target {name}", flush=True)
+    exp = np.load(path)
+    cfg = inputs.CONFIGS[name]
+    p = inputs.make_dmd_problem(cfg)
+    assert np.array_equal(p["data"]["t"], exp["t"]), "seeded inputs differ from the stored run"
+    dev = _lib.to_device_dmd_problem(p)
+    op = _lib.DmdTarget(cfg)
+    out = op(dev["teacher"], dev["fake"], dev["x0_v"], dev["x0_a"], dev["eps_v"], dev["eps_a"],
+             dev["text"], dev["text_mask"], dev["t"])
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    worst = {}
+    for b in range(cfg.B):
+        for m, i in (("v", 0), ("a", 1)):
+            rows = exp[f"rows_{m}"][b]
+            g = got[f"delta_{m}"][b, rows]
+            e = rel_l2(g, exp[f"delta_{m}"][b])
+            e_st = rel_l2(g, exp[f"st_delta_{m}"][b])
+            cond = rel_l2(exp[f"st_delta_{m}"][b], exp[f"delta_{m}"][b])
+            if cond <= 0.5 * TOL_FIELD:
+                assert e <= TOL_FIELD and e_st <= TOL_FIELD, (name, b, m, e, e_st)
+                worst[m] = max(worst.get(m, 0.0), e)
+            else:
+                assert e <= cond + TOL_FIELD and e_st <= cond + TOL_FIELD, (name, b, m, e, e_st, cond)
+                print(f"  {name} b={b} delta_{m}: ill-conditioned: gap to exact oracle {e:.3f}, "
+                      f"to bf16-storage oracle {e_st:.3f}; storage sensitivity {cond:.3f}", flush=True)
+            c_cond = abs(exp["st_scales"][b, i] / exp["scales"][b, i] - 1)
+            assert abs(got["scales"][b, i] / exp["scales"][b, i] - 1) <= TOL_FIELD + c_cond
+            assert np.all(np.isfinite(got[f"delta_{m}"][b]))
+        l_cond = abs(exp["st_loss"][b] / exp["loss"][b] - 1)
+        assert abs(got["loss"][b] / exp["loss"][b] - 1) <= TOL_DMD_LOSS + l_cond, (b, got["loss"][b], exp["loss"][b])
+    print(name, "DMD worst sampled rel-L2:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)

@@ -241,3 +241,16 @@ def test_scm_target_batch_independence():
     single = run_scm(dict(p, cfg=RAGGED.replace(B=1), data=one))
     for k in ("J_v", "J_a", "gbar_v", "gbar_a", "loss"):
         assert np.array_equal(full[k][1:2], single[k]), k
+
+
+# ---------------------------------------------------------------------------
+# The block as a rectified-flow velocity model behind the TrigFlow wrapper
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [inputs.CONFIGS["tiny"].replace(param="rf"), RAGGED.replace(param="rf"),
+                                 inputs.CONFIGS["small"].replace(param="rf")], ids=lambda c: c.name + "-rf")
+def test_scm_target_rf_wrapper_matches_oracle(cfg):
+    say(f"scm_target {cfg.name} through the TrigFlow wrapper")
+    p = inputs.make_problem(cfg)
+    got = run_scm(p)
+    ref = oracle.scm_target(p)
+    check_against_oracle(cfg, got, ref)
