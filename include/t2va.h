@@ -127,7 +127,7 @@ typedef struct {
   int64_t o_batch_stride, o_row_stride;
   int has_tangent; /* 0: forward only (qd, kd, vdt, od must be NULL) */
   int out_dtype;   /* T2VA_DTYPE_BF16 or T2VA_DTYPE_FP32 */
-  float scale;     /* logit scale; 0 selects 1/sqrt(dh) */
+  float scale;     /* logit scale, finite and >= 0; 0 selects 1/sqrt(dh) */
 } t2va_attn_desc;
 
 /*

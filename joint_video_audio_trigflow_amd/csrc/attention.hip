@@ -13,8 +13,11 @@
 // do = dA/l - (mu~/l) o.  Keys j >= nk[b] (padded text, section 6.3 of the
 // deep read) get logit -inf.
 //
-// Work decomposition: a workgroup of 12 waves (three per SIMD) owns 192 query
-// rows of one (sample, head); a wave owns 16 rows.  Products are computed
+// Work decomposition: a workgroup of 12 waves (three per SIMD) owns the query
+// rows of one (sample, head); a JVP wave owns 16 rows, a forward-only wave two
+// blocks of 16 that share every K and V^T fragment it reads from LDS (one
+// 1 KB fragment per MFMA would make LDS bandwidth, not the matrix cores, the
+// bound of the forward kernel).  Products are computed
 // transposed so that one lane column owns one query row throughout, using
 // v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8(l/16)..+7;
 // B: k = 8(l/16)..+7, column l%16; C: column l%16, rows 4(l/16)+r):
@@ -48,18 +51,27 @@ namespace {
 #define T2VA_ATTN_PIPE_JVP 1
 #endif
 #ifndef T2VA_ATTN_PIPE_FWD
-#define T2VA_ATTN_PIPE_FWD 0
+#define T2VA_ATTN_PIPE_FWD 1
+#endif
+#ifndef T2VA_ATTN_MB_FWD
+#define T2VA_ATTN_MB_FWD 2
 #endif
 constexpr int kLoadWaves = 8;         // waves that issue the LDS loads
 constexpr int BN = 64;                // keys per LDS stage
 
 template <int DH, bool TAN>
 struct AttnCfg {
-  // waves per workgroup: 12 (three per SIMD) by default; 16 query rows per wave
+  // waves per workgroup: 12 (three per SIMD) by default; MB blocks of 16
+  // query rows per wave.  Every K / V^T fragment a wave reads from LDS feeds
+  // MB (forward) or three (JVP: K for S and dS, V for O and dO) MFMAs.
   static constexpr int NW = TAN ? T2VA_ATTN_WAVES_JVP : T2VA_ATTN_WAVES_FWD;
   static constexpr bool PIPE = TAN ? T2VA_ATTN_PIPE_JVP : T2VA_ATTN_PIPE_FWD;
+  static constexpr int MB = TAN ? 1 : T2VA_ATTN_MB_FWD;
+  // row sums on the matrix cores (forward); the JVP kernel keeps them on the
+  // VALU, where its register budget has room and the matrix cores do not
+  static constexpr bool MFMA_SUMS = !TAN;
   static constexpr int THREADS = 64 * NW;
-  static constexpr int BM = 16 * NW;       // query rows per workgroup
+  static constexpr int BM = 16 * MB * NW;  // query rows per workgroup
   static constexpr int KSTEPS = DH / 32;   // MFMA k-steps over the head dimension
   static constexpr int DT = DH / 16;       // 16-row tiles of the head dimension
   static constexpr int CPR = DH / 8;       // 16-byte chunks per K row
@@ -126,19 +138,20 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int q_row = qb * C::BM + wave * 16 + l16;
-  const int q_ld = min(q_row, p.Nq - 1);
+  const int q_row0 = qb * C::BM + wave * 16 * C::MB + l16;   // + 16 mb for row block mb
   const int nk = min(max(p.nk[b], 1), p.Nk);
 
   const float scale = p.scale;
   const float c_log2 = scale * 1.4426950408889634f;
 
   // Q^T (and dQ^T) as B operands: lane holds Q[q_row][32 s + 8 g .. +7].
-  bf16x8 qf[C::KSTEPS], qdf[TAN ? C::KSTEPS : 1];
-  {
+  bf16x8 qf[C::MB][C::KSTEPS], qdf[TAN ? C::KSTEPS : 1];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int q_ld = min(q_row0 + 16 * mb, p.Nq - 1);
     const bf16 *qp = p.q + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * g;
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
+    for (int s = 0; s < C::KSTEPS; ++s) qf[mb][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
     if constexpr (TAN) {
       const bf16 *qdp = p.qd + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * g;
 #pragma unroll
@@ -213,36 +226,35 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   for (int u = 0; u < 2; ++u) voff[u] = l16 * BN + 8 * vslot(l16, 4 * u + g);
 
   // ---- logits of one 32-key sub-tile u of a stage buffer ----
-  // S[t][r] holds key 32 u + 8 g + 4 t + r.
-  auto compute_s = [&](int buf, int u, floatx4 (&S)[2], floatx4 (&Sd)[2]) {
+  // S[mb][t][r] holds key 32 u + 8 g + 4 t + r of row block mb.
+  auto compute_s = [&](int buf, int u, floatx4 (&S)[C::MB][2], floatx4 (&Sd)[2]) {
     const bf16 *kt = sK(buf) + 32 * u * DH;
     const bf16 *kdt = sKd(buf) + 32 * u * DH;
+    // the first k-step starts from a zero accumulator operand (no VALU clears)
+    const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        S[t][r] = 0.f;
-        if constexpr (TAN) Sd[t][r] = 0.f;
-      }
-#pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + koff(t, s));
-        S[t] = mfma16(ka, qf[s], S[t]);
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) S[mb][t] = mfma16(ka, qf[mb][s], s == 0 ? zero4 : S[mb][t]);
         if constexpr (TAN) {
           const bf16x8 kda = *reinterpret_cast<const bf16x8 *>(kdt + koff(t, s));
-          Sd[t] = mfma16(kda, qf[s], Sd[t]);
+          Sd[t] = mfma16(kda, qf[0][s], s == 0 ? zero4 : Sd[t]);
           Sd[t] = mfma16(ka, qdf[s], Sd[t]);
         }
       }
     }
   };
-  auto mask_s = [&](int kb, floatx4 (&S)[2], floatx4 (&Sd)[2]) {
+  auto mask_s = [&](int kb, floatx4 (&S)[C::MB][2], floatx4 (&Sd)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (kb + 8 * g + 4 * t + r >= nk) {
-          S[t][r] = -INFINITY;
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) S[mb][t][r] = -INFINITY;
           if constexpr (TAN) Sd[t][r] = 0.f;
         }
   };
@@ -277,12 +289,13 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     return mx * c_log2;
   };
 
-  floatx4 O[C::DT], Od[TAN ? C::DT : 1];
+  floatx4 O[C::MB][C::DT], Od[TAN ? C::DT : 1];
 #pragma unroll
   for (int e = 0; e < C::DT; ++e)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      O[e][r] = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) O[mb][e][r] = 0.f;
       if constexpr (TAN) Od[e][r] = 0.f;
     }
   // m_run is a reference max (log2 units), not the exact running max: it is
@@ -304,39 +317,77 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
 #define T2VA_ATTN_CENTRE 1
 #endif
   constexpr float kLazy = TAN ? T2VA_ATTN_LAZY_JVP : 16.f;
-  float m_run, l_part = 0.f, mu_part = 0.f, c_ref = 0.f;
-
-  // p = 2^(s c - m_run) and p ds as bf16 B operands (keys 8g..8g+7), row sums
-  auto softmax = [&](const floatx4 (&S)[2], const floatx4 (&Sd)[2], bf16x8 &P, bf16x8 &PS) {
-    float lsum = 0.f, musum = 0.f;
+  // Forward: the row sums l = sum p run on the matrix cores: an all-ones A
+  // operand times the bf16 weights P^T gives the sum over the sub-tile's 32
+  // keys in every row of the 16x16 result, so each lane gets the full sum of
+  // its query row with no lane exchange, from the same bf16-rounded weights
+  // as O.  JVP: l and mu~ = sum p (ds - c) are per-lane VALU partial sums,
+  // combined over the four lanes of a row at the end.
+  float m_run[C::MB], thr[C::MB], c_ref = 0.f, l_part[C::MB], mu_part = 0.f;
+  floatx4 Lacc[C::MFMA_SUMS ? C::MB : 1];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int t = m >> 2, r = m & 3;
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][r], c_log2, -m_run));
-      lsum += pv;
-      P[m] = (bf16)pv;
-      if constexpr (TAN) {
-        const float ps = pv * __builtin_fmaf(Sd[t][r], scale, -c_ref);   // p (ds - c)
-        musum += ps;
-        PS[m] = (bf16)ps;
+  for (int mb = 0; mb < C::MB; ++mb) {
+    l_part[mb] = 0.f;
+    if constexpr (C::MFMA_SUMS)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Lacc[mb][r] = 0.f;
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) ones[m] = (bf16)1.f;
+  // a row needs a raise once a raw logit exceeds (m_run + kLazy)/c_log2
+  auto set_thr = [&](int mb) { thr[mb] = (m_run[mb] + kLazy) / c_log2; };
+
+  // p = 2^(s c - m_run) and p (ds - c) as bf16 B operands (keys 8g..8g+7)
+  auto softmax = [&](const floatx4 (&S)[C::MB][2], const floatx4 (&Sd)[2], bf16x8 (&P)[C::MB],
+                     bf16x8 &PS) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      float lsum = 0.f, musum = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int t = m >> 2, r = m & 3;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][t][r], c_log2, -m_run[mb]));
+        P[mb][m] = (bf16)pv;
+        if constexpr (!C::MFMA_SUMS) lsum += pv;
+        if constexpr (TAN) {
+          const float ps = pv * __builtin_fmaf(Sd[t][r], scale, -c_ref);   // p (ds - c)
+          musum += ps;
+          PS[m] = (bf16)ps;
+        }
       }
+      if constexpr (!C::MFMA_SUMS) l_part[mb] += lsum;
+      if constexpr (TAN) mu_part += musum;
     }
-    l_part += lsum;
-    if constexpr (TAN) mu_part += musum;
   };
-  auto pv_accum = [&](int buf, int u, const bf16x8 &P, const bf16x8 &PS) {
+  auto pv_accum = [&](int buf, int u, const bf16x8 (&P)[C::MB], const bf16x8 &PS) {
     const bf16 *vt = sVT(buf) + voff[u];
     const bf16 *vdt = sVdT(buf) + voff[u];
+    if constexpr (C::MFMA_SUMS)
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) Lacc[mb] = mfma16(ones, P[mb], Lacc[mb]);
 #pragma unroll
     for (int e = 0; e < C::DT; ++e) {
       const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vt + 16 * e * BN);
-      O[e] = mfma16(va, P, O[e]);
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) O[mb][e] = mfma16(va, P[mb], O[mb][e]);
       if constexpr (TAN) {
         const bf16x8 vda = *reinterpret_cast<const bf16x8 *>(vdt + 16 * e * BN);
         Od[e] = mfma16(va, PS, Od[e]);
-        Od[e] = mfma16(vda, P, Od[e]);
+        Od[e] = mfma16(vda, P[0], Od[e]);
       }
     }
+  };
+  // any lane's own logits past its row's threshold (no lane exchange)
+  auto outgrown = [&](const floatx4 (&S)[C::MB][2]) {
+    bool any = false;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const float mx = fmaxf(fmaxf(fmaxf(S[mb][0][0], S[mb][0][1]), fmaxf(S[mb][0][2], S[mb][0][3])),
+                             fmaxf(fmaxf(S[mb][1][0], S[mb][1][1]), fmaxf(S[mb][1][2], S[mb][1][3])));
+      any = any || (mx > thr[mb]);
+    }
+    return __any(any);
   };
 
   // ---- main loop over 32-key sub-tiles; 64-key stages in two LDS buffers ----
@@ -348,19 +399,24 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   wait_loads();
   __syncthreads();
   if (nst > 1) issue(1, BN);
-  floatx4 S[2], Sd[2];
-  bf16x8 P, PS;
+  floatx4 S[C::MB][2], Sd[2];
+  bf16x8 P[C::MB], PS;
   compute_s(0, 0, S, Sd);
   if (nst == 1) mask_s(0, S, Sd);
   // key 0 is always valid, so this is finite
-  if constexpr (TAN) { m_run = row_max_arg(S, Sd, c_ref); if (!T2VA_ATTN_CENTRE) c_ref = 0.f; }
-  else m_run = row_max(S);
+  if constexpr (TAN) { m_run[0] = row_max_arg(S[0], Sd, c_ref); if (!T2VA_ATTN_CENTRE) c_ref = 0.f; }
+  else {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) m_run[mb] = row_max(S[mb]);
+  }
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) set_thr(mb);
   int j = 0;
-  floatx4 Sn[2], Sdn[2];
+  floatx4 Sn[C::MB][2], Sdn[2];
   for (;;) {
     for (; j < nsub; ++j) {
       const int u = j & 1, st = j >> 1, cur = st & 1;
-      if (__any(row_max(S) > m_run + kLazy)) break;   // rare: raise m_run outside
+      if (outgrown(S)) break;   // rare: raise m_run outside
       if constexpr (C::PIPE) {
       if (u == 1 && j + 1 < nsub) {                     // the next stage landed: publish it
         wait_loads();
@@ -375,7 +431,8 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        S[t] = Sn[t];
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) S[mb][t] = Sn[mb][t];
         if constexpr (TAN) Sd[t] = Sdn[t];
       }
       if (j + 1 < nsub && ((j + 1) >> 1) == nst - 1) mask_s(32 * (j + 1), S, Sd);
@@ -398,28 +455,45 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     if (j >= nsub) break;
     // raise the reference max of the rows that outgrew it; rescale the
     // accumulators and re-centre the tangent weights on the new max key
-    float sd_max = 0.f;
-    const float mx = TAN ? row_max_arg(S, Sd, sd_max) : row_max(S);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float c_new = (TAN && T2VA_ATTN_CENTRE && mx > m_run) ? sd_max : c_ref;
-    const float delta = c_ref - c_new;   // dA += delta A, mu~ += delta l
-    m_run = m_new;
-    c_ref = c_new;
-    if constexpr (TAN) mu_part = alpha * (mu_part + delta * l_part);
-    l_part *= alpha;
 #pragma unroll
-    for (int e = 0; e < C::DT; ++e)
+    for (int mb = 0; mb < C::MB; ++mb) {
+      float sd_max = 0.f;
+      const float mx = TAN ? row_max_arg(S[mb], Sd, sd_max) : row_max(S[mb]);
+      const float m_new = fmaxf(m_run[mb], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[mb] - m_new);
+      const float c_new = (TAN && T2VA_ATTN_CENTRE && mx > m_run[mb]) ? sd_max : c_ref;
+      const float delta = c_ref - c_new;   // dA += delta A, mu~ += delta l
+      m_run[mb] = m_new;
+      set_thr(mb);
+      if constexpr (C::MFMA_SUMS) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (TAN) Od[e][r] = alpha * __builtin_fmaf(delta, O[e][r], Od[e][r]);
-        O[e][r] *= alpha;
+        for (int r = 0; r < 4; ++r) Lacc[mb][r] *= alpha;
+      } else {
+        if constexpr (TAN) mu_part = alpha * (mu_part + delta * l_part[mb]);
+        l_part[mb] *= alpha;
       }
+      if constexpr (TAN) c_ref = c_new;
+#pragma unroll
+      for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (TAN) Od[e][r] = alpha * __builtin_fmaf(delta, O[mb][e][r], Od[e][r]);
+          O[mb][e][r] *= alpha;
+        }
+    }
   }
 
   // ---- epilogue: combine the four lanes of a row, normalise, store ----
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) {
+  const int q_row = q_row0 + 16 * mb;
+  float l_tot;
+  if constexpr (C::MFMA_SUMS) {
+    l_tot = Lacc[mb][0];
+  } else {
+    l_tot = l_part[mb] + __shfl_xor(l_part[mb], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+  }
   const float inv_l = 1.f / l_tot;
   float mu = 0.f;
   if constexpr (TAN) {
@@ -428,14 +502,14 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   }
   if (q_row < p.Nq) {
     if (p.lse && g == 0)
-      p.lse[((int64_t)b * p.H + h) * p.Nq + q_row] = m_run * 0.6931471805599453f + logf(l_tot);
+      p.lse[((int64_t)b * p.H + h) * p.Nq + q_row] = m_run[mb] * 0.6931471805599453f + logf(l_tot);
     const int64_t obase = (int64_t)b * p.o_bs + (int64_t)q_row * p.o_rs + h * DH + 4 * g;
 #pragma unroll
     for (int e = 0; e < C::DT; ++e) {
       float o4[4], od4[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        o4[r] = O[e][r] * inv_l;
+        o4[r] = O[mb][e][r] * inv_l;
         if constexpr (TAN) od4[r] = Od[e][r] * inv_l - mu * o4[r];
       }
       if (p.out_dt == 0) {
@@ -456,6 +530,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
               make_float4(od4[0], od4[1], od4[2], od4[3]);
       }
     }
+  }
   }
 }
 

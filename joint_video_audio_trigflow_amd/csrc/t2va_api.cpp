@@ -450,6 +450,8 @@ t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, c
   if (!tan && (qd || kd || vdt || od))
     return fail(T2VA_INVALID_ARG, "tangent pointers given with has_tangent = 0");
   if (!valid_dtype(d.out_dtype)) return fail(T2VA_INVALID_ARG, "bad out_dtype");
+  if (!(d.scale >= 0.f) || !isfinite(d.scale))
+    return fail(T2VA_INVALID_ARG, "scale = %g must be finite and >= 0 (0: 1/sqrt(dh))", (double)d.scale);
   const void *ptrs[] = {q, k, vt, qd, kd, vdt, nk_valid, o, od};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(T2VA_INVALID_ARG, "operands must be 16-byte aligned");
