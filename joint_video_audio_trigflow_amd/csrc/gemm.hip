@@ -151,12 +151,212 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   }
 }
 
-bool g_attr_set = false;
+// ---------------------------------------------------------------------------
+// Large-tile variant for the wide projections (the fused QKV and the input
+// projections): 256x256x64 tiles, 8 waves in 2x4, each wave 128x64 as 4x2
+// tiles of v_mfma_f32_32x32x16_bf16 (or 4 waves of 128x128).  Every A fragment
+// a wave reads from LDS feeds two MFMAs and every W fragment four, and two
+// waves per SIMD hide one another's LDS and barrier waits.  Tiles go from global memory straight
+// into LDS with buffer_load_dwordx4 ... lds: one instruction moves 8 rows x
+// 128 B; the 16-byte slot of chunk c of row r is c ^ ((r >> 1) & 7), so the 16
+// rows one 16-lane group reads hit 16 different bank groups.  Rows past M (or
+// N) lie past the buffer descriptor's end and load as zeros.
+// ---------------------------------------------------------------------------
+constexpr int LBM = 256, LBN = 256;
+constexpr int kLStageElems = (LBM + LBN) * BK;                      // unpadded rows
+constexpr size_t kLLdsBytes = 2 * kLStageElems * sizeof(bf16);      // 128 KB
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ int lslot(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+#ifndef T2VA_GEMM_LARGE_WAVES
+#define T2VA_GEMM_LARGE_WAVES 8
+#endif
+constexpr int kLWaves = T2VA_GEMM_LARGE_WAVES;        // 4 (2x2 of 128x128) or 8 (2x4 of 128x64)
+constexpr int kLThreads = 64 * kLWaves;
+constexpr int kLJ = kLWaves == 4 ? 4 : 2;             // 32-column tiles per wave
+constexpr int kLGroups = 32 / kLWaves;                // 8-row load groups per wave and operand
+
+__global__ __launch_bounds__(kLThreads) void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
+                                                                     int tiles_m) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16 *smem = reinterpret_cast<bf16 *>(smem_raw);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wm = kLWaves == 4 ? wave >> 1 : wave >> 2;
+  const int wn = kLWaves == 4 ? wave & 1 : wave & 3;
+  // column-tile-major order within groups of 8 row tiles: neighbouring
+  // workgroups share W column tiles and A row tiles in L2
+  const int bid = blockIdx.x;
+  const int group = bid / (8 * tiles_n);
+  const int first_m = group * 8;
+  const int gsize = min(tiles_m - first_m, 8);
+  const int tm = first_m + (bid % (8 * tiles_n)) % gsize;
+  const int tn = (bid % (8 * tiles_n)) / gsize;
+  const int bz = blockIdx.y;
+  const int m0 = tm * LBM, n0 = tn * LBN;
+
+  // descriptors end after the last valid row: rows >= M (N) read zeros
+  const int m_rows = max(min(p.M - m0, LBM), 0), n_rows = max(min(p.N - n0, LBN), 0);
+  const bf16 *A = p.A + (int64_t)bz * p.a_bs + (int64_t)m0 * p.lda;
+  const bf16 *W = p.W + (int64_t)n0 * p.ldw;
+  const __amdgpu_buffer_rsrc_t rA = gemm_rsrc(A, (uint32_t)(m_rows > 0 ? ((int64_t)(m_rows - 1) * p.lda + p.K) * 2 : 0));
+  const __amdgpu_buffer_rsrc_t rW = gemm_rsrc(W, (uint32_t)(n_rows > 0 ? ((int64_t)(n_rows - 1) * p.ldw + p.K) * 2 : 0));
+
+  // each wave loads kLGroups of the 32 row groups (8 rows each) of A and of W per stage
+  uint32_t aoff[kLGroups], woff[kLGroups];
+#pragma unroll
+  for (int r = 0; r < kLGroups; ++r) {
+    const int grp = wave * kLGroups + r;
+    const int row = grp * 8 + (lane >> 3);
+    const int c = lslot(row, lane & 7);          // the slot map is an involution
+    aoff[r] = (uint32_t)((row * p.lda + 8 * c) * 2);
+    woff[r] = (uint32_t)((row * p.ldw + 8 * c) * 2);
+  }
+  auto issue = [&](int stage, int k0) {
+    bf16 *sA = smem + stage * kLStageElems;
+    bf16 *sW = sA + LBM * BK;
+    const uint32_t kb = (uint32_t)(k0 * 2);
+#pragma unroll
+    for (int r = 0; r < kLGroups; ++r) {
+      const int grp = wave * kLGroups + r;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(sA + grp * 512), 16, aoff[r] + kb, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void *)(sW + grp * 512), 16, woff[r] + kb, 0, 0, 0);
+    }
+  };
+
+  // fragment read offsets (elements) for k-step s: row R, chunk 2 s + hi
+  int abase[4], wbase[kLJ], ax[4], wx[kLJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + i * 32 + l32;
+    abase[i] = ra * BK;
+    ax[i] = (ra >> 1) & 7;
+  }
+#pragma unroll
+  for (int j = 0; j < kLJ; ++j) {
+    const int rw = wn * 32 * kLJ + j * 32 + l32;
+    wbase[j] = rw * BK;
+    wx[j] = (rw >> 1) & 7;
+  }
+
+  floatx16 acc[4][kLJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < kLJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int KT = p.K / BK;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < KT) issue(stage ^ 1, (kt + 1) * BK);
+    const bf16 *sA = smem + stage * kLStageElems;
+    const bf16 *sW = sA + LBM * BK;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      bf16x8 a[4], b[kLJ];
+      const int c = 2 * s + hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sA + abase[i] + 8 * (c ^ ax[i]));
+#pragma unroll
+      for (int j = 0; j < kLJ; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(sW + wbase[j] + 8 * (c ^ wx[j]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < kLJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    // the next stage has landed (this wave's loads) and every wave is done
+    // reading this one before it is refilled
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // Epilogue.  MFMA 32x32 output: lane holds column l32 and rows 8*(v/4) + 4*hi + v%4.
+  const float *bias = p.bias ? p.bias + (int64_t)bz * p.bias_bs : nullptr;
+#pragma unroll
+  for (int j = 0; j < kLJ; ++j) {
+    const int col = n0 + wn * 32 * kLJ + j * 32 + l32;
+    if (col >= p.N) continue;
+    const float bcol = bias ? bias[col] : 0.f;
+    if (col < p.n_split) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+          if (row < p.M) {
+            const float val = acc[i][j][v] + bcol;
+            const int64_t off = (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col;
+            if (p.c_dt == 0)
+              reinterpret_cast<bf16 *>(p.C)[off] = (bf16)val;
+            else
+              reinterpret_cast<float *>(p.C)[off] = val;
+          }
+        }
+      }
+    } else {
+      const int cc = col - p.n_split;
+      const int h = cc / p.dh, e = cc % p.dh;
+      bf16 *vt = p.VT + (int64_t)bz * p.vt_bs + (int64_t)h * p.vt_hs + (int64_t)e * p.vt_rs;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row = m0 + wm * 128 + i * 32 + 8 * g + 4 * hi;
+          // rows in [M, vt_rows) read zero A rows: they store the zero padding
+          if (row + 3 < p.vt_rows) {
+            bf16x4 pk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pk[u] = (bf16)(acc[i][j][4 * g + u] + bcol);
+            *reinterpret_cast<bf16x4 *>(vt + row) = pk;
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (row + u < p.vt_rows) vt[row + u] = (bf16)(acc[i][j][4 * g + u] + bcol);
+          }
+        }
+      }
+    }
+  }
+}
+
+bool g_attr_set = false, g_lattr_set = false;
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (p.M <= 0 || p.batch <= 0) return hipSuccess;
+  const int rows = max(p.M, p.VT ? p.vt_rows : 0);
+  // the large tile for wide outputs with many rows; per-(batch, tile) byte
+  // extents must fit the 32-bit buffer descriptors
+  const bool large = p.N >= 1024 && rows >= 2048 &&
+                     (int64_t)LBM * p.lda * 2 < ((int64_t)1 << 31) &&
+                     (int64_t)LBN * p.ldw * 2 < ((int64_t)1 << 31);
+  if (large) {
+    if (!g_lattr_set) {
+      hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_large_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLLdsBytes);
+      if (e != hipSuccess) return e;
+      g_lattr_set = true;
+    }
+    const int tiles_n = (p.N + LBN - 1) / LBN;
+    const int tiles_m = (rows + LBM - 1) / LBM;
+    dim3 grid(tiles_n * tiles_m, p.batch);
+    hipLaunchKernelGGL(gemm_bf16_large_kernel, grid, dim3(kLThreads), kLLdsBytes, s, p, tiles_n, tiles_m);
+    return hipGetLastError();
+  }
   if (!g_attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
