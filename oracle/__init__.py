@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the joint sCM target, the joint DMD term and the stage-3 mix.
+"""fp64 CPU oracle for the joint sCM target, its training backward, the joint DMD term and
+the stage-3 mix.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py, never by the product path.
@@ -11,3 +12,4 @@ from .scm_oracle import (  # noqa: F401
 from .dmd_oracle import (  # noqa: F401
     dmd_sample, dmd_target, guided, residual_scale, stage3_loss, teacher_prediction,
 )
+from .grad_oracle import scm_loss_and_grads, student_fields, student_x0_torch  # noqa: F401
