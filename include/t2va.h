@@ -230,6 +230,49 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
                             t2va_stream stream);
 
 /* ------------------------------------------------------------------------ */
+/* Training backward of the joint sCM loss                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Gradients of the student's weights, fp32 device arrays shaped like the
+ * weights of t2va_block_weights (overwritten, not accumulated into). */
+typedef struct {
+  float *w_in_v;  /* [d, Cv] */
+  float *w_in_a;  /* [d, Ca] */
+  float *w_t;     /* [d, d]  */
+  float *w_qkv;   /* [3d, d] */
+  float *w_out_v; /* [Cv, d] */
+  float *w_out_a; /* [Ca, d] */
+} t2va_block_grads;
+
+/* Exact workspace size in bytes for t2va_scm_grad (0 if the descriptor is invalid). */
+size_t t2va_scm_grad_workspace_bytes(const t2va_scm_desc *desc);
+
+/*
+ * t2va_scm_grad - the joint sCM target (as t2va_scm_target: gbar, norms, loss)
+ * and the gradient of sum_b L_b with respect to every student weight
+ * (deep read, section 3.1: r = F_S - sg(F_S) - gbar, L_b = sum_m w_m ||r^m||^2).
+ * gbar is a constant (stop-gradient) target, so the gradient flows only
+ * through the student's primal forward pass:
+ *   dL/dF_S^m = -2 w_m gbar^m,  dL/dx0_S^m = 2 w_m gbar^m / sin t
+ *   (behind the TrigFlow wrapper, dL/dv = -t_rf dL/dx0),
+ * then back through the output projections, the joint attention (softmax
+ * backward, keys = video, audio and valid text), the fused QKV projection,
+ * the input projections and the time-embedding linear layer.  Divide by B
+ * for the gradient of the batch mean.
+ * Inputs and the target's outputs as in t2va_scm_target (J and r are not
+ * produced); grads: all six pointers required.
+ * workspace: at least t2va_scm_grad_workspace_bytes(desc) bytes, 256-byte aligned.
+ * Errors: as t2va_scm_target, plus T2VA_INVALID_ARG for NULL gradient pointers.
+ * Deterministic: no atomics; every reduction runs in a fixed order.
+ */
+t2va_status t2va_scm_grad(const t2va_scm_desc *desc, const t2va_block_weights *teacher,
+                          const t2va_block_weights *student, const void *z0_v, const void *z0_a,
+                          const void *eps_v, const void *eps_a, const void *text,
+                          const uint8_t *text_mask, const double *t_host, float *gbar_v, float *gbar_a,
+                          float *norms, float *loss, const t2va_block_grads *grads, void *workspace,
+                          size_t workspace_bytes, t2va_stream stream);
+
+/* ------------------------------------------------------------------------ */
 /* Joint DMD term and the stage-3 objective                                  */
 /* ------------------------------------------------------------------------ */
 
@@ -304,7 +347,8 @@ t2va_status t2va_stage3_mix(int B, double lam_scm, double lam_dmd, const float *
 #define T2VA_PHASE_STUDENT_ATTN 2 /* student attention forward + JVP       */
 #define T2VA_PHASE_GEMM 3         /* all projection GEMMs                  */
 #define T2VA_PHASE_OTHER 4        /* embedding, compaction, elementwise    */
-#define T2VA_NUM_PHASES 5
+#define T2VA_PHASE_BWD_ATTN 5     /* attention backward (t2va_scm_grad)    */
+#define T2VA_NUM_PHASES 6
 
 /*
  * t2va_profile_enable - with max_calls > 0, the next up to max_calls calls of

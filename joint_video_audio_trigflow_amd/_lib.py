@@ -24,8 +24,8 @@ NOISE, FIELD = 0, 1
 PARAM_X0, PARAM_RF = 0, 1
 ABI_VERSION = 2
 MAX_BATCH = 64
-NUM_PHASES = 5
-PHASES = ("total", "teacher_attn", "student_attn", "gemm", "other")
+NUM_PHASES = 6
+PHASES = ("total", "teacher_attn", "student_attn", "gemm", "other", "bwd_attn")
 
 
 class T2VAError(RuntimeError):
@@ -65,6 +65,10 @@ class BlockWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_in_v", "w_in_a", "w_t", "w_qkv", "w_out_v", "w_out_a")]
 
 
+class BlockGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_in_v", "w_in_a", "w_t", "w_qkv", "w_out_v", "w_out_a")]
+
+
 WEIGHT_NAMES = ("w_in_v", "w_in_a", "w_t", "w_qkv", "w_out_v", "w_out_a")
 
 _lib = None
@@ -96,6 +100,12 @@ def load() -> ctypes.CDLL:
     lib.t2va_scm_target.argtypes = ([ctypes.POINTER(ScmDesc), ctypes.POINTER(BlockWeights),
                                      ctypes.POINTER(BlockWeights)] + [vp] * 5 + [vp, dp]
                                     + [f32p] * 8 + [vp, ctypes.c_size_t, vp])
+    lib.t2va_scm_grad_workspace_bytes.restype = ctypes.c_size_t
+    lib.t2va_scm_grad_workspace_bytes.argtypes = [ctypes.POINTER(ScmDesc)]
+    lib.t2va_scm_grad.restype = i32
+    lib.t2va_scm_grad.argtypes = ([ctypes.POINTER(ScmDesc), ctypes.POINTER(BlockWeights),
+                                   ctypes.POINTER(BlockWeights)] + [vp] * 5 + [vp, dp]
+                                  + [f32p] * 4 + [ctypes.POINTER(BlockGrads), vp, ctypes.c_size_t, vp])
     lib.t2va_dmd_workspace_bytes.restype = ctypes.c_size_t
     lib.t2va_dmd_workspace_bytes.argtypes = [ctypes.POINTER(DmdDesc)]
     lib.t2va_dmd_target.restype = i32
@@ -262,6 +272,53 @@ class ScmTarget:
             _ptr(o["r_a"]), _ptr(o["norms"]), _ptr(o["loss"]), self.ws_ptr, self.ws_bytes,
             _stream(self.device)))
         return o
+
+
+def grad_workspace_bytes(desc: ScmDesc) -> int:
+    n = load().t2va_scm_grad_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        raise T2VAError(1, load().t2va_last_error().decode())
+    return n
+
+
+class ScmGrad:
+    """Holds device buffers for repeated calls of t2va_scm_grad on one shape:
+    the target's gbar, norms and loss, and fp32 gradients of the six student
+    weights (of sum_b L_b)."""
+
+    def __init__(self, cfg, device="cuda", in_dtype=DTYPE_BF16, weight_dtype=DTYPE_BF16):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.desc = scm_desc(cfg, in_dtype, weight_dtype)
+        self.ws_bytes = grad_workspace_bytes(self.desc)
+        self.workspace = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.workspace.data_ptr()
+        self.ws_ptr = ctypes.c_void_p((base + 255) // 256 * 256)
+        B, d = cfg.B, cfg.d
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.out = {
+            "gbar_v": torch.empty((B, cfg.Nv, cfg.Cv), **f32),
+            "gbar_a": torch.empty((B, cfg.Na, cfg.Ca), **f32),
+            "norms": torch.empty((B, 2), **f32),
+            "loss": torch.empty((B,), **f32),
+        }
+        shapes = {"w_in_v": (d, cfg.Cv), "w_in_a": (d, cfg.Ca), "w_t": (d, d), "w_qkv": (3 * d, d),
+                  "w_out_v": (cfg.Cv, d), "w_out_a": (cfg.Ca, d)}
+        self.grads = {k: torch.empty(v, **f32) for k, v in shapes.items()}
+        self._gs = BlockGrads()
+        for k, v in self.grads.items():
+            setattr(self._gs, k, v.data_ptr())
+
+    def __call__(self, teacher: dict, student: dict, z0_v, z0_a, eps_v, eps_a, text, text_mask, t):
+        lib = load()
+        tw, sw = ScmTarget.weights_struct(teacher), ScmTarget.weights_struct(student)
+        o = self.out
+        _check(lib.t2va_scm_grad(
+            ctypes.byref(self.desc), ctypes.byref(tw), ctypes.byref(sw), _ptr(z0_v), _ptr(z0_a),
+            _ptr(eps_v), _ptr(eps_a), _ptr(text), _ptr(text_mask), _t_host(t),
+            _ptr(o["gbar_v"]), _ptr(o["gbar_a"]), _ptr(o["norms"]), _ptr(o["loss"]), ctypes.byref(self._gs),
+            self.ws_ptr, self.ws_bytes, _stream(self.device)))
+        return o, self.grads
 
 
 def dmd_desc(cfg, in_dtype: int, weight_dtype: int, cfg_v=None, cfg_a=None) -> DmdDesc:

@@ -1,0 +1,450 @@
+// Joint attention backward on bf16 MFMA (gfx950), for the training backward of
+// the joint sCM loss: the loss reaches the student's weights only through its
+// primal forward pass (the target gbar is under stop-gradient; deep read of
+// TurboT2VA, section 3.1), so the attention backward is the ordinary one of
+// the primal softmax attention:
+//   P = softmax(scale Q K^T) (keys >= nk[b] excluded), dP = dO V^T,
+//   dS = P * (dP - D) with D_i = sum_e dO_ie O_ie,
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// P is recomputed from the forward's log-sum-exp (log2 units), so no running
+// max is needed.  Two kernels, both deterministic (no atomics):
+//
+// * dQ: a wave owns 16 query rows and streams key tiles; in registers it keeps
+//   Q and dO as B operands; per 32-key sub-tile it forms S^T = K Q^T and
+//   dP^T = V dO^T (A: K and V rows from LDS, read in the permuted row order
+//   that makes the 8 values a lane holds the 8 keys of its B operand), then
+//   dQ^T += K^T dS^T (A: K^T rows from LDS, B: dS^T from registers).
+// * dK/dV: a wave owns 16 keys and streams query tiles; in registers it keeps
+//   K and V as B operands; per 32-query sub-tile it forms S = Q K^T and
+//   dP = dO V^T (A: Q and dO rows from LDS, permuted), then
+//   dV^T += dO^T P and dK^T += Q^T dS (A: dO^T and Q^T rows from LDS).
+//
+// Each kernel therefore reads its streamed operand in both layouts (rows for
+// the contraction over the head dimension, transposed for the contraction over
+// tokens); the transposed copies are written beforehand by a transpose kernel.
+// Tiles go straight from global memory into LDS (buffer_load ... lds),
+// double-buffered in 64-token stages, with the swizzles of attn_tiles.h.
+#include "attn_tiles.h"
+#include "common.h"
+
+#include <math.h>
+
+namespace t2va {
+
+namespace {
+
+#ifndef T2VA_BWD_WAVES
+#define T2VA_BWD_WAVES 8
+#endif
+constexpr int BT = 64;          // streamed tokens per LDS stage
+constexpr int kBwdLoaders = 8;  // waves that issue the LDS loads
+
+template <int DH>
+struct BwdCfg {
+  static constexpr int NW = T2VA_BWD_WAVES;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BW = 16 * NW;        // rows (queries or keys) per workgroup
+  static constexpr int KSTEPS = DH / 32;
+  static constexpr int DT = DH / 16;
+  static constexpr int CPR = DH / 8;
+  static constexpr int ROW_ELEMS = BT * DH;   // row tile [BT][DH]
+  static constexpr int T_ELEMS = DH * BT;     // transposed tile [DH][BT]
+  static constexpr int RCH = ROW_ELEMS / 512 / kBwdLoaders;
+  static constexpr int TCH = T_ELEMS / 512 / kBwdLoaders;
+  static constexpr int ROWS_PER_CHUNK = 512 / DH;
+  // dQ stage: K rows, V rows, K^T; dK/dV stage: Q rows, dO rows, Q^T, dO^T, lse2, D
+  static constexpr int DQ_STAGE = 2 * ROW_ELEMS + T_ELEMS;
+  static constexpr int DKV_STAGE = 2 * ROW_ELEMS + 2 * T_ELEMS + 2 * BT * 2;  // + 2 x 64 floats
+  static constexpr size_t DQ_LDS = (size_t)2 * DQ_STAGE * sizeof(bf16);
+  static constexpr size_t DKV_LDS = (size_t)2 * DKV_STAGE * sizeof(bf16);
+};
+
+// Per-lane byte offsets (at token 0) of the chunks a loading wave moves into a
+// row tile / a transposed tile; chunk j of the tile holds 512 elements.
+template <int DH>
+struct TileOffsets {
+  using C = BwdCfg<DH>;
+  uint32_t row[C::RCH], tr[C::TCH];
+  __device__ void init(int lw, int lane, int64_t rs, int64_t trs) {
+#pragma unroll
+    for (int r = 0; r < C::RCH; ++r) {
+      const int chunk = lw + kBwdLoaders * r;
+      const int rr = chunk * C::ROWS_PER_CHUNK + lane / C::CPR;
+      const int c = kslot<C::CPR>(rr, lane % C::CPR);
+      row[r] = (uint32_t)((rr * rs + 8 * c) * 2);
+    }
+#pragma unroll
+    for (int r = 0; r < C::TCH; ++r) {
+      const int chunk = lw + kBwdLoaders * r;
+      const int e = chunk * 8 + lane / 8;
+      tr[r] = (uint32_t)((e * trs + 8 * vslot(e, lane % 8)) * 2);
+    }
+  }
+};
+
+// A-operand read offsets (elements) of a row tile: half t, k-step s of a
+// 32-row sub-tile (add 32 * DH per sub-tile); rows in the order 8(i/4)+4t+i%4.
+template <int DH>
+struct RowReader {
+  int base[2], xs[2];
+  __device__ void init(int l16, int g) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = 8 * (l16 >> 2) + 4 * t + (l16 & 3);
+      const int x = kslot<DH / 8>(row, 0);
+      base[t] = row * DH + 8 * (g ^ (x & 3));
+      xs[t] = x >> 2;
+    }
+  }
+  __device__ int off(int u, int t, int s) const { return 32 * u * DH + base[t] + 32 * (s ^ xs[t]); }
+};
+
+// A-operand read offsets of a transposed tile: row e = 16 et + l16, token
+// chunk g of 32-token sub-tile u.
+struct TrReader {
+  int base[2];
+  __device__ void init(int l16, int g) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) base[u] = l16 * BT + 8 * vslot(l16, 4 * u + g);
+  }
+  __device__ int off(int u, int et) const { return base[u] + 16 * et * BT; }
+};
+
+__device__ __forceinline__ void xcd_tile(int w, int per_xcd, int total, int &L) {
+  L = (w & 7) * per_xcd + (w >> 3);
+  if (L >= total) L = -1;
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dq_kernel(AttnBwdParams p, int nqb,
+                                                                              int per_xcd, int total) {
+  using C = BwdCfg<DH>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16 *const lds = reinterpret_cast<bf16 *>(smem_raw);
+  auto sK = [&](int buf) { return lds + buf * C::DQ_STAGE; };
+  auto sV = [&](int buf) { return lds + buf * C::DQ_STAGE + C::ROW_ELEMS; };
+  auto sKT = [&](int buf) { return lds + buf * C::DQ_STAGE + 2 * C::ROW_ELEMS; };
+
+  int L;
+  xcd_tile(blockIdx.x, per_xcd, total, L);
+  if (L < 0) return;
+  const int qb = L % nqb, bh = L / nqb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int q_row = qb * C::BW + wave * 16 + l16;
+  const int q_ld = min(q_row, p.Nq - 1);
+  const int nk = min(max(p.nk[b], 1), p.Nk);
+  const float c_log2 = p.scale * 1.4426950408889634f;
+
+  bf16x8 qf[C::KSTEPS], dof[C::KSTEPS];
+  {
+    const bf16 *qp = p.q + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * g;
+    const bf16 *dp = p.dout + (int64_t)b * p.do_bs + (int64_t)q_ld * p.do_rs + h * DH + 8 * g;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
+      dof[s] = *reinterpret_cast<const bf16x8 *>(dp + 32 * s);
+    }
+  }
+  const int64_t sidx = ((int64_t)b * p.H + h) * p.Nq + q_ld;
+  const float lse2 = p.lse2[sidx], Dq = p.D[sidx];
+
+  // K and V row descriptors end after key row nk-1 (rows past it load as
+  // zeros); K^T columns past nk hold finite values (zeros or padded text
+  // keys) and meet zero weights.
+  const uint32_t k_bytes = (uint32_t)(((int64_t)(nk - 1) * p.k_rs + DH) * 2);
+  const uint32_t v_bytes = (uint32_t)(((int64_t)(nk - 1) * p.v_rs + DH) * 2);
+  const uint32_t kt_bytes = (uint32_t)((int64_t)DH * p.kt_rs * 2);
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.k + (int64_t)b * p.k_bs + h * DH, k_bytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.v + (int64_t)b * p.v_bs + h * DH, v_bytes);
+  const __amdgpu_buffer_rsrc_t rKT = make_rsrc(p.kt + (int64_t)b * p.kt_bs + (int64_t)h * p.kt_hs, kt_bytes);
+  const int lw = wave % kBwdLoaders;
+  const bool loader = wave < kBwdLoaders;
+  TileOffsets<DH> ko, vo;
+  ko.init(lw, lane, p.k_rs, p.kt_rs);
+  vo.init(lw, lane, p.v_rs, p.kt_rs);
+  auto issue = [&](int buf, int k0) {
+    if (!loader) return;
+    const uint32_t kst = (uint32_t)(k0 * p.k_rs * 2), vst = (uint32_t)(k0 * p.v_rs * 2), tst = (uint32_t)(k0 * 2);
+#pragma unroll
+    for (int r = 0; r < C::RCH; ++r) {
+      const int chunk = lw + kBwdLoaders * r;
+      load_lds16(rK, ko.row[r] + kst, sK(buf) + chunk * 512);
+      load_lds16(rV, vo.row[r] + vst, sV(buf) + chunk * 512);
+    }
+#pragma unroll
+    for (int r = 0; r < C::TCH; ++r) {
+      const int chunk = lw + kBwdLoaders * r;
+      load_lds16(rKT, ko.tr[r] + tst, sKT(buf) + chunk * 512);
+    }
+  };
+
+  RowReader<DH> rr;
+  rr.init(l16, g);
+  TrReader tr;
+  tr.init(l16, g);
+
+  floatx4 acc[C::DT];
+#pragma unroll
+  for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[e][r] = 0.f;
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  const int nst = (nk + BT - 1) / BT;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < nst) issue(cur ^ 1, (st + 1) * BT);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      floatx4 S[2], dP[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sK(cur) + rr.off(u, t, s));
+          const bf16x8 va = *reinterpret_cast<const bf16x8 *>(sV(cur) + rr.off(u, t, s));
+          S[t] = mfma16(ka, qf[s], s == 0 ? zero4 : S[t]);
+          dP[t] = mfma16(va, dof[s], s == 0 ? zero4 : dP[t]);
+        }
+      }
+      bf16x8 dS;
+      const int kbase = st * BT + 32 * u + 8 * g;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int t = m >> 2, r = m & 3;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][r], c_log2, -lse2));
+        if (kbase + 4 * t + r >= nk) pv = 0.f;
+        dS[m] = (bf16)(pv * (dP[t][r] - Dq));
+      }
+#pragma unroll
+      for (int e = 0; e < C::DT; ++e) {
+        const bf16x8 kta = *reinterpret_cast<const bf16x8 *>(sKT(cur) + tr.off(u, e));
+        acc[e] = mfma16(kta, dS, acc[e]);
+      }
+    }
+    // this wave's loads of the next stage have landed and every wave is done
+    // with the current stage before it is refilled
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (q_row < p.Nq) {
+    bf16 *dst = p.dq + (int64_t)b * p.dq_bs + (int64_t)q_row * p.dq_rs + h * DH + 4 * g;
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) {
+      bf16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc[e][r] * p.scale);
+      *reinterpret_cast<bf16x4 *>(dst + 16 * e) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dkv_kernel(AttnBwdParams p, int nkb,
+                                                                               int per_xcd, int total) {
+  using C = BwdCfg<DH>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16 *const lds = reinterpret_cast<bf16 *>(smem_raw);
+  auto sQ = [&](int buf) { return lds + buf * C::DKV_STAGE; };
+  auto sDO = [&](int buf) { return lds + buf * C::DKV_STAGE + C::ROW_ELEMS; };
+  auto sQT = [&](int buf) { return lds + buf * C::DKV_STAGE + 2 * C::ROW_ELEMS; };
+  auto sDOT = [&](int buf) { return lds + buf * C::DKV_STAGE + 2 * C::ROW_ELEMS + C::T_ELEMS; };
+  auto sL = [&](int buf) {
+    return reinterpret_cast<float *>(lds + buf * C::DKV_STAGE + 2 * C::ROW_ELEMS + 2 * C::T_ELEMS);
+  };
+  auto sD = [&](int buf) { return sL(buf) + BT; };
+
+  int L;
+  xcd_tile(blockIdx.x, per_xcd, total, L);
+  if (L < 0) return;
+  const int kb = L % nkb, bh = L / nkb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int k_row = kb * C::BW + wave * 16 + l16;
+  const int k_ld = min(k_row, p.Nk - 1);
+  const int nk = min(max(p.nk[b], 1), p.Nk);
+  const bool k_valid = k_row < nk;
+  const float c_log2 = p.scale * 1.4426950408889634f;
+
+  bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
+  {
+    const bf16 *kp = p.k + (int64_t)b * p.k_bs + (int64_t)k_ld * p.k_rs + h * DH + 8 * g;
+    const bf16 *vp = p.v + (int64_t)b * p.v_bs + (int64_t)k_ld * p.v_rs + h * DH + 8 * g;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+      kf[s] = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
+      vf[s] = *reinterpret_cast<const bf16x8 *>(vp + 32 * s);
+    }
+  }
+
+  // Q and dO row descriptors end after query row Nq-1; the transposed copies
+  // are zero past Nq; lse2 and D past Nq load as zeros and those queries'
+  // weights are masked.
+  const int Nq = p.Nq;
+  const uint32_t q_bytes = (uint32_t)(((int64_t)(Nq - 1) * p.q_rs + DH) * 2);
+  const uint32_t do_bytes = (uint32_t)(((int64_t)(Nq - 1) * p.do_rs + DH) * 2);
+  const uint32_t qt_bytes = (uint32_t)((int64_t)DH * p.qt_rs * 2);
+  const uint32_t s_bytes = (uint32_t)(Nq * 4);
+  const __amdgpu_buffer_rsrc_t rQ = make_rsrc(p.q + (int64_t)b * p.q_bs + h * DH, q_bytes);
+  const __amdgpu_buffer_rsrc_t rDO = make_rsrc(p.dout + (int64_t)b * p.do_bs + h * DH, do_bytes);
+  const __amdgpu_buffer_rsrc_t rQT = make_rsrc(p.qt + (int64_t)b * p.qt_bs + (int64_t)h * p.qt_hs, qt_bytes);
+  const __amdgpu_buffer_rsrc_t rDOT = make_rsrc(p.dot + (int64_t)b * p.qt_bs + (int64_t)h * p.qt_hs, qt_bytes);
+  const int64_t srow = ((int64_t)b * p.H + h) * Nq;
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.lse2 + srow, s_bytes);
+  const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.D + srow, s_bytes);
+  const int lw = wave % kBwdLoaders;
+  const bool loader = wave < kBwdLoaders;
+  TileOffsets<DH> qo, doo;
+  qo.init(lw, lane, p.q_rs, p.qt_rs);
+  doo.init(lw, lane, p.do_rs, p.qt_rs);
+  auto issue = [&](int buf, int q0) {
+    if (!loader) return;
+    const uint32_t qst = (uint32_t)(q0 * p.q_rs * 2), dst = (uint32_t)(q0 * p.do_rs * 2), tst = (uint32_t)(q0 * 2);
+#pragma unroll
+    for (int r = 0; r < C::RCH; ++r) {
+      const int chunk = lw + kBwdLoaders * r;
+      load_lds16(rQ, qo.row[r] + qst, sQ(buf) + chunk * 512);
+      load_lds16(rDO, doo.row[r] + dst, sDO(buf) + chunk * 512);
+    }
+#pragma unroll
+    for (int r = 0; r < C::TCH; ++r) {
+      const int chunk = lw + kBwdLoaders * r;
+      load_lds16(rQT, qo.tr[r] + tst, sQT(buf) + chunk * 512);
+      load_lds16(rDOT, qo.tr[r] + tst, sDOT(buf) + chunk * 512);
+    }
+    if (lw == 0) {   // 64 lanes x 4 B: the stage's lse2 and D
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (lds_void *)sL(buf), 4, (uint32_t)((q0 + lane) * 4), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (lds_void *)sD(buf), 4, (uint32_t)((q0 + lane) * 4), 0, 0, 0);
+    }
+  };
+
+  RowReader<DH> rr;
+  rr.init(l16, g);
+  TrReader tr;
+  tr.init(l16, g);
+
+  floatx4 dK[C::DT], dV[C::DT];
+#pragma unroll
+  for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dK[e][r] = 0.f;
+      dV[e][r] = 0.f;
+    }
+  const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  const int nst = (Nq + BT - 1) / BT;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < nst) issue(cur ^ 1, (st + 1) * BT);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      floatx4 S[2], dP[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ(cur) + rr.off(u, t, s));
+          const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sDO(cur) + rr.off(u, t, s));
+          S[t] = mfma16(qa, kf[s], s == 0 ? zero4 : S[t]);
+          dP[t] = mfma16(da, vf[s], s == 0 ? zero4 : dP[t]);
+        }
+      }
+      // this lane's queries: 32 u + 8 g + m of the stage, m = 4 t + r
+      const float4 l0 = *reinterpret_cast<const float4 *>(sL(cur) + 32 * u + 8 * g);
+      const float4 l1 = *reinterpret_cast<const float4 *>(sL(cur) + 32 * u + 8 * g + 4);
+      const float4 d0 = *reinterpret_cast<const float4 *>(sD(cur) + 32 * u + 8 * g);
+      const float4 d1 = *reinterpret_cast<const float4 *>(sD(cur) + 32 * u + 8 * g + 4);
+      const float lq[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      const float dq[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      const int qbase = st * BT + 32 * u + 8 * g;
+      bf16x8 P, dS;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int t = m >> 2, r = m & 3;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][r], c_log2, -lq[m]));
+        if (!k_valid || qbase + m >= Nq) pv = 0.f;
+        P[m] = (bf16)pv;
+        dS[m] = (bf16)(pv * (dP[t][r] - dq[m]));
+      }
+#pragma unroll
+      for (int e = 0; e < C::DT; ++e) {
+        const bf16x8 doa = *reinterpret_cast<const bf16x8 *>(sDOT(cur) + tr.off(u, e));
+        const bf16x8 qta = *reinterpret_cast<const bf16x8 *>(sQT(cur) + tr.off(u, e));
+        dV[e] = mfma16(doa, P, dV[e]);
+        dK[e] = mfma16(qta, dS, dK[e]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (k_row < p.Nk) {
+    const int64_t o = (int64_t)b * p.dk_bs + (int64_t)k_row * p.dk_rs + h * DH + 4 * g;
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) {
+      bf16x4 vk, vv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        vk[r] = (bf16)(dK[e][r] * p.scale);
+        vv[r] = (bf16)dV[e][r];
+      }
+      *reinterpret_cast<bf16x4 *>(p.dk + o + 16 * e) = vk;
+      *reinterpret_cast<bf16x4 *>(p.dv + o + 16 * e) = vv;
+    }
+  }
+}
+
+template <int DH>
+hipError_t launch_bwd_impl(const AttnBwdParams &p, hipStream_t s) {
+  using C = BwdCfg<DH>;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_dq_kernel<DH>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::DQ_LDS);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void *)attn_bwd_dkv_kernel<DH>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::DKV_LDS);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int nqb = (p.Nq + C::BW - 1) / C::BW;
+  int total = nqb * p.H * p.B;
+  int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DH>), dim3(per_xcd * 8), dim3(C::THREADS), C::DQ_LDS, s, p, nqb,
+                     per_xcd, total);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkb = (p.Nk + C::BW - 1) / C::BW;
+  total = nkb * p.H * p.B;
+  per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DH>), dim3(per_xcd * 8), dim3(C::THREADS), C::DKV_LDS, s, p, nkb,
+                     per_xcd, total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_bwd(int dh, const AttnBwdParams &p, hipStream_t s) {
+  if (dh == 128) return launch_bwd_impl<128>(p, s);
+  if (dh == 64) return launch_bwd_impl<64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace t2va

@@ -1,0 +1,197 @@
+// HBM-bound steps of the training backward of the joint sCM loss: the seed
+// dL/dy of the block's output, layout changes (transposes) between the
+// backward GEMMs and the attention backward, the attention backward's row
+// terms D = rowsum(dO * O) and log2-unit log-sum-exp, the time-embedding
+// gradient, and the fixed-order reduction of split-K partial products.
+//
+// Method: TurboT2VA deep read (robotworld.top, arXiv 2608.24674), section 3.1:
+// r = F_theta - sg(F_theta) - gbar and L = sum_m w_m ||r^m||^2, so
+// dL/dF_theta^m = -2 w_m gbar^m with gbar constant; F_theta = (cos t z - x0)/sin t.
+#include "common.h"
+
+namespace t2va {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// dy[b][i] = bf16(coef[b] gbar[b][i]), coef = 2 w bo / sin t: the gradient of
+// sum_m w_m ||r^m||^2 at the block's output y (x0 = y, or x0 = z_rf - t_rf y).
+__global__ __launch_bounds__(kThreads) void seed_kernel(CoefTable coef, float w, const float *gbar, bf16 *dy,
+                                                        int64_t n) {
+  const int bi = blockIdx.y;
+  const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (i0 >= n) return;
+  const Coef c = coef.c[bi];
+  const float bo = coef.rf ? -c.t_emb : 1.f;
+  const float k = 2.f * w * bo * c.inv_sin;
+  float f[8];
+  load8(gbar + (int64_t)bi * n + i0, f);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] *= k;
+  store8(dy + (int64_t)bi * n + i0, f);
+}
+
+// dst[c][r] = src[r][c] for one (b, h) slice per blockIdx.z; rows r in
+// [R, Rpad) of dst are written as zeros.  64x64 tiles through LDS.
+template <typename TS>
+__global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeParams p) {
+  __shared__ float tile[64][65];
+  const int bh = blockIdx.z;
+  const int b = bh / p.H, h = bh % p.H;
+  const TS *src = reinterpret_cast<const TS *>(p.src) + (int64_t)b * p.s_bs + (int64_t)h * p.s_hs;
+  bf16 *dst = p.dst + (int64_t)b * p.d_bs + (int64_t)h * p.d_hs;
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < p.R && c < p.C) ? to_f32(src[(int64_t)r * p.s_rs + c]) : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < p.C && r < p.Rpad) dst[(int64_t)c * p.d_rs + r] = (bf16)tile[tx][i];
+  }
+}
+
+// D[b][h][q] = sum_e dO[q][h dh + e] O[q][h dh + e]; lse2 = lse log2(e).
+// One wave per (b, q): lanes split the d columns, then a per-head reduction.
+__global__ __launch_bounds__(kThreads) void rowterm_kernel(const bf16 *dO, const bf16 *O, int64_t bs,
+                                                           int64_t rs, int B, int H, int dh, int Nq,
+                                                           const float *lse, float *lse2, float *D) {
+  const int lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (idx >= (int64_t)B * Nq) return;
+  const int b = (int)(idx / Nq), q = (int)(idx % Nq);
+  const bf16 *a = dO + (int64_t)b * bs + (int64_t)q * rs;
+  const bf16 *o = O + (int64_t)b * bs + (int64_t)q * rs;
+  // each head's dh columns are handled by dh/8 consecutive lanes (8 columns each)
+  const int lanes_per_head = dh / 8;
+  const int heads_per_pass = 64 / lanes_per_head;
+  for (int h0 = 0; h0 < H; h0 += heads_per_pass) {
+    const int h = h0 + lane / lanes_per_head;
+    float acc = 0.f;
+    if (h < H) {
+      float fa[8], fo[8];
+      load8(a + h * dh + (lane % lanes_per_head) * 8, fa);
+      load8(o + h * dh + (lane % lanes_per_head) * 8, fo);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += fa[j] * fo[j];
+    }
+    for (int off = lanes_per_head / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (h < H && lane % lanes_per_head == 0) {
+      const int64_t s = ((int64_t)b * H + h) * Nq + q;
+      D[s] = acc;
+      lse2[s] = lse[s] * 1.4426950408889634f;
+    }
+  }
+}
+
+// X[b][r][0:cols] = 0 for r in [r0, r1): the dQ columns of the text rows.
+__global__ __launch_bounds__(kThreads) void zero_rows_kernel(bf16 *X, int64_t bs, int64_t rs, int r0, int r1,
+                                                             int cols) {
+  const int b = blockIdx.y;
+  const int r = r0 + blockIdx.x;
+  if (r >= r1) return;
+  bf16 *row = X + (int64_t)b * bs + (int64_t)r * rs;
+  for (int c = threadIdx.x * 8; c < cols; c += kThreads * 8) {
+    const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    store8(row + c, z);
+  }
+}
+
+// part[b][chunk][j] = sum over rows of chunk `chunk` of dX[b][row][j].
+__global__ __launch_bounds__(kThreads) void colsum_kernel(const bf16 *dX, int64_t bs, int64_t rs, int rows,
+                                                          int cols, int rows_per_chunk, int nchunk,
+                                                          float *part) {
+  const int j = blockIdx.x * kThreads + threadIdx.x;
+  const int chunk = blockIdx.y, b = blockIdx.z;
+  if (j >= cols) return;
+  const int r0 = chunk * rows_per_chunk, r1 = min(rows, r0 + rows_per_chunk);
+  const bf16 *x = dX + (int64_t)b * bs + j;
+  float acc = 0.f;
+  for (int r = r0; r < r1; ++r) acc += to_f32(x[(int64_t)r * rs]);
+  part[((int64_t)b * nchunk + chunk) * cols + j] = acc;
+}
+
+// dW_t[i][j] = sum_b (sum_chunk part[b][chunk][i]) E[b][j]: the gradient of
+// tau = W_t e through the bias of every video and audio row.
+__global__ __launch_bounds__(kThreads) void time_grad_kernel(const float *part, int B, int nchunk, int d,
+                                                             const float *E, float *dWt) {
+  const int i = blockIdx.y;
+  const int j = blockIdx.x * kThreads + threadIdx.x;
+  if (j >= d) return;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b) {
+    float g = 0.f;
+    for (int c = 0; c < nchunk; ++c) g += part[((int64_t)b * nchunk + c) * d + i];
+    acc += g * E[(int64_t)b * d + j];
+  }
+  dWt[(int64_t)i * d + j] = acc;
+}
+
+// out[i] = sum_s part[s][i] in order s = 0, 1, ... (split-K partial products).
+__global__ __launch_bounds__(kThreads) void reduce_splits_kernel(const float *part, int splits, int64_t n,
+                                                                 float *out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int s = 0; s < splits; ++s) acc += part[(int64_t)s * n + i];
+  out[i] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_seed(const CoefTable &coef, float w, const float *gbar, bf16 *dy, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((unsigned)((n / 8 + kThreads - 1) / kThreads), coef.B);
+  hipLaunchKernelGGL(seed_kernel, grid, dim3(kThreads), 0, s, coef, w, gbar, dy, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const TransposeParams &p, int src_fp32, hipStream_t s) {
+  if (p.R <= 0 && p.Rpad <= 0) return hipSuccess;
+  dim3 grid((unsigned)((p.Rpad + 63) / 64), (unsigned)((p.C + 63) / 64), (unsigned)(p.B * p.H));
+  if (src_fp32)
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowterms(const bf16 *dO, const bf16 *O, int64_t bs, int64_t rs, int B, int H, int dh, int Nq,
+                           const float *lse, float *lse2, float *D, hipStream_t s) {
+  const int64_t rows = (int64_t)B * Nq;
+  const unsigned blocks = (unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64));
+  hipLaunchKernelGGL(rowterm_kernel, dim3(blocks), dim3(kThreads), 0, s, dO, O, bs, rs, B, H, dh, Nq, lse,
+                     lse2, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(bf16 *X, int64_t bs, int64_t rs, int B, int r0, int r1, int cols, hipStream_t s) {
+  if (r1 <= r0) return hipSuccess;
+  hipLaunchKernelGGL(zero_rows_kernel, dim3(r1 - r0, B), dim3(kThreads), 0, s, X, bs, rs, r0, r1, cols);
+  return hipGetLastError();
+}
+
+int colsum_chunks(int rows) { return (rows + 511) / 512; }
+
+hipError_t launch_time_grad(const bf16 *dX, int64_t bs, int64_t rs, int B, int rows, int d, const float *E,
+                            float *part, float *dWt, hipStream_t s) {
+  const int nchunk = colsum_chunks(rows);
+  hipLaunchKernelGGL(colsum_kernel, dim3((d + kThreads - 1) / kThreads, nchunk, B), dim3(kThreads), 0, s, dX,
+                     bs, rs, rows, d, 512, nchunk, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(time_grad_kernel, dim3((d + kThreads - 1) / kThreads, d), dim3(kThreads), 0, s, part, B,
+                     nchunk, d, E, dWt);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_splits(const float *part, int splits, int64_t n, float *out, hipStream_t s) {
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     s, part, splits, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace t2va

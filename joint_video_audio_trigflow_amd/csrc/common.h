@@ -169,7 +169,7 @@ hipError_t launch_mix(int B, float a, const float *x, float c, const float *y, f
 // C = A W^T (+ bias) for `batch` independent problems.
 struct GemmParams {
   const bf16 *A; int64_t lda, a_bs;
-  const bf16 *W; int64_t ldw;             // W [N, K], shared by all batches
+  const bf16 *W; int64_t ldw, w_bs;       // W [N, K]; w_bs = 0 shares it across batches
   void *C; int64_t ldc, c_bs; int c_dt;   // columns [0, n_split) go to C
   const float *bias; int64_t bias_bs;     // nullable, fp32 [batch][N]
   bf16 *VT; int64_t vt_bs, vt_hs, vt_rs;  // columns >= n_split: V^T[b][h][c][row]
@@ -191,5 +191,43 @@ struct AttnParams {
   float scale;
 };
 hipError_t launch_attention(int dh, bool tangent, const AttnParams &p, hipStream_t s);
+
+// Attention backward for one (sample, head) grid: dQ, dK, dV from Q, K, V, dO,
+// the forward's log2-unit log-sum-exp and D = rowsum(dO * O).  Row-major
+// operands [b][row][h*dh + e] (strides *_bs, *_rs); transposed operands
+// [b][h][e][token] (strides *_bs, *_hs, *_rs).
+struct AttnBwdParams {
+  const bf16 *q, *k, *v, *dout;          // row-major
+  const bf16 *qt, *kt, *dot;             // transposed (Q^T, K^T, dO^T)
+  const float *lse2, *D;                 // [B][H][Nq]
+  const int32_t *nk;
+  bf16 *dq, *dk, *dv;                    // row-major outputs
+  int64_t q_bs, q_rs, k_bs, k_rs, v_bs, v_rs, do_bs, do_rs;
+  int64_t qt_bs, qt_hs, qt_rs, kt_bs, kt_hs, kt_rs;
+  int64_t dq_bs, dq_rs, dk_bs, dk_rs;    // dv uses dk's strides
+  int B, H, Nq, Nk;
+  float scale;
+};
+hipError_t launch_attention_bwd(int dh, const AttnBwdParams &p, hipStream_t s);
+
+// ---- the training backward's HBM-bound steps ----
+// dy = bf16(2 w bo / sin t * gbar) per sample (bo = 1, or -t_rf behind the wrapper).
+hipError_t launch_seed(const CoefTable &coef, float w, const float *gbar, bf16 *dy, int64_t n, hipStream_t s);
+// dst[c][r] = src[r][c] per (b, h) slice; dst rows r in [R, Rpad) are zeros.
+struct TransposeParams {
+  const void *src; int64_t s_bs, s_hs, s_rs;
+  bf16 *dst; int64_t d_bs, d_hs, d_rs;
+  int B, H, R, C, Rpad;
+};
+hipError_t launch_transpose(const TransposeParams &p, int src_fp32, hipStream_t s);
+// D = rowsum(dO * O) per (b, h, q) and lse2 = lse * log2(e).
+hipError_t launch_rowterms(const bf16 *dO, const bf16 *O, int64_t bs, int64_t rs, int B, int H, int dh, int Nq,
+                           const float *lse, float *lse2, float *D, hipStream_t s);
+hipError_t launch_zero_rows(bf16 *X, int64_t bs, int64_t rs, int B, int r0, int r1, int cols, hipStream_t s);
+// dW_t = sum_b (sum_rows dX[b]) e_b^T with fixed-order partial sums (part: B * colsum_chunks(rows) * d floats).
+int colsum_chunks(int rows);
+hipError_t launch_time_grad(const bf16 *dX, int64_t bs, int64_t rs, int B, int rows, int d, const float *E,
+                            float *part, float *dWt, hipStream_t s);
+hipError_t launch_reduce_splits(const float *part, int splits, int64_t n, float *out, hipStream_t s);
 
 }  // namespace t2va

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   const int m0 = tm * BM, n0 = tn * BN;
 
   const bf16 *A = p.A + (int64_t)bz * p.a_bs;
-  const bf16 *W = p.W;
+  const bf16 *W = p.W + (int64_t)bz * p.w_bs;
 
   // global -> register staging: 4 16-byte chunks of A and of W per thread
   uint4 ra[4], rw[4];
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kLThreads) void gemm_bf16_large_kernel(GemmParams p
   // descriptors end after the last valid row: rows >= M (N) read zeros
   const int m_rows = max(min(p.M - m0, LBM), 0), n_rows = max(min(p.N - n0, LBN), 0);
   const bf16 *A = p.A + (int64_t)bz * p.a_bs + (int64_t)m0 * p.lda;
-  const bf16 *W = p.W + (int64_t)n0 * p.ldw;
+  const bf16 *W = p.W + (int64_t)bz * p.w_bs + (int64_t)n0 * p.ldw;
   const __amdgpu_buffer_rsrc_t rA = gemm_rsrc(A, (uint32_t)(m_rows > 0 ? ((int64_t)(m_rows - 1) * p.lda + p.K) * 2 : 0));
   const __amdgpu_buffer_rsrc_t rW = gemm_rsrc(W, (uint32_t)(n_rows > 0 ? ((int64_t)(n_rows - 1) * p.ldw + p.K) * 2 : 0));
 

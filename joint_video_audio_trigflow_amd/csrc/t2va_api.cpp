@@ -12,6 +12,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -193,6 +194,83 @@ Layout make_layout(const t2va_scm_desc &d) {
   return L;
 }
 
+// Workspace of t2va_scm_grad: the target's layout, then the backward's buffers.
+struct GradLayout {
+  Layout base;
+  int ldq, split_v, split_a, split_all;
+  int64_t kc_v, kc_a, kc_all, kp_v, kp_a, kp_all;   // split-K chunk and padded token counts
+  size_t lse, lse2, Dq, wt_out_v, wt_out_a, wt_qkv, dy_v, dy_a, dO, dOT, QT, KT, Vrm, dQKV, dX;
+  size_t dyT_v, oT_v, dyT_a, oT_a, dqkvT, xT, dxT_v, zT_v, dxT_a, zT_a, tpart, part;
+  size_t total;
+};
+
+// Split-K factor for a weight gradient contracted over `tokens` rows with
+// `tiles` output tiles: enough workgroups to fill the chip, chunks of >= 512 tokens.
+int grad_splits(int64_t tokens, int tiles) {
+  int s = (int)std::min<int64_t>(std::max<int64_t>(tokens / 512, 1), 32);
+  while (s > 1 && (int64_t)tiles * (s / 2) >= 512) s /= 2;
+  return s;
+}
+
+GradLayout make_grad_layout(const t2va_scm_desc &d) {
+  GradLayout G;
+  G.base = make_layout(d);
+  const Layout &L = G.base;
+  const size_t B = d.B, D = d.d, H = d.H;
+  const int64_t Nv = d.Nv, Na = d.Na, Nq = L.Nq, NA = L.N_all;
+  G.ldq = (int)align_up((size_t)Nq, 64);
+  const int tiles_out_v = (d.Cv + 127) / 128 * ((d.d + 127) / 128);
+  const int tiles_out_a = (d.Ca + 127) / 128 * ((d.d + 127) / 128);
+  const int tiles_qkv = (3 * d.d + 255) / 256 * ((d.d + 255) / 256);
+  G.split_v = grad_splits(B * Nv, tiles_out_v);
+  G.split_a = grad_splits(B * Na, tiles_out_a);
+  G.split_all = grad_splits(B * NA, tiles_qkv);
+  G.kc_v = (int64_t)align_up((size_t)((B * Nv + G.split_v - 1) / G.split_v), 64);
+  G.kc_a = (int64_t)align_up((size_t)((B * Na + G.split_a - 1) / G.split_a), 64);
+  G.kc_all = (int64_t)align_up((size_t)((B * NA + G.split_all - 1) / G.split_all), 64);
+  G.kp_v = G.kc_v * G.split_v;
+  G.kp_a = G.kc_a * G.split_a;
+  G.kp_all = G.kc_all * G.split_all;
+  size_t off = L.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t bfs = sizeof(bf16), fs = sizeof(float);
+  G.lse = take(B * H * Nq * fs);
+  G.lse2 = take(B * H * Nq * fs);
+  G.Dq = take(B * H * Nq * fs);
+  G.wt_out_v = take(D * d.Cv * bfs);
+  G.wt_out_a = take(D * d.Ca * bfs);
+  G.wt_qkv = take(D * 3 * D * bfs);
+  G.dy_v = take(B * Nv * d.Cv * bfs);
+  G.dy_a = take(B * Na * d.Ca * bfs);
+  G.dO = take(B * Nq * D * bfs);
+  G.dOT = take(B * D * G.ldq * bfs);
+  G.QT = take(B * D * G.ldq * bfs);
+  G.KT = take(B * D * (size_t)L.ldv * bfs);
+  G.Vrm = take(B * NA * D * bfs);
+  G.dQKV = take(B * NA * 3 * D * bfs);
+  G.dX = take(B * Nq * D * bfs);
+  G.dyT_v = take((size_t)d.Cv * G.kp_v * bfs);
+  G.oT_v = take(D * G.kp_v * bfs);
+  G.dyT_a = take((size_t)d.Ca * G.kp_a * bfs);
+  G.oT_a = take(D * G.kp_a * bfs);
+  G.dqkvT = take(3 * D * G.kp_all * bfs);
+  G.xT = take(D * G.kp_all * bfs);
+  G.dxT_v = take(D * G.kp_v * bfs);
+  G.zT_v = take((size_t)d.Cv * G.kp_v * bfs);
+  G.dxT_a = take(D * G.kp_a * bfs);
+  G.zT_a = take((size_t)d.Ca * G.kp_a * bfs);
+  G.tpart = take(B * (size_t)colsum_chunks((int)Nq) * D * fs);
+  const size_t part_elems = std::max({(size_t)G.split_v * d.Cv * D, (size_t)G.split_a * d.Ca * D,
+                                      (size_t)G.split_all * 3 * D * D});
+  G.part = take(part_elems * fs);
+  G.total = off;
+  return G;
+}
+
 t2va_status check_desc(const t2va_scm_desc *d) {
   if (!d) return fail(T2VA_INVALID_ARG, "desc is NULL");
   if (t2va_status st = check_shape(d->B, d->Nv, d->Na, d->Nt, d->Cv, d->Ca, d->d, d->H,
@@ -346,10 +424,10 @@ struct Block {
 
   t2va_status gemm(const bf16 *A, int64_t lda, int64_t a_bs, const bf16 *Wt, int64_t ldw, void *Cp,
                    int64_t ldc, int64_t c_bs, int c_dt, const float *bias, int64_t bias_bs, int M,
-                   int N, int K, int batch, bf16 *vt, int n_split) const {
+                   int N, int K, int batch, bf16 *vt, int n_split, int64_t w_bs = 0) const {
     GemmParams g;
     g.A = A; g.lda = lda; g.a_bs = a_bs;
-    g.W = Wt; g.ldw = ldw;
+    g.W = Wt; g.ldw = ldw; g.w_bs = w_bs;
     g.C = Cp; g.ldc = ldc; g.c_bs = c_bs; g.c_dt = c_dt;
     g.bias = bias; g.bias_bs = bias_bs;
     g.VT = vt; g.vt_bs = vt_bs; g.vt_hs = vt_hs; g.vt_rs = ldv; g.vt_rows = ldv;
@@ -384,13 +462,13 @@ struct Block {
   // the tangent operands are the batches that follow (QK + B qk_bs, VT + B
   // vt_bs) and the tangent output goes to O + B o_bs.
   t2va_status attention(const bf16 *QK, const bf16 *VT, const int32_t *nk, bf16 *O, bool tan,
-                        int phase) const {
+                        int phase, float *lse = nullptr) const {
     AttnParams p;
     p.q = QK; p.k = QK + D; p.vt = VT;
     p.qd = tan ? QK + (int64_t)B * qk_bs : nullptr;
     p.kd = tan ? QK + (int64_t)B * qk_bs + D : nullptr;
     p.vdt = tan ? VT + (int64_t)B * vt_bs : nullptr;
-    p.nk = nk; p.o = O; p.od = tan ? O + (int64_t)B * o_bs : nullptr; p.lse = nullptr;
+    p.nk = nk; p.o = O; p.od = tan ? O + (int64_t)B * o_bs : nullptr; p.lse = lse;
     p.q_bs = qk_bs; p.q_rs = 2 * D; p.k_bs = qk_bs; p.k_rs = 2 * D;
     p.vt_bs = vt_bs; p.vt_hs = vt_hs; p.vt_rs = ldv;
     p.o_bs = o_bs; p.o_rs = D;
@@ -402,6 +480,121 @@ struct Block {
     return T2VA_OK;
   }
 };
+
+// Argument checks shared by t2va_scm_target and t2va_scm_grad (no HIP calls).
+t2va_status validate_scm(const t2va_scm_desc *desc, const t2va_block_weights *const *wb,
+                         const void *z0_v, const void *z0_a, const void *eps_v, const void *eps_a,
+                         const void *text, const uint8_t *text_mask, const double *t_host,
+                         const float *J_v, const float *J_a, const float *gbar_v, const float *gbar_a,
+                         const float *r_v, const float *r_a, const float *loss, const void *workspace,
+                         size_t workspace_bytes, size_t needed) {
+  if (t2va_status st = check_desc(desc)) return st;
+  const t2va_scm_desc &d = *desc;
+  if (t2va_status st = check_t(d.B, t_host)) return st;
+  if (t2va_status st = check_weights(wb, 2, "teacher", "student")) return st;
+  const void *req[] = {z0_v, z0_a, eps_v, eps_a, gbar_v, gbar_a, loss};
+  for (const void *p : req)
+    if (!p) return fail(T2VA_INVALID_ARG, "z0, eps, gbar and loss pointers are required");
+  if (d.Nt > 0 && (!text || !text_mask))
+    return fail(T2VA_INVALID_ARG, "text and text_mask are required when Nt > 0");
+  const void *al[] = {z0_v, z0_a, eps_v, eps_a, text, J_v, J_a, gbar_v, gbar_a, r_v, r_a};
+  for (const void *p : al)
+    if (p && !aligned16(p)) return fail(T2VA_INVALID_ARG, "tensor operands must be 16-byte aligned");
+  if (!workspace) return fail(T2VA_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(T2VA_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < needed)
+    return fail(T2VA_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, needed);
+  return T2VA_OK;
+}
+
+// The launch sequence of the joint sCM target (validated arguments).  With
+// lse_student, the student's attention also writes its primal log-sum-exp
+// (for the backward).  W receives the bf16 views of both blocks' weights.
+t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_weights *const *wb,
+                    const void *z0_v, const void *z0_a, const void *eps_v, const void *eps_a,
+                    const void *text, const uint8_t *text_mask, const double *t_host, float *J_v,
+                    float *J_a, float *gbar_v, float *gbar_a, float *r_v, float *r_a, float *norms,
+                    float *loss, void *workspace, float *lse_student, const bf16 *(&W)[2][6],
+                    hipStream_t s, bool prof) {
+  char *ws = (char *)workspace;
+  const Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
+  const int B = d.B, D = d.d, Nq = L.Nq;
+  const int64_t nv = blk.nv, na = blk.na;
+  const CoefTable coef = make_coef(B, t_host, d.beta, d.gamma, d.param);
+
+  HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
+
+  bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
+  float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
+  bf16 *X = (bf16 *)(ws + L.X), *QK = (bf16 *)(ws + L.QK), *VT = (bf16 *)(ws + L.VT);
+  bf16 *O = (bf16 *)(ws + L.O);
+  int32_t *nk = (int32_t *)(ws + L.nk);
+  float *x0T_v = (float *)(ws + L.x0T_v), *x0T_a = (float *)(ws + L.x0T_a);
+  float *x0S_v = (float *)(ws + L.x0S_v), *x0S_a = (float *)(ws + L.x0S_a);
+  float *part_v = (float *)(ws + L.part_v), *part_a = (float *)(ws + L.part_a);
+
+  // z_t = cos t z0 + sin t eps (bf16 GEMM input), half 0 of zv / za.
+  HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v,
+                          nullptr, zv, nv, nv, 0, nv, s), "noise");
+  HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a,
+                          nullptr, za, na, na, 0, na, s), "noise");
+  HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
+  HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
+  if (d.Nt > 0)
+    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, 0, nk, s), "text rows");
+  else
+    HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
+
+#define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
+
+  // ---------------- teacher: x0_T = G_T(z_t, t, c) ----------------
+  T2VA_CALL(blk.project_in(W[0], zv, za, tau, X, QK, VT, B));
+  T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
+  T2VA_CALL(blk.project_out(W[0], O, x0T_v, x0T_a, B));
+
+  // ---------------- F_T (tangent of the student's latent inputs) ----------------
+  HIP_TRY(launch_trigflow(2, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v, x0T_v,
+                          zv + (int64_t)B * nv, nv, nv, nv, nv, s), "teacher field");
+  HIP_TRY(launch_trigflow(2, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a, x0T_a,
+                          za + (int64_t)B * na, na, na, na, na, s), "teacher field");
+
+  // ---------------- student: G_S and its JVP ----------------
+  // Batches [0, B) carry the primal rows, [B, 2B) their tangents.
+  HIP_TRY(launch_time_linear(E, 2 * B, D, W[1][2], tau, s), "student time linear");
+  if (d.Nt > 0)
+    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X + (int64_t)B * blk.x_bs,
+                             blk.x_bs, 1, nullptr, s), "tangent text rows");
+  T2VA_CALL(blk.project_in(W[1], zv, za, tau, X, QK, VT, 2 * B));
+  T2VA_CALL(blk.attention(QK, VT, nk, O, true, T2VA_PHASE_STUDENT_ATTN, lse_student));
+  T2VA_CALL(blk.project_out(W[1], O, x0S_v, x0S_a, 2 * B));
+#undef T2VA_CALL
+
+  // ---------------- g, norms, gbar, r, loss ----------------
+  GParams gp;
+  gp.z0[0] = z0_v; gp.z0[1] = z0_a; gp.eps[0] = eps_v; gp.eps[1] = eps_a;
+  gp.x0T[0] = x0T_v; gp.x0T[1] = x0T_a;
+  gp.x0S[0] = x0S_v; gp.x0S[1] = x0S_a;
+  gp.Gd[0] = x0S_v + (int64_t)B * nv; gp.Gd[1] = x0S_a + (int64_t)B * na;
+  gp.x_bs[0] = nv; gp.x_bs[1] = na;
+  gp.J[0] = J_v; gp.J[1] = J_a;
+  gp.g[0] = gbar_v; gp.g[1] = gbar_a;
+  gp.partial[0] = part_v; gp.partial[1] = part_a;
+  gp.n[0] = nv; gp.n[1] = na;
+  gp.nblk[0] = L.nblk_v; gp.nblk[1] = L.nblk_a;
+  gp.in_dt = d.in_dtype;
+  HIP_TRY(launch_scm_direction(coef, gp, s), "sCM direction");
+  NormParams np;
+  np.mode = 0;
+  np.g[0] = gbar_v; np.g[1] = gbar_a; np.r[0] = r_v; np.r[1] = r_a;
+  np.partial[0] = part_v; np.partial[1] = part_a;
+  np.partial2[0] = np.partial2[1] = nullptr;
+  np.n[0] = nv; np.n[1] = na;
+  np.nblk[0] = L.nblk_v; np.nblk[1] = L.nblk_a;
+  np.norms = norms; np.loss = loss;
+  np.eps = d.eps_scm; np.w[0] = d.w_v; np.w[1] = d.w_a;
+  HIP_TRY(launch_normalise(B, np, s), "normalise");
+  return T2VA_OK;
+}
 
 }  // namespace
 
@@ -496,7 +689,7 @@ t2va_status t2va_profile_enable(int max_calls) {
   for (hipEvent_t e : g_prof.pool) hipEventDestroy(e);
   g_prof = Profiler();
   if (max_calls == 0) return T2VA_OK;
-  const size_t n = (size_t)max_calls * 32;
+  const size_t n = (size_t)max_calls * 64;   // up to 32 timed phases per call
   g_prof.pool.resize(n, nullptr);
   for (size_t i = 0; i < n; ++i) HIP_TRY(hipEventCreate(&g_prof.pool[i]), "hipEventCreate");
   g_prof.max_calls = max_calls;
@@ -515,7 +708,8 @@ t2va_status t2va_profile_read(double *ms_out, int *n_calls) {
     ms_out[r.phase] += ms;
     (void)other;
   }
-  double parts = ms_out[T2VA_PHASE_TEACHER_ATTN] + ms_out[T2VA_PHASE_STUDENT_ATTN] + ms_out[T2VA_PHASE_GEMM];
+  double parts = ms_out[T2VA_PHASE_TEACHER_ATTN] + ms_out[T2VA_PHASE_STUDENT_ATTN] + ms_out[T2VA_PHASE_GEMM] +
+                 ms_out[T2VA_PHASE_BWD_ATTN];
   ms_out[T2VA_PHASE_OTHER] = ms_out[T2VA_PHASE_TOTAL] - parts;
   *n_calls = g_prof.calls;
   g_prof.recs.clear();
@@ -532,110 +726,181 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
                             float *loss, void *workspace, size_t workspace_bytes,
                             t2va_stream stream) {
   g_err.clear();
-  // ---------------- validation (before any HIP call) ----------------
-  if (t2va_status st = check_desc(desc)) return st;
-  const t2va_scm_desc &d = *desc;
-  if (t2va_status st = check_t(d.B, t_host)) return st;
   const t2va_block_weights *wb[2] = {teacher, student};
-  if (t2va_status st = check_weights(wb, 2, "teacher", "student")) return st;
-  const void *req[] = {z0_v, z0_a, eps_v, eps_a, gbar_v, gbar_a, loss};
-  for (const void *p : req)
-    if (!p) return fail(T2VA_INVALID_ARG, "z0, eps, gbar and loss pointers are required");
-  if (d.Nt > 0 && (!text || !text_mask))
-    return fail(T2VA_INVALID_ARG, "text and text_mask are required when Nt > 0");
-  const void *al[] = {z0_v, z0_a, eps_v, eps_a, text, J_v, J_a, gbar_v, gbar_a, r_v, r_a};
-  for (const void *p : al)
-    if (p && !aligned16(p)) return fail(T2VA_INVALID_ARG, "tensor operands must be 16-byte aligned");
-  const Layout L = make_layout(d);
-  if (!workspace) return fail(T2VA_INVALID_ARG, "workspace is NULL");
-  if (((uintptr_t)workspace & 255u) != 0) return fail(T2VA_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < L.total)
-    return fail(T2VA_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
-
-  // ---------------- launch sequence ----------------
+  const size_t needed = check_desc(desc) == T2VA_OK ? make_layout(*desc).total : 0;
+  if (t2va_status st = validate_scm(desc, wb, z0_v, z0_a, eps_v, eps_a, text, text_mask, t_host, J_v, J_a,
+                                    gbar_v, gbar_a, r_v, r_a, loss, workspace, workspace_bytes, needed))
+    return st;
   hipStream_t s = (hipStream_t)stream;
   const bool prof = g_prof.active();
   if (prof) g_prof.calls++;
   PhaseScope total(s, T2VA_PHASE_TOTAL, prof);
+  const bf16 *W[2][6];
+  return run_scm(*desc, make_layout(*desc), wb, z0_v, z0_a, eps_v, eps_a, text, text_mask, t_host, J_v, J_a,
+                 gbar_v, gbar_a, r_v, r_a, norms, loss, workspace, nullptr, W, s, prof);
+}
 
+// ---------------------------------------------------------------------------
+// Training backward of the joint sCM loss.
+// ---------------------------------------------------------------------------
+size_t t2va_scm_grad_workspace_bytes(const t2va_scm_desc *desc) {
+  g_err.clear();
+  if (check_desc(desc) != T2VA_OK) return 0;
+  return make_grad_layout(*desc).total;
+}
+
+t2va_status t2va_scm_grad(const t2va_scm_desc *desc, const t2va_block_weights *teacher,
+                          const t2va_block_weights *student, const void *z0_v, const void *z0_a,
+                          const void *eps_v, const void *eps_a, const void *text,
+                          const uint8_t *text_mask, const double *t_host, float *gbar_v, float *gbar_a,
+                          float *norms, float *loss, const t2va_block_grads *grads, void *workspace,
+                          size_t workspace_bytes, t2va_stream stream) {
+  g_err.clear();
+  const t2va_block_weights *wb[2] = {teacher, student};
+  const bool ok_desc = check_desc(desc) == T2VA_OK;
+  const size_t needed = ok_desc ? make_grad_layout(*desc).total : 0;
+  if (t2va_status st = validate_scm(desc, wb, z0_v, z0_a, eps_v, eps_a, text, text_mask, t_host, nullptr,
+                                    nullptr, gbar_v, gbar_a, nullptr, nullptr, loss, workspace,
+                                    workspace_bytes, needed))
+    return st;
+  if (!grads) return fail(T2VA_INVALID_ARG, "grads is NULL");
+  float *gout[6] = {grads->w_in_v, grads->w_in_a, grads->w_t, grads->w_qkv, grads->w_out_v, grads->w_out_a};
+  for (float *g : gout)
+    if (!g) return fail(T2VA_INVALID_ARG, "every gradient pointer is required");
+  const t2va_scm_desc &d = *desc;
+  const GradLayout G = make_grad_layout(d);
+  const Layout &L = G.base;
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool prof = g_prof.active();
+  if (prof) g_prof.calls++;
+  PhaseScope total(s, T2VA_PHASE_TOTAL, prof);
   char *ws = (char *)workspace;
+  const bf16 *W[2][6];
+  float *lse = (float *)(ws + G.lse);
+  if (t2va_status st = run_scm(d, L, wb, z0_v, z0_a, eps_v, eps_a, text, text_mask, t_host, nullptr, nullptr,
+                               gbar_v, gbar_a, nullptr, nullptr, norms, loss, workspace, lse, W, s, prof))
+    return st;
+
   const Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
-  const int B = d.B, D = d.d, Nq = L.Nq;
+  const int B = d.B, D = d.d, H = d.H, dh = L.dh, Nv = d.Nv, Na = d.Na, Nq = L.Nq, NA = L.N_all;
   const int64_t nv = blk.nv, na = blk.na;
   const CoefTable coef = make_coef(B, t_host, d.beta, d.gamma, d.param);
-
-  const bf16 *W[2][6];
-  HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
-
-  bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
-  float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
+  const bf16 *const *Ws = W[1];
+  bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);   // primal halves: the block's inputs
+  const float *E = (const float *)(ws + L.E);
   bf16 *X = (bf16 *)(ws + L.X), *QK = (bf16 *)(ws + L.QK), *VT = (bf16 *)(ws + L.VT);
   bf16 *O = (bf16 *)(ws + L.O);
-  int32_t *nk = (int32_t *)(ws + L.nk);
-  float *x0T_v = (float *)(ws + L.x0T_v), *x0T_a = (float *)(ws + L.x0T_a);
-  float *x0S_v = (float *)(ws + L.x0S_v), *x0S_a = (float *)(ws + L.x0S_a);
-  float *part_v = (float *)(ws + L.part_v), *part_a = (float *)(ws + L.part_a);
+  const int32_t *nk = (const int32_t *)(ws + L.nk);
+  float *lse2 = (float *)(ws + G.lse2), *Dq = (float *)(ws + G.Dq);
+  bf16 *wt_out_v = (bf16 *)(ws + G.wt_out_v), *wt_out_a = (bf16 *)(ws + G.wt_out_a);
+  bf16 *wt_qkv = (bf16 *)(ws + G.wt_qkv);
+  bf16 *dy_v = (bf16 *)(ws + G.dy_v), *dy_a = (bf16 *)(ws + G.dy_a);
+  bf16 *dO = (bf16 *)(ws + G.dO), *dOT = (bf16 *)(ws + G.dOT), *QT = (bf16 *)(ws + G.QT);
+  bf16 *KT = (bf16 *)(ws + G.KT), *Vrm = (bf16 *)(ws + G.Vrm), *dQKV = (bf16 *)(ws + G.dQKV);
+  bf16 *dX = (bf16 *)(ws + G.dX);
+  float *part = (float *)(ws + G.part);
+  const int64_t o_bs = (int64_t)Nq * D, x_bs = (int64_t)NA * D, g_bs = (int64_t)NA * 3 * D;
 
-  // z_t = cos t z0 + sin t eps (bf16 GEMM input), half 0 of zv / za.
-  HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v,
-                          nullptr, zv, nv, nv, 0, nv, s), "noise");
-  HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a,
-                          nullptr, za, na, na, 0, na, s), "noise");
-  HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
-  HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
-  if (d.Nt > 0)
-    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, 0, nk, s), "text rows");
-  else
-    HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
-
+  // dst[c][r] = src[r][c] per (b, h); see TransposeParams
+  auto transpose = [&](const void *src, int src_f32, int64_t s_bs, int64_t s_hs, int64_t s_rs, bf16 *dst,
+                       int64_t d_bs, int64_t d_hs, int64_t d_rs, int nb, int nh, int R, int C,
+                       int Rpad) -> t2va_status {
+    TransposeParams tp;
+    tp.src = src; tp.s_bs = s_bs; tp.s_hs = s_hs; tp.s_rs = s_rs;
+    tp.dst = dst; tp.d_bs = d_bs; tp.d_hs = d_hs; tp.d_rs = d_rs;
+    tp.B = nb; tp.H = nh; tp.R = R; tp.C = C; tp.Rpad = Rpad;
+    HIP_TRY(launch_transpose(tp, src_f32, s), "transpose");
+    return T2VA_OK;
+  };
+  // rows [0, R) of B samples (batch stride s_bs, row stride s_rs, C columns)
+  // -> dst [C][kp] with sample b at columns [b R, (b + 1) R) and zeros up to kp
+  auto gather_t = [&](const bf16 *src, int64_t s_bs, int64_t s_rs, int R, int C, bf16 *dst,
+                      int64_t kp) -> t2va_status {
+    if (t2va_status st = transpose(src, 0, s_bs, 0, s_rs, dst, R, 0, kp, B, 1, R, C, R)) return st;
+    const int tail = (int)(kp - (int64_t)B * R);
+    if (tail > 0)
+      return transpose(src, 0, 0, 0, s_rs, dst + (int64_t)B * R, 0, 0, kp, 1, 1, 0, C, tail);
+    return T2VA_OK;
+  };
+  // out [M][N] fp32 = A [M][kp] . Wt [N][kp]^T, split-K over `splits` chunks of kc
+  auto wgrad = [&](const bf16 *A, const bf16 *Wt, int64_t kp, int64_t kc, int splits, int M, int N,
+                   float *out) -> t2va_status {
+    if (splits == 1)
+      return blk.gemm(A, kp, 0, Wt, kp, out, N, 0, 1, nullptr, 0, M, N, (int)kc, 1, nullptr, N, 0);
+    if (t2va_status st = blk.gemm(A, kp, kc, Wt, kp, part, N, (int64_t)M * N, 1, nullptr, 0, M, N, (int)kc,
+                                  splits, nullptr, N, kc))
+      return st;
+    HIP_TRY(launch_reduce_splits(part, splits, (int64_t)M * N, out, s), "split-K reduce");
+    return T2VA_OK;
+  };
 #define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
 
-  // ---------------- teacher: x0_T = G_T(z_t, t, c) ----------------
-  T2VA_CALL(blk.project_in(W[0], zv, za, tau, X, QK, VT, B));
-  T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
-  T2VA_CALL(blk.project_out(W[0], O, x0T_v, x0T_a, B));
+  // ---- dL/dy at the block's outputs, and dO = dy W_out ----
+  HIP_TRY(launch_seed(coef, (float)d.w_v, gbar_v, dy_v, nv, s), "seed");
+  HIP_TRY(launch_seed(coef, (float)d.w_a, gbar_a, dy_a, na, s), "seed");
+  T2VA_CALL(transpose(Ws[4], 0, 0, 0, D, wt_out_v, 0, 0, d.Cv, 1, 1, d.Cv, D, d.Cv));
+  T2VA_CALL(transpose(Ws[5], 0, 0, 0, D, wt_out_a, 0, 0, d.Ca, 1, 1, d.Ca, D, d.Ca));
+  T2VA_CALL(transpose(Ws[3], 0, 0, 0, D, wt_qkv, 0, 0, 3 * D, 1, 1, 3 * D, D, 3 * D));
+  T2VA_CALL(blk.gemm(dy_v, d.Cv, nv, wt_out_v, d.Cv, dO, D, o_bs, 0, nullptr, 0, Nv, D, d.Cv, B, nullptr, D));
+  T2VA_CALL(blk.gemm(dy_a, d.Ca, na, wt_out_a, d.Ca, dO + (int64_t)Nv * D, D, o_bs, 0, nullptr, 0, Na, D,
+                     d.Ca, B, nullptr, D));
 
-  // ---------------- F_T (tangent of the student's latent inputs) ----------------
-  HIP_TRY(launch_trigflow(2, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v, x0T_v,
-                          zv + (int64_t)B * nv, nv, nv, nv, nv, s), "teacher field");
-  HIP_TRY(launch_trigflow(2, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a, x0T_a,
-                          za + (int64_t)B * na, na, na, na, na, s), "teacher field");
+  // ---- attention backward ----
+  HIP_TRY(launch_rowterms(dO, O, o_bs, D, B, H, dh, Nq, lse, lse2, Dq, s), "row terms");
+  T2VA_CALL(transpose(QK, 0, blk.qk_bs, dh, 2 * D, QT, (int64_t)D * G.ldq, (int64_t)dh * G.ldq, G.ldq, B, H,
+                      Nq, dh, G.ldq));
+  T2VA_CALL(transpose(QK + D, 0, blk.qk_bs, dh, 2 * D, KT, (int64_t)D * L.ldv, (int64_t)dh * L.ldv, L.ldv, B,
+                      H, NA, dh, L.ldv));
+  T2VA_CALL(transpose(VT, 0, blk.vt_bs, blk.vt_hs, L.ldv, Vrm, x_bs, dh, D, B, H, dh, NA, dh));
+  T2VA_CALL(transpose(dO, 0, o_bs, dh, D, dOT, (int64_t)D * G.ldq, (int64_t)dh * G.ldq, G.ldq, B, H, Nq, dh,
+                      G.ldq));
+  HIP_TRY(launch_zero_rows(dQKV, g_bs, 3 * D, B, Nq, NA, D, s), "zero rows");
+  {
+    AttnBwdParams ap;
+    ap.q = QK; ap.k = QK + D; ap.v = Vrm; ap.dout = dO;
+    ap.qt = QT; ap.kt = KT; ap.dot = dOT;
+    ap.lse2 = lse2; ap.D = Dq; ap.nk = nk;
+    ap.dq = dQKV; ap.dk = dQKV + D; ap.dv = dQKV + 2 * D;
+    ap.q_bs = blk.qk_bs; ap.q_rs = 2 * D; ap.k_bs = blk.qk_bs; ap.k_rs = 2 * D;
+    ap.v_bs = x_bs; ap.v_rs = D; ap.do_bs = o_bs; ap.do_rs = D;
+    ap.qt_bs = (int64_t)D * G.ldq; ap.qt_hs = (int64_t)dh * G.ldq; ap.qt_rs = G.ldq;
+    ap.kt_bs = (int64_t)D * L.ldv; ap.kt_hs = (int64_t)dh * L.ldv; ap.kt_rs = L.ldv;
+    ap.dq_bs = g_bs; ap.dq_rs = 3 * D; ap.dk_bs = g_bs; ap.dk_rs = 3 * D;
+    ap.B = B; ap.H = H; ap.Nq = Nq; ap.Nk = NA;
+    ap.scale = (float)(1.0 / sqrt((double)dh));
+    PhaseScope ps(s, T2VA_PHASE_BWD_ATTN, prof);
+    HIP_TRY(launch_attention_bwd(dh, ap, s), "attention backward");
+  }
 
-  // ---------------- student: G_S and its JVP ----------------
-  // Batches [0, B) carry the primal rows, [B, 2B) their tangents.
-  HIP_TRY(launch_time_linear(E, 2 * B, D, W[1][2], tau, s), "student time linear");
-  if (d.Nt > 0)
-    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X + (int64_t)B * blk.x_bs,
-                             blk.x_bs, 1, nullptr, s), "tangent text rows");
-  T2VA_CALL(blk.project_in(W[1], zv, za, tau, X, QK, VT, 2 * B));
-  T2VA_CALL(blk.attention(QK, VT, nk, O, true, T2VA_PHASE_STUDENT_ATTN));
-  T2VA_CALL(blk.project_out(W[1], O, x0S_v, x0S_a, 2 * B));
+  // ---- dX = dQKV W_qkv (video and audio rows), dW_qkv = dQKV^T X ----
+  T2VA_CALL(blk.gemm(dQKV, 3 * D, g_bs, wt_qkv, 3 * D, dX, D, o_bs, 0, nullptr, 0, Nq, D, 3 * D, B, nullptr, D));
+  bf16 *dqkvT = (bf16 *)(ws + G.dqkvT), *xT = (bf16 *)(ws + G.xT);
+  T2VA_CALL(gather_t(dQKV, g_bs, 3 * D, NA, 3 * D, dqkvT, G.kp_all));
+  T2VA_CALL(gather_t(X, x_bs, D, NA, D, xT, G.kp_all));
+  T2VA_CALL(wgrad(dqkvT, xT, G.kp_all, G.kc_all, G.split_all, 3 * D, D, grads->w_qkv));
+
+  // ---- output projections: dW_out = dy^T O ----
+  bf16 *dyT_v = (bf16 *)(ws + G.dyT_v), *oT_v = (bf16 *)(ws + G.oT_v);
+  bf16 *dyT_a = (bf16 *)(ws + G.dyT_a), *oT_a = (bf16 *)(ws + G.oT_a);
+  T2VA_CALL(gather_t(dy_v, nv, d.Cv, Nv, d.Cv, dyT_v, G.kp_v));
+  T2VA_CALL(gather_t(O, o_bs, D, Nv, D, oT_v, G.kp_v));
+  T2VA_CALL(wgrad(dyT_v, oT_v, G.kp_v, G.kc_v, G.split_v, d.Cv, D, grads->w_out_v));
+  T2VA_CALL(gather_t(dy_a, na, d.Ca, Na, d.Ca, dyT_a, G.kp_a));
+  T2VA_CALL(gather_t(O + (int64_t)Nv * D, o_bs, D, Na, D, oT_a, G.kp_a));
+  T2VA_CALL(wgrad(dyT_a, oT_a, G.kp_a, G.kc_a, G.split_a, d.Ca, D, grads->w_out_a));
+
+  // ---- input projections: dW_in = dX^T z_in; time embedding: dW_t = (sum_rows dX) e^T ----
+  bf16 *dxT_v = (bf16 *)(ws + G.dxT_v), *zT_v = (bf16 *)(ws + G.zT_v);
+  bf16 *dxT_a = (bf16 *)(ws + G.dxT_a), *zT_a = (bf16 *)(ws + G.zT_a);
+  T2VA_CALL(gather_t(dX, o_bs, D, Nv, D, dxT_v, G.kp_v));
+  T2VA_CALL(gather_t(zv, nv, d.Cv, Nv, d.Cv, zT_v, G.kp_v));
+  T2VA_CALL(wgrad(dxT_v, zT_v, G.kp_v, G.kc_v, G.split_v, D, d.Cv, grads->w_in_v));
+  T2VA_CALL(gather_t(dX + (int64_t)Nv * D, o_bs, D, Na, D, dxT_a, G.kp_a));
+  T2VA_CALL(gather_t(za, na, d.Ca, Na, d.Ca, zT_a, G.kp_a));
+  T2VA_CALL(wgrad(dxT_a, zT_a, G.kp_a, G.kc_a, G.split_a, D, d.Ca, grads->w_in_a));
+  HIP_TRY(launch_time_grad(dX, o_bs, D, B, Nq, D, E, (float *)(ws + G.tpart), grads->w_t, s), "time grad");
 #undef T2VA_CALL
-
-  // ---------------- g, norms, gbar, r, loss ----------------
-  GParams gp;
-  gp.z0[0] = z0_v; gp.z0[1] = z0_a; gp.eps[0] = eps_v; gp.eps[1] = eps_a;
-  gp.x0T[0] = x0T_v; gp.x0T[1] = x0T_a;
-  gp.x0S[0] = x0S_v; gp.x0S[1] = x0S_a;
-  gp.Gd[0] = x0S_v + (int64_t)B * nv; gp.Gd[1] = x0S_a + (int64_t)B * na;
-  gp.x_bs[0] = nv; gp.x_bs[1] = na;
-  gp.J[0] = J_v; gp.J[1] = J_a;
-  gp.g[0] = gbar_v; gp.g[1] = gbar_a;
-  gp.partial[0] = part_v; gp.partial[1] = part_a;
-  gp.n[0] = nv; gp.n[1] = na;
-  gp.nblk[0] = L.nblk_v; gp.nblk[1] = L.nblk_a;
-  gp.in_dt = d.in_dtype;
-  HIP_TRY(launch_scm_direction(coef, gp, s), "sCM direction");
-  NormParams np;
-  np.mode = 0;
-  np.g[0] = gbar_v; np.g[1] = gbar_a; np.r[0] = r_v; np.r[1] = r_a;
-  np.partial[0] = part_v; np.partial[1] = part_a;
-  np.partial2[0] = np.partial2[1] = nullptr;
-  np.n[0] = nv; np.n[1] = na;
-  np.nblk[0] = L.nblk_v; np.nblk[1] = L.nblk_a;
-  np.norms = norms; np.loss = loss;
-  np.eps = d.eps_scm; np.w[0] = d.w_v; np.w[1] = d.w_a;
-  HIP_TRY(launch_normalise(B, np, s), "normalise");
   return T2VA_OK;
 }
 
