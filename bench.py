@@ -151,6 +151,36 @@ def time_dmd(cfg, problem, steps, scm_ms) -> dict:
             "stage3_ms_per_step": scm_ms + ms}
 
 
+def time_grad(cfg, problem, dev, steps, nk) -> dict:
+    """The sCM target plus the training backward of its loss (gradients of all
+    student weights), timed after the sCM steps on the same resident inputs."""
+    import torch
+    from joint_video_audio_trigflow_amd import _lib
+    dt = _lib.DTYPE_BF16 if cfg.in_dtype == "bf16" else _lib.DTYPE_FP32
+    op = _lib.ScmGrad(cfg, in_dtype=dt, weight_dtype=dt)
+    call = lambda: op(dev["teacher"], dev["student"], dev["z0_v"], dev["z0_a"], dev["eps_v"],
+                      dev["eps_a"], dev["text"], dev["text_mask"], dev["t"])
+    call()
+    torch.cuda.synchronize()
+    _lib.profile_enable(steps)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phases, n = _lib.profile_read()
+    _lib.profile_enable(0)
+    ms = 1000.0 * elapsed / steps
+    bwd_ms = phases["bwd_attn"] / n
+    # algorithmic attention-backward work: 2.5x the forward's 4 d Nq nk (dP, dV, dQ, dK and
+    # recomputing S); the two kernels also recompute dP, 14 d Nq nk in all
+    flops = sum(10.0 * cfg.d * cfg.Nq * k for k in nk)
+    return {"steps": steps, "ms_per_call": ms, "samples_per_s": cfg.B / (ms * 1e-3),
+            "phases_ms_per_call": {k: v / n for k, v in phases.items()},
+            "attn_bwd_tflops": flops / (bwd_ms * 1e-3) / 1e12,
+            "attn_bwd_flops_per_launch": flops}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +191,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dmd-steps", type=int, default=5,
                     help="also time the joint DMD term on the same workload (0: skip)")
+    ap.add_argument("--grad-steps", type=int, default=5,
+                    help="also time the target plus its training backward (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (for scaling HBM counters)")
     args = ap.parse_args()
@@ -242,6 +274,8 @@ def main() -> int:
     }
     if args.dmd_steps > 0:
         rec["dmd_target"] = time_dmd(cfg, problem, args.dmd_steps, ms_step)
+    if args.grad_steps > 0:
+        rec["scm_grad"] = time_grad(cfg, problem, dev, args.grad_steps, nk)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -168,3 +168,73 @@ def test_full_size_dmd_against_stored_oracle(name):
         l_cond = abs(exp["st_loss"][b] / exp["loss"][b] - 1)
         assert abs(got["loss"][b] / exp["loss"][b] - 1) <= TOL_DMD_LOSS + l_cond, (b, got["loss"][b], exp["loss"][b])
     print(name, "DMD worst sampled rel-L2:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
+
+
+def _grad_probes():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("make_grad_expected",
+                                                  os.path.join(GOLDEN, "make_grad_expected.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_full_size_grad_standard_against_stored_oracle():
+    """The training backward at the standard workload (6,400 queries, 6,502
+    valid keys, 16 heads) against the stored fp64 autograd run: per weight the
+    norm, four seeded projections and 2,048 seeded entries."""
+    from joint_video_audio_trigflow_amd import _lib
+    print("full-size scm_grad standard", flush=True)
+    mod = _grad_probes()
+    exp = np.load(os.path.join(GOLDEN, "expected_grad_standard.npz"))
+    cfg = inputs.CONFIGS["standard"]
+    p = inputs.make_problem(cfg)
+    assert np.array_equal(p["data"]["t"], exp["t"])
+    dev = _lib.to_device_problem(p)
+    op = _lib.ScmGrad(cfg)
+    out, grads = op(dev["teacher"], dev["student"], dev["z0_v"], dev["z0_a"], dev["eps_v"], dev["eps_a"],
+                    dev["text"], dev["text_mask"], dev["t"])
+    torch.cuda.synchronize()
+    errs = {}
+    for k in mod.WEIGHTS:
+        g = grads[k].cpu().numpy().astype(np.float64)
+        nrm = float(exp[f"{k}_norm"])
+        dirs, idx = mod.probes(g.shape, k)
+        assert np.array_equal(idx, exp[f"{k}_idx"])
+        assert abs(np.linalg.norm(g) / nrm - 1) <= TOL_FIELD, k
+        proj = np.array([np.sum(g * dv) for dv in dirs])
+        # |<delta, u>| <= ||delta|| <= tol ||g|| for unit directions u
+        assert np.all(np.abs(proj - exp[f"{k}_proj"]) <= TOL_FIELD * nrm), k
+        errs[k] = rel_l2(g.reshape(-1)[idx], exp[f"{k}_val"])
+        assert errs[k] <= TOL_FIELD, (k, errs[k])
+    print("standard grad sampled rel-L2:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+
+
+def test_full_size_grad_high_res_properties():
+    """The training backward at the high-resolution shape, in the launch
+    configuration bench.py times: finite, deterministic, its target outputs
+    equal t2va_scm_target's, and doubling both modality weights doubles every
+    gradient exactly (the seed is the only place they enter, and scaling by 2
+    commutes with every rounding)."""
+    from joint_video_audio_trigflow_amd import _lib
+    print("full-size scm_grad high-res properties", flush=True)
+    cfg = inputs.CONFIGS["high-res"]
+    p = inputs.make_problem(cfg)
+    dev = _lib.to_device_problem(p)
+    args = (dev["teacher"], dev["student"], dev["z0_v"], dev["z0_a"], dev["eps_v"], dev["eps_a"],
+            dev["text"], dev["text_mask"], dev["t"])
+    op = _lib.ScmGrad(cfg)
+    out, g1 = op(*args)
+    g1 = {k: v.clone() for k, v in g1.items()}
+    loss1 = out["loss"].clone()
+    _, g2 = op(*args)
+    for k in g1:
+        assert torch.isfinite(g1[k]).all(), k
+        assert torch.equal(g1[k], g2[k]), k
+    tgt = _lib.ScmTarget(cfg)(*args)
+    assert torch.equal(loss1, tgt["loss"])
+    op2 = _lib.ScmGrad(cfg.replace(w_v=2 * cfg.w_v, w_a=2 * cfg.w_a))
+    _, g3 = op2(*args)
+    torch.cuda.synchronize()
+    for k in g1:
+        assert torch.equal(g3[k], 2 * g1[k]), k
