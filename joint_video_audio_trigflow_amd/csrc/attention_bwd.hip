@@ -9,12 +9,12 @@
 // P is recomputed from the forward's log-sum-exp (log2 units), so no running
 // max is needed.  Two kernels, both deterministic (no atomics):
 //
-// * dQ: a wave owns 16 query rows and streams key tiles; in registers it keeps
-//   Q and dO as B operands; per 32-key sub-tile it forms S^T = K Q^T and
+// * dQ: a wave owns two blocks of 16 query rows and streams key tiles; in
+//   registers it keeps Q and dO as B operands; per 32-key sub-tile it forms S^T = K Q^T and
 //   dP^T = V dO^T (A: K and V rows from LDS, read in the permuted row order
 //   that makes the 8 values a lane holds the 8 keys of its B operand), then
 //   dQ^T += K^T dS^T (A: K^T rows from LDS, B: dS^T from registers).
-// * dK/dV: a wave owns 16 keys and streams query tiles; in registers it keeps
+// * dK/dV: a wave (12 per workgroup) owns 16 keys and streams query tiles; in registers it keeps
 //   K and V as B operands; per 32-query sub-tile it forms S = Q K^T and
 //   dP = dO V^T (A: Q and dO rows from LDS, permuted), then
 //   dV^T += dO^T P and dK^T += Q^T dS (A: dO^T and Q^T rows from LDS).
@@ -33,17 +33,30 @@ namespace t2va {
 
 namespace {
 
-#ifndef T2VA_BWD_WAVES
-#define T2VA_BWD_WAVES 8
+#ifndef T2VA_BWD_WAVES_DQ
+#define T2VA_BWD_WAVES_DQ 8
+#endif
+#ifndef T2VA_BWD_WAVES_DKV
+#define T2VA_BWD_WAVES_DKV 12
+#endif
+#ifndef T2VA_BWD_MB_DQ
+#define T2VA_BWD_MB_DQ 2
+#endif
+#ifndef T2VA_BWD_MB_DKV
+#define T2VA_BWD_MB_DKV 1
 #endif
 constexpr int BT = 64;          // streamed tokens per LDS stage
 constexpr int kBwdLoaders = 8;  // waves that issue the LDS loads
 
 template <int DH>
 struct BwdCfg {
-  static constexpr int NW = T2VA_BWD_WAVES;
-  static constexpr int THREADS = 64 * NW;
-  static constexpr int BW = 16 * NW;        // rows (queries or keys) per workgroup
+  static constexpr int NW_DQ = T2VA_BWD_WAVES_DQ, NW_DKV = T2VA_BWD_WAVES_DKV;
+  static constexpr int THREADS_DQ = 64 * NW_DQ, THREADS_DKV = 64 * NW_DKV;
+  // blocks of 16 rows per wave (queries for dQ, keys for dK/dV): every
+  // fragment a wave reads from LDS feeds MB MFMAs
+  static constexpr int MB_DQ = T2VA_BWD_MB_DQ, MB_DKV = T2VA_BWD_MB_DKV;
+  static constexpr int BW_DQ = 16 * MB_DQ * NW_DQ;     // queries per dQ workgroup
+  static constexpr int BW_DKV = 16 * MB_DKV * NW_DKV;  // keys per dK/dV workgroup
   static constexpr int KSTEPS = DH / 32;
   static constexpr int DT = DH / 16;
   static constexpr int CPR = DH / 8;
@@ -119,7 +132,7 @@ __device__ __forceinline__ void xcd_tile(int w, int per_xcd, int total, int &L) 
 // dQ
 // ---------------------------------------------------------------------------
 template <int DH>
-__global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dq_kernel(AttnBwdParams p, int nqb,
+__global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kernel(AttnBwdParams p, int nqb,
                                                                               int per_xcd, int total) {
   using C = BwdCfg<DH>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -135,23 +148,27 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dq_kernel(A
   const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int q_row = qb * C::BW + wave * 16 + l16;
-  const int q_ld = min(q_row, p.Nq - 1);
+  constexpr int MB = C::MB_DQ;
+  const int q_row0 = qb * C::BW_DQ + wave * 16 * MB + l16;   // + 16 mb for row block mb
   const int nk = min(max(p.nk[b], 1), p.Nk);
   const float c_log2 = p.scale * 1.4426950408889634f;
 
-  bf16x8 qf[C::KSTEPS], dof[C::KSTEPS];
-  {
+  bf16x8 qf[MB][C::KSTEPS], dof[MB][C::KSTEPS];
+  float lse2[MB], Dq[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int q_ld = min(q_row0 + 16 * mb, p.Nq - 1);
     const bf16 *qp = p.q + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * g;
     const bf16 *dp = p.dout + (int64_t)b * p.do_bs + (int64_t)q_ld * p.do_rs + h * DH + 8 * g;
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
-      qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
-      dof[s] = *reinterpret_cast<const bf16x8 *>(dp + 32 * s);
+      qf[mb][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
+      dof[mb][s] = *reinterpret_cast<const bf16x8 *>(dp + 32 * s);
     }
+    const int64_t sidx = ((int64_t)b * p.H + h) * p.Nq + q_ld;
+    lse2[mb] = p.lse2[sidx];
+    Dq[mb] = p.D[sidx];
   }
-  const int64_t sidx = ((int64_t)b * p.H + h) * p.Nq + q_ld;
-  const float lse2 = p.lse2[sidx], Dq = p.D[sidx];
 
   // K and V row descriptors end after key row nk-1 (rows past it load as
   // zeros); K^T columns past nk hold finite values (zeros or padded text
@@ -188,11 +205,13 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dq_kernel(A
   TrReader tr;
   tr.init(l16, g);
 
-  floatx4 acc[C::DT];
+  floatx4 acc[MB][C::DT];
 #pragma unroll
-  for (int e = 0; e < C::DT; ++e)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[e][r] = 0.f;
+    for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[mb][e][r] = 0.f;
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   const int nst = (nk + BT - 1) / BT;
@@ -204,30 +223,43 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dq_kernel(A
     if (st + 1 < nst) issue(cur ^ 1, (st + 1) * BT);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      floatx4 S[2], dP[2];
+      floatx4 S[MB][2], dP[MB][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
           const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sK(cur) + rr.off(u, t, s));
           const bf16x8 va = *reinterpret_cast<const bf16x8 *>(sV(cur) + rr.off(u, t, s));
-          S[t] = mfma16(ka, qf[s], s == 0 ? zero4 : S[t]);
-          dP[t] = mfma16(va, dof[s], s == 0 ? zero4 : dP[t]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            S[mb][t] = mfma16(ka, qf[mb][s], s == 0 ? zero4 : S[mb][t]);
+            dP[mb][t] = mfma16(va, dof[mb][s], s == 0 ? zero4 : dP[mb][t]);
+          }
         }
       }
-      bf16x8 dS;
-      const int kbase = st * BT + 32 * u + 8 * g;
+      // keys past nk (last stage only) get zero weight
+      if (st == nst - 1) {
+        const int kbase = st * BT + 32 * u + 8 * g;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int t = m >> 2, r = m & 3;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][r], c_log2, -lse2));
-        if (kbase + 4 * t + r >= nk) pv = 0.f;
-        dS[m] = (bf16)(pv * (dP[t][r] - Dq));
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            if (kbase + m >= nk) S[mb][m >> 2][m & 3] = -INFINITY;
       }
+      bf16x8 dS[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int t = m >> 2, r = m & 3;
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][t][r], c_log2, -lse2[mb]));
+          dS[mb][m] = (bf16)(pv * (dP[mb][t][r] - Dq[mb]));
+        }
 #pragma unroll
       for (int e = 0; e < C::DT; ++e) {
         const bf16x8 kta = *reinterpret_cast<const bf16x8 *>(sKT(cur) + tr.off(u, e));
-        acc[e] = mfma16(kta, dS, acc[e]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb][e] = mfma16(kta, dS[mb], acc[mb][e]);
       }
     }
     // this wave's loads of the next stage have landed and every wave is done
@@ -236,14 +268,18 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dq_kernel(A
     __syncthreads();
   }
 
-  if (q_row < p.Nq) {
-    bf16 *dst = p.dq + (int64_t)b * p.dq_bs + (int64_t)q_row * p.dq_rs + h * DH + 4 * g;
 #pragma unroll
-    for (int e = 0; e < C::DT; ++e) {
-      bf16x4 v;
+  for (int mb = 0; mb < MB; ++mb) {
+    const int q_row = q_row0 + 16 * mb;
+    if (q_row < p.Nq) {
+      bf16 *dst = p.dq + (int64_t)b * p.dq_bs + (int64_t)q_row * p.dq_rs + h * DH + 4 * g;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc[e][r] * p.scale);
-      *reinterpret_cast<bf16x4 *>(dst + 16 * e) = v;
+      for (int e = 0; e < C::DT; ++e) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)(acc[mb][e][r] * p.scale);
+        *reinterpret_cast<bf16x4 *>(dst + 16 * e) = v;
+      }
     }
   }
 }
@@ -252,7 +288,7 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dq_kernel(A
 // dK, dV
 // ---------------------------------------------------------------------------
 template <int DH>
-__global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dkv_kernel(AttnBwdParams p, int nkb,
+__global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_kernel(AttnBwdParams p, int nkb,
                                                                                int per_xcd, int total) {
   using C = BwdCfg<DH>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -273,20 +309,23 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dkv_kernel(
   const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int k_row = kb * C::BW + wave * 16 + l16;
-  const int k_ld = min(k_row, p.Nk - 1);
+  constexpr int MB = C::MB_DKV;
+  const int k_row0 = kb * C::BW_DKV + wave * 16 * MB + l16;   // + 16 mb for key block mb
   const int nk = min(max(p.nk[b], 1), p.Nk);
-  const bool k_valid = k_row < nk;
   const float c_log2 = p.scale * 1.4426950408889634f;
 
-  bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
-  {
+  bf16x8 kf[MB][C::KSTEPS], vf[MB][C::KSTEPS];
+  float kmask[MB];   // 1 for valid keys, 0 for keys past nk
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int k_ld = min(k_row0 + 16 * mb, p.Nk - 1);
+    kmask[mb] = k_row0 + 16 * mb < nk ? 1.f : 0.f;
     const bf16 *kp = p.k + (int64_t)b * p.k_bs + (int64_t)k_ld * p.k_rs + h * DH + 8 * g;
     const bf16 *vp = p.v + (int64_t)b * p.v_bs + (int64_t)k_ld * p.v_rs + h * DH + 8 * g;
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) {
-      kf[s] = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
-      vf[s] = *reinterpret_cast<const bf16x8 *>(vp + 32 * s);
+      kf[mb][s] = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
+      vf[mb][s] = *reinterpret_cast<const bf16x8 *>(vp + 32 * s);
     }
   }
 
@@ -336,14 +375,16 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dkv_kernel(
   TrReader tr;
   tr.init(l16, g);
 
-  floatx4 dK[C::DT], dV[C::DT];
+  floatx4 dK[MB][C::DT], dV[MB][C::DT];
 #pragma unroll
-  for (int e = 0; e < C::DT; ++e)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dK[e][r] = 0.f;
-      dV[e][r] = 0.f;
-    }
+    for (int e = 0; e < C::DT; ++e)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dK[mb][e][r] = 0.f;
+        dV[mb][e][r] = 0.f;
+      }
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   const int nst = (Nq + BT - 1) / BT;
@@ -355,15 +396,18 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dkv_kernel(
     if (st + 1 < nst) issue(cur ^ 1, (st + 1) * BT);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      floatx4 S[2], dP[2];
+      floatx4 S[MB][2], dP[MB][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
           const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ(cur) + rr.off(u, t, s));
           const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sDO(cur) + rr.off(u, t, s));
-          S[t] = mfma16(qa, kf[s], s == 0 ? zero4 : S[t]);
-          dP[t] = mfma16(da, vf[s], s == 0 ? zero4 : dP[t]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            S[mb][t] = mfma16(qa, kf[mb][s], s == 0 ? zero4 : S[mb][t]);
+            dP[mb][t] = mfma16(da, vf[mb][s], s == 0 ? zero4 : dP[mb][t]);
+          }
         }
       }
       // this lane's queries: 32 u + 8 g + m of the stage, m = 4 t + r
@@ -373,40 +417,52 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS), 1) void attn_bwd_dkv_kernel(
       const float4 d1 = *reinterpret_cast<const float4 *>(sD(cur) + 32 * u + 8 * g + 4);
       const float lq[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
       const float dq[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      // queries past Nq (last stage only) and keys past nk get zero weight
+      float lqm[8];
       const int qbase = st * BT + 32 * u + 8 * g;
-      bf16x8 P, dS;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int t = m >> 2, r = m & 3;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[t][r], c_log2, -lq[m]));
-        if (!k_valid || qbase + m >= Nq) pv = 0.f;
-        P[m] = (bf16)pv;
-        dS[m] = (bf16)(pv * (dP[t][r] - dq[m]));
-      }
+      for (int m = 0; m < 8; ++m) lqm[m] = (st == nst - 1 && qbase + m >= Nq) ? INFINITY : lq[m];
+      bf16x8 P[MB], dS[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int t = m >> 2, r = m & 3;
+          const float pv = kmask[mb] * __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][t][r], c_log2, -lqm[m]));
+          P[mb][m] = (bf16)pv;
+          dS[mb][m] = (bf16)(pv * (dP[mb][t][r] - dq[m]));
+        }
 #pragma unroll
       for (int e = 0; e < C::DT; ++e) {
         const bf16x8 doa = *reinterpret_cast<const bf16x8 *>(sDOT(cur) + tr.off(u, e));
         const bf16x8 qta = *reinterpret_cast<const bf16x8 *>(sQT(cur) + tr.off(u, e));
-        dV[e] = mfma16(doa, P, dV[e]);
-        dK[e] = mfma16(qta, dS, dK[e]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          dV[mb][e] = mfma16(doa, P[mb], dV[mb][e]);
+          dK[mb][e] = mfma16(qta, dS[mb], dK[mb][e]);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
-  if (k_row < p.Nk) {
-    const int64_t o = (int64_t)b * p.dk_bs + (int64_t)k_row * p.dk_rs + h * DH + 4 * g;
 #pragma unroll
-    for (int e = 0; e < C::DT; ++e) {
-      bf16x4 vk, vv;
+  for (int mb = 0; mb < MB; ++mb) {
+    const int k_row = k_row0 + 16 * mb;
+    if (k_row < p.Nk) {
+      const int64_t o = (int64_t)b * p.dk_bs + (int64_t)k_row * p.dk_rs + h * DH + 4 * g;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        vk[r] = (bf16)(dK[e][r] * p.scale);
-        vv[r] = (bf16)dV[e][r];
+      for (int e = 0; e < C::DT; ++e) {
+        bf16x4 vk, vv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          vk[r] = (bf16)(dK[mb][e][r] * p.scale);
+          vv[r] = (bf16)dV[mb][e][r];
+        }
+        *reinterpret_cast<bf16x4 *>(p.dk + o + 16 * e) = vk;
+        *reinterpret_cast<bf16x4 *>(p.dv + o + 16 * e) = vv;
       }
-      *reinterpret_cast<bf16x4 *>(p.dk + o + 16 * e) = vk;
-      *reinterpret_cast<bf16x4 *>(p.dv + o + 16 * e) = vv;
     }
   }
 }
@@ -424,17 +480,17 @@ hipError_t launch_bwd_impl(const AttnBwdParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int nqb = (p.Nq + C::BW - 1) / C::BW;
+  const int nqb = (p.Nq + C::BW_DQ - 1) / C::BW_DQ;
   int total = nqb * p.H * p.B;
   int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DH>), dim3(per_xcd * 8), dim3(C::THREADS), C::DQ_LDS, s, p, nqb,
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DH>), dim3(per_xcd * 8), dim3(C::THREADS_DQ), C::DQ_LDS, s, p, nqb,
                      per_xcd, total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nkb = (p.Nk + C::BW - 1) / C::BW;
+  const int nkb = (p.Nk + C::BW_DKV - 1) / C::BW_DKV;
   total = nkb * p.H * p.B;
   per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DH>), dim3(per_xcd * 8), dim3(C::THREADS), C::DKV_LDS, s, p, nkb,
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DH>), dim3(per_xcd * 8), dim3(C::THREADS_DKV), C::DKV_LDS, s, p, nkb,
                      per_xcd, total);
   return hipGetLastError();
 }
