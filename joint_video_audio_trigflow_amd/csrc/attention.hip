@@ -113,6 +113,9 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   const int l16 = lane & 15, g = lane >> 4;
   const int q_row0 = qb * C::BM + wave * 16 * C::MB + l16;   // + 16 mb for row block mb
   const int nk = min(max(p.nk[b], 1), p.Nk);
+  // forward only: also store the output over the first nk_split keys (a
+  // multiple of 32, at most nk) into o2
+  const int nk_split = (!TAN && p.o2) ? p.nk_split : -1;
 
   const float scale = p.scale;
   const float c_log2 = scale * 1.4426950408889634f;
@@ -363,6 +366,34 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     return __any(any);
   };
 
+  // Forward only: the normalised output of the keys seen so far into `dst`
+  // (o's strides).  Used mid-loop for the prefix snapshot and not for the JVP.
+  auto store_prefix = [&](void *dst) {
+    if constexpr (!TAN) {
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const int q_row = q_row0 + 16 * mb;
+        if (q_row < p.Nq) {
+          const float inv_l = 1.f / Lacc[mb][0];
+          const int64_t obase = (int64_t)b * p.o_bs + (int64_t)q_row * p.o_rs + h * DH + 4 * g;
+#pragma unroll
+          for (int e = 0; e < C::DT; ++e) {
+            if (p.out_dt == 0) {
+              bf16x4 a;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) a[r] = (bf16)(O[mb][e][r] * inv_l);
+              *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(dst) + obase + 16 * e) = a;
+            } else {
+              *reinterpret_cast<float4 *>(reinterpret_cast<float *>(dst) + obase + 16 * e) =
+                  make_float4(O[mb][e][0] * inv_l, O[mb][e][1] * inv_l, O[mb][e][2] * inv_l,
+                              O[mb][e][3] * inv_l);
+            }
+          }
+        }
+      }
+    }
+  };
+
   // ---- main loop over 32-key sub-tiles; 64-key stages in two LDS buffers ----
   // The logits of sub-tile j+1 are computed in the same basic block as the
   // softmax of sub-tile j, so the matrix cores work while the VALU exponentiates.
@@ -398,6 +429,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       compute_s(u == 0 ? cur : cur ^ 1, u ^ 1, Sn, Sdn);   // (unused past the end)
       softmax(S, Sd, P, PS);
       pv_accum(cur, u, P, PS);
+      if (!TAN && 32 * (j + 1) == nk_split) store_prefix(p.o2);
       if (u == 1) {                                     // stage consumed: refill its buffer
         __syncthreads();
         if (st + 2 < nst) issue(cur, (st + 2) * BN);
@@ -412,6 +444,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       } else {
       softmax(S, Sd, P, PS);
       pv_accum(cur, u, P, PS);
+      if (!TAN && 32 * (j + 1) == nk_split) store_prefix(p.o2);
       if (j + 1 < nsub) {
         if (u == 1) {
           // one barrier: every wave is done with this stage's buffer and the

@@ -184,6 +184,10 @@ struct AttnParams {
   const bf16 *q, *k, *vt, *qd, *kd, *vdt;
   const int32_t *nk;
   void *o, *od;
+  // forward only (nullable): o2 receives the output over the first nk_split
+  // keys, a multiple of 32 no larger than any nk[b] (same strides as o)
+  void *o2;
+  int nk_split;
   float *lse;
   int64_t q_bs, q_rs, k_bs, k_rs, vt_bs, vt_hs, vt_rs, o_bs, o_rs;
   int B, H, Nq, Nk;

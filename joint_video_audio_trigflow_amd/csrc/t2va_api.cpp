@@ -462,13 +462,14 @@ struct Block {
   // the tangent operands are the batches that follow (QK + B qk_bs, VT + B
   // vt_bs) and the tangent output goes to O + B o_bs.
   t2va_status attention(const bf16 *QK, const bf16 *VT, const int32_t *nk, bf16 *O, bool tan,
-                        int phase, float *lse = nullptr) const {
+                        int phase, float *lse = nullptr, bf16 *O_prefix = nullptr, int nk_split = 0) const {
     AttnParams p;
     p.q = QK; p.k = QK + D; p.vt = VT;
     p.qd = tan ? QK + (int64_t)B * qk_bs : nullptr;
     p.kd = tan ? QK + (int64_t)B * qk_bs + D : nullptr;
     p.vdt = tan ? VT + (int64_t)B * vt_bs : nullptr;
     p.nk = nk; p.o = O; p.od = tan ? O + (int64_t)B * o_bs : nullptr; p.lse = lse;
+    p.o2 = O_prefix; p.nk_split = nk_split;
     p.q_bs = qk_bs; p.q_rs = 2 * D; p.k_bs = qk_bs; p.k_rs = 2 * D;
     p.vt_bs = vt_bs; p.vt_hs = vt_hs; p.vt_rs = ldv;
     p.o_bs = o_bs; p.o_rs = D;
@@ -666,6 +667,7 @@ t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, c
   p.q = (const bf16 *)q; p.k = (const bf16 *)k; p.vt = (const bf16 *)vt;
   p.qd = (const bf16 *)qd; p.kd = (const bf16 *)kd; p.vdt = (const bf16 *)vdt;
   p.nk = nk_valid; p.o = o; p.od = od; p.lse = lse;
+  p.o2 = nullptr; p.nk_split = 0;
   p.q_bs = d.q_batch_stride; p.q_rs = d.q_row_stride;
   p.k_bs = d.k_batch_stride; p.k_rs = d.k_row_stride;
   p.vt_bs = d.vt_batch_stride; p.vt_hs = d.vt_head_stride; p.vt_rs = d.vt_row_stride;
@@ -974,7 +976,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
     HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, 0, nk, s), "text rows");
   else
     HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
-  if (guided) HIP_TRY(launch_fill_nk(nk_null, B, Nq, s), "fill nk");
+  if (guided && Nq % 32 != 0) HIP_TRY(launch_fill_nk(nk_null, B, Nq, s), "fill nk");
 
 #define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
   // ---------------- teacher: conditional and null-condition passes ----------------
@@ -983,9 +985,16 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   // [0, B) conditional, [B, 2B) unconditional.
   HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
   T2VA_CALL(blk.project_in(W[0], zv, za, tau, X, QK, VT, B));
-  T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
-  if (guided)
-    T2VA_CALL(blk.attention(QK, VT, nk_null, O + (int64_t)B * blk.o_bs, false, T2VA_PHASE_TEACHER_ATTN));
+  if (guided && Nq % 32 == 0) {
+    // the text keys follow the video and audio keys, so the null-condition
+    // output is the running state after the first Nq keys: one pass stores both
+    T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN, nullptr,
+                            O + (int64_t)B * blk.o_bs, Nq));
+  } else {
+    T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
+    if (guided)
+      T2VA_CALL(blk.attention(QK, VT, nk_null, O + (int64_t)B * blk.o_bs, false, T2VA_PHASE_TEACHER_ATTN));
+  }
   T2VA_CALL(blk.project_out(W[0], O, xT_v, xT_a, guided ? 2 * B : B));
 
   // ---------------- fake-score block ----------------
