@@ -19,14 +19,19 @@ import sys
 
 def short(name: str) -> str:
     for key, label in (("attn_fwd_jvp_kernel<128, true>", "attn_fwd_jvp<128,true> (student fwd+JVP)"),
-                       ("attn_fwd_jvp_kernel<128, false>", "attn_fwd_jvp<128,false> (teacher fwd)"),
-                       ("gemm_bf16_kernel", "gemm_bf16"),
+                       ("attn_fwd_jvp_kernel<128, false>", "attn_fwd_jvp<128,false> (forward: teacher, fake)"),
+                       ("attn_bwd_dkv_kernel<128>", "attn_bwd_dkv<128> (backward dK, dV)"),
+                       ("attn_bwd_dq_kernel<128>", "attn_bwd_dq<128> (backward dQ)"),
+                       ("gemm_bf16_large_kernel", "gemm_bf16_large (256x256 tiles)"),
+                       ("gemm_bf16_kernel", "gemm_bf16 (128x128 tiles)"),
                        ("copyBuffer", "copyBuffer"),
                        ("elementwise_kernel", "torch copy")):
         if key in name:
             return label
     for key in ("trigflow_kernel", "text_rows_kernel", "scm_direction_kernel", "normalise_kernel",
-                "time_linear_kernel", "time_embedding_kernel", "cast_kernel"):
+                "time_linear_kernel", "time_embedding_kernel", "cast_kernel", "dmd_direction_kernel",
+                "transpose_kernel", "rowterm_kernel", "seed_kernel", "colsum_kernel", "time_grad_kernel",
+                "reduce_splits_kernel", "zero_rows_kernel", "fill_nk_kernel", "mix_kernel"):
         if key in name:
             return key
     return name[:60]
