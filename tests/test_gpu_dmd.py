@@ -146,3 +146,22 @@ def test_dmd_target_rf_wrapper_matches_oracle(cfg):
     got = run_dmd(p)
     ref = oracle.dmd_target(p)
     check(cfg, got, ref)
+
+
+ALLPAD = inputs.Config("allpad", B=2, Nv=96, Na=40, Nt=16, Ntv=0, Cv=64, Ca=64, d=256, H=2,
+                       in_dtype="bf16", index=13)
+ONETOK = inputs.Config("onetoken", B=2, Nv=1, Na=1, Nt=3, Ntv=2, Cv=64, Ca=64, d=128, H=1,
+                       in_dtype="bf16", index=16)
+
+
+@pytest.mark.parametrize("cfg", [ALLPAD, ONETOK, inputs.CONFIGS["small"].replace(B=1, Nv=1568)],
+                         ids=lambda c: c.name + f"-nq{c.Nq}")
+def test_dmd_target_edge_cases(cfg):
+    """All text padded (the null condition equals the condition), one token per
+    modality, and Nq a multiple of 32 but not of 64 (the single guided pass
+    stores its null output in the middle of a 64-key stage)."""
+    say(f"dmd_target edge case {cfg.name} Nq={cfg.Nq}")
+    p = inputs.make_dmd_problem(cfg)
+    got = run_dmd(p)
+    ref = oracle.dmd_target(p)
+    check(cfg, got, ref)

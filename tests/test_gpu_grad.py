@@ -50,8 +50,15 @@ def run_grad(problem):
             dev, dt)
 
 
+ALLPAD = inputs.Config("allpad", B=2, Nv=96, Na=40, Nt=16, Ntv=0, Cv=64, Ca=64, d=256, H=2,
+                       in_dtype="bf16", index=13)
+MAXB = inputs.Config("maxbatch", B=64, Nv=64, Na=32, Nt=8, Ntv=5, Cv=64, Ca=64, d=128, H=2,
+                     in_dtype="bf16", mask_mode="scatter", index=14)
+ONETOK = inputs.Config("onetoken", B=2, Nv=1, Na=1, Nt=3, Ntv=2, Cv=64, Ca=64, d=128, H=1,
+                       in_dtype="bf16", index=16)
+
 CASES = [inputs.CONFIGS["tiny"], RAGGED, RAGGED64, inputs.CONFIGS["tiny"].replace(param="rf"),
-         RAGGED.replace(param="rf"), inputs.CONFIGS["small"]]
+         RAGGED.replace(param="rf"), inputs.CONFIGS["small"], ALLPAD, MAXB, ONETOK]
 
 
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name + ("-rf" if c.param == "rf" else ""))

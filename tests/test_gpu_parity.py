@@ -254,3 +254,26 @@ def test_scm_target_rf_wrapper_matches_oracle(cfg):
     got = run_scm(p)
     ref = oracle.scm_target(p)
     check_against_oracle(cfg, got, ref)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases of the target: every text position padded, the largest batch the
+# coefficient table holds, gamma = 0, and one token per modality.
+# ---------------------------------------------------------------------------
+ALLPAD = inputs.Config("allpad", B=2, Nv=96, Na=40, Nt=16, Ntv=0, Cv=64, Ca=64, d=256, H=2,
+                       in_dtype="bf16", index=13)
+MAXB = inputs.Config("maxbatch", B=64, Nv=64, Na=32, Nt=8, Ntv=5, Cv=64, Ca=64, d=128, H=2,
+                     in_dtype="bf16", mask_mode="scatter", index=14)
+GAMMA0 = inputs.Config("gamma0", B=2, Nv=100, Na=30, Nt=10, Ntv=7, Cv=128, Ca=64, d=256, H=4,
+                       in_dtype="bf16", beta=0.5, gamma=0.0, index=15)
+ONETOK = inputs.Config("onetoken", B=2, Nv=1, Na=1, Nt=3, Ntv=2, Cv=64, Ca=64, d=128, H=1,
+                       in_dtype="bf16", index=16)
+
+
+@pytest.mark.parametrize("cfg", [ALLPAD, MAXB, GAMMA0, ONETOK], ids=lambda c: c.name)
+def test_scm_target_edge_cases(cfg):
+    say(f"scm_target edge case {cfg.name}")
+    p = inputs.make_problem(cfg)
+    got = run_scm(p)
+    ref = oracle.scm_target(p)
+    check_against_oracle(cfg, got, ref)
