@@ -164,7 +164,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
 // ---------------------------------------------------------------------------
 constexpr int LBM = 256, LBN = 256;
 constexpr int kLStageElems = (LBM + LBN) * BK;                      // unpadded rows
-constexpr size_t kLLdsBytes = 2 * kLStageElems * sizeof(bf16);      // 128 KB
+constexpr int kEpiLD = 128 + 8;   // staged epilogue: per wave [64 cols][128 rows + 8] bf16
+constexpr size_t kLLdsBytes = 2 * kLStageElems * sizeof(bf16) > (size_t)8 * 64 * kEpiLD * sizeof(bf16)
+                                  ? 2 * kLStageElems * sizeof(bf16)                 // 128 KB of stages
+                                  : (size_t)8 * 64 * kEpiLD * sizeof(bf16);         // 136 KB epilogue
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -285,6 +288,68 @@ __global__ __launch_bounds__(kLThreads) void gemm_bf16_large_kernel(GemmParams p
 
   // Epilogue.  MFMA 32x32 output: lane holds column l32 and rows 8*(v/4) + 4*hi + v%4.
   const float *bias = p.bias ? p.bias + (int64_t)bz * p.bias_bs : nullptr;
+  if constexpr (kLWaves == 8) {
+    // bf16 outputs go through LDS (free after the main loop's last barrier):
+    // the wave's 128x64 tile is stored column-major, then written to global
+    // memory in 16-byte row chunks (row-major C) or token chunks (V^T).
+    if (p.c_dt == 0 && (p.n_split % 64 == 0 || p.n_split >= p.N)) {
+      bf16 *st = smem + wave * 64 * kEpiLD;
+      const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 64;
+#pragma unroll
+      for (int j = 0; j < kLJ; ++j) {
+        const int cl = j * 32 + l32;
+        const float bcol = (bias && wcol0 + cl < p.N) ? bias[wcol0 + cl] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 pk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pk[u] = (bf16)(acc[i][j][4 * g + u] + bcol);
+            *reinterpret_cast<bf16x4 *>(st + cl * kEpiLD + i * 32 + 8 * g + 4 * hi) = pk;
+          }
+      }
+      if (wcol0 >= p.n_split) {
+        // V^T: chunk q = column q / 16, tokens 8 (q % 16) .. + 7
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int q = lane + 64 * k;
+          const int c = q >> 4, rc = q & 15;
+          const int col = wcol0 + c, row = wrow0 + 8 * rc;
+          if (col >= p.N || row >= p.vt_rows) continue;
+          const bf16x8 v = *reinterpret_cast<const bf16x8 *>(st + c * kEpiLD + 8 * rc);
+          const int cc = col - p.n_split;
+          bf16 *vt = p.VT + (int64_t)bz * p.vt_bs + (int64_t)(cc / p.dh) * p.vt_hs + (int64_t)(cc % p.dh) * p.vt_rs;
+          if (row + 8 <= p.vt_rows) {
+            *reinterpret_cast<bf16x8 *>(vt + row) = v;
+          } else {
+            for (int u = 0; u < 8; ++u)
+              if (row + u < p.vt_rows) vt[row + u] = v[u];
+          }
+        }
+      } else {
+        // row-major C: chunk q = row q / 8, columns 8 (q % 8) .. + 7
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int q = lane + 64 * k;
+          const int r = q >> 3, c8 = (q & 7) * 8;
+          const int row = wrow0 + r, col = wcol0 + c8;
+          if (row >= p.M || col >= p.N) continue;
+          bf16x8 v;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = st[(c8 + u) * kEpiLD + r];
+          bf16 *dst = reinterpret_cast<bf16 *>(p.C) + (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col;
+          if (col + 8 <= p.N && ((p.ldc | col) & 7) == 0) {
+            *reinterpret_cast<bf16x8 *>(dst) = v;
+          } else {
+            for (int u = 0; u < 8; ++u)
+              if (col + u < p.N) dst[u] = v[u];
+          }
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < kLJ; ++j) {
     const int col = n0 + wn * 32 * kLJ + j * 32 + l32;
