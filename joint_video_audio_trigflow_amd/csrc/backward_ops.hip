@@ -33,7 +33,50 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(CoefTable coef, float w,
 }
 
 // dst[c][r] = src[r][c] for one (b, h) slice per blockIdx.z; rows r in
-// [R, Rpad) of dst are written as zeros.  64x64 tiles through LDS.
+// [R, Rpad) of dst are written as zeros.  64x64 tiles through LDS; bf16
+// sources with 8-aligned rows move 16 bytes per lane on both sides.
+__global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][64 + 8];
+  const int bh = blockIdx.z;
+  const int b = bh / p.H, h = bh % p.H;
+  const bf16 *src = reinterpret_cast<const bf16 *>(p.src) + (int64_t)b * p.s_bs + (int64_t)h * p.s_hs;
+  bf16 *dst = p.dst + (int64_t)b * p.d_bs + (int64_t)h * p.d_hs;
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int t = threadIdx.x;
+  // load: 64 rows x 8 chunks of 8 columns; thread t -> row t / 8 (+ 32), chunk t % 8
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = t / 8 + 32 * k, ch = (t % 8) * 8;
+    const int r = r0 + i, c = c0 + ch;
+    bf16x8 v;
+    if (r < p.R && c + 8 <= p.C) {
+      v = *reinterpret_cast<const bf16x8 *>(src + (int64_t)r * p.s_rs + c);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (r < p.R && c + u < p.C) ? src[(int64_t)r * p.s_rs + c + u] : (bf16)0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tile[ch + u][i] = v[u];
+  }
+  __syncthreads();
+  // store: 64 dst rows (source columns) x 8 chunks of 8 source rows
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = t / 8 + 32 * k, ch = (t % 8) * 8;
+    const int c = c0 + i, r = r0 + ch;
+    if (c >= p.C) continue;
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(&tile[i][ch]);
+    bf16 *d = dst + (int64_t)c * p.d_rs + r;
+    if (r + 8 <= p.Rpad && (((uintptr_t)d) & 15) == 0) {
+      *reinterpret_cast<bf16x8 *>(d) = v;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (r + u < p.Rpad) d[u] = v[u];
+    }
+  }
+}
+
 template <typename TS>
 __global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeParams p) {
   __shared__ float tile[64][65];
@@ -100,33 +143,35 @@ __global__ __launch_bounds__(kThreads) void zero_rows_kernel(bf16 *X, int64_t bs
   }
 }
 
-// part[b][chunk][j] = sum over rows of chunk `chunk` of dX[b][row][j].
+// part[b][chunk][j] = sum over rows of chunk `chunk` of dX[b][row][j]; a
+// thread sums 8 adjacent columns (cols and rs are multiples of 8).
 __global__ __launch_bounds__(kThreads) void colsum_kernel(const bf16 *dX, int64_t bs, int64_t rs, int rows,
                                                           int cols, int rows_per_chunk, int nchunk,
                                                           float *part) {
-  const int j = blockIdx.x * kThreads + threadIdx.x;
+  const int j = (blockIdx.x * kThreads + threadIdx.x) * 8;
   const int chunk = blockIdx.y, b = blockIdx.z;
   if (j >= cols) return;
   const int r0 = chunk * rows_per_chunk, r1 = min(rows, r0 + rows_per_chunk);
   const bf16 *x = dX + (int64_t)b * bs + j;
-  float acc = 0.f;
-  for (int r = r0; r < r1; ++r) acc += to_f32(x[(int64_t)r * rs]);
-  part[((int64_t)b * nchunk + chunk) * cols + j] = acc;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = r0; r < r1; ++r) {
+    float f[8];
+    load8(x + (int64_t)r * rs, f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += f[u];
+  }
+  store8(part + ((int64_t)b * nchunk + chunk) * cols + j, acc);
 }
 
-// dW_t[i][j] = sum_b (sum_chunk part[b][chunk][i]) E[b][j]: the gradient of
-// tau = W_t e through the bias of every video and audio row.
-__global__ __launch_bounds__(kThreads) void time_grad_kernel(const float *part, int B, int nchunk, int d,
-                                                             const float *E, float *dWt) {
+// dW_t[i][j] = sum_b dtau[b][i] E[b][j]: the gradient of tau = W_t e through
+// the bias of every video and audio row (dtau = the column sums of dX).
+__global__ __launch_bounds__(kThreads) void time_grad_kernel(const float *dtau, int B, int d, const float *E,
+                                                             float *dWt) {
   const int i = blockIdx.y;
   const int j = blockIdx.x * kThreads + threadIdx.x;
   if (j >= d) return;
   float acc = 0.f;
-  for (int b = 0; b < B; ++b) {
-    float g = 0.f;
-    for (int c = 0; c < nchunk; ++c) g += part[((int64_t)b * nchunk + c) * d + i];
-    acc += g * E[(int64_t)b * d + j];
-  }
+  for (int b = 0; b < B; ++b) acc += dtau[(int64_t)b * d + i] * E[(int64_t)b * d + j];
   dWt[(int64_t)i * d + j] = acc;
 }
 
@@ -152,8 +197,12 @@ hipError_t launch_seed(const CoefTable &coef, float w, const float *gbar, bf16 *
 hipError_t launch_transpose(const TransposeParams &p, int src_fp32, hipStream_t s) {
   if (p.R <= 0 && p.Rpad <= 0) return hipSuccess;
   dim3 grid((unsigned)((p.Rpad + 63) / 64), (unsigned)((p.C + 63) / 64), (unsigned)(p.B * p.H));
+  const bool vec = !src_fp32 && p.s_rs % 8 == 0 && p.s_bs % 8 == 0 && p.s_hs % 8 == 0 &&
+                   ((uintptr_t)p.src & 15) == 0;
   if (src_fp32)
     hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(kThreads), 0, s, p);
+  else if (vec)
+    hipLaunchKernelGGL(transpose16_kernel, grid, dim3(kThreads), 0, s, p);
   else
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
@@ -174,17 +223,23 @@ hipError_t launch_zero_rows(bf16 *X, int64_t bs, int64_t rs, int B, int r0, int 
   return hipGetLastError();
 }
 
-int colsum_chunks(int rows) { return (rows + 511) / 512; }
+int colsum_chunks(int rows) { return (rows + 127) / 128; }
 
 hipError_t launch_time_grad(const bf16 *dX, int64_t bs, int64_t rs, int B, int rows, int d, const float *E,
                             float *part, float *dWt, hipStream_t s) {
   const int nchunk = colsum_chunks(rows);
-  hipLaunchKernelGGL(colsum_kernel, dim3((d + kThreads - 1) / kThreads, nchunk, B), dim3(kThreads), 0, s, dX,
-                     bs, rs, rows, d, 512, nchunk, part);
+  hipLaunchKernelGGL(colsum_kernel, dim3((d / 8 + kThreads - 1) / kThreads, nchunk, B), dim3(kThreads), 0, s,
+                     dX, bs, rs, rows, d, 128, nchunk, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(time_grad_kernel, dim3((d + kThreads - 1) / kThreads, d), dim3(kThreads), 0, s, part, B,
-                     nchunk, d, E, dWt);
+  // dtau[b] = sum over chunks in order, after the partials
+  float *dtau = part + (int64_t)B * nchunk * d;
+  for (int b = 0; b < B; ++b) {
+    e = launch_reduce_splits(part + (int64_t)b * nchunk * d, nchunk, d, dtau + (int64_t)b * d, s);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(time_grad_kernel, dim3((d + kThreads - 1) / kThreads, d), dim3(kThreads), 0, s, dtau, B, d,
+                     E, dWt);
   return hipGetLastError();
 }
 

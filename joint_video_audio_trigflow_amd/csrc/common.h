@@ -228,7 +228,8 @@ hipError_t launch_transpose(const TransposeParams &p, int src_fp32, hipStream_t 
 hipError_t launch_rowterms(const bf16 *dO, const bf16 *O, int64_t bs, int64_t rs, int B, int H, int dh, int Nq,
                            const float *lse, float *lse2, float *D, hipStream_t s);
 hipError_t launch_zero_rows(bf16 *X, int64_t bs, int64_t rs, int B, int r0, int r1, int cols, hipStream_t s);
-// dW_t = sum_b (sum_rows dX[b]) e_b^T with fixed-order partial sums (part: B * colsum_chunks(rows) * d floats).
+// dW_t = sum_b (sum_rows dX[b]) e_b^T with fixed-order partial sums
+// (part: B * (colsum_chunks(rows) + 1) * d floats).
 int colsum_chunks(int rows);
 hipError_t launch_time_grad(const bf16 *dX, int64_t bs, int64_t rs, int B, int rows, int d, const float *E,
                             float *part, float *dWt, hipStream_t s);

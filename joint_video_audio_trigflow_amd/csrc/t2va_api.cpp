@@ -263,7 +263,7 @@ GradLayout make_grad_layout(const t2va_scm_desc &d) {
   G.zT_v = take((size_t)d.Cv * G.kp_v * bfs);
   G.dxT_a = take(D * G.kp_a * bfs);
   G.zT_a = take((size_t)d.Ca * G.kp_a * bfs);
-  G.tpart = take(B * (size_t)colsum_chunks((int)Nq) * D * fs);
+  G.tpart = take(B * (size_t)(colsum_chunks((int)Nq) + 1) * D * fs);   // partial sums, then dtau
   const size_t part_elems = std::max({(size_t)G.split_v * d.Cv * D, (size_t)G.split_a * d.Ca * D,
                                       (size_t)G.split_all * 3 * D * D});
   G.part = take(part_elems * fs);
