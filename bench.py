@@ -37,9 +37,10 @@ def workload_name(cfg) -> str:
 
 def attention_kernel_digest() -> str:
     """SHA-256 of the source text the attention kernel is compiled from:
-    attention.hip, the shared types and load/store helpers at the top of
-    common.h, and the AttnParams declaration (the other kernels' coefficient
-    tables and parameter blocks do not count)."""
+    attention.hip, its tile helpers (attn_tiles.h), the shared types and
+    load/store helpers at the top of common.h, and the AttnParams declaration
+    (the other kernels' coefficient tables and parameter blocks do not
+    count)."""
     import hashlib
     csrc = os.path.join(ROOT, "joint_video_audio_trigflow_amd", "csrc")
     common = open(os.path.join(csrc, "common.h")).read()
@@ -47,7 +48,8 @@ def attention_kernel_digest() -> str:
     a = common.index("struct AttnParams")
     params = common[a:common.index("};", a) + 2]
     attn = open(os.path.join(csrc, "attention.hip")).read()
-    return hashlib.sha256((attn + head + params).encode()).hexdigest()
+    tiles = open(os.path.join(csrc, "attn_tiles.h")).read()
+    return hashlib.sha256((attn + tiles + head + params).encode()).hexdigest()
 
 
 def counted_traffic(cfg):

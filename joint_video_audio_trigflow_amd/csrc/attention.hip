@@ -30,7 +30,8 @@
 //
 // Key tiles (K, dK, V^T, dV^T) go from global memory straight into LDS with
 // buffer_load_dwordx4 ... lds (no staging registers; SGPR descriptors and
-// 32-bit lane offsets), double-buffered in 64-key stages.  16-byte slots are
+// 32-bit lane offsets), in 64-key stages: a three-slot ring for K (and dK) and
+// a two-slot ring for V^T (and dV^T), one barrier per stage.  16-byte slots are
 // XOR-swizzled so that every 16-lane group of an operand read hits 16
 // different bank groups.
 #include "attn_tiles.h"
@@ -48,12 +49,6 @@ namespace {
 #ifndef T2VA_ATTN_WAVES_FWD
 #define T2VA_ATTN_WAVES_FWD 12
 #endif
-#ifndef T2VA_ATTN_PIPE_JVP
-#define T2VA_ATTN_PIPE_JVP 1
-#endif
-#ifndef T2VA_ATTN_PIPE_FWD
-#define T2VA_ATTN_PIPE_FWD 1
-#endif
 #ifndef T2VA_ATTN_MB_FWD
 #define T2VA_ATTN_MB_FWD 2
 #endif
@@ -66,7 +61,6 @@ struct AttnCfg {
   // query rows per wave.  Every K / V^T fragment a wave reads from LDS feeds
   // MB (forward) or three (JVP: K for S and dS, V for O and dO) MFMAs.
   static constexpr int NW = TAN ? T2VA_ATTN_WAVES_JVP : T2VA_ATTN_WAVES_FWD;
-  static constexpr bool PIPE = TAN ? T2VA_ATTN_PIPE_JVP : T2VA_ATTN_PIPE_FWD;
   static constexpr int MB = TAN ? 1 : T2VA_ATTN_MB_FWD;
   // row sums on the matrix cores (forward); the JVP kernel keeps them on the
   // VALU, where its register budget has room and the matrix cores do not
@@ -79,8 +73,10 @@ struct AttnCfg {
   static constexpr int K_ELEMS = BN * DH;  // K tile [BN][DH], swizzled slots
   static constexpr int V_ELEMS = DH * BN;  // V^T tile [DH][BN], swizzled slots
   static constexpr int NSTREAM = TAN ? 2 : 1;
-  static constexpr int BUF_ELEMS = NSTREAM * (K_ELEMS + V_ELEMS);          // one stage
-  static constexpr size_t LDS_BYTES = (size_t)2 * BUF_ELEMS * sizeof(bf16);  // two stages
+  // rings of three K stages ([K | dK] each) and two V^T stages ([V^T | dV^T])
+  static constexpr int KBUF_ELEMS = NSTREAM * K_ELEMS;
+  static constexpr int VBUF_ELEMS = NSTREAM * V_ELEMS;
+  static constexpr size_t LDS_BYTES = (size_t)(3 * KBUF_ELEMS + 2 * VBUF_ELEMS) * sizeof(bf16);
   // one direct load instruction moves 64 lanes x 16 B = 1 KB = 512 elements
   static constexpr int KCH = K_ELEMS / 512 / kLoadWaves;   // per loading wave, per operand tile
   static constexpr int VCH = V_ELEMS / 512 / kLoadWaves;
@@ -93,11 +89,11 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   using C = AttnCfg<DH, TAN>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16 *const lds = reinterpret_cast<bf16 *>(smem_raw);
-  // per stage: [K | V^T | dK | dV^T]
-  auto sK = [&](int buf) { return lds + buf * C::BUF_ELEMS; };
-  auto sVT = [&](int buf) { return lds + buf * C::BUF_ELEMS + C::K_ELEMS; };
-  auto sKd = [&](int buf) { return lds + buf * C::BUF_ELEMS + C::K_ELEMS + C::V_ELEMS; };
-  auto sVdT = [&](int buf) { return lds + buf * C::BUF_ELEMS + 2 * C::K_ELEMS + C::V_ELEMS; };
+  // LDS: K ring [3][K | dK], then V^T ring [2][V^T | dV^T]
+  auto sK = [&](int kb) { return lds + kb * C::KBUF_ELEMS; };
+  auto sKd = [&](int kb) { return lds + kb * C::KBUF_ELEMS + C::K_ELEMS; };
+  auto sVT = [&](int vb) { return lds + 3 * C::KBUF_ELEMS + vb * C::VBUF_ELEMS; };
+  auto sVdT = [&](int vb) { return lds + 3 * C::KBUF_ELEMS + vb * C::VBUF_ELEMS + C::V_ELEMS; };
 
   // XCD-aware order: hardware places workgroup w on XCD w % 8; give each XCD a
   // contiguous range of logical tiles so one head's K/V stay in that XCD's L2.
@@ -165,20 +161,24 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     const int e = chunk * 8 + lane / 8;
     vvo[r] = (uint32_t)((e * p.vt_rs + 8 * vslot(e, lane % 8)) * 2);
   }
-  auto issue = [&](int buf, int k0) {
+  auto issue_k = [&](int kb, int k0) {
     if (!loader) return;
-    const uint32_t kstep = (uint32_t)(k0 * p.k_rs * 2), vstep = (uint32_t)(k0 * 2);
+    const uint32_t kstep = (uint32_t)(k0 * p.k_rs * 2);
 #pragma unroll
     for (int r = 0; r < C::KCH; ++r) {
       const int chunk = lw + kLoadWaves * r;
-      load_lds16(rK, kvo[r] + kstep, sK(buf) + chunk * 512);
-      if constexpr (TAN) load_lds16(rKd, kvo[r] + kstep, sKd(buf) + chunk * 512);
+      load_lds16(rK, kvo[r] + kstep, sK(kb) + chunk * 512);
+      if constexpr (TAN) load_lds16(rKd, kvo[r] + kstep, sKd(kb) + chunk * 512);
     }
+  };
+  auto issue_v = [&](int vb, int k0) {
+    if (!loader) return;
+    const uint32_t vstep = (uint32_t)(k0 * 2);
 #pragma unroll
     for (int r = 0; r < C::VCH; ++r) {
       const int chunk = lw + kLoadWaves * r;
-      load_lds16(rV, vvo[r] + vstep, sVT(buf) + chunk * 512);
-      if constexpr (TAN) load_lds16(rVd, vvo[r] + vstep, sVdT(buf) + chunk * 512);
+      load_lds16(rV, vvo[r] + vstep, sVT(vb) + chunk * 512);
+      if constexpr (TAN) load_lds16(rVd, vvo[r] + vstep, sVdT(vb) + chunk * 512);
     }
   };
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0); };
@@ -394,15 +394,21 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     }
   };
 
-  // ---- main loop over 32-key sub-tiles; 64-key stages in two LDS buffers ----
+  // ---- main loop over 32-key sub-tiles of 64-key stages ----
   // The logits of sub-tile j+1 are computed in the same basic block as the
   // softmax of sub-tile j, so the matrix cores work while the VALU exponentiates.
+  // Stage st's K sits in ring slot st % 3 and its V^T in slot st % 2.  The
+  // sub-tiles of stage st read K of st (first) and of st+1 (second) and V^T of
+  // st (both), so one barrier per stage, at its start, suffices: it publishes
+  // K of st+1 and V^T of st (loaded during stage st-1) and frees the slots of
+  // K and V^T of st-1, which then receive K of st+2 and V^T of st+1.
   const int nst = (nk + BN - 1) / BN;
   const int nsub = 2 * nst;
-  issue(0, 0);
+  issue_k(0, 0);
   wait_loads();
   __syncthreads();
-  if (nst > 1) issue(1, BN);
+  if (nst > 1) issue_k(1, BN);
+  issue_v(0, 0);
   floatx4 S[C::MB][2], Sd[2];
   bf16x8 P[C::MB], PS;
   compute_s(0, 0, S, Sd);
@@ -419,21 +425,19 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   floatx4 Sn[C::MB][2], Sdn[2];
   for (;;) {
     for (; j < nsub; ++j) {
-      const int u = j & 1, st = j >> 1, cur = st & 1;
+      const int u = j & 1, st = j >> 1;
       if (outgrown(S)) break;   // rare: raise m_run outside
-      if constexpr (C::PIPE) {
-      if (u == 1 && j + 1 < nsub) {                     // the next stage landed: publish it
+      if (u == 0) {
         wait_loads();
         __syncthreads();
+        if (st + 2 < nst) issue_k((st + 2) % 3, (st + 2) * BN);
+        if (st + 1 < nst) issue_v((st + 1) & 1, (st + 1) * BN);
       }
-      compute_s(u == 0 ? cur : cur ^ 1, u ^ 1, Sn, Sdn);   // (unused past the end)
+      // K of the next sub-tile (unused past the end)
+      compute_s(u == 0 ? st % 3 : (st + 1) % 3, u ^ 1, Sn, Sdn);
       softmax(S, Sd, P, PS);
-      pv_accum(cur, u, P, PS);
+      pv_accum(st & 1, u, P, PS);
       if (!TAN && 32 * (j + 1) == nk_split) store_prefix(p.o2);
-      if (u == 1) {                                     // stage consumed: refill its buffer
-        __syncthreads();
-        if (st + 2 < nst) issue(cur, (st + 2) * BN);
-      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -441,22 +445,6 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
         if constexpr (TAN) Sd[t] = Sdn[t];
       }
       if (j + 1 < nsub && ((j + 1) >> 1) == nst - 1) mask_s(32 * (j + 1), S, Sd);
-      } else {
-      softmax(S, Sd, P, PS);
-      pv_accum(cur, u, P, PS);
-      if (!TAN && 32 * (j + 1) == nk_split) store_prefix(p.o2);
-      if (j + 1 < nsub) {
-        if (u == 1) {
-          // one barrier: every wave is done with this stage's buffer and the
-          // next stage (whose loads this wave waited for) is visible
-          wait_loads();
-          __syncthreads();
-          if (st + 2 < nst) issue(cur, (st + 2) * BN);
-        }
-        compute_s(u == 0 ? cur : cur ^ 1, u ^ 1, S, Sd);
-        if (((j + 1) >> 1) == nst - 1) mask_s(32 * (j + 1), S, Sd);
-      }
-      }
     }
     if (j >= nsub) break;
     // raise the reference max of the rows that outgrew it; rescale the

@@ -30,7 +30,7 @@ def short(name: str) -> str:
             return label
     for key in ("trigflow_kernel", "text_rows_kernel", "scm_direction_kernel", "normalise_kernel",
                 "time_linear_kernel", "time_embedding_kernel", "cast_kernel", "dmd_direction_kernel",
-                "transpose_kernel", "rowterm_kernel", "seed_kernel", "colsum_kernel", "time_grad_kernel",
+                "transpose16_kernel", "transpose_kernel", "rowterm_kernel", "seed_kernel", "colsum_kernel", "time_grad_kernel",
                 "reduce_splits_kernel", "zero_rows_kernel", "fill_nk_kernel", "mix_kernel"):
         if key in name:
             return key
