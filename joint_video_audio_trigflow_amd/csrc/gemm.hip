@@ -171,8 +171,15 @@ constexpr size_t kLLdsBytes = 2 * kLStageElems * sizeof(bf16) > (size_t)8 * 64 *
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Buffer resource over [base, base + bytes) (loads past the end return zeros).
+// Both arguments are wave-uniform; readfirstlane keeps the descriptor in SGPRs
+// (a VGPR descriptor makes the compiler wrap each load in a waterfall loop).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(lo | (hi << 32)), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
 }
 __device__ __forceinline__ int lslot(int row, int c) { return c ^ ((row >> 1) & 7); }
 
@@ -184,7 +191,10 @@ constexpr int kLThreads = 64 * kLWaves;
 constexpr int kLJ = kLWaves == 4 ? 4 : 2;             // 32-column tiles per wave
 constexpr int kLGroups = 32 / kLWaves;                // 8-row load groups per wave and operand
 
-__global__ __launch_bounds__(kLThreads) void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
+// One workgroup per CU (its LDS), so two waves per SIMD: the register budget is
+// 256 per wave, which the fragment double buffer below uses.
+__global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
                                                                      int tiles_m) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16 *smem = reinterpret_cast<bf16 *>(smem_raw);
@@ -266,19 +276,28 @@ __global__ __launch_bounds__(kLThreads) void gemm_bf16_large_kernel(GemmParams p
     if (kt + 1 < KT) issue(stage ^ 1, (kt + 1) * BK);
     const bf16 *sA = smem + stage * kLStageElems;
     const bf16 *sW = sA + LBM * BK;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 a[4], b[kLJ];
+    // fragments of k-step s+1 are read while the MFMAs of k-step s run
+    bf16x8 a[2][4], b[2][kLJ];
+    auto read_frags = [&](int s, int x) {
       const int c = 2 * s + hi;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8 *>(sA + abase[i] + 8 * (c ^ ax[i]));
+      for (int i = 0; i < 4; ++i) a[x][i] = *reinterpret_cast<const bf16x8 *>(sA + abase[i] + 8 * (c ^ ax[i]));
 #pragma unroll
-      for (int j = 0; j < kLJ; ++j) b[j] = *reinterpret_cast<const bf16x8 *>(sW + wbase[j] + 8 * (c ^ wx[j]));
+      for (int j = 0; j < kLJ; ++j) b[x][j] = *reinterpret_cast<const bf16x8 *>(sW + wbase[j] + 8 * (c ^ wx[j]));
+    };
+    read_frags(0, 0);
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      if (s + 1 < BK / 16) read_frags(s + 1, (s + 1) & 1);
+      // keep the reads ahead of this k-step's MFMAs (the scheduler would
+      // otherwise sink each read next to its first use)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < kLJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // the next stage has landed (this wave's loads) and every wave is done
     // reading this one before it is refilled
