@@ -355,14 +355,14 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     }
   };
   // any lane's own logits past its row's threshold (no lane exchange)
+  // (plain compares: a max tree over MFMA results would first quieten each
+  // input, one extra VALU op per logit)
   auto outgrown = [&](const floatx4 (&S)[C::MB][2]) {
     bool any = false;
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
-      const float mx = fmaxf(fmaxf(fmaxf(S[mb][0][0], S[mb][0][1]), fmaxf(S[mb][0][2], S[mb][0][3])),
-                             fmaxf(fmaxf(S[mb][1][0], S[mb][1][1]), fmaxf(S[mb][1][2], S[mb][1][3])));
-      any = any || (mx > thr[mb]);
-    }
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) any |= S[mb][m >> 2][m & 3] > thr[mb];
     return __any(any);
   };
 
