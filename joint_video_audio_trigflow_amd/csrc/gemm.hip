@@ -15,6 +15,8 @@
 // (V^T[b][h][c][row]), the layout the attention kernel stages V from.
 #include "common.h"
 
+#include <type_traits>
+
 namespace t2va {
 
 namespace {
@@ -158,16 +160,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
 // a wave reads from LDS feeds two MFMAs and every W fragment four, and two
 // waves per SIMD hide one another's LDS and barrier waits.  Tiles go from global memory straight
 // into LDS with buffer_load_dwordx4 ... lds: one instruction moves 8 rows x
-// 128 B; the 16-byte slot of chunk c of row r is c ^ ((r >> 1) & 7), so the 16
-// rows one 16-lane group reads hit 16 different bank groups.  Rows past M (or
-// N) lie past the buffer descriptor's end and load as zeros.
+// 128 B, its 16-byte chunks XOR-swizzled within each row (lslot below) so
+// that operand reads are free of bank conflicts.  Rows past M (or N) lie past
+// the buffer descriptor's end and load as zeros.
 // ---------------------------------------------------------------------------
 constexpr int LBM = 256, LBN = 256;
 constexpr int kLStageElems = (LBM + LBN) * BK;                      // unpadded rows
-constexpr int kEpiLD = 128 + 8;   // staged epilogue: per wave [64 cols][128 rows + 8] bf16
-constexpr size_t kLLdsBytes = 2 * kLStageElems * sizeof(bf16) > (size_t)8 * 64 * kEpiLD * sizeof(bf16)
+constexpr int kEpiElems = 128 * 64;   // staged epilogue: one wave's 128x64 bf16 tile (16 KB)
+constexpr size_t kLLdsBytes = 2 * kLStageElems * sizeof(bf16) > (size_t)8 * kEpiElems * sizeof(bf16)
                                   ? 2 * kLStageElems * sizeof(bf16)                 // 128 KB of stages
-                                  : (size_t)8 * 64 * kEpiLD * sizeof(bf16);         // 136 KB epilogue
+                                  : (size_t)8 * kEpiElems * sizeof(bf16);
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -181,7 +183,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(lo | (hi << 32)), (short)0,
                                            __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
 }
-__device__ __forceinline__ int lslot(int row, int c) { return c ^ ((row >> 1) & 7); }
+// 16-byte slot of chunk c (of 8) of a 128-byte tile row.  A 32x32x16 operand
+// read takes one chunk from 32 consecutive rows; with this XOR key any 8
+// consecutive rows cover all 8 slots (distinct banks when the LDS serves 128 B
+// per clock) and any 16 rows are distinct in (row parity, slot) (distinct
+// banks at 256 B per clock).  The map is an involution.
+__device__ __forceinline__ int lxor(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int lslot(int row, int c) { return c ^ lxor(row); }
+
+// Staged epilogue layouts (per wave, 16 KB, no padding): 8-byte units (4 bf16)
+// are XOR-swizzled within each line by a key of the line index, so that the
+// 8-byte stores of 16 (or 32) consecutive lanes, one line each, hit distinct
+// banks.  A 16-byte read of chunk c of a line then finds both of its halves in
+// chunk c ^ (key >> 1), swapped when the key is odd.
+__device__ __forceinline__ int ekey_row(int m) { return (m & 15) ^ ((m >> 4) & 1); }   // 16 units per line
+__device__ __forceinline__ int ekey_col(int n) { return n & 31; }                       // 32 units per line
+__device__ __forceinline__ bf16x8 read_chunk(const bf16 *line, int c, int key) {
+  bf16x8 v = *reinterpret_cast<const bf16x8 *>(line + 8 * (c ^ (key >> 1)));
+  if (key & 1) {
+    bf16x8 w;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u] = v[u + 4];
+      w[u + 4] = v[u];
+    }
+    v = w;
+  }
+  return v;
+}
 
 #ifndef T2VA_GEMM_LARGE_WAVES
 #define T2VA_GEMM_LARGE_WAVES 8
@@ -250,13 +279,13 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
   for (int i = 0; i < 4; ++i) {
     const int ra = wm * 128 + i * 32 + l32;
     abase[i] = ra * BK;
-    ax[i] = (ra >> 1) & 7;
+    ax[i] = lxor(ra);
   }
 #pragma unroll
   for (int j = 0; j < kLJ; ++j) {
     const int rw = wn * 32 * kLJ + j * 32 + l32;
     wbase[j] = rw * BK;
-    wx[j] = (rw >> 1) & 7;
+    wx[j] = lxor(rw);
   }
 
   floatx16 acc[4][kLJ];
@@ -267,10 +296,20 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // bf16 tiles staged through LDS on the way out (8 waves): row-major outputs
+  // take the product transposed (W fragments as the A operand), so that a lane
+  // holds one output row and four consecutive columns per register group;
+  // V^T outputs keep the plain order (a lane holds one column, runs of rows).
+  const int wcol0 = n0 + wn * 32 * kLJ, wrow0 = m0 + wm * 128;
+  const bool staged = kLWaves == 8 && p.c_dt == 0 && (p.n_split % 64 == 0 || p.n_split >= p.N);
+  const bool rowmajor = staged && wcol0 < p.n_split;
+
   const int KT = p.K / BK;
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  auto main_loop = [&](auto order) {
+  constexpr bool kSwap = decltype(order)::value;
   for (int kt = 0; kt < KT; ++kt) {
     const int stage = kt & 1;
     if (kt + 1 < KT) issue(stage ^ 1, (kt + 1) * BK);
@@ -296,7 +335,8 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < kLJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[s & 1][j], a[s & 1][i], acc[i][j], 0, 0, 0)
+                            : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // the next stage has landed (this wave's loads) and every wave is done
@@ -304,19 +344,59 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  };
+  if (rowmajor) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
 
-  // Epilogue.  MFMA 32x32 output: lane holds column l32 and rows 8*(v/4) + 4*hi + v%4.
+  // Epilogue.  MFMA 32x32 output: lane holds column l32 and rows 8*(v/4) + 4*hi + v%4
+  // of each 32x32 tile (with the transposed product: row l32, columns 8*(v/4) + 4*hi + v%4).
   const float *bias = p.bias ? p.bias + (int64_t)bz * p.bias_bs : nullptr;
-  if constexpr (kLWaves == 8) {
-    // bf16 outputs go through LDS (free after the main loop's last barrier):
-    // the wave's 128x64 tile is stored column-major, then written to global
-    // memory in 16-byte row chunks (row-major C) or token chunks (V^T).
-    if (p.c_dt == 0 && (p.n_split % 64 == 0 || p.n_split >= p.N)) {
-      bf16 *st = smem + wave * 64 * kEpiLD;
-      const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 64;
+  if (staged) {
+    // LDS is free after the main loop's last barrier; each wave stages its own
+    // 128x64 tile and writes it out in 16-byte chunks
+    bf16 *st = smem + wave * kEpiElems;
+    if (rowmajor) {
+      // [128 rows][64 columns]: row m = 32 i + l32; unit 8 j + 2 k + hi holds
+      // columns 32 j + 8 k + 4 hi .. + 3
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = i * 32 + l32, key = ekey_row(m);
+#pragma unroll
+        for (int j = 0; j < kLJ; ++j)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int c0 = j * 32 + 8 * k + 4 * hi;
+            bf16x4 pk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float bc = (bias && wcol0 + c0 + u < p.N) ? bias[wcol0 + c0 + u] : 0.f;
+              pk[u] = (bf16)(acc[i][j][4 * k + u] + bc);
+            }
+            *reinterpret_cast<bf16x4 *>(st + m * 64 + 4 * ((8 * j + 2 * k + hi) ^ key)) = pk;
+          }
+      }
+      // chunk q = row q / 8, columns 8 (q % 8) .. + 7
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int q = lane + 64 * k;
+        const int r = q >> 3, c = q & 7;
+        const int row = wrow0 + r, col = wcol0 + 8 * c;
+        if (row >= p.M || col >= p.N) continue;
+        const bf16x8 v = read_chunk(st + r * 64, c, ekey_row(r));
+        bf16 *dst = reinterpret_cast<bf16 *>(p.C) + (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col;
+        if (col + 8 <= p.N && ((p.ldc | col) & 7) == 0) {
+          *reinterpret_cast<bf16x8 *>(dst) = v;
+        } else {
+          for (int u = 0; u < 8; ++u)
+            if (col + u < p.N) dst[u] = v[u];
+        }
+      }
+    } else {
+      // V^T, [64 columns][128 rows]: column n = 32 j + l32; unit 8 i + 2 g + hi
+      // holds rows 32 i + 8 g + 4 hi .. + 3
 #pragma unroll
       for (int j = 0; j < kLJ; ++j) {
-        const int cl = j * 32 + l32;
+        const int cl = j * 32 + l32, key = ekey_col(cl);
         const float bcol = (bias && wcol0 + cl < p.N) ? bias[wcol0 + cl] : 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -325,49 +405,28 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
             bf16x4 pk;
 #pragma unroll
             for (int u = 0; u < 4; ++u) pk[u] = (bf16)(acc[i][j][4 * g + u] + bcol);
-            *reinterpret_cast<bf16x4 *>(st + cl * kEpiLD + i * 32 + 8 * g + 4 * hi) = pk;
+            *reinterpret_cast<bf16x4 *>(st + cl * 128 + 4 * ((8 * i + 2 * g + hi) ^ key)) = pk;
           }
       }
-      if (wcol0 >= p.n_split) {
-        // V^T: chunk q = column q / 16, tokens 8 (q % 16) .. + 7
+      // chunk q = column q / 16, tokens 8 (q % 16) .. + 7
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int q = lane + 64 * k;
-          const int c = q >> 4, rc = q & 15;
-          const int col = wcol0 + c, row = wrow0 + 8 * rc;
-          if (col >= p.N || row >= p.vt_rows) continue;
-          const bf16x8 v = *reinterpret_cast<const bf16x8 *>(st + c * kEpiLD + 8 * rc);
-          const int cc = col - p.n_split;
-          bf16 *vt = p.VT + (int64_t)bz * p.vt_bs + (int64_t)(cc / p.dh) * p.vt_hs + (int64_t)(cc % p.dh) * p.vt_rs;
-          if (row + 8 <= p.vt_rows) {
-            *reinterpret_cast<bf16x8 *>(vt + row) = v;
-          } else {
-            for (int u = 0; u < 8; ++u)
-              if (row + u < p.vt_rows) vt[row + u] = v[u];
-          }
-        }
-      } else {
-        // row-major C: chunk q = row q / 8, columns 8 (q % 8) .. + 7
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int q = lane + 64 * k;
-          const int r = q >> 3, c8 = (q & 7) * 8;
-          const int row = wrow0 + r, col = wcol0 + c8;
-          if (row >= p.M || col >= p.N) continue;
-          bf16x8 v;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = st[(c8 + u) * kEpiLD + r];
-          bf16 *dst = reinterpret_cast<bf16 *>(p.C) + (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col;
-          if (col + 8 <= p.N && ((p.ldc | col) & 7) == 0) {
-            *reinterpret_cast<bf16x8 *>(dst) = v;
-          } else {
-            for (int u = 0; u < 8; ++u)
-              if (col + u < p.N) dst[u] = v[u];
-          }
+      for (int k = 0; k < 16; ++k) {
+        const int q = lane + 64 * k;
+        const int c = q >> 4, rc = q & 15;
+        const int col = wcol0 + c, row = wrow0 + 8 * rc;
+        if (col >= p.N || row >= p.vt_rows) continue;
+        const bf16x8 v = read_chunk(st + c * 128, rc, ekey_col(c));
+        const int cc = col - p.n_split;
+        bf16 *vt = p.VT + (int64_t)bz * p.vt_bs + (int64_t)(cc / p.dh) * p.vt_hs + (int64_t)(cc % p.dh) * p.vt_rs;
+        if (row + 8 <= p.vt_rows) {
+          *reinterpret_cast<bf16x8 *>(vt + row) = v;
+        } else {
+          for (int u = 0; u < 8; ++u)
+            if (row + u < p.vt_rows) vt[row + u] = v[u];
         }
       }
-      return;
     }
+    return;
   }
 #pragma unroll
   for (int j = 0; j < kLJ; ++j) {

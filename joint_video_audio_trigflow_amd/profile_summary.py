@@ -6,6 +6,14 @@ WRITE_SIZE) of bench.py, plus the same counters for bench.py
 a markdown summary with per-kernel average durations, counter values per
 dispatch, the calibration factors and the resulting HBM traffic per launch.
 Usage: python -m joint_video_audio_trigflow_amd.profile_summary <rocprof output dir>
+
+With --clock <dir>, it reads one --pmc --kernel-trace run per subdirectory of
+<dir> instead and prints, per attention and GEMM kernel, the average of each
+counter per dispatch and these derived figures (MI355X: 8 XCDs, 256 CUs,
+1024 SIMDs; GRBM_GUI_ACTIVE reads as the sum over the XCDs):
+  clock      = GRBM_GUI_ACTIVE / 8 / kernel duration
+  MFMA busy  = SQ_VALU_MFMA_BUSY_CYCLES / 1024 / (GRBM_GUI_ACTIVE / 8)
+  LDS active = SQ_LDS_IDX_ACTIVE / 256 / (GRBM_GUI_ACTIVE / 8)
 """
 from __future__ import annotations
 
@@ -68,7 +76,49 @@ def main(d):
     return dict(fetch_factor=f_fac, write_factor=w_fac, bytes=out, fetch=fetch, write=write)
 
 
+def clock_table(d):
+    """Counters of the kernels that matter, from every <d>/*/ pmc run."""
+    keep = ("attn_", "gemm_")
+    vals = collections.defaultdict(dict)
+    durs = collections.defaultdict(list)
+    for sub in sorted(glob.glob(os.path.join(d, "*", ""))):
+        cc = glob.glob(os.path.join(sub, "*counter_collection.csv"))
+        tr = glob.glob(os.path.join(sub, "*kernel_trace.csv"))
+        if not cc:
+            continue
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in csv.DictReader(open(cc[0])):
+            k = short(r["Kernel_Name"])
+            if k.startswith(keep):
+                agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for k, cs in agg.items():
+            for c, v in cs.items():
+                vals[k][c] = sum(v) / len(v)
+        for r in csv.DictReader(open(tr[0])) if tr else []:
+            k = short(r["Kernel_Name"])
+            if k.startswith(keep):
+                durs[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    print("| kernel | ms | clock GHz | MFMA busy | LDS active | counters per dispatch |\n|---|---|---|---|---|---|")
+    out = {}
+    for k, cs in sorted(vals.items()):
+        t = sum(durs[k]) / len(durs[k]) if durs[k] else float("nan")
+        cyc = cs.get("GRBM_GUI_ACTIVE", float("nan")) / 8
+        row = dict(ms=t * 1e3, clock_ghz=cyc / t / 1e9,
+                   mfma_busy=cs.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / 1024 / cyc,
+                   lds_active=cs.get("SQ_LDS_IDX_ACTIVE", float("nan")) / 256 / cyc, counters=cs)
+        out[k] = row
+        cstr = ", ".join(f"{c} {v:.4g}" for c, v in sorted(cs.items()))
+        print(f"| {k} | {row['ms']:.3f} | {row['clock_ghz']:.2f} | {100 * row['mfma_busy']:.1f} % | "
+              f"{100 * row['lds_active']:.1f} % | {cstr} |")
+    return out
+
+
 if __name__ == "__main__":
+    if sys.argv[1] == "--clock":
+        res = clock_table(sys.argv[2])
+        if len(sys.argv) > 3:
+            json.dump(res, open(sys.argv[3], "w"), indent=1)
+        sys.exit(0)
     res = main(sys.argv[1])
     if len(sys.argv) > 2:
         json.dump(res, open(sys.argv[2], "w"), indent=1)
