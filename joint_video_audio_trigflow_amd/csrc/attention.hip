@@ -188,18 +188,17 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   // key chunk g of sub-tile u (add 16 * BN per d-tile).
   // K slot of k-step s is 4 s + g; with the XOR key x of the row it is
   // (4 s + g) ^ x = 4 (s ^ (x >> 2)) + (g ^ (x & 3)), so one XOR per read.
-  int kbase_off[2], kxs[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = 8 * (l16 >> 2) + 4 * t + (l16 & 3);
-    const int x = kslot<C::CPR>(row, 0);                 // the row's XOR key
-    kbase_off[t] = row * DH + 8 * (g ^ (x & 3));
-    kxs[t] = x >> 2;
-  }
-  auto koff = [&](int t, int s) { return kbase_off[t] + 32 * (s ^ kxs[t]); };
-  int voff[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) voff[u] = l16 * BN + 8 * vslot(l16, 4 * u + g);
+  // Rows 8 (l16 / 4) + 4 t + l16 % 4 of the two halves t share their key (it
+  // depends on row bits the half does not touch), so half 1 is half 0 moved
+  // by four rows.
+  const int krow = 8 * (l16 >> 2) + (l16 & 3);
+  const int kx = kslot<C::CPR>(krow, 0);                 // the rows' XOR key
+  const int kbase_off = krow * DH + 8 * (g ^ (kx & 3));
+  auto koff = [&](int t, int s) { return kbase_off + 4 * DH * t + 32 * (s ^ (kx >> 2)); };
+  // V^T chunk 4 u + g of row l16: sub-tile 1 flips bit 2 of the slot, i.e.
+  // element offset bit 5 (the rest of the offset has that bit clear)
+  const int voff0 = l16 * BN + 8 * vslot(l16, g);
+  auto voff = [&](int u) { return voff0 ^ (32 * u); };
 
   // ---- logits of one 32-key sub-tile u of a stage buffer ----
   // S[mb][t][r] holds key 32 u + 8 g + 4 t + r of row block mb.
@@ -337,8 +336,8 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     }
   };
   auto pv_accum = [&](int buf, int u, const bf16x8 (&P)[C::MB], const bf16x8 &PS) {
-    const bf16 *vt = sVT(buf) + voff[u];
-    const bf16 *vdt = sVdT(buf) + voff[u];
+    const bf16 *vt = sVT(buf) + voff(u);
+    const bf16 *vdt = sVdT(buf) + voff(u);
     if constexpr (C::MFMA_SUMS)
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) Lacc[mb] = mfma16(ones, P[mb], Lacc[mb]);
