@@ -123,6 +123,27 @@ struct TrReader {
   __device__ int off(int u, int et) const { return base[u] + 16 * et * BT; }
 };
 
+// Eight consecutive floats from each of two LDS rows (16-byte aligned).  The
+// reads are plain ds_read_b128 written out, with their wait in the same
+// block: left to the compiler, a read of LDS that buffer-to-LDS loads also
+// write gets an s_waitcnt vmcnt(0) in front, which would make every sub-tile
+// wait for the next stage's prefetch (these rows were published by the
+// stage's barrier; the loads in flight target the other stage buffer).
+__device__ __forceinline__ void read_stage_stats(const float *a, const float *b, float4 &a0, float4 &a1,
+                                                 float4 &b0, float4 &b1) {
+  typedef __attribute__((address_space(3))) const float lds_float;
+  const uint32_t pa = (uint32_t)(uintptr_t)(lds_float *)a, pb = (uint32_t)(uintptr_t)(lds_float *)b;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:16\n\t"
+      "ds_read_b128 %2, %5\n\t"
+      "ds_read_b128 %3, %5 offset:16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+      : "v"(pa), "v"(pb)
+      : "memory");
+}
+
 __device__ __forceinline__ void xcd_tile(int w, int per_xcd, int total, int &L) {
   L = (w & 7) * per_xcd + (w >> 3);
   if (L >= total) L = -1;
@@ -411,10 +432,8 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
         }
       }
       // this lane's queries: 32 u + 8 g + m of the stage, m = 4 t + r
-      const float4 l0 = *reinterpret_cast<const float4 *>(sL(cur) + 32 * u + 8 * g);
-      const float4 l1 = *reinterpret_cast<const float4 *>(sL(cur) + 32 * u + 8 * g + 4);
-      const float4 d0 = *reinterpret_cast<const float4 *>(sD(cur) + 32 * u + 8 * g);
-      const float4 d1 = *reinterpret_cast<const float4 *>(sD(cur) + 32 * u + 8 * g + 4);
+      float4 l0, l1, d0, d1;
+      read_stage_stats(sL(cur) + 32 * u + 8 * g, sD(cur) + 32 * u + 8 * g, l0, l1, d0, d1);
       const float lq[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
       const float dq[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
       // queries past Nq (last stage only) and keys past nk get zero weight
