@@ -335,21 +335,36 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       if constexpr (TAN) mu_part += musum;
     }
   };
+  // The forward kernel reads the V^T fragments of d-tile e+1 before the MFMAs
+  // of d-tile e, held in that order by scheduling barriers (left alone, the
+  // scheduler sinks each read next to its first use); 3 % faster.  The JVP
+  // kernel has no registers to spare for it (the same change spills in its
+  // loop) and keeps the compiler's order.
   auto pv_accum = [&](int buf, int u, const bf16x8 (&P)[C::MB], const bf16x8 &PS) {
     const bf16 *vt = sVT(buf) + voff(u);
     const bf16 *vdt = sVdT(buf) + voff(u);
     if constexpr (C::MFMA_SUMS)
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) Lacc[mb] = mfma16(ones, P[mb], Lacc[mb]);
+    if constexpr (TAN) {
 #pragma unroll
-    for (int e = 0; e < C::DT; ++e) {
-      const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vt + 16 * e * BN);
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) O[mb][e] = mfma16(va, P[mb], O[mb][e]);
-      if constexpr (TAN) {
+      for (int e = 0; e < C::DT; ++e) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vt + 16 * e * BN);
+        O[0][e] = mfma16(va, P[0], O[0][e]);
         const bf16x8 vda = *reinterpret_cast<const bf16x8 *>(vdt + 16 * e * BN);
         Od[e] = mfma16(va, PS, Od[e]);
         Od[e] = mfma16(vda, P[0], Od[e]);
+      }
+    } else {
+      bf16x8 va[2];
+      va[0] = *reinterpret_cast<const bf16x8 *>(vt);
+#pragma unroll
+      for (int e = 0; e < C::DT; ++e) {
+        if (e + 1 < C::DT) va[(e + 1) & 1] = *reinterpret_cast<const bf16x8 *>(vt + 16 * (e + 1) * BN);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) O[mb][e] = mfma16(va[e & 1], P[mb], O[mb][e]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
