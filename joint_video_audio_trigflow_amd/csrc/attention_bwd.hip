@@ -276,11 +276,16 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kerne
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][t][r], c_log2, -lse2[mb]));
           dS[mb][m] = (bf16)(pv * (dP[mb][t][r] - Dq[mb]));
         }
+      // K^T fragments of d-tile e+1 read ahead of the MFMAs of d-tile e
+      bf16x8 kta[2];
+      kta[0] = *reinterpret_cast<const bf16x8 *>(sKT(cur) + tr.off(u, 0));
 #pragma unroll
       for (int e = 0; e < C::DT; ++e) {
-        const bf16x8 kta = *reinterpret_cast<const bf16x8 *>(sKT(cur) + tr.off(u, e));
+        if (e + 1 < C::DT) kta[(e + 1) & 1] = *reinterpret_cast<const bf16x8 *>(sKT(cur) + tr.off(u, e + 1));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb][e] = mfma16(kta, dS[mb], acc[mb][e]);
+        for (int mb = 0; mb < MB; ++mb) acc[mb][e] = mfma16(kta[e & 1], dS[mb], acc[mb][e]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // this wave's loads of the next stage have landed and every wave is done
@@ -451,15 +456,26 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
           P[mb][m] = (bf16)pv;
           dS[mb][m] = (bf16)(pv * (dP[mb][t][r] - dq[m]));
         }
+      // the dO^T and Q^T fragments of d-tile e+1 are read before the MFMAs of
+      // d-tile e (held in that order by scheduling barriers; left alone, the
+      // scheduler sinks each read next to its use and every MFMA pair waits
+      // for an LDS round trip)
+      bf16x8 doa[2], qta[2];
+      doa[0] = *reinterpret_cast<const bf16x8 *>(sDOT(cur) + tr.off(u, 0));
+      qta[0] = *reinterpret_cast<const bf16x8 *>(sQT(cur) + tr.off(u, 0));
 #pragma unroll
       for (int e = 0; e < C::DT; ++e) {
-        const bf16x8 doa = *reinterpret_cast<const bf16x8 *>(sDOT(cur) + tr.off(u, e));
-        const bf16x8 qta = *reinterpret_cast<const bf16x8 *>(sQT(cur) + tr.off(u, e));
+        if (e + 1 < C::DT) {
+          doa[(e + 1) & 1] = *reinterpret_cast<const bf16x8 *>(sDOT(cur) + tr.off(u, e + 1));
+          qta[(e + 1) & 1] = *reinterpret_cast<const bf16x8 *>(sQT(cur) + tr.off(u, e + 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          dV[mb][e] = mfma16(doa, P[mb], dV[mb][e]);
-          dK[mb][e] = mfma16(qta, dS[mb], dK[mb][e]);
+          dV[mb][e] = mfma16(doa[e & 1], P[mb], dV[mb][e]);
+          dK[mb][e] = mfma16(qta[e & 1], dS[mb], dK[mb][e]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
