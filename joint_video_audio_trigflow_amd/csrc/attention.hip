@@ -147,6 +147,13 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   // loop-invariant byte offsets of this lane's 16-byte chunks (at key 0)
   const int lw = wave % kLoadWaves;
   const bool loader = wave < kLoadWaves;
+  // Per-lane byte offsets of this lane's 16-byte chunks (at key 0).  Chunk r
+  // of a loading wave lies a uniform number of rows after chunk 0
+  // (8 r K_ROWS_PER_CHUNK key rows, 64 r V^T rows) and has the same XOR key
+  // (the swizzles read only low row bits).  The JVP kernel keeps only chunk
+  // 0's offset and adds the rest as a uniform per-stage offset, two registers
+  // it needs elsewhere; the forward kernel keeps one offset per chunk (the
+  // other way round its register allocation turns out worse).
   uint32_t kvo[C::KCH], vvo[C::VCH];
 #pragma unroll
   for (int r = 0; r < C::KCH; ++r) {
@@ -161,24 +168,36 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     const int e = chunk * 8 + lane / 8;
     vvo[r] = (uint32_t)((e * p.vt_rs + 8 * vslot(e, lane % 8)) * 2);
   }
+  // offset of chunk r of stage k0: per-lane part + uniform part
+  auto k_off = [&](int r, int k0) -> uint32_t {
+    if constexpr (TAN)
+      return kvo[0] + (uint32_t)__builtin_amdgcn_readfirstlane(
+                          (int)((k0 + kLoadWaves * C::K_ROWS_PER_CHUNK * r) * p.k_rs * 2));
+    else
+      return kvo[r] + (uint32_t)(k0 * p.k_rs * 2);
+  };
+  auto v_off = [&](int r, int k0) -> uint32_t {
+    if constexpr (TAN)
+      return vvo[0] + (uint32_t)__builtin_amdgcn_readfirstlane((int)((k0 + kLoadWaves * 8 * r * p.vt_rs) * 2));
+    else
+      return vvo[r] + (uint32_t)(k0 * 2);
+  };
   auto issue_k = [&](int kb, int k0) {
     if (!loader) return;
-    const uint32_t kstep = (uint32_t)(k0 * p.k_rs * 2);
 #pragma unroll
     for (int r = 0; r < C::KCH; ++r) {
       const int chunk = lw + kLoadWaves * r;
-      load_lds16(rK, kvo[r] + kstep, sK(kb) + chunk * 512);
-      if constexpr (TAN) load_lds16(rKd, kvo[r] + kstep, sKd(kb) + chunk * 512);
+      load_lds16(rK, k_off(r, k0), sK(kb) + chunk * 512);
+      if constexpr (TAN) load_lds16(rKd, k_off(r, k0), sKd(kb) + chunk * 512);
     }
   };
   auto issue_v = [&](int vb, int k0) {
     if (!loader) return;
-    const uint32_t vstep = (uint32_t)(k0 * 2);
 #pragma unroll
     for (int r = 0; r < C::VCH; ++r) {
       const int chunk = lw + kLoadWaves * r;
-      load_lds16(rV, vvo[r] + vstep, sVT(vb) + chunk * 512);
-      if constexpr (TAN) load_lds16(rVd, vvo[r] + vstep, sVdT(vb) + chunk * 512);
+      load_lds16(rV, v_off(r, k0), sVT(vb) + chunk * 512);
+      if constexpr (TAN) load_lds16(rVd, v_off(r, k0), sVdT(vb) + chunk * 512);
     }
   };
   auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0); };
@@ -207,6 +226,25 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     const bf16 *kdt = sKd(buf) + 32 * u * DH;
     // the first k-step starts from a zero accumulator operand (no VALU clears)
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (TAN) {
+      // both key halves at each k-step: the two tangent-logit chains (and
+      // the two logit chains) interleave, so no MFMA waits on the one before
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        bf16x8 ka[2], kda[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          ka[t] = *reinterpret_cast<const bf16x8 *>(kt + koff(t, s));
+          kda[t] = *reinterpret_cast<const bf16x8 *>(kdt + koff(t, s));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) Sd[t] = mfma16(kda[t], qf[0][s], s == 0 ? zero4 : Sd[t]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) S[0][t] = mfma16(ka[t], qf[0][s], s == 0 ? zero4 : S[0][t]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) Sd[t] = mfma16(ka[t], qdf[s], Sd[t]);
+      }
+    } else {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -214,12 +252,8 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
         const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + koff(t, s));
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb) S[mb][t] = mfma16(ka, qf[mb][s], s == 0 ? zero4 : S[mb][t]);
-        if constexpr (TAN) {
-          const bf16x8 kda = *reinterpret_cast<const bf16x8 *>(kdt + koff(t, s));
-          Sd[t] = mfma16(kda, qf[0][s], s == 0 ? zero4 : Sd[t]);
-          Sd[t] = mfma16(ka, qdf[s], Sd[t]);
-        }
       }
+    }
     }
   };
   auto mask_s = [&](int kb, floatx4 (&S)[C::MB][2], floatx4 (&Sd)[2]) {
