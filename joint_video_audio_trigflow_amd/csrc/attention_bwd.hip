@@ -423,18 +423,22 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       floatx4 S[MB][2], dP[MB][2];
+      // both query halves at each k-step: four accumulation chains alternate
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        bf16x8 qa[2], da[2];
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sQ(cur) + rr.off(u, t, s));
-          const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sDO(cur) + rr.off(u, t, s));
+        for (int t = 0; t < 2; ++t) {
+          qa[t] = *reinterpret_cast<const bf16x8 *>(sQ(cur) + rr.off(u, t, s));
+          da[t] = *reinterpret_cast<const bf16x8 *>(sDO(cur) + rr.off(u, t, s));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            S[mb][t] = mfma16(qa, kf[mb][s], s == 0 ? zero4 : S[mb][t]);
-            dP[mb][t] = mfma16(da, vf[mb][s], s == 0 ? zero4 : dP[mb][t]);
+            S[mb][t] = mfma16(qa[t], kf[mb][s], s == 0 ? zero4 : S[mb][t]);
+            dP[mb][t] = mfma16(da[t], vf[mb][s], s == 0 ? zero4 : dP[mb][t]);
           }
-        }
       }
       // this lane's queries: 32 u + 8 g + m of the stage, m = 4 t + r
       float4 l0, l1, d0, d1;
