@@ -15,9 +15,9 @@
 //
 // Work decomposition: a workgroup of 12 waves (three per SIMD) owns the query
 // rows of one (sample, head); a JVP wave owns 16 rows, a forward-only wave two
-// blocks of 16 that share every K and V^T fragment it reads from LDS (one
-// 1 KB fragment per MFMA would make LDS bandwidth, not the matrix cores, the
-// bound of the forward kernel).  Products are computed
+// blocks of 16 that share every K and V^T fragment it reads from LDS (so each
+// 1 KB fragment feeds two MFMAs; with one block per wave the forward kernel
+// measured 36 % of the bf16 peak instead of 41 %).  Products are computed
 // transposed so that one lane column owns one query row throughout, using
 // v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8(l/16)..+7;
 // B: k = 8(l/16)..+7, column l%16; C: column l%16, rows 4(l/16)+r):
@@ -58,8 +58,9 @@ constexpr int BN = 64;                // keys per LDS stage
 template <int DH, bool TAN>
 struct AttnCfg {
   // waves per workgroup: 12 (three per SIMD) by default; MB blocks of 16
-  // query rows per wave.  Every K / V^T fragment a wave reads from LDS feeds
-  // MB (forward) or three (JVP: K for S and dS, V for O and dO) MFMAs.
+  // query rows per wave.  In the forward kernel every K / V^T fragment a wave
+  // reads from LDS feeds MB MFMAs; in the JVP kernel each pair of fragments
+  // (K and dK, or V^T and dV^T) feeds three (S, dS twice; O, dO twice).
   static constexpr int NW = TAN ? T2VA_ATTN_WAVES_JVP : T2VA_ATTN_WAVES_FWD;
   static constexpr int MB = TAN ? 1 : T2VA_ATTN_MB_FWD;
   // row sums on the matrix cores (forward); the JVP kernel keeps them on the
@@ -144,7 +145,6 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     rKd = make_rsrc(p.kd + (int64_t)b * p.k_bs + h * DH, k_bytes);
     rVd = make_rsrc(p.vdt + (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs, v_bytes);
   }
-  // loop-invariant byte offsets of this lane's 16-byte chunks (at key 0)
   const int lw = wave % kLoadWaves;
   const bool loader = wave < kLoadWaves;
   // Per-lane byte offsets of this lane's 16-byte chunks (at key 0).  Chunk r
@@ -246,14 +246,14 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       }
     } else {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + koff(t, s));
+        for (int s = 0; s < C::KSTEPS; ++s) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + koff(t, s));
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) S[mb][t] = mfma16(ka, qf[mb][s], s == 0 ? zero4 : S[mb][t]);
+          for (int mb = 0; mb < C::MB; ++mb) S[mb][t] = mfma16(ka, qf[mb][s], s == 0 ? zero4 : S[mb][t]);
+        }
       }
-    }
     }
   };
   auto mask_s = [&](int kb, floatx4 (&S)[C::MB][2], floatx4 (&Sd)[2]) {
@@ -321,9 +321,6 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   // re-centres) once a row's max grows by more than 4 (a factor of 16).
 #ifndef T2VA_ATTN_LAZY_JVP
 #define T2VA_ATTN_LAZY_JVP 4.f
-#endif
-#ifndef T2VA_ATTN_CENTRE
-#define T2VA_ATTN_CENTRE 1
 #endif
   constexpr float kLazy = TAN ? T2VA_ATTN_LAZY_JVP : 16.f;
   // Forward: the row sums l = sum p run on the matrix cores: an all-ones A
@@ -402,9 +399,8 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       }
     }
   };
-  // any lane's own logits past its row's threshold (no lane exchange)
-  // (plain compares: a max tree over MFMA results would first quieten each
-  // input, one extra VALU op per logit)
+  // any lane's own logits past its row's threshold (no lane exchange); plain
+  // compares, which compile to fewer operations than fmaxf's NaN rules allow
   auto outgrown = [&](const floatx4 (&S)[C::MB][2]) {
     bool any = false;
 #pragma unroll
@@ -462,7 +458,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   compute_s(0, 0, S, Sd);
   if (nst == 1) mask_s(0, S, Sd);
   // key 0 is always valid, so this is finite
-  if constexpr (TAN) { m_run[0] = row_max_arg(S[0], Sd, c_ref); if (!T2VA_ATTN_CENTRE) c_ref = 0.f; }
+  if constexpr (TAN) m_run[0] = row_max_arg(S[0], Sd, c_ref);
   else {
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) m_run[mb] = row_max(S[mb]);
@@ -508,7 +504,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       const float mx = TAN ? row_max_arg(S[mb], Sd, sd_max) : row_max(S[mb]);
       const float m_new = fmaxf(m_run[mb], mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run[mb] - m_new);
-      const float c_new = (TAN && T2VA_ATTN_CENTRE && mx > m_run[mb]) ? sd_max : c_ref;
+      const float c_new = (TAN && mx > m_run[mb]) ? sd_max : c_ref;
       const float delta = c_ref - c_new;   // dA += delta A, mu~ += delta l
       m_run[mb] = m_new;
       set_thr(mb);
