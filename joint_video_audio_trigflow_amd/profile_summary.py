@@ -4,7 +4,8 @@ Reads a --kernel-trace --stats directory and two --pmc runs (FETCH_SIZE,
 WRITE_SIZE) of bench.py, plus the same counters for bench.py
 --copy-calibration (a plain device-to-device copy of known size), and prints
 a markdown summary with per-kernel average durations, counter values per
-dispatch, the calibration factors and the resulting HBM traffic per launch.
+dispatch, the calibration factors, the resulting HBM traffic per launch and
+the achieved HBM bandwidth (traffic over the traced average duration).
 Usage: python -m joint_video_audio_trigflow_amd.profile_summary <rocprof output dir>
 
 With --clock <dir>, it reads one --pmc --kernel-trace run per subdirectory of
@@ -73,7 +74,19 @@ def main(d):
             b = (fetch[k] * f_fac + write[k] * w_fac) * 1024
             out[k] = b
             print(f"| {k} | {fetch[k]:.0f} | {write[k]:.0f} | {b / 1e9:.3f} GB |")
-    return dict(fetch_factor=f_fac, write_factor=w_fac, bytes=out, fetch=fetch, write=write)
+    # achieved HBM bandwidth: counted bytes per dispatch over the traced
+    # average duration (same kernel names; the two runs share the workload)
+    avg_ms = {short(r["Name"]): float(r["AverageNs"]) / 1e6 for r in stats}
+    print("\nAchieved HBM bandwidth (counted bytes per dispatch / traced average duration; "
+          "MI355X HBM3E peak 8 TB/s):\n")
+    print("| kernel | avg ms | HBM bytes/dispatch | TB/s | % of 8 TB/s |\n|---|---|---|---|---|")
+    bw = {}
+    for k, b in sorted(out.items(), key=lambda kv: -kv[1]):
+        if k in avg_ms and avg_ms[k] > 0 and k != "copyBuffer":
+            tbs = b / (avg_ms[k] * 1e-3) / 1e12
+            bw[k] = tbs
+            print(f"| {k} | {avg_ms[k]:.4f} | {b / 1e9:.3f} GB | {tbs:.2f} | {100 * tbs / 8:.0f} % |")
+    return dict(fetch_factor=f_fac, write_factor=w_fac, bytes=out, fetch=fetch, write=write, tb_per_s=bw)
 
 
 def clock_table(d):
