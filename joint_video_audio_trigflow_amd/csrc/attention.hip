@@ -226,9 +226,10 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     const bf16 *kdt = sKd(buf) + 32 * u * DH;
     // the first k-step starts from a zero accumulator operand (no VALU clears)
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // Both key halves at each k-step: the accumulation chains of the two
+    // halves (logits, and tangent logits in the JVP kernel) interleave, so no
+    // MFMA waits on the one just before it.
     if constexpr (TAN) {
-      // both key halves at each k-step: the two tangent-logit chains (and
-      // the two logit chains) interleave, so no MFMA waits on the one before
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s) {
         bf16x8 ka[2], kda[2];
@@ -246,13 +247,14 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        bf16x8 ka[2];
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kt + koff(t, s));
+        for (int t = 0; t < 2; ++t) ka[t] = *reinterpret_cast<const bf16x8 *>(kt + koff(t, s));
 #pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb) S[mb][t] = mfma16(ka, qf[mb][s], s == 0 ? zero4 : S[mb][t]);
-        }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) S[mb][t] = mfma16(ka[t], qf[mb][s], s == 0 ? zero4 : S[mb][t]);
       }
     }
   };
