@@ -245,18 +245,22 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kerne
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       floatx4 S[MB][2], dP[MB][2];
+      // both key halves at each k-step: the accumulation chains alternate
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        bf16x8 ka[2], va[2];
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sK(cur) + rr.off(u, t, s));
-          const bf16x8 va = *reinterpret_cast<const bf16x8 *>(sV(cur) + rr.off(u, t, s));
+        for (int t = 0; t < 2; ++t) {
+          ka[t] = *reinterpret_cast<const bf16x8 *>(sK(cur) + rr.off(u, t, s));
+          va[t] = *reinterpret_cast<const bf16x8 *>(sV(cur) + rr.off(u, t, s));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            S[mb][t] = mfma16(ka, qf[mb][s], s == 0 ? zero4 : S[mb][t]);
-            dP[mb][t] = mfma16(va, dof[mb][s], s == 0 ? zero4 : dP[mb][t]);
+            S[mb][t] = mfma16(ka[t], qf[mb][s], s == 0 ? zero4 : S[mb][t]);
+            dP[mb][t] = mfma16(va[t], dof[mb][s], s == 0 ? zero4 : dP[mb][t]);
           }
-        }
       }
       // keys past nk (last stage only) get zero weight
       if (st == nst - 1) {
