@@ -39,6 +39,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace t2va {
 
 namespace {
@@ -82,11 +84,56 @@ struct AttnCfg {
   static constexpr int KCH = K_ELEMS / 512 / kLoadWaves;   // per loading wave, per operand tile
   static constexpr int VCH = V_ELEMS / 512 / kLoadWaves;
   static constexpr int K_ROWS_PER_CHUNK = 512 / DH;
+  // partial result of one piece of a split tile (floats): for each of the
+  // BM rows and its four lanes g (index 4 row + g, row within the tile),
+  // (lse, mu) and the normalised o (and do) of the lane's four columns of each
+  // d-tile
+  static constexpr int PIECE_STATS = 2 * MB * THREADS;
+  static constexpr int PIECE_O = 4 * MB * DT * THREADS;
+  static constexpr int PIECE_FLOATS = PIECE_STATS + PIECE_O + (TAN ? 4 * DT * THREADS : 0);
 };
+
+// Tail split.  A launch has one workgroup per compute unit at a time, so the
+// tiles of an XCD run in rounds, and a last round with few tiles leaves most of
+// the XCD idle.  Each XCD therefore runs its first n_full tiles whole and cuts
+// its last `rem` tiles into k pieces over consecutive ranges of 64-key stages,
+// dispatched after every whole tile.  A piece stores its own normalised result
+// o_i, do_i, log-sum-exp and mean tangent logit mu_i; with w_i the softmax of
+// the log-sum-exps over the pieces, o = sum w_i o_i, mu = sum w_i mu_i and
+// do = sum w_i (do_i + (mu_i - mu) o_i) (each piece's do_i is centred on its
+// own mu_i), which the combine kernel forms in piece order.
+constexpr int kMaxPieces = 4;
+constexpr int kMinPieceStages = 8;   // no piece shorter than 512 keys (at the longest sample)
+struct SplitArgs {
+  int n_full, rem, k;
+};
+
+// Four consecutive output columns of one row (and of its tangent): bf16 or
+// fp32 as p.out_dt says, at element offset `at` of o (od).
+template <bool TAN>
+__device__ __forceinline__ void store_out4(const AttnParams &p, int64_t at, const float (&o4)[4],
+                                           const float (&od4)[4]) {
+  if (p.out_dt == 0) {
+    bf16x4 a;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = (bf16)o4[r];
+    *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(p.o) + at) = a;
+    if constexpr (TAN) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = (bf16)od4[r];
+      *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(p.od) + at) = a;
+    }
+  } else {
+    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.o) + at) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    if constexpr (TAN)
+      *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.od) + at) =
+          make_float4(od4[0], od4[1], od4[2], od4[3]);
+  }
+}
 
 template <int DH, bool TAN>
 __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_kernel(AttnParams p, int nqb,
-                                                                   int per_xcd, int total) {
+                                                                   int per_xcd, int total, SplitArgs sp) {
   using C = AttnCfg<DH, TAN>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16 *const lds = reinterpret_cast<bf16 *>(smem_raw);
@@ -98,8 +145,19 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
 
   // XCD-aware order: hardware places workgroup w on XCD w % 8; give each XCD a
   // contiguous range of logical tiles so one head's K/V stay in that XCD's L2.
+  // The last `rem` tiles of the range run as sp.k pieces each (slot: the split
+  // tile's index among all split tiles).
   const int w = blockIdx.x;
-  const int L = (w & 7) * per_xcd + (w >> 3);
+  const int xcd = w & 7, wi = w >> 3;
+  int L, piece = 0, slot = -1;
+  if (wi < sp.n_full) {
+    L = xcd * per_xcd + wi;
+  } else {
+    const int tt = (wi - sp.n_full) / sp.k;
+    piece = wi - sp.n_full - tt * sp.k;
+    L = xcd * per_xcd + sp.n_full + tt;
+    slot = xcd * sp.rem + tt;
+  }
   if (L >= total) return;
   const int qb = L % nqb;
   const int bh = L / nqb;
@@ -109,10 +167,38 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int q_row0 = qb * C::BM + wave * 16 * C::MB + l16;   // + 16 mb for row block mb
-  const int nk = min(max(p.nk[b], 1), p.Nk);
+  const int nk_b = min(max(p.nk[b], 1), p.Nk);
+  // this workgroup's keys [key0, key0 + nk): all of them, or piece `piece` of
+  // sp.k over whole 64-key stages (empty when the sample has fewer stages)
+  int key0 = 0, nk = nk_b;
+  float *part = nullptr;
+  if (slot >= 0) {
+    const int nst_b = (nk_b + BN - 1) / BN;
+    const int s0 = piece * nst_b / sp.k, s1 = (piece + 1) * nst_b / sp.k;
+    key0 = s0 * BN;
+    nk = min(nk_b, s1 * BN) - key0;
+    part = p.part + (size_t)(slot * sp.k + piece) * C::PIECE_FLOATS;
+  }
   // forward only: also store the output over the first nk_split keys (a
-  // multiple of 32, at most nk) into o2
-  const int nk_split = (!TAN && p.o2) ? p.nk_split : -1;
+  // multiple of 32, at most nk) into o2 (never in a split tile)
+  const int nk_split = (!TAN && p.o2 && slot < 0) ? p.nk_split : -1;
+  if (nk <= 0) {
+    // an empty piece: weight zero in the combination
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const int pi = 4 * (q_row0 + 16 * mb - qb * C::BM) + g;
+      *reinterpret_cast<float2 *>(part + 2 * pi) = make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int e = 0; e < C::DT; ++e) {
+        *reinterpret_cast<float4 *>(part + C::PIECE_STATS + 4 * (e * C::MB * C::THREADS + pi)) =
+            make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (TAN)
+          *reinterpret_cast<float4 *>(part + C::PIECE_STATS + C::PIECE_O + 4 * (e * C::THREADS + pi)) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    return;
+  }
 
   const float scale = p.scale;
   const float c_log2 = scale * 1.4426950408889634f;
@@ -136,14 +222,17 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   // The K descriptors end after key row nk-1, so rows >= nk load as zeros
   // (their logits are masked).  V^T columns in [nk, round_up(nk, 64)) are read
   // as stored; the caller keeps them finite, and their weights are zero.
+  // Descriptors start at key key0 (so stage offsets below are relative to it).
   const uint32_t k_bytes = (uint32_t)(((int64_t)(nk - 1) * p.k_rs + DH) * 2);
-  const uint32_t v_bytes = (uint32_t)((int64_t)DH * p.vt_rs * 2);
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.k + (int64_t)b * p.k_bs + h * DH, k_bytes);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.vt + (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs, v_bytes);
+  const uint32_t v_bytes = (uint32_t)(((int64_t)DH * p.vt_rs - key0) * 2);
+  const int64_t k_at = (int64_t)b * p.k_bs + (int64_t)key0 * p.k_rs + h * DH;
+  const int64_t v_at = (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs + key0;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.k + k_at, k_bytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.vt + v_at, v_bytes);
   __amdgpu_buffer_rsrc_t rKd = rK, rVd = rV;
   if constexpr (TAN) {
-    rKd = make_rsrc(p.kd + (int64_t)b * p.k_bs + h * DH, k_bytes);
-    rVd = make_rsrc(p.vdt + (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs, v_bytes);
+    rKd = make_rsrc(p.kd + k_at, k_bytes);
+    rVd = make_rsrc(p.vdt + v_at, v_bytes);
   }
   const int lw = wave % kLoadWaves;
   const bool loader = wave < kLoadWaves;
@@ -545,9 +634,30 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     mu = mu_part + __shfl_xor(mu_part, 16);
     mu = (mu + __shfl_xor(mu, 32)) * inv_l;
   }
+  const float lse = m_run[mb] * 0.6931471805599453f + logf(l_tot);
+  if (part) {
+    // a piece of a split tile: its own normalised result, for every row; the
+    // mean tangent logit is mu (centred on c_ref) plus c_ref
+    const int pi = 4 * (q_row - qb * C::BM) + g;
+    *reinterpret_cast<float2 *>(part + 2 * pi) = make_float2(lse, TAN ? mu + c_ref : 0.f);
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) {
+      float o4[4], od4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        o4[r] = O[mb][e][r] * inv_l;
+        if constexpr (TAN) od4[r] = Od[e][r] * inv_l - mu * o4[r];
+      }
+      *reinterpret_cast<float4 *>(part + C::PIECE_STATS + 4 * (e * C::MB * C::THREADS + pi)) =
+          make_float4(o4[0], o4[1], o4[2], o4[3]);
+      if constexpr (TAN)
+        *reinterpret_cast<float4 *>(part + C::PIECE_STATS + C::PIECE_O + 4 * (e * C::THREADS + pi)) =
+            make_float4(od4[0], od4[1], od4[2], od4[3]);
+    }
+    continue;
+  }
   if (q_row < p.Nq) {
-    if (p.lse && g == 0)
-      p.lse[((int64_t)b * p.H + h) * p.Nq + q_row] = m_run[mb] * 0.6931471805599453f + logf(l_tot);
+    if (p.lse && g == 0) p.lse[((int64_t)b * p.H + h) * p.Nq + q_row] = lse;
     const int64_t obase = (int64_t)b * p.o_bs + (int64_t)q_row * p.o_rs + h * DH + 4 * g;
 #pragma unroll
     for (int e = 0; e < C::DT; ++e) {
@@ -557,26 +667,148 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
         o4[r] = O[mb][e][r] * inv_l;
         if constexpr (TAN) od4[r] = Od[e][r] * inv_l - mu * o4[r];
       }
-      if (p.out_dt == 0) {
-        bf16x4 a;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = (bf16)o4[r];
-        *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(p.o) + obase + 16 * e) = a;
-        if constexpr (TAN) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) a[r] = (bf16)od4[r];
-          *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(p.od) + obase + 16 * e) = a;
-        }
-      } else {
-        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.o) + obase + 16 * e) =
-            make_float4(o4[0], o4[1], o4[2], o4[3]);
-        if constexpr (TAN)
-          *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.od) + obase + 16 * e) =
-              make_float4(od4[0], od4[1], od4[2], od4[3]);
-      }
+      store_out4<TAN>(p, obase + 16 * e, o4, od4);
     }
   }
   }
+}
+
+// Merges the pieces of the split tiles (one workgroup per split tile, each
+// thread the rows and columns it held in the attention kernel); pieces are
+// taken in key order, so the result does not depend on which finished first.
+template <int DH, bool TAN>
+__global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_combine_kernel(AttnParams p, int nqb,
+                                                                   int per_xcd, int total, SplitArgs sp) {
+  using C = AttnCfg<DH, TAN>;
+  const int slot = blockIdx.x;
+  const int xcd = slot / sp.rem, tt = slot - xcd * sp.rem;
+  const int L = xcd * per_xcd + sp.n_full + tt;
+  if (L >= total) return;
+  const int qb = L % nqb, bh = L / nqb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const float *part = p.part + (size_t)slot * sp.k * C::PIECE_FLOATS;
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int row = wave * 16 * C::MB + 16 * mb + l16;   // within the tile
+    const int q_row = qb * C::BM + row;
+    if (q_row >= p.Nq) continue;
+    const int pi = 4 * row + g;
+    float lse[kMaxPieces], mu[kMaxPieces], wgt[kMaxPieces];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxPieces; ++i) {
+      lse[i] = -INFINITY;
+      mu[i] = 0.f;
+      if (i < sp.k) {
+        const float2 v = *reinterpret_cast<const float2 *>(part + (size_t)i * C::PIECE_FLOATS + 2 * pi);
+        lse[i] = v.x;
+        mu[i] = v.y;
+      }
+      mx = fmaxf(mx, lse[i]);
+    }
+    float wsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxPieces; ++i) {
+      wgt[i] = expf(lse[i] - mx);   // 0 for an empty piece (and pieces past k)
+      wsum += wgt[i];
+    }
+    const float inv = 1.f / wsum;
+    float mu_all = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxPieces; ++i) {
+      wgt[i] *= inv;
+      mu_all += wgt[i] * mu[i];
+    }
+    if (p.lse && g == 0) p.lse[((int64_t)b * p.H + h) * p.Nq + q_row] = mx + logf(wsum);
+    const int64_t obase = (int64_t)b * p.o_bs + (int64_t)q_row * p.o_rs + h * DH + 4 * g;
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) {
+      float o4[4] = {0.f, 0.f, 0.f, 0.f}, od4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kMaxPieces; ++i) {
+        if (i >= sp.k) break;
+        const float *pp = part + (size_t)i * C::PIECE_FLOATS + C::PIECE_STATS;
+        const float4 a = *reinterpret_cast<const float4 *>(pp + 4 * (e * C::MB * C::THREADS + pi));
+        const float av[4] = {a.x, a.y, a.z, a.w};
+        float dv[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (TAN) {
+          const float4 d = *reinterpret_cast<const float4 *>(pp + C::PIECE_O + 4 * (e * C::THREADS + pi));
+          dv[0] = d.x; dv[1] = d.y; dv[2] = d.z; dv[3] = d.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          o4[r] += wgt[i] * av[r];
+          if constexpr (TAN) od4[r] += wgt[i] * (dv[r] + (mu[i] - mu_all) * av[r]);
+        }
+      }
+      store_out4<TAN>(p, obase + 16 * e, o4, od4);
+    }
+  }
+}
+
+// Workgroups of the attention kernel that one XCD holds at once (0: unknown),
+// queried once per device.
+template <int DH, bool TAN>
+int xcd_slots() {
+  using C = AttnCfg<DH, TAN>;
+  static int cache[64];   // 0: not queried yet, -1: unknown
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (cache[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    const bool ok =
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_jvp_kernel<DH, TAN>, C::THREADS,
+                                                     C::LDS_BYTES) == hipSuccess;
+    if (!ok) (void)hipGetLastError();
+    cache[dev] = (ok && cus >= 8 && per_cu >= 1) ? per_cu * (cus / 8) : -1;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
+}
+
+// The tail split of an XCD's per_xcd tiles when it holds `slots` at once: the
+// k <= kMaxPieces that minimises the time of the last round(s),
+// ceil(rem k / slots) / k whole-tile times, ties to the smaller k; k = 1 (no
+// split) when nothing is gained, a piece would span fewer than
+// kMinPieceStages stages of the longest sample, or the scratch holds fewer
+// than 8 rem k pieces.
+SplitArgs plan_split(int per_xcd, int slots, int nst_max, size_t cap_pieces) {
+  SplitArgs sp{per_xcd, 0, 1};
+  if (slots <= 0) return sp;
+  const int rem = per_xcd % slots;
+  if (rem == 0) return sp;
+  int best_k = 1;
+  int64_t best_num = 1, best_den = 1;   // cost as a fraction ceil(rem k / slots) / k
+  for (int k = 2; k <= kMaxPieces; ++k) {
+    if (nst_max / k < kMinPieceStages || (size_t)8 * rem * k > cap_pieces) break;
+    const int64_t num = (rem * k + slots - 1) / slots;
+    if (num * best_den < best_num * k) {
+      best_k = k;
+      best_num = num;
+      best_den = k;
+    }
+  }
+  if (best_k == 1) return sp;
+  sp.n_full = per_xcd - rem;
+  sp.rem = rem;
+  sp.k = best_k;
+  return sp;
+}
+
+constexpr size_t kCapPieces = 768;   // scratch for at most this many pieces
+
+template <int DH, bool TAN>
+size_t split_bytes(int B, int H, int Nq) {
+  using C = AttnCfg<DH, TAN>;
+  const int64_t total = (int64_t)B * H * ((Nq + C::BM - 1) / C::BM);
+  const size_t pieces = std::min<size_t>(kCapPieces, (size_t)kMaxPieces * 8 * ((total + 7) / 8));
+  return pieces * C::PIECE_FLOATS * sizeof(float);
 }
 
 template <int DH, bool TAN>
@@ -593,8 +825,17 @@ hipError_t launch_impl(const AttnParams &p, hipStream_t s) {
   const int nqb = (p.Nq + C::BM - 1) / C::BM;
   const int total = nqb * p.H * p.B;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((attn_fwd_jvp_kernel<DH, TAN>), dim3(per_xcd * 8), dim3(C::THREADS),
-                     C::LDS_BYTES, s, p, nqb, per_xcd, total);
+  // split the tail only with scratch, and never with the prefix output
+  const size_t cap = (p.part && !p.o2) ? p.part_bytes / (sizeof(float) * C::PIECE_FLOATS) : 0;
+  const SplitArgs sp = cap ? plan_split(per_xcd, xcd_slots<DH, TAN>(), (p.Nk + BN - 1) / BN, cap)
+                           : SplitArgs{per_xcd, 0, 1};
+  hipLaunchKernelGGL((attn_fwd_jvp_kernel<DH, TAN>), dim3(8 * (sp.n_full + sp.rem * sp.k)),
+                     dim3(C::THREADS), C::LDS_BYTES, s, p, nqb, per_xcd, total, sp);
+  if (sp.rem > 0) {
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL((attn_combine_kernel<DH, TAN>), dim3(8 * sp.rem), dim3(C::THREADS), 0, s, p, nqb,
+                       per_xcd, total, sp);
+  }
   return hipGetLastError();
 }
 
@@ -604,6 +845,12 @@ hipError_t launch_attention(int dh, bool tangent, const AttnParams &p, hipStream
   if (dh == 128) return tangent ? launch_impl<128, true>(p, s) : launch_impl<128, false>(p, s);
   if (dh == 64) return tangent ? launch_impl<64, true>(p, s) : launch_impl<64, false>(p, s);
   return hipErrorInvalidValue;
+}
+
+size_t attention_split_bytes(int dh, int B, int H, int Nq) {
+  if (dh == 128) return std::max(split_bytes<128, true>(B, H, Nq), split_bytes<128, false>(B, H, Nq));
+  if (dh == 64) return std::max(split_bytes<64, true>(B, H, Nq), split_bytes<64, false>(B, H, Nq));
+  return 0;
 }
 
 }  // namespace t2va

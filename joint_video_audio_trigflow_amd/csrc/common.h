@@ -193,8 +193,16 @@ struct AttnParams {
   int B, H, Nq, Nk;
   int out_dt;
   float scale;
+  // nullable scratch of part_bytes bytes: with it, the last tiles of each
+  // XCD's range may run split over key ranges and be merged by a second kernel
+  // (not with o2)
+  float *part = nullptr;
+  size_t part_bytes = 0;
 };
 hipError_t launch_attention(int dh, bool tangent, const AttnParams &p, hipStream_t s);
+// Scratch bytes that let launch_attention split the tail of a B x H x Nq launch
+// (forward or JVP) as far as it would.
+size_t attention_split_bytes(int dh, int B, int H, int Nq);
 
 // Attention backward for one (sample, head) grid: dQ, dK, dV from Q, K, V, dO,
 // the forward's log2-unit log-sum-exp and D = rowsum(dO * O).  Row-major

@@ -151,8 +151,8 @@ hipError_t prepare_weights(const t2va_block_weights *const *wb, int count, int w
 // ---------------------------------------------------------------------------
 struct Layout {
   int Nq, N_all, dh, ldv, nblk_v, nblk_a;
-  size_t wts, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v, x0S_a, part_v, part_a;
-  size_t total;
+  size_t wts, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v, x0S_a, part_v, part_a, apart;
+  size_t total, apart_bytes;
   size_t w_elems[6];  // per-block weight element counts
 };
 
@@ -190,6 +190,8 @@ Layout make_layout(const t2va_scm_desc &d) {
   L.x0S_a = take(2 * B * d.Na * d.Ca * sizeof(float));
   L.part_v = take(B * L.nblk_v * sizeof(float));
   L.part_a = take(B * L.nblk_a * sizeof(float));
+  L.apart_bytes = attention_split_bytes(L.dh, d.B, d.H, L.Nq);
+  L.apart = take(L.apart_bytes);
   L.total = off;
   return L;
 }
@@ -304,8 +306,8 @@ t2va_status check_weights(const t2va_block_weights *const *wb, int n, const char
 // Workspace layout of t2va_dmd_target.
 struct DmdLayout {
   int ldv, nblk_v, nblk_a;
-  size_t wts, zv, za, E, tau, X, QK, VT, nk, nk_null, O, xT_v, xT_a, xF_v, xF_a, pa_v, pa_a, ps_v, ps_a;
-  size_t total;
+  size_t wts, zv, za, E, tau, X, QK, VT, nk, nk_null, O, xT_v, xT_a, xF_v, xF_a, pa_v, pa_a, ps_v, ps_a, apart;
+  size_t total, apart_bytes;
   size_t w_elems[6];
 };
 
@@ -345,6 +347,8 @@ DmdLayout make_dmd_layout(const t2va_dmd_desc &d) {
   L.pa_a = take(B * L.nblk_a * sizeof(float));
   L.ps_v = take(B * L.nblk_v * sizeof(float));
   L.ps_a = take(B * L.nblk_a * sizeof(float));
+  L.apart_bytes = attention_split_bytes(d.d / d.H, d.B, d.H, Nq);
+  L.apart = take(L.apart_bytes);
   L.total = off;
   return L;
 }
@@ -408,6 +412,8 @@ struct Block {
   int64_t nv, na, x_bs, qk_bs, vt_hs, vt_bs, o_bs;
   hipStream_t s;
   bool prof;
+  float *apart = nullptr;   // attention scratch for split tails (nullable)
+  size_t apart_bytes = 0;
 
   Block(int B_, int Nv_, int Na_, int Nt, int Cv_, int Ca_, int d, int H_, int ldv_, hipStream_t s_,
         bool prof_)
@@ -476,6 +482,8 @@ struct Block {
     p.B = B; p.H = H; p.Nq = Nq; p.Nk = NA;
     p.out_dt = T2VA_DTYPE_BF16;
     p.scale = (float)(1.0 / sqrt((double)dh));
+    p.part = apart;
+    p.part_bytes = apart_bytes;
     PhaseScope ps(s, phase, prof);
     HIP_TRY(launch_attention(dh, tan, p, s), "attention");
     return T2VA_OK;
@@ -518,7 +526,9 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
                     float *loss, void *workspace, float *lse_student, const bf16 *(&W)[2][6],
                     hipStream_t s, bool prof) {
   char *ws = (char *)workspace;
-  const Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
+  Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
+  blk.apart = (float *)(ws + L.apart);
+  blk.apart_bytes = L.apart_bytes;
   const int B = d.B, D = d.d, Nq = L.Nq;
   const int64_t nv = blk.nv, na = blk.na;
   const CoefTable coef = make_coef(B, t_host, d.beta, d.gamma, d.param);
@@ -949,7 +959,9 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   PhaseScope total(s, T2VA_PHASE_TOTAL, prof);
 
   char *ws = (char *)workspace;
-  const Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
+  Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
+  blk.apart = (float *)(ws + L.apart);
+  blk.apart_bytes = L.apart_bytes;
   const int B = d.B, D = d.d, Nq = d.Nv + d.Na;
   const int64_t nv = blk.nv, na = blk.na;
   const CoefTable coef = make_coef(B, t_host, 0.0, 0.0, d.param);
