@@ -10,7 +10,10 @@ high-resolution shape (B=1, 28,672 video + 256 audio + 256 text tokens with
 
 Prints one JSON line.  The roofline object covers the dominant kernel, the
 student attention forward+JVP, timed with HIP events recorded by the library
-around each of its launches on the launch stream during the timed steps.
+around each of its launches on the launch stream during the timed steps.  One
+launch is two dispatches at this shape: the attention kernel and the small
+kernel that merges the key-range pieces of the split tail tiles; the time,
+the flops and the counted traffic all cover both.
 """
 from __future__ import annotations
 
@@ -53,9 +56,10 @@ def attention_kernel_digest() -> str:
 
 
 def counted_traffic(cfg):
-    """HBM bytes per launch of the student attention kernel, from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE runs (copy-calibrated), or None if those
-    counters were taken on another workload or on a different kernel source."""
+    """HBM bytes per launch of the student attention (its kernel and the
+    combine kernel of the split tail), from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE runs (copy-calibrated), or None if those counters
+    were taken on another workload or on a different kernel source."""
     path = os.path.join(ROOT, "profiles", "attn_fwd_jvp_high_res_counters.json")
     if cfg.name != "high-res" or not os.path.exists(path):
         return None
@@ -269,7 +273,8 @@ def main() -> int:
                    "tokens": cfg.N_all, "valid_keys": nk, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": counted_traffic(cfg),
-                     "kernel": f"attn_fwd_jvp_kernel<{cfg.dh},true>", "flops_per_launch": flops,
+                     "kernel": f"attn_fwd_jvp_kernel<{cfg.dh},true> + attn_combine_kernel<{cfg.dh},true>",
+                     "flops_per_launch": flops,
                      "avg_launch_ms": attn_ms},
         "phases_ms_per_step": {k: v / ncalls for k, v in phases.items()},
         "teacher_attn_tflops": teacher_tf,

@@ -29,6 +29,8 @@ import sys
 def short(name: str) -> str:
     for key, label in (("attn_fwd_jvp_kernel<128, true>", "attn_fwd_jvp<128,true> (student fwd+JVP)"),
                        ("attn_fwd_jvp_kernel<128, false>", "attn_fwd_jvp<128,false> (forward: teacher, fake)"),
+                       ("attn_combine_kernel<128, true>", "attn_combine<128,true> (JVP split-tail merge)"),
+                       ("attn_combine_kernel<128, false>", "attn_combine<128,false> (forward split-tail merge)"),
                        ("attn_bwd_dkv_kernel<128>", "attn_bwd_dkv<128> (backward dK, dV)"),
                        ("attn_bwd_dq_kernel<128>", "attn_bwd_dq<128> (backward dQ)"),
                        ("gemm_bf16_large_kernel", "gemm_bf16_large (256x256 tiles)"),
