@@ -93,20 +93,6 @@ struct AttnCfg {
   static constexpr int PIECE_FLOATS = PIECE_STATS + PIECE_O + (TAN ? 4 * DT * THREADS : 0);
 };
 
-// Tail split.  A launch has one workgroup per compute unit at a time, so the
-// tiles of an XCD run in rounds, and a last round with few tiles leaves most of
-// the XCD idle.  Each XCD therefore runs its first n_full tiles whole and cuts
-// its last `rem` tiles into k pieces over consecutive ranges of 64-key stages,
-// dispatched after every whole tile.  A piece stores its own normalised result
-// o_i, do_i, log-sum-exp and mean tangent logit mu_i; with w_i the softmax of
-// the log-sum-exps over the pieces, o = sum w_i o_i, mu = sum w_i mu_i and
-// do = sum w_i (do_i + (mu_i - mu) o_i) (each piece's do_i is centred on its
-// own mu_i), which the combine kernel forms in piece order.
-constexpr int kMaxPieces = 4;
-constexpr int kMinPieceStages = 8;   // no piece shorter than 512 keys (at the longest sample)
-struct SplitArgs {
-  int n_full, rem, k;
-};
 
 // Four consecutive output columns of one row (and of its tangent): bf16 or
 // fp32 as p.out_dt says, at element offset `at` of o (od).
@@ -143,21 +129,9 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   auto sVT = [&](int vb) { return lds + 3 * C::KBUF_ELEMS + vb * C::VBUF_ELEMS; };
   auto sVdT = [&](int vb) { return lds + 3 * C::KBUF_ELEMS + vb * C::VBUF_ELEMS + C::V_ELEMS; };
 
-  // XCD-aware order: hardware places workgroup w on XCD w % 8; give each XCD a
-  // contiguous range of logical tiles so one head's K/V stay in that XCD's L2.
-  // The last `rem` tiles of the range run as sp.k pieces each (slot: the split
-  // tile's index among all split tiles).
-  const int w = blockIdx.x;
-  const int xcd = w & 7, wi = w >> 3;
-  int L, piece = 0, slot = -1;
-  if (wi < sp.n_full) {
-    L = xcd * per_xcd + wi;
-  } else {
-    const int tt = (wi - sp.n_full) / sp.k;
-    piece = wi - sp.n_full - tt * sp.k;
-    L = xcd * per_xcd + sp.n_full + tt;
-    slot = xcd * sp.rem + tt;
-  }
+  // XCD-aware order, with the XCD's last tiles split (split_item)
+  const SplitItem it = split_item(blockIdx.x, per_xcd, sp);
+  const int L = it.L, piece = it.piece, slot = it.slot;
   if (L >= total) return;
   const int qb = L % nqb;
   const int bh = L / nqb;
@@ -173,8 +147,8 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   int key0 = 0, nk = nk_b;
   float *part = nullptr;
   if (slot >= 0) {
-    const int nst_b = (nk_b + BN - 1) / BN;
-    const int s0 = piece * nst_b / sp.k, s1 = (piece + 1) * nst_b / sp.k;
+    int s0, s1;
+    piece_stages((nk_b + BN - 1) / BN, piece, sp.k, s0, s1);
     key0 = s0 * BN;
     nk = min(nk_b, s1 * BN) - key0;
     part = p.part + (size_t)(slot * sp.k + piece) * C::PIECE_FLOATS;
@@ -674,15 +648,18 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
 }
 
 // Merges the pieces of the split tiles (one workgroup per split tile, each
-// thread the rows and columns it held in the attention kernel); pieces are
-// taken in key order, so the result does not depend on which finished first.
+// thread the rows and columns it held in the attention kernel).  A piece holds
+// its own normalised result o_i, do_i, log-sum-exp and mean tangent logit
+// mu_i; with w_i the softmax of the log-sum-exps over the pieces,
+// o = sum w_i o_i, mu = sum w_i mu_i and do = sum w_i (do_i + (mu_i - mu) o_i)
+// (each do_i is centred on its own mu_i).  Pieces are taken in key order, so
+// the result does not depend on which finished first.
 template <int DH, bool TAN>
 __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_combine_kernel(AttnParams p, int nqb,
                                                                    int per_xcd, int total, SplitArgs sp) {
   using C = AttnCfg<DH, TAN>;
   const int slot = blockIdx.x;
-  const int xcd = slot / sp.rem, tt = slot - xcd * sp.rem;
-  const int L = xcd * per_xcd + sp.n_full + tt;
+  const int L = split_tile(slot, per_xcd, sp);
   if (L >= total) return;
   const int qb = L % nqb, bh = L / nqb;
   const int b = bh / p.H, h = bh % p.H;
@@ -749,57 +726,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_combine_k
   }
 }
 
-// Workgroups of the attention kernel that one XCD holds at once (0: unknown),
-// queried once per device.
-template <int DH, bool TAN>
-int xcd_slots() {
-  using C = AttnCfg<DH, TAN>;
-  static int cache[64];   // 0: not queried yet, -1: unknown
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  if (cache[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    const bool ok =
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_jvp_kernel<DH, TAN>, C::THREADS,
-                                                     C::LDS_BYTES) == hipSuccess;
-    if (!ok) (void)hipGetLastError();
-    cache[dev] = (ok && cus >= 8 && per_cu >= 1) ? per_cu * (cus / 8) : -1;
-  }
-  return cache[dev] > 0 ? cache[dev] : 0;
-}
 
-// The tail split of an XCD's per_xcd tiles when it holds `slots` at once: the
-// k <= kMaxPieces that minimises the time of the last round(s),
-// ceil(rem k / slots) / k whole-tile times, ties to the smaller k; k = 1 (no
-// split) when nothing is gained, a piece would span fewer than
-// kMinPieceStages stages of the longest sample, or the scratch holds fewer
-// than 8 rem k pieces.
-SplitArgs plan_split(int per_xcd, int slots, int nst_max, size_t cap_pieces) {
-  SplitArgs sp{per_xcd, 0, 1};
-  if (slots <= 0) return sp;
-  const int rem = per_xcd % slots;
-  if (rem == 0) return sp;
-  int best_k = 1;
-  int64_t best_num = 1, best_den = 1;   // cost as a fraction ceil(rem k / slots) / k
-  for (int k = 2; k <= kMaxPieces; ++k) {
-    if (nst_max / k < kMinPieceStages || (size_t)8 * rem * k > cap_pieces) break;
-    const int64_t num = (rem * k + slots - 1) / slots;
-    if (num * best_den < best_num * k) {
-      best_k = k;
-      best_num = num;
-      best_den = k;
-    }
-  }
-  if (best_k == 1) return sp;
-  sp.n_full = per_xcd - rem;
-  sp.rem = rem;
-  sp.k = best_k;
-  return sp;
-}
 
 constexpr size_t kCapPieces = 768;   // scratch for at most this many pieces
 
@@ -827,8 +754,11 @@ hipError_t launch_impl(const AttnParams &p, hipStream_t s) {
   const int per_xcd = (total + 7) / 8;
   // split the tail only with scratch, and never with the prefix output
   const size_t cap = (p.part && !p.o2) ? p.part_bytes / (sizeof(float) * C::PIECE_FLOATS) : 0;
-  const SplitArgs sp = cap ? plan_split(per_xcd, xcd_slots<DH, TAN>(), (p.Nk + BN - 1) / BN, cap)
-                           : SplitArgs{per_xcd, 0, 1};
+  static int slots[kMaxDevices];
+  const SplitArgs sp =
+      cap ? plan_split(per_xcd, xcd_slots(attn_fwd_jvp_kernel<DH, TAN>, C::THREADS, C::LDS_BYTES, slots),
+                       (p.Nk + BN - 1) / BN, cap)
+          : SplitArgs{per_xcd, 0, 1};
   hipLaunchKernelGGL((attn_fwd_jvp_kernel<DH, TAN>), dim3(8 * (sp.n_full + sp.rem * sp.k)),
                      dim3(C::THREADS), C::LDS_BYTES, s, p, nqb, per_xcd, total, sp);
   if (sp.rem > 0) {

@@ -27,6 +27,8 @@
 #include "attn_tiles.h"
 #include "common.h"
 
+#include <algorithm>
+
 #include <math.h>
 
 namespace t2va {
@@ -70,6 +72,12 @@ struct BwdCfg {
   static constexpr int DKV_STAGE = 2 * ROW_ELEMS + 2 * T_ELEMS + 2 * BT * 2;  // + 2 x 64 floats
   static constexpr size_t DQ_LDS = (size_t)2 * DQ_STAGE * sizeof(bf16);
   static constexpr size_t DKV_LDS = (size_t)2 * DKV_STAGE * sizeof(bf16);
+  // partial results of one piece of a split tile (floats): for each row of
+  // the tile and lane group g (index 4 row + g), the lane's four columns of
+  // each d-tile, already scaled; dK/dV: the dK part, then the dV part
+  static constexpr int PIECE_DQ = 4 * MB_DQ * DT * THREADS_DQ;
+  static constexpr int PIECE_DKV_HALF = 4 * MB_DKV * DT * THREADS_DKV;
+  static constexpr int PIECE_DKV = 2 * PIECE_DKV_HALF;
 };
 
 // Per-lane byte offsets (at token 0) of the chunks a loading wave moves into a
@@ -144,17 +152,13 @@ __device__ __forceinline__ void read_stage_stats(const float *a, const float *b,
       : "memory");
 }
 
-__device__ __forceinline__ void xcd_tile(int w, int per_xcd, int total, int &L) {
-  L = (w & 7) * per_xcd + (w >> 3);
-  if (L >= total) L = -1;
-}
 
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
 template <int DH>
 __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kernel(AttnBwdParams p, int nqb,
-                                                                              int per_xcd, int total) {
+                                                                              int per_xcd, int total, SplitArgs sp) {
   using C = BwdCfg<DH>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16 *const lds = reinterpret_cast<bf16 *>(smem_raw);
@@ -162,16 +166,36 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kerne
   auto sV = [&](int buf) { return lds + buf * C::DQ_STAGE + C::ROW_ELEMS; };
   auto sKT = [&](int buf) { return lds + buf * C::DQ_STAGE + 2 * C::ROW_ELEMS; };
 
-  int L;
-  xcd_tile(blockIdx.x, per_xcd, total, L);
-  if (L < 0) return;
-  const int qb = L % nqb, bh = L / nqb;
+  // XCD-aware order; a split tile's pieces cover consecutive key stages
+  const SplitItem it = split_item(blockIdx.x, per_xcd, sp);
+  if (it.L >= total) return;
+  const int qb = it.L % nqb, bh = it.L / nqb;
   const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   constexpr int MB = C::MB_DQ;
   const int q_row0 = qb * C::BW_DQ + wave * 16 * MB + l16;   // + 16 mb for row block mb
-  const int nk = min(max(p.nk[b], 1), p.Nk);
+  const int nk_b = min(max(p.nk[b], 1), p.Nk);
+  // this workgroup's keys [key0, key0 + nk)
+  int key0 = 0, nk = nk_b;
+  float *part = nullptr;
+  if (it.slot >= 0) {
+    int s0, s1;
+    piece_stages((nk_b + BT - 1) / BT, it.piece, sp.k, s0, s1);
+    key0 = s0 * BT;
+    nk = min(nk_b, s1 * BT) - key0;
+    part = p.part + (size_t)(it.slot * sp.k + it.piece) * C::PIECE_DQ;
+  }
+  if (nk <= 0) {   // an empty piece (a sample shorter than the longest) adds zero
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int pi = 4 * (q_row0 + 16 * mb - qb * C::BW_DQ) + g;
+#pragma unroll
+      for (int e = 0; e < C::DT; ++e)
+        *reinterpret_cast<float4 *>(part + 4 * (e * MB * C::THREADS_DQ + pi)) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
   const float c_log2 = p.scale * 1.4426950408889634f;
 
   bf16x8 qf[MB][C::KSTEPS], dof[MB][C::KSTEPS];
@@ -191,15 +215,16 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kerne
     Dq[mb] = p.D[sidx];
   }
 
-  // K and V row descriptors end after key row nk-1 (rows past it load as
-  // zeros); K^T columns past nk hold finite values (zeros or padded text
-  // keys) and meet zero weights.
+  // Descriptors start at key key0.  K and V row descriptors end after key
+  // row nk-1 (rows past it load as zeros); K^T columns past nk hold finite
+  // values (zeros or padded text keys) and meet zero weights.
   const uint32_t k_bytes = (uint32_t)(((int64_t)(nk - 1) * p.k_rs + DH) * 2);
   const uint32_t v_bytes = (uint32_t)(((int64_t)(nk - 1) * p.v_rs + DH) * 2);
-  const uint32_t kt_bytes = (uint32_t)((int64_t)DH * p.kt_rs * 2);
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.k + (int64_t)b * p.k_bs + h * DH, k_bytes);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.v + (int64_t)b * p.v_bs + h * DH, v_bytes);
-  const __amdgpu_buffer_rsrc_t rKT = make_rsrc(p.kt + (int64_t)b * p.kt_bs + (int64_t)h * p.kt_hs, kt_bytes);
+  const uint32_t kt_bytes = (uint32_t)(((int64_t)DH * p.kt_rs - key0) * 2);
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.k + (int64_t)b * p.k_bs + (int64_t)key0 * p.k_rs + h * DH, k_bytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.v + (int64_t)b * p.v_bs + (int64_t)key0 * p.v_rs + h * DH, v_bytes);
+  const __amdgpu_buffer_rsrc_t rKT =
+      make_rsrc(p.kt + (int64_t)b * p.kt_bs + (int64_t)h * p.kt_hs + key0, kt_bytes);
   const int lw = wave % kBwdLoaders;
   const bool loader = wave < kBwdLoaders;
   TileOffsets<DH> ko, vo;
@@ -301,7 +326,14 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kerne
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int q_row = q_row0 + 16 * mb;
-    if (q_row < p.Nq) {
+    if (part) {   // a piece of a split tile: its scaled partial dQ, every row
+      const int pi = 4 * (q_row - qb * C::BW_DQ) + g;
+#pragma unroll
+      for (int e = 0; e < C::DT; ++e)
+        *reinterpret_cast<float4 *>(part + 4 * (e * MB * C::THREADS_DQ + pi)) =
+            make_float4(acc[mb][e][0] * p.scale, acc[mb][e][1] * p.scale, acc[mb][e][2] * p.scale,
+                        acc[mb][e][3] * p.scale);
+    } else if (q_row < p.Nq) {
       bf16 *dst = p.dq + (int64_t)b * p.dq_bs + (int64_t)q_row * p.dq_rs + h * DH + 4 * g;
 #pragma unroll
       for (int e = 0; e < C::DT; ++e) {
@@ -319,7 +351,7 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kerne
 // ---------------------------------------------------------------------------
 template <int DH>
 __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_kernel(AttnBwdParams p, int nkb,
-                                                                               int per_xcd, int total) {
+                                                                               int per_xcd, int total, SplitArgs sp) {
   using C = BwdCfg<DH>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16 *const lds = reinterpret_cast<bf16 *>(smem_raw);
@@ -332,16 +364,39 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
   };
   auto sD = [&](int buf) { return sL(buf) + BT; };
 
-  int L;
-  xcd_tile(blockIdx.x, per_xcd, total, L);
-  if (L < 0) return;
-  const int kb = L % nkb, bh = L / nkb;
+  // XCD-aware order; a split tile's pieces cover consecutive query stages
+  const SplitItem it = split_item(blockIdx.x, per_xcd, sp);
+  if (it.L >= total) return;
+  const int kb = it.L % nkb, bh = it.L / nkb;
   const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   constexpr int MB = C::MB_DKV;
   const int k_row0 = kb * C::BW_DKV + wave * 16 * MB + l16;   // + 16 mb for key block mb
   const int nk = min(max(p.nk[b], 1), p.Nk);
+  // this workgroup's queries [q0, q0 + Nq)
+  int q0 = 0, Nq = p.Nq;
+  float *part = nullptr;
+  if (it.slot >= 0) {
+    int s0, s1;
+    piece_stages((p.Nq + BT - 1) / BT, it.piece, sp.k, s0, s1);
+    q0 = s0 * BT;
+    Nq = min(p.Nq, s1 * BT) - q0;
+    part = p.part + (size_t)(it.slot * sp.k + it.piece) * C::PIECE_DKV;
+  }
+  if (Nq <= 0) {   // an empty piece adds zero
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int pi = 4 * (k_row0 + 16 * mb - kb * C::BW_DKV) + g;
+#pragma unroll
+      for (int e = 0; e < C::DT; ++e) {
+        *reinterpret_cast<float4 *>(part + 4 * (e * MB * C::THREADS_DKV + pi)) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4 *>(part + C::PIECE_DKV_HALF + 4 * (e * MB * C::THREADS_DKV + pi)) =
+            make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    return;
+  }
   const float c_log2 = p.scale * 1.4426950408889634f;
 
   bf16x8 kf[MB][C::KSTEPS], vf[MB][C::KSTEPS];
@@ -359,19 +414,20 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
     }
   }
 
-  // Q and dO row descriptors end after query row Nq-1; the transposed copies
-  // are zero past Nq; lse2 and D past Nq load as zeros and those queries'
-  // weights are masked.
-  const int Nq = p.Nq;
+  // Descriptors start at query q0.  Q and dO row descriptors end after query
+  // row Nq-1; the transposed copies are zero past the last query; lse2 and D
+  // past Nq load as zeros and those queries' weights are masked.
   const uint32_t q_bytes = (uint32_t)(((int64_t)(Nq - 1) * p.q_rs + DH) * 2);
   const uint32_t do_bytes = (uint32_t)(((int64_t)(Nq - 1) * p.do_rs + DH) * 2);
-  const uint32_t qt_bytes = (uint32_t)((int64_t)DH * p.qt_rs * 2);
+  const uint32_t qt_bytes = (uint32_t)(((int64_t)DH * p.qt_rs - q0) * 2);
   const uint32_t s_bytes = (uint32_t)(Nq * 4);
-  const __amdgpu_buffer_rsrc_t rQ = make_rsrc(p.q + (int64_t)b * p.q_bs + h * DH, q_bytes);
-  const __amdgpu_buffer_rsrc_t rDO = make_rsrc(p.dout + (int64_t)b * p.do_bs + h * DH, do_bytes);
-  const __amdgpu_buffer_rsrc_t rQT = make_rsrc(p.qt + (int64_t)b * p.qt_bs + (int64_t)h * p.qt_hs, qt_bytes);
-  const __amdgpu_buffer_rsrc_t rDOT = make_rsrc(p.dot + (int64_t)b * p.qt_bs + (int64_t)h * p.qt_hs, qt_bytes);
-  const int64_t srow = ((int64_t)b * p.H + h) * Nq;
+  const __amdgpu_buffer_rsrc_t rQ = make_rsrc(p.q + (int64_t)b * p.q_bs + (int64_t)q0 * p.q_rs + h * DH, q_bytes);
+  const __amdgpu_buffer_rsrc_t rDO =
+      make_rsrc(p.dout + (int64_t)b * p.do_bs + (int64_t)q0 * p.do_rs + h * DH, do_bytes);
+  const int64_t qt_at = (int64_t)b * p.qt_bs + (int64_t)h * p.qt_hs + q0;
+  const __amdgpu_buffer_rsrc_t rQT = make_rsrc(p.qt + qt_at, qt_bytes);
+  const __amdgpu_buffer_rsrc_t rDOT = make_rsrc(p.dot + qt_at, qt_bytes);
+  const int64_t srow = ((int64_t)b * p.H + h) * p.Nq + q0;
   const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.lse2 + srow, s_bytes);
   const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.D + srow, s_bytes);
   const int lw = wave % kBwdLoaders;
@@ -493,7 +549,17 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int k_row = k_row0 + 16 * mb;
-    if (k_row < p.Nk) {
+    if (part) {   // a piece of a split tile: its partial dK (scaled) and dV, every row
+      const int pi = 4 * (k_row - kb * C::BW_DKV) + g;
+#pragma unroll
+      for (int e = 0; e < C::DT; ++e) {
+        float *pk = part + 4 * (e * MB * C::THREADS_DKV + pi);
+        *reinterpret_cast<float4 *>(pk) = make_float4(dK[mb][e][0] * p.scale, dK[mb][e][1] * p.scale,
+                                                      dK[mb][e][2] * p.scale, dK[mb][e][3] * p.scale);
+        *reinterpret_cast<float4 *>(pk + C::PIECE_DKV_HALF) =
+            make_float4(dV[mb][e][0], dV[mb][e][1], dV[mb][e][2], dV[mb][e][3]);
+      }
+    } else if (k_row < p.Nk) {
       const int64_t o = (int64_t)b * p.dk_bs + (int64_t)k_row * p.dk_rs + h * DH + 4 * g;
 #pragma unroll
       for (int e = 0; e < C::DT; ++e) {
@@ -510,6 +576,99 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
   }
 }
 
+// Sum of the pieces of each split dQ tile (one workgroup per split tile, each
+// thread the rows and columns it held in the dQ kernel), in piece order.
+template <int DH>
+__global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_merge_kernel(AttnBwdParams p, int nqb,
+                                                                                    int per_xcd, int total,
+                                                                                    SplitArgs sp) {
+  using C = BwdCfg<DH>;
+  constexpr int MB = C::MB_DQ;
+  const int slot = blockIdx.x;
+  const int L = split_tile(slot, per_xcd, sp);
+  if (L >= total) return;
+  const int qb = L % nqb, bh = L / nqb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const float *part = p.part + (size_t)slot * sp.k * C::PIECE_DQ;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int row = wave * 16 * MB + 16 * mb + l16;
+    const int q_row = qb * C::BW_DQ + row;
+    if (q_row >= p.Nq) continue;
+    const int pi = 4 * row + g;
+    bf16 *dst = p.dq + (int64_t)b * p.dq_bs + (int64_t)q_row * p.dq_rs + h * DH + 4 * g;
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int i = 0; i < sp.k; ++i) {
+        const float4 v = *reinterpret_cast<const float4 *>(part + (size_t)i * C::PIECE_DQ +
+                                                           4 * (e * MB * C::THREADS_DQ + pi));
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+      }
+      bf16x4 o;
+      o[0] = (bf16)a.x; o[1] = (bf16)a.y; o[2] = (bf16)a.z; o[3] = (bf16)a.w;
+      *reinterpret_cast<bf16x4 *>(dst + 16 * e) = o;
+    }
+  }
+}
+
+// Sum of the pieces of each split dK/dV tile, in piece order.
+template <int DH>
+__global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_merge_kernel(AttnBwdParams p,
+                                                                                      int nkb, int per_xcd,
+                                                                                      int total, SplitArgs sp) {
+  using C = BwdCfg<DH>;
+  constexpr int MB = C::MB_DKV;
+  const int slot = blockIdx.x;
+  const int L = split_tile(slot, per_xcd, sp);
+  if (L >= total) return;
+  const int kb = L % nkb, bh = L / nkb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const float *part = p.part + (size_t)slot * sp.k * C::PIECE_DKV;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int row = wave * 16 * MB + 16 * mb + l16;
+    const int k_row = kb * C::BW_DKV + row;
+    if (k_row >= p.Nk) continue;
+    const int pi = 4 * row + g;
+    const int64_t o = (int64_t)b * p.dk_bs + (int64_t)k_row * p.dk_rs + h * DH + 4 * g;
+#pragma unroll
+    for (int e = 0; e < C::DT; ++e) {
+      float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak;
+      for (int i = 0; i < sp.k; ++i) {
+        const float *pk = part + (size_t)i * C::PIECE_DKV + 4 * (e * MB * C::THREADS_DKV + pi);
+        const float4 vk = *reinterpret_cast<const float4 *>(pk);
+        const float4 vv = *reinterpret_cast<const float4 *>(pk + C::PIECE_DKV_HALF);
+        ak.x += vk.x; ak.y += vk.y; ak.z += vk.z; ak.w += vk.w;
+        av.x += vv.x; av.y += vv.y; av.z += vv.z; av.w += vv.w;
+      }
+      bf16x4 ok, ov;
+      ok[0] = (bf16)ak.x; ok[1] = (bf16)ak.y; ok[2] = (bf16)ak.z; ok[3] = (bf16)ak.w;
+      ov[0] = (bf16)av.x; ov[1] = (bf16)av.y; ov[2] = (bf16)av.z; ov[3] = (bf16)av.w;
+      *reinterpret_cast<bf16x4 *>(p.dk + o + 16 * e) = ok;
+      *reinterpret_cast<bf16x4 *>(p.dv + o + 16 * e) = ov;
+    }
+  }
+}
+
+constexpr size_t kCapPiecesBwd = 768;   // scratch for at most this many pieces
+
+template <int DH>
+size_t bwd_split_bytes(int B, int H, int Nq, int Nk) {
+  using C = BwdCfg<DH>;
+  auto need = [](int64_t tiles, int piece_floats) {
+    return std::min<size_t>(kCapPiecesBwd, (size_t)kMaxPieces * 8 * ((tiles + 7) / 8)) * piece_floats *
+           sizeof(float);
+  };
+  const int64_t tq = (int64_t)B * H * ((Nq + C::BW_DQ - 1) / C::BW_DQ);
+  const int64_t tk = (int64_t)B * H * ((Nk + C::BW_DKV - 1) / C::BW_DKV);
+  return std::max(need(tq, C::PIECE_DQ), need(tk, C::PIECE_DKV));
+}
+
 template <int DH>
 hipError_t launch_bwd_impl(const AttnBwdParams &p, hipStream_t s) {
   using C = BwdCfg<DH>;
@@ -523,18 +682,39 @@ hipError_t launch_bwd_impl(const AttnBwdParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
+  static int slots_dq[kMaxDevices], slots_dkv[kMaxDevices];
+  // dQ: query tiles, split over key stages
   const int nqb = (p.Nq + C::BW_DQ - 1) / C::BW_DQ;
   int total = nqb * p.H * p.B;
   int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DH>), dim3(per_xcd * 8), dim3(C::THREADS_DQ), C::DQ_LDS, s, p, nqb,
-                     per_xcd, total);
+  size_t cap = p.part ? p.part_bytes / (sizeof(float) * C::PIECE_DQ) : 0;
+  SplitArgs sp = cap ? plan_split(per_xcd, xcd_slots(attn_bwd_dq_kernel<DH>, C::THREADS_DQ, C::DQ_LDS, slots_dq),
+                                  (p.Nk + BT - 1) / BT, cap)
+                     : SplitArgs{per_xcd, 0, 1};
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DH>), dim3(8 * (sp.n_full + sp.rem * sp.k)), dim3(C::THREADS_DQ),
+                     C::DQ_LDS, s, p, nqb, per_xcd, total, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (sp.rem > 0) {
+    hipLaunchKernelGGL((attn_bwd_dq_merge_kernel<DH>), dim3(8 * sp.rem), dim3(C::THREADS_DQ), 0, s, p, nqb,
+                       per_xcd, total, sp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // dK/dV: key tiles, split over query stages (the same scratch: the dQ merge
+  // has read it by the time these pieces write, on the one stream)
   const int nkb = (p.Nk + C::BW_DKV - 1) / C::BW_DKV;
   total = nkb * p.H * p.B;
   per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DH>), dim3(per_xcd * 8), dim3(C::THREADS_DKV), C::DKV_LDS, s, p, nkb,
-                     per_xcd, total);
+  cap = p.part ? p.part_bytes / (sizeof(float) * C::PIECE_DKV) : 0;
+  sp = cap ? plan_split(per_xcd, xcd_slots(attn_bwd_dkv_kernel<DH>, C::THREADS_DKV, C::DKV_LDS, slots_dkv),
+                        (p.Nq + BT - 1) / BT, cap)
+           : SplitArgs{per_xcd, 0, 1};
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DH>), dim3(8 * (sp.n_full + sp.rem * sp.k)), dim3(C::THREADS_DKV),
+                     C::DKV_LDS, s, p, nkb, per_xcd, total, sp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (sp.rem > 0)
+    hipLaunchKernelGGL((attn_bwd_dkv_merge_kernel<DH>), dim3(8 * sp.rem), dim3(C::THREADS_DKV), 0, s, p, nkb,
+                       per_xcd, total, sp);
   return hipGetLastError();
 }
 
@@ -544,6 +724,12 @@ hipError_t launch_attention_bwd(int dh, const AttnBwdParams &p, hipStream_t s) {
   if (dh == 128) return launch_bwd_impl<128>(p, s);
   if (dh == 64) return launch_bwd_impl<64>(p, s);
   return hipErrorInvalidValue;
+}
+
+size_t attention_bwd_split_bytes(int dh, int B, int H, int Nq, int Nk) {
+  if (dh == 128) return bwd_split_bytes<128>(B, H, Nq, Nk);
+  if (dh == 64) return bwd_split_bytes<64>(B, H, Nq, Nk);
+  return 0;
 }
 
 }  // namespace t2va

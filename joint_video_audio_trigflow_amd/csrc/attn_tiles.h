@@ -1,6 +1,7 @@
-// Shared device helpers of the attention kernels (forward, forward + JVP and
+// Shared helpers of the attention kernels (forward, forward + JVP and
 // backward): direct global -> LDS tile loads through buffer descriptors, the
-// XOR slot swizzles of the two LDS tile layouts, and the 16x16x32 bf16 MFMA.
+// XOR slot swizzles of the two LDS tile layouts, the 16x16x32 bf16 MFMA, and
+// the tail split of a launch (work decomposition and its host-side plan).
 //
 // Row tiles [64 tokens][dh] (K, V, Q or dO rows) put chunk c of row r in slot
 // kslot(r, c); transposed tiles [dh][64 tokens] (V^T, K^T, Q^T, dO^T) put key
@@ -39,6 +40,94 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t vo
 
 __device__ __forceinline__ floatx4 mfma16(const bf16x8 &a, const bf16x8 &b, const floatx4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Tail split.  These kernels run one workgroup per compute unit at a time, so
+// each XCD runs its tiles in rounds, and a last round with few tiles leaves
+// most of the XCD idle.  Each XCD therefore runs its first n_full tiles whole
+// and cuts its last `rem` tiles into k pieces over consecutive ranges of
+// 64-token stages of the streamed operand, dispatched after every whole tile.
+// Each piece stores a partial result into scratch and a second kernel merges
+// the pieces of every split tile in piece order.
+// ---------------------------------------------------------------------------
+constexpr int kMaxPieces = 4;
+constexpr int kMinPieceStages = 8;   // no piece shorter than 8 stages (at the longest sample)
+constexpr int kMaxDevices = 64;
+struct SplitArgs {
+  int n_full, rem, k;
+};
+
+// Workgroup w of a split launch: hardware places w on XCD w % 8, and each XCD
+// gets a contiguous range of per_xcd logical tiles (so one head's streamed
+// operands stay in that XCD's L2).  Its first n_full workgroups run tiles
+// whole; the next rem * k run the remaining tiles as k pieces each.  slot is
+// the split tile's index among all split tiles (-1: a whole tile).
+struct SplitItem {
+  int L, piece, slot;
+};
+__device__ __forceinline__ SplitItem split_item(int w, int per_xcd, const SplitArgs &sp) {
+  const int xcd = w & 7, wi = w >> 3;
+  if (wi < sp.n_full) return {xcd * per_xcd + wi, 0, -1};
+  const int tt = (wi - sp.n_full) / sp.k;
+  return {xcd * per_xcd + sp.n_full + tt, wi - sp.n_full - tt * sp.k, xcd * sp.rem + tt};
+}
+// the logical tile of split slot `slot` (merge kernels: one workgroup per slot)
+__device__ __forceinline__ int split_tile(int slot, int per_xcd, const SplitArgs &sp) {
+  const int xcd = slot / sp.rem;
+  return xcd * per_xcd + sp.n_full + (slot - xcd * sp.rem);
+}
+// stages [s0, s1) of piece `piece` of k over nst stages (empty when nst < k)
+__device__ __forceinline__ void piece_stages(int nst, int piece, int k, int &s0, int &s1) {
+  s0 = piece * nst / k;
+  s1 = (piece + 1) * nst / k;
+}
+
+// The split of an XCD's per_xcd tiles when it holds `slots` workgroups at
+// once: the k <= kMaxPieces that minimises the time of the last round(s),
+// ceil(rem k / slots) / k whole-tile times, ties to the smaller k; no split
+// when nothing is gained, a piece would span fewer than kMinPieceStages of the
+// nst_max stages, or the scratch holds fewer than 8 rem k pieces.
+inline SplitArgs plan_split(int per_xcd, int slots, int nst_max, size_t cap_pieces) {
+  SplitArgs sp{per_xcd, 0, 1};
+  if (slots <= 0) return sp;
+  const int rem = per_xcd % slots;
+  if (rem == 0) return sp;
+  int best_k = 1;
+  int64_t best_num = 1, best_den = 1;   // cost as the fraction ceil(rem k / slots) / k
+  for (int k = 2; k <= kMaxPieces; ++k) {
+    if (nst_max / k < kMinPieceStages || (size_t)8 * rem * k > cap_pieces) break;
+    const int64_t num = (rem * k + slots - 1) / slots;
+    if (num * best_den < best_num * k) {
+      best_k = k;
+      best_num = num;
+      best_den = k;
+    }
+  }
+  if (best_k == 1) return sp;
+  sp.n_full = per_xcd - rem;
+  sp.rem = rem;
+  sp.k = best_k;
+  return sp;
+}
+
+// Workgroups of `kernel` (threads, dynamic LDS) one XCD holds at once, 0 if
+// unknown; queried once per device into `cache` (0: not yet, -1: unknown).
+template <typename Kernel>
+int xcd_slots(Kernel kernel, int threads, size_t lds, int (&cache)[kMaxDevices]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (cache[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    const bool ok = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                    hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) == hipSuccess;
+    if (!ok) (void)hipGetLastError();
+    cache[dev] = (ok && cus >= 8 && per_cu >= 1) ? per_cu * (cus / 8) : -1;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
 }
 
 }  // namespace

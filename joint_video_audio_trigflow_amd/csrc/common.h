@@ -219,8 +219,15 @@ struct AttnBwdParams {
   int64_t dq_bs, dq_rs, dk_bs, dk_rs;    // dv uses dk's strides
   int B, H, Nq, Nk;
   float scale;
+  // nullable scratch of part_bytes bytes: with it, the last tiles of each
+  // XCD's range may run split (dQ over keys, dK/dV over queries) and be summed
+  // by a second kernel
+  float *part = nullptr;
+  size_t part_bytes = 0;
 };
 hipError_t launch_attention_bwd(int dh, const AttnBwdParams &p, hipStream_t s);
+// Scratch bytes that let launch_attention_bwd split the tails of its two kernels.
+size_t attention_bwd_split_bytes(int dh, int B, int H, int Nq, int Nk);
 
 // ---- the training backward's HBM-bound steps ----
 // dy = bf16(2 w bo / sin t * gbar) per sample (bo = 1, or -t_rf behind the wrapper).

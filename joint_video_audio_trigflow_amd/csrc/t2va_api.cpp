@@ -203,7 +203,7 @@ struct GradLayout {
   int64_t kc_v, kc_a, kc_all, kp_v, kp_a, kp_all;   // split-K chunk and padded token counts
   size_t lse, lse2, Dq, wt_out_v, wt_out_a, wt_qkv, dy_v, dy_a, dO, dOT, QT, KT, Vrm, dQKV, dX;
   size_t dyT_v, oT_v, dyT_a, oT_a, dqkvT, xT, dxT_v, zT_v, dxT_a, zT_a, tpart, part;
-  size_t total;
+  size_t total, part_bytes;
 };
 
 // Split-K factor for a weight gradient contracted over `tokens` rows with
@@ -268,7 +268,9 @@ GradLayout make_grad_layout(const t2va_scm_desc &d) {
   G.tpart = take(B * (size_t)(colsum_chunks((int)Nq) + 1) * D * fs);   // partial sums, then dtau
   const size_t part_elems = std::max({(size_t)G.split_v * d.Cv * D, (size_t)G.split_a * d.Ca * D,
                                       (size_t)G.split_all * 3 * D * D});
-  G.part = take(part_elems * fs);
+  // also the attention backward's scratch (used before the weight gradients, on one stream)
+  G.part_bytes = std::max(part_elems * fs, attention_bwd_split_bytes(L.dh, d.B, d.H, L.Nq, L.N_all));
+  G.part = take(G.part_bytes);
   G.total = off;
   return G;
 }
@@ -881,6 +883,8 @@ t2va_status t2va_scm_grad(const t2va_scm_desc *desc, const t2va_block_weights *t
     ap.dq_bs = g_bs; ap.dq_rs = 3 * D; ap.dk_bs = g_bs; ap.dk_rs = 3 * D;
     ap.B = B; ap.H = H; ap.Nq = Nq; ap.Nk = NA;
     ap.scale = (float)(1.0 / sqrt((double)dh));
+    ap.part = (float *)(ws + G.part);
+    ap.part_bytes = G.part_bytes;
     PhaseScope ps(s, T2VA_PHASE_BWD_ATTN, prof);
     HIP_TRY(launch_attention_bwd(dh, ap, s), "attention backward");
   }
