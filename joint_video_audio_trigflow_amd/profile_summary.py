@@ -33,6 +33,8 @@ def short(name: str) -> str:
                        ("attn_combine_kernel<128, false>", "attn_combine<128,false> (forward split-tail merge)"),
                        ("attn_bwd_dkv_kernel<128>", "attn_bwd_dkv<128> (backward dK, dV)"),
                        ("attn_bwd_dq_kernel<128>", "attn_bwd_dq<128> (backward dQ)"),
+                       ("attn_bwd_dkv_merge_kernel<128>", "attn_bwd_dkv_merge<128> (split-tail sum)"),
+                       ("attn_bwd_dq_merge_kernel<128>", "attn_bwd_dq_merge<128> (split-tail sum)"),
                        ("gemm_bf16_large_kernel", "gemm_bf16_large (256x256 tiles)"),
                        ("gemm_bf16_kernel", "gemm_bf16 (128x128 tiles)"),
                        ("copyBuffer", "copyBuffer"),
