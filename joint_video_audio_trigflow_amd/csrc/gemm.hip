@@ -233,15 +233,23 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
   const int l32 = lane & 31, hi = lane >> 5;
   const int wm = kLWaves == 4 ? wave >> 1 : wave >> 2;
   const int wn = kLWaves == 4 ? wave & 1 : wave & 3;
-  // column-tile-major order within groups of 8 row tiles: neighbouring
-  // workgroups share W column tiles and A row tiles in L2
-  const int bid = blockIdx.x;
+  // Hardware places workgroup w on XCD w % 8, and each XCD has its own L2:
+  // give each XCD a contiguous range of logical tiles (batch-major), so the
+  // tiles an XCD runs at once form a compact block.  Logical order within a
+  // batch: column-tile-major within bands of 8 row tiles, so 32 consecutive
+  // tiles are 8 row tiles x 4 column tiles sharing their A and W slices in L2.
+  const int tiles = tiles_n * tiles_m;
+  const int total = tiles * p.batch;
+  const int per_xcd = (total + 7) / 8;
+  const int L = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (L >= total) return;
+  const int bz = L / tiles;
+  const int bid = L - bz * tiles;
   const int group = bid / (8 * tiles_n);
   const int first_m = group * 8;
   const int gsize = min(tiles_m - first_m, 8);
   const int tm = first_m + (bid % (8 * tiles_n)) % gsize;
   const int tn = (bid % (8 * tiles_n)) / gsize;
-  const int bz = blockIdx.y;
   const int m0 = tm * LBM, n0 = tn * LBN;
 
   // descriptors end after the last valid row: rows >= M (N) read zeros
@@ -496,8 +504,9 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
     }
     const int tiles_n = (p.N + LBN - 1) / LBN;
     const int tiles_m = (rows + LBM - 1) / LBM;
-    dim3 grid(tiles_n * tiles_m, p.batch);
-    hipLaunchKernelGGL(gemm_bf16_large_kernel, grid, dim3(kLThreads), kLLdsBytes, s, p, tiles_n, tiles_m);
+    const int64_t total = (int64_t)tiles_n * tiles_m * p.batch;
+    hipLaunchKernelGGL(gemm_bf16_large_kernel, dim3((unsigned)((total + 7) / 8 * 8)), dim3(kLThreads), kLLdsBytes,
+                       s, p, tiles_n, tiles_m);
     return hipGetLastError();
   }
   if (!g_attr_set) {
