@@ -66,19 +66,19 @@ struct SplitArgs {
 struct SplitItem {
   int L, piece, slot;
 };
-__device__ __forceinline__ SplitItem split_item(int w, int per_xcd, const SplitArgs &sp) {
+__host__ __device__ __forceinline__ SplitItem split_item(int w, int per_xcd, const SplitArgs &sp) {
   const int xcd = w & 7, wi = w >> 3;
   if (wi < sp.n_full) return {xcd * per_xcd + wi, 0, -1};
   const int tt = (wi - sp.n_full) / sp.k;
   return {xcd * per_xcd + sp.n_full + tt, wi - sp.n_full - tt * sp.k, xcd * sp.rem + tt};
 }
 // the logical tile of split slot `slot` (merge kernels: one workgroup per slot)
-__device__ __forceinline__ int split_tile(int slot, int per_xcd, const SplitArgs &sp) {
+__host__ __device__ __forceinline__ int split_tile(int slot, int per_xcd, const SplitArgs &sp) {
   const int xcd = slot / sp.rem;
   return xcd * per_xcd + sp.n_full + (slot - xcd * sp.rem);
 }
 // stages [s0, s1) of piece `piece` of k over nst stages (empty when nst < k)
-__device__ __forceinline__ void piece_stages(int nst, int piece, int k, int &s0, int &s1) {
+__host__ __device__ __forceinline__ void piece_stages(int nst, int piece, int k, int &s0, int &s1) {
   s0 = piece * nst / k;
   s1 = (piece + 1) * nst / k;
 }
