@@ -23,7 +23,12 @@
  *   - Work is asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  Outputs are valid once the caller synchronises that stream.
  *   - Results are deterministic: no floating-point atomics; reductions run in
- *     a fixed order, so identical inputs give bitwise-identical outputs.
+ *     a fixed order, so identical inputs give bitwise-identical outputs on a
+ *     given device configuration.  (The attention launches of the entry points
+ *     that take a workspace cut the last tiles of each XCD into key or query
+ *     ranges merged in a fixed order; how they cut depends on the device's
+ *     compute-unit count, so a GPU with another count, or another partition
+ *     mode, may differ in the last bits.)
  *   - Calls on the same stream are ordered; calls on different streams that
  *     share a workspace race.
  */
@@ -139,7 +144,9 @@ typedef struct {
  * (deep read, section 3.1, J_theta equation; section 4.2: the JVP passes
  * through the cross-modal transformer; section 6.3: padded text positions are
  * removed from the keys).  Softmax state and accumulators are fp32; P and
- * P*dS enter the matrix cores as bf16.
+ * P*dS enter the matrix cores as bf16.  This entry point has no workspace and
+ * always runs every tile whole (the workspace-carrying entry points may split
+ * the last tiles, which changes rounding in the last bits only).
  *   nk_valid  device int32 [B], each in [1, Nk].  Values outside that range
  *             are clamped to it by the kernel.
  * Errors: T2VA_INVALID_ARG (null/misaligned pointers, strides not multiples
@@ -182,7 +189,9 @@ typedef struct {
 } t2va_block_weights;
 
 /* Exact workspace size in bytes for t2va_scm_target with this descriptor
- * (0 if the descriptor is invalid; t2va_last_error() says why). */
+ * (0 if the descriptor is invalid; t2va_last_error() says why).  It covers the
+ * activations and tangents of both blocks, partial sums, and the scratch in
+ * which the attention launches merge the pieces of their split last tiles. */
 size_t t2va_scm_workspace_bytes(const t2va_scm_desc *desc);
 
 /*
