@@ -316,26 +316,40 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (KT > 1) issue(1, BK);
+  // Two LDS stages, one barrier per k-tile, placed before the tile's last
+  // k-step: that step's fragments are already in registers, so after the
+  // barrier (which publishes tile kt+1 and frees tile kt's stage for tile kt+2)
+  // the first fragments of tile kt+1 are read while the last MFMAs of tile kt
+  // run, and no k-tile starts by waiting for an LDS read.
   auto main_loop = [&](auto order) {
   constexpr bool kSwap = decltype(order)::value;
+  bf16x8 a[2][4], b[2][kLJ];
+  auto read_frags = [&](const bf16 *sA, int s, int x) {
+    const bf16 *sW = sA + LBM * BK;
+    const int c = 2 * s + hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[x][i] = *reinterpret_cast<const bf16x8 *>(sA + abase[i] + 8 * (c ^ ax[i]));
+#pragma unroll
+    for (int j = 0; j < kLJ; ++j) b[x][j] = *reinterpret_cast<const bf16x8 *>(sW + wbase[j] + 8 * (c ^ wx[j]));
+  };
+  static_assert((BK / 16) % 2 == 0, "the next tile's first fragments go to register set 0");
+  read_frags(smem, 0, 0);
   for (int kt = 0; kt < KT; ++kt) {
     const int stage = kt & 1;
-    if (kt + 1 < KT) issue(stage ^ 1, (kt + 1) * BK);
     const bf16 *sA = smem + stage * kLStageElems;
-    const bf16 *sW = sA + LBM * BK;
-    // fragments of k-step s+1 are read while the MFMAs of k-step s run
-    bf16x8 a[2][4], b[2][kLJ];
-    auto read_frags = [&](int s, int x) {
-      const int c = 2 * s + hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[x][i] = *reinterpret_cast<const bf16x8 *>(sA + abase[i] + 8 * (c ^ ax[i]));
-#pragma unroll
-      for (int j = 0; j < kLJ; ++j) b[x][j] = *reinterpret_cast<const bf16x8 *>(sW + wbase[j] + 8 * (c ^ wx[j]));
-    };
-    read_frags(0, 0);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) read_frags(s + 1, (s + 1) & 1);
+      if (s + 1 < BK / 16) {
+        // fragments of k-step s+1 are read while the MFMAs of k-step s run
+        read_frags(sA, s + 1, (s + 1) & 1);
+      } else {
+        // this wave's loads of tile kt+1 have landed and every wave has read
+        // its last fragments of tile kt
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < KT) read_frags(smem + (stage ^ 1) * kLStageElems, 0, 0);
+      }
       // keep the reads ahead of this k-step's MFMAs (the scheduler would
       // otherwise sink each read next to its first use)
       __builtin_amdgcn_sched_barrier(0);
@@ -346,11 +360,10 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
           acc[i][j] = kSwap ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[s & 1][j], a[s & 1][i], acc[i][j], 0, 0, 0)
                             : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      // tile kt+2 into the stage every wave has finished reading, issued
+      // behind the last k-step's MFMAs
+      if (s + 1 == BK / 16 && kt + 2 < KT) issue(stage, (kt + 2) * BK);
     }
-    // the next stage has landed (this wave's loads) and every wave is done
-    // reading this one before it is refilled
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
   };
   if (rowmajor) main_loop(std::true_type{});
