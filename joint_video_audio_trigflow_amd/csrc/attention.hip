@@ -532,8 +532,13 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   for (int mb = 0; mb < C::MB; ++mb) set_thr(mb);
   int j = 0;
   floatx4 Sn[C::MB][2], Sdn[2];
+  // the prefix output (forward with o2) is stored between two runs of the
+  // inner loop, after the sub-tile that ends at key nk_split, so the loop
+  // body carries no store code
+  bool prefix_due = !TAN && nk_split > 0;
   for (;;) {
-    for (; j < nsub; ++j) {
+    const int jend = prefix_due ? nk_split / 32 : nsub;
+    for (; j < jend; ++j) {
       const int u = j & 1, st = j >> 1;
       if (outgrown(S)) break;   // rare: raise m_run outside
       if (u == 0) {
@@ -551,7 +556,6 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       softmax(S, Sd, P, PS);
       if constexpr (!TAN) __builtin_amdgcn_s_setprio(0);
       pv_accum(st & 1, u, P, PS);
-      if (!TAN && 32 * (j + 1) == nk_split) store_prefix(p.o2);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -560,7 +564,12 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       }
       if (j + 1 < nsub && ((j + 1) >> 1) == nst - 1) mask_s(32 * (j + 1), S, Sd);
     }
-    if (j >= nsub) break;
+    if (j >= jend) {
+      if (!prefix_due) break;
+      store_prefix(p.o2);
+      prefix_due = false;
+      continue;
+    }
     // raise the reference max of the rows that outgrew it; rescale the
     // accumulators and re-centre the tangent weights on the new max key
 #pragma unroll
