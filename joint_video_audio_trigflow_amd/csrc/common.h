@@ -178,6 +178,9 @@ struct GemmParams {
   int M, N, K, batch;
 };
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s);
+// Two GEMMs in one launch when both take the 128x128 tile (else one after the
+// other): a small one then runs beside the other instead of after it.
+hipError_t launch_gemm_pair(const GemmParams &a, const GemmParams &b, hipStream_t s);
 
 // Attention forward (+JVP).
 struct AttnParams {

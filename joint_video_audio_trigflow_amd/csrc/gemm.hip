@@ -27,16 +27,26 @@ constexpr int kThreads = 256;
 constexpr int kStageElems = (BM + BN) * LROW;
 constexpr size_t kLdsBytes = 2 * kStageElems * sizeof(bf16);
 
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int tiles_n) {
+// Two independent problems can share one launch (the first tiles1 workgroups
+// of each batch row run p1, the rest p2): a problem with few tiles then runs
+// beside a larger one instead of after it.
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p1, GemmParams p2, int tiles_n1,
+                                                             int tiles_n2, int tiles1) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16 *smem = reinterpret_cast<bf16 *>(smem_raw);
+
+  const bool second = (int)blockIdx.x >= tiles1;
+  const GemmParams &p = second ? p2 : p1;
+  const int tiles_n = second ? tiles_n2 : tiles_n1;
+  const int bx = second ? (int)blockIdx.x - tiles1 : (int)blockIdx.x;
+  const int bz = blockIdx.y;
+  if (bz >= p.batch) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
-  const int bz = blockIdx.y;
+  const int tn = bx % tiles_n, tm = bx / tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
 
   const bf16 *A = p.A + (int64_t)bz * p.a_bs;
@@ -500,15 +510,32 @@ bool g_attr_set = false, g_lattr_set = false;
 
 }  // namespace
 
+namespace {
+// the large tile for wide outputs with many rows; per-(batch, tile) byte
+// extents must fit the 32-bit buffer descriptors
+bool use_large(const GemmParams &p) {
+  const int rows = max(p.M, p.VT ? p.vt_rows : 0);
+  return p.N >= 1024 && rows >= 2048 && (int64_t)LBM * p.lda * 2 < ((int64_t)1 << 31) &&
+         (int64_t)LBN * p.ldw * 2 < ((int64_t)1 << 31);
+}
+int small_tiles(const GemmParams &p) {
+  return ((p.N + BN - 1) / BN) * ((max(p.M, p.VT ? p.vt_rows : 0) + BM - 1) / BM);
+}
+hipError_t set_small_attr() {
+  if (!g_attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    if (e != hipSuccess) return e;
+    g_attr_set = true;
+  }
+  return hipSuccess;
+}
+}  // namespace
+
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (p.M <= 0 || p.batch <= 0) return hipSuccess;
   const int rows = max(p.M, p.VT ? p.vt_rows : 0);
-  // the large tile for wide outputs with many rows; per-(batch, tile) byte
-  // extents must fit the 32-bit buffer descriptors
-  const bool large = p.N >= 1024 && rows >= 2048 &&
-                     (int64_t)LBM * p.lda * 2 < ((int64_t)1 << 31) &&
-                     (int64_t)LBN * p.ldw * 2 < ((int64_t)1 << 31);
-  if (large) {
+  if (use_large(p)) {
     if (!g_lattr_set) {
       hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_large_kernel,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLLdsBytes);
@@ -522,16 +549,24 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
                        s, p, tiles_n, tiles_m);
     return hipGetLastError();
   }
-  if (!g_attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    if (e != hipSuccess) return e;
-    g_attr_set = true;
-  }
+  if (hipError_t e = set_small_attr()) return e;
   const int tiles_n = (p.N + BN - 1) / BN;
-  const int tiles_m = (max(p.M, p.VT ? p.vt_rows : 0) + BM - 1) / BM;
-  dim3 grid(tiles_n * tiles_m, p.batch);
-  hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(kThreads), kLdsBytes, s, p, tiles_n);
+  const int tiles = small_tiles(p);
+  hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tiles, p.batch), dim3(kThreads), kLdsBytes, s, p, p, tiles_n, tiles_n,
+                     tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_pair(const GemmParams &a, const GemmParams &b, hipStream_t s) {
+  const bool a_on = a.M > 0 && a.batch > 0, b_on = b.M > 0 && b.batch > 0;
+  if (!a_on || !b_on || use_large(a) || use_large(b)) {
+    if (hipError_t e = launch_gemm(a, s)) return e;
+    return launch_gemm(b, s);
+  }
+  if (hipError_t e = set_small_attr()) return e;
+  const int ta = small_tiles(a);
+  hipLaunchKernelGGL(gemm_bf16_kernel, dim3(ta + small_tiles(b), max(a.batch, b.batch)), dim3(kThreads),
+                     kLdsBytes, s, a, b, (a.N + BN - 1) / BN, (b.N + BN - 1) / BN, ta);
   return hipGetLastError();
 }
 

@@ -430,9 +430,9 @@ struct Block {
     o_bs = (int64_t)Nq * D;
   }
 
-  t2va_status gemm(const bf16 *A, int64_t lda, int64_t a_bs, const bf16 *Wt, int64_t ldw, void *Cp,
-                   int64_t ldc, int64_t c_bs, int c_dt, const float *bias, int64_t bias_bs, int M,
-                   int N, int K, int batch, bf16 *vt, int n_split, int64_t w_bs = 0) const {
+  GemmParams params(const bf16 *A, int64_t lda, int64_t a_bs, const bf16 *Wt, int64_t ldw, void *Cp,
+                    int64_t ldc, int64_t c_bs, int c_dt, const float *bias, int64_t bias_bs, int M, int N,
+                    int K, int batch, bf16 *vt, int n_split, int64_t w_bs = 0) const {
     GemmParams g;
     g.A = A; g.lda = lda; g.a_bs = a_bs;
     g.W = Wt; g.ldw = ldw; g.w_bs = w_bs;
@@ -441,6 +441,14 @@ struct Block {
     g.VT = vt; g.vt_bs = vt_bs; g.vt_hs = vt_hs; g.vt_rs = ldv; g.vt_rows = ldv;
     g.n_split = n_split; g.dh = dh;
     g.M = M; g.N = N; g.K = K; g.batch = batch;
+    return g;
+  }
+
+  t2va_status gemm(const bf16 *A, int64_t lda, int64_t a_bs, const bf16 *Wt, int64_t ldw, void *Cp,
+                   int64_t ldc, int64_t c_bs, int c_dt, const float *bias, int64_t bias_bs, int M,
+                   int N, int K, int batch, bf16 *vt, int n_split, int64_t w_bs = 0) const {
+    const GemmParams g = params(A, lda, a_bs, Wt, ldw, Cp, ldc, c_bs, c_dt, bias, bias_bs, M, N, K, batch, vt,
+                                n_split, w_bs);
     PhaseScope ps(s, T2VA_PHASE_GEMM, prof);
     HIP_TRY(launch_gemm(g, s), "gemm");
     return T2VA_OK;
@@ -458,12 +466,15 @@ struct Block {
     return gemm(X, D, x_bs, W[3], D, QK, 2 * D, qk_bs, 0, nullptr, 0, NA, 3 * D, D, batch, VT, 2 * D);
   }
 
-  // O [batch, Nq, D] -> fp32 x0^v [batch, Nv, Cv] and x0^a [batch, Na, Ca].
+  // O [batch, Nq, D] -> fp32 x0^v [batch, Nv, Cv] and x0^a [batch, Na, Ca], in one launch: the
+  // audio rows are few, and alone they would leave most of the chip idle.
   t2va_status project_out(const bf16 *const *W, const bf16 *O, float *xv, float *xa, int batch) const {
-    if (t2va_status st = gemm(O, D, o_bs, W[4], D, xv, Cv, nv, 1, nullptr, 0, Nv, Cv, D, batch, nullptr, Cv))
-      return st;
-    return gemm(O + (int64_t)Nv * D, D, o_bs, W[5], D, xa, Ca, na, 1, nullptr, 0, Na, Ca, D, batch,
-                nullptr, Ca);
+    const GemmParams gv = params(O, D, o_bs, W[4], D, xv, Cv, nv, 1, nullptr, 0, Nv, Cv, D, batch, nullptr, Cv);
+    const GemmParams ga = params(O + (int64_t)Nv * D, D, o_bs, W[5], D, xa, Ca, na, 1, nullptr, 0, Na, Ca, D,
+                                 batch, nullptr, Ca);
+    PhaseScope ps(s, T2VA_PHASE_GEMM, prof);
+    HIP_TRY(launch_gemm_pair(gv, ga, s), "gemm");
+    return T2VA_OK;
   }
 
   // Attention of the B problems in QK/VT over nk[b] keys into O; with `tan`,
