@@ -154,8 +154,20 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     part = p.part + (size_t)(slot * sp.k + piece) * C::PIECE_FLOATS;
   }
   // forward only: also store the output over the first nk_split keys (a
-  // multiple of 32, at most nk) into o2 (never in a split tile)
-  const int nk_split = (!TAN && p.o2 && slot < 0) ? p.nk_split : -1;
+  // multiple of 32, at most nk) into o2.  A split tile's piece that holds key
+  // nk_split - 1 but not all its keys stores its partial result over the keys
+  // before it into the prefix bank (the merge takes the other pieces' full
+  // partials, or nothing, by their key ranges).
+  int nk_split = -1;
+  float *ppart = nullptr;
+  if (!TAN && p.o2) {
+    if (slot < 0) {
+      nk_split = p.nk_split;
+    } else if (key0 < p.nk_split && p.nk_split < key0 + nk) {
+      nk_split = p.nk_split - key0;
+      ppart = part + (size_t)sp.pbank * C::PIECE_FLOATS;
+    }
+  }
   if (nk <= 0) {
     // an empty piece: weight zero in the combination
 #pragma unroll
@@ -475,14 +487,24 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     return __any(any);
   };
 
-  // Forward only: the normalised output of the keys seen so far into `dst`
-  // (o's strides).  Used mid-loop for the prefix snapshot and not for the JVP.
+  // Forward only: the normalised output of the keys seen so far into o2 (o's
+  // strides), or for a piece, its partial result into the prefix bank.  Used
+  // mid-loop for the prefix snapshot and not for the JVP.
   auto store_prefix = [&](void *dst) {
     if constexpr (!TAN) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
         const int q_row = q_row0 + 16 * mb;
-        if (q_row < p.Nq) {
+        if (ppart) {
+          const float inv_l = 1.f / Lacc[mb][0];
+          const int pi = 4 * (q_row - qb * C::BM) + g;
+          *reinterpret_cast<float2 *>(ppart + 2 * pi) =
+              make_float2(m_run[mb] * 0.6931471805599453f + logf(Lacc[mb][0]), 0.f);
+#pragma unroll
+          for (int e = 0; e < C::DT; ++e)
+            *reinterpret_cast<float4 *>(ppart + C::PIECE_STATS + 4 * (e * C::MB * C::THREADS + pi)) =
+                make_float4(O[mb][e][0] * inv_l, O[mb][e][1] * inv_l, O[mb][e][2] * inv_l, O[mb][e][3] * inv_l);
+        } else if (q_row < p.Nq) {
           const float inv_l = 1.f / Lacc[mb][0];
           const int64_t obase = (int64_t)b * p.o_bs + (int64_t)q_row * p.o_rs + h * DH + 4 * g;
 #pragma unroll
@@ -732,6 +754,54 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_combine_k
       }
       store_out4<TAN>(p, obase + 16 * e, o4, od4);
     }
+    if constexpr (!TAN) {
+      if (p.o2) {
+        // the output over the first nk_split keys: per piece its full partial
+        // (keys all before nk_split), its prefix partial (the piece holding
+        // the boundary) or nothing (keys all after)
+        const int nk_b = min(max(p.nk[b], 1), p.Nk);
+        float plse[kMaxPieces];
+        const float *src[kMaxPieces];
+        float pmx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kMaxPieces; ++i) {
+          plse[i] = -INFINITY;
+          src[i] = nullptr;
+          if (i < sp.k) {
+            int s0, s1;
+            piece_stages((nk_b + BN - 1) / BN, i, sp.k, s0, s1);
+            const int k0 = s0 * BN, k1 = min(nk_b, s1 * BN);
+            const float *bank0 = part + (size_t)i * C::PIECE_FLOATS;
+            src[i] = k1 <= p.nk_split ? bank0
+                     : (k0 < p.nk_split ? bank0 + (size_t)sp.pbank * C::PIECE_FLOATS : nullptr);
+            if (src[i]) plse[i] = reinterpret_cast<const float2 *>(src[i] + 2 * pi)->x;
+          }
+          pmx = fmaxf(pmx, plse[i]);
+        }
+        float pw[kMaxPieces], psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < kMaxPieces; ++i) {
+          pw[i] = expf(plse[i] - pmx);
+          psum += pw[i];
+        }
+        const float pinv = 1.f / psum;
+#pragma unroll
+        for (int e = 0; e < C::DT; ++e) {
+          float o4[4] = {0.f, 0.f, 0.f, 0.f}, unused[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < kMaxPieces; ++i) {
+            if (!src[i]) continue;
+            const float4 a = *reinterpret_cast<const float4 *>(src[i] + C::PIECE_STATS +
+                                                               4 * (e * C::MB * C::THREADS + pi));
+            const float w = pw[i] * pinv;
+            o4[0] += w * a.x; o4[1] += w * a.y; o4[2] += w * a.z; o4[3] += w * a.w;
+          }
+          AttnParams q = p;
+          q.o = p.o2;
+          store_out4<false>(q, obase + 16 * e, o4, unused);
+        }
+      }
+    }
   }
 }
 
@@ -740,11 +810,11 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_combine_k
 constexpr size_t kCapPieces = 768;   // scratch for at most this many pieces
 
 template <int DH, bool TAN>
-size_t split_bytes(int B, int H, int Nq) {
+size_t split_bytes(int B, int H, int Nq, bool prefix) {
   using C = AttnCfg<DH, TAN>;
   const int64_t total = (int64_t)B * H * ((Nq + C::BM - 1) / C::BM);
   const size_t pieces = std::min<size_t>(kCapPieces, (size_t)kMaxPieces * 8 * ((total + 7) / 8));
-  return pieces * C::PIECE_FLOATS * sizeof(float);
+  return pieces * C::PIECE_FLOATS * sizeof(float) * (prefix && !TAN ? 2 : 1);
 }
 
 template <int DH, bool TAN>
@@ -761,13 +831,17 @@ hipError_t launch_impl(const AttnParams &p, hipStream_t s) {
   const int nqb = (p.Nq + C::BM - 1) / C::BM;
   const int total = nqb * p.H * p.B;
   const int per_xcd = (total + 7) / 8;
-  // split the tail only with scratch, and never with the prefix output
-  const size_t cap = (p.part && !p.o2) ? p.part_bytes / (sizeof(float) * C::PIECE_FLOATS) : 0;
+  // split the tail only with scratch; with the prefix output (forward) every
+  // piece needs a second partial in the prefix bank
+  const bool two_banks = !TAN && p.o2;
+  const size_t cap =
+      p.part ? p.part_bytes / (sizeof(float) * C::PIECE_FLOATS) / (two_banks ? 2 : 1) : 0;
   static int slots[kMaxDevices];
-  const SplitArgs sp =
+  SplitArgs sp =
       cap ? plan_split(per_xcd, xcd_slots(attn_fwd_jvp_kernel<DH, TAN>, C::THREADS, C::LDS_BYTES, slots),
                        (p.Nk + BN - 1) / BN, cap)
-          : SplitArgs{per_xcd, 0, 1};
+          : SplitArgs{per_xcd, 0, 1, 0};
+  sp.pbank = 8 * sp.rem * sp.k;
   hipLaunchKernelGGL((attn_fwd_jvp_kernel<DH, TAN>), dim3(8 * (sp.n_full + sp.rem * sp.k)),
                      dim3(C::THREADS), C::LDS_BYTES, s, p, nqb, per_xcd, total, sp);
   if (sp.rem > 0) {
@@ -786,9 +860,11 @@ hipError_t launch_attention(int dh, bool tangent, const AttnParams &p, hipStream
   return hipErrorInvalidValue;
 }
 
-size_t attention_split_bytes(int dh, int B, int H, int Nq) {
-  if (dh == 128) return std::max(split_bytes<128, true>(B, H, Nq), split_bytes<128, false>(B, H, Nq));
-  if (dh == 64) return std::max(split_bytes<64, true>(B, H, Nq), split_bytes<64, false>(B, H, Nq));
+size_t attention_split_bytes(int dh, int B, int H, int Nq, bool prefix) {
+  if (dh == 128)
+    return std::max(split_bytes<128, true>(B, H, Nq, prefix), split_bytes<128, false>(B, H, Nq, prefix));
+  if (dh == 64)
+    return std::max(split_bytes<64, true>(B, H, Nq, prefix), split_bytes<64, false>(B, H, Nq, prefix));
   return 0;
 }
 

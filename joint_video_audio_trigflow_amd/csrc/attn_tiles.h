@@ -56,6 +56,7 @@ constexpr int kMinPieceStages = 8;   // no piece shorter than 8 stages (at the l
 constexpr int kMaxDevices = 64;
 struct SplitArgs {
   int n_full, rem, k;
+  int pbank;   // forward with a prefix output: pieces before the second (prefix) bank
 };
 
 // Workgroup w of a split launch: hardware places w on XCD w % 8, and each XCD
@@ -89,7 +90,7 @@ __host__ __device__ __forceinline__ void piece_stages(int nst, int piece, int k,
 // when nothing is gained, a piece would span fewer than kMinPieceStages of the
 // nst_max stages, or the scratch holds fewer than 8 rem k pieces.
 inline SplitArgs plan_split(int per_xcd, int slots, int nst_max, size_t cap_pieces) {
-  SplitArgs sp{per_xcd, 0, 1};
+  SplitArgs sp{per_xcd, 0, 1, 0};
   if (slots <= 0) return sp;
   const int rem = per_xcd % slots;
   if (rem == 0) return sp;

@@ -198,14 +198,15 @@ struct AttnParams {
   float scale;
   // nullable scratch of part_bytes bytes: with it, the last tiles of each
   // XCD's range may run split over key ranges and be merged by a second kernel
-  // (not with o2)
+  // (with o2, each piece needs room for two partial results)
   float *part = nullptr;
   size_t part_bytes = 0;
 };
 hipError_t launch_attention(int dh, bool tangent, const AttnParams &p, hipStream_t s);
 // Scratch bytes that let launch_attention split the tail of a B x H x Nq launch
-// (forward or JVP) as far as it would.
-size_t attention_split_bytes(int dh, int B, int H, int Nq);
+// (forward or JVP; `prefix`: forward launches with the o2 output) as far as it
+// would.
+size_t attention_split_bytes(int dh, int B, int H, int Nq, bool prefix = false);
 
 // Attention backward for one (sample, head) grid: dQ, dK, dV from Q, K, V, dO,
 // the forward's log2-unit log-sum-exp and D = rowsum(dO * O).  Row-major

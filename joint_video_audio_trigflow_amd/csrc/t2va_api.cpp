@@ -349,7 +349,7 @@ DmdLayout make_dmd_layout(const t2va_dmd_desc &d) {
   L.pa_a = take(B * L.nblk_a * sizeof(float));
   L.ps_v = take(B * L.nblk_v * sizeof(float));
   L.ps_a = take(B * L.nblk_a * sizeof(float));
-  L.apart_bytes = attention_split_bytes(d.d / d.H, d.B, d.H, Nq);
+  L.apart_bytes = attention_split_bytes(d.d / d.H, d.B, d.H, Nq, true);
   L.apart = take(L.apart_bytes);
   L.total = off;
   return L;
