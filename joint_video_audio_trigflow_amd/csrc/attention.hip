@@ -30,8 +30,9 @@
 //
 // Key tiles (K, dK, V^T, dV^T) go from global memory straight into LDS with
 // buffer_load_dwordx4 ... lds (no staging registers; SGPR descriptors and
-// 32-bit lane offsets), in 64-key stages: a three-slot ring for K (and dK) and
-// a two-slot ring for V^T (and dV^T), one barrier per stage.  16-byte slots are
+// 32-bit lane offsets), in stages of BN keys (64 in the JVP kernel, 128 in the
+// forward kernel, which halves its barriers): a three-slot ring for K (and dK)
+// and a two-slot ring for V^T (and dV^T), one barrier per stage.  16-byte slots are
 // XOR-swizzled so that every 16-lane group of an operand read hits 16
 // different bank groups.
 #include "attn_tiles.h"
@@ -55,7 +56,16 @@ namespace {
 #define T2VA_ATTN_MB_FWD 2
 #endif
 constexpr int kLoadWaves = 8;         // waves that issue the LDS loads
-constexpr int BN = 64;                // keys per LDS stage
+
+// 16-byte slot of key chunk kc of V^T row e for rows of VCPR chunks: 8 chunks
+// (64 keys): the shared swizzle; 16 chunks (128 keys, rows 256 B apart, i.e.
+// on the same banks): XOR with the row's low four bits, so the 16 rows a
+// 16-lane group reads at one chunk index fall on 16 distinct slots.
+template <int VCPR>
+__device__ __forceinline__ int vslot_n(int e, int kc) {
+  if constexpr (VCPR == 8) return vslot(e, kc);
+  else return kc ^ (e & 15);
+}
 
 template <int DH, bool TAN>
 struct AttnCfg {
@@ -69,6 +79,12 @@ struct AttnCfg {
   // VALU, where its register budget has room and the matrix cores do not
   static constexpr bool MFMA_SUMS = !TAN;
   static constexpr int THREADS = 64 * NW;
+  // keys per LDS stage (one barrier each): 64 for the JVP kernel, whose
+  // tangent tiles double its LDS; 128 for the forward, which then also fills
+  // the 160 KB and needs half as many barriers
+  static constexpr int BN = TAN ? 64 : 128;
+  static constexpr int SUB = BN / 32;      // 32-key sub-tiles per stage
+  static constexpr int VCPR = BN / 8;      // 16-byte chunks per V^T row
   static constexpr int BM = 16 * MB * NW;  // query rows per workgroup
   static constexpr int KSTEPS = DH / 32;   // MFMA k-steps over the head dimension
   static constexpr int DT = DH / 16;       // 16-row tiles of the head dimension
@@ -121,6 +137,7 @@ template <int DH, bool TAN>
 __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_kernel(AttnParams p, int nqb,
                                                                    int per_xcd, int total, SplitArgs sp) {
   using C = AttnCfg<DH, TAN>;
+  constexpr int BN = C::BN;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16 *const lds = reinterpret_cast<bf16 *>(smem_raw);
   // LDS: K ring [3][K | dK], then V^T ring [2][V^T | dV^T]
@@ -143,7 +160,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   const int q_row0 = qb * C::BM + wave * 16 * C::MB + l16;   // + 16 mb for row block mb
   const int nk_b = min(max(p.nk[b], 1), p.Nk);
   // this workgroup's keys [key0, key0 + nk): all of them, or piece `piece` of
-  // sp.k over whole 64-key stages (empty when the sample has fewer stages)
+  // sp.k over whole BN-key stages (empty when the sample has fewer stages)
   int key0 = 0, nk = nk_b;
   float *part = nullptr;
   if (slot >= 0) {
@@ -204,9 +221,9 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     }
   }
 
-  // ---- global -> LDS staging of one 64-key stage ----
+  // ---- global -> LDS staging of one BN-key stage ----
   // The K descriptors end after key row nk-1, so rows >= nk load as zeros
-  // (their logits are masked).  V^T columns in [nk, round_up(nk, 64)) are read
+  // (their logits are masked).  V^T columns in [nk, round_up(nk, BN)) are read
   // as stored; the caller keeps them finite, and their weights are zero.
   // Descriptors start at key key0 (so stage offsets below are relative to it).
   const uint32_t k_bytes = (uint32_t)(((int64_t)(nk - 1) * p.k_rs + DH) * 2);
@@ -224,11 +241,9 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   const bool loader = wave < kLoadWaves;
   // Per-lane byte offsets of this lane's 16-byte chunks (at key 0).  Chunk r
   // of a loading wave lies a uniform number of rows after chunk 0
-  // (8 r K_ROWS_PER_CHUNK key rows, 64 r V^T rows) and has the same XOR key
-  // (the swizzles read only low row bits).  The JVP kernel keeps only chunk
-  // 0's offset and adds the rest as a uniform per-stage offset, two registers
-  // it needs elsewhere; the forward kernel keeps one offset per chunk (the
-  // other way round its register allocation turns out worse).
+  // (8 r K_ROWS_PER_CHUNK key rows, 8 r 512 / BN V^T rows) and has the same
+  // XOR key (the swizzles read only low row bits), so only chunk 0's offset
+  // lives in a VGPR and the rest is a uniform per-stage offset.
   uint32_t kvo[C::KCH], vvo[C::VCH];
 #pragma unroll
   for (int r = 0; r < C::KCH; ++r) {
@@ -240,22 +255,17 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
 #pragma unroll
   for (int r = 0; r < C::VCH; ++r) {
     const int chunk = lw + kLoadWaves * r;
-    const int e = chunk * 8 + lane / 8;
-    vvo[r] = (uint32_t)((e * p.vt_rs + 8 * vslot(e, lane % 8)) * 2);
+    const int e = chunk * (512 / BN) + lane / C::VCPR;   // a 1 KB chunk holds 512 / BN rows
+    vvo[r] = (uint32_t)((e * p.vt_rs + 8 * vslot_n<C::VCPR>(e, lane % C::VCPR)) * 2);
   }
   // offset of chunk r of stage k0: per-lane part + uniform part
   auto k_off = [&](int r, int k0) -> uint32_t {
-    if constexpr (TAN)
-      return kvo[0] + (uint32_t)__builtin_amdgcn_readfirstlane(
-                          (int)((k0 + kLoadWaves * C::K_ROWS_PER_CHUNK * r) * p.k_rs * 2));
-    else
-      return kvo[r] + (uint32_t)(k0 * p.k_rs * 2);
+    return kvo[0] + (uint32_t)__builtin_amdgcn_readfirstlane(
+                        (int)((k0 + kLoadWaves * C::K_ROWS_PER_CHUNK * r) * p.k_rs * 2));
   };
   auto v_off = [&](int r, int k0) -> uint32_t {
-    if constexpr (TAN)
-      return vvo[0] + (uint32_t)__builtin_amdgcn_readfirstlane((int)((k0 + kLoadWaves * 8 * r * p.vt_rs) * 2));
-    else
-      return vvo[r] + (uint32_t)(k0 * 2);
+    return vvo[0] + (uint32_t)__builtin_amdgcn_readfirstlane(
+                        (int)((k0 + kLoadWaves * (512 / BN) * r * p.vt_rs) * 2));
   };
   auto issue_k = [&](int kb, int k0) {
     if (!loader) return;
@@ -279,7 +289,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
 
   // Per-lane swizzled read offsets (elements).  K: half t, k-step s, within a
   // 32-key sub-tile (add 32 * DH per sub-tile).  V^T: rows l16 (+16 per d-tile),
-  // key chunk g of sub-tile u (add 16 * BN per d-tile).
+  // key chunk g of 32-key sub-tile u (add 16 * BN per d-tile).
   // K slot of k-step s is 4 s + g; with the XOR key x of the row it is
   // (4 s + g) ^ x = 4 (s ^ (x >> 2)) + (g ^ (x & 3)), so one XOR per read.
   // Rows 8 (l16 / 4) + 4 t + l16 % 4 of the two halves t share their key (it
@@ -289,9 +299,9 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   const int kx = kslot<C::CPR>(krow, 0);                 // the rows' XOR key
   const int kbase_off = krow * DH + 8 * (g ^ (kx & 3));
   auto koff = [&](int t, int s) { return kbase_off + 4 * DH * t + 32 * (s ^ (kx >> 2)); };
-  // V^T chunk 4 u + g of row l16: sub-tile 1 flips bit 2 of the slot, i.e.
-  // element offset bit 5 (the rest of the offset has that bit clear)
-  const int voff0 = l16 * BN + 8 * vslot(l16, g);
+  // V^T chunk 4 u + g of row l16: with g < 4, slot(4 u + g) = slot(g) ^ 4 u
+  // (both swizzles XOR with a row key), i.e. element offset XOR 32 u
+  const int voff0 = l16 * BN + 8 * vslot_n<C::VCPR>(l16, g);
   auto voff = [&](int u) { return voff0 ^ (32 * u); };
 
   // ---- logits of one 32-key sub-tile u of a stage buffer ----
@@ -525,7 +535,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
     }
   };
 
-  // ---- main loop over 32-key sub-tiles of 64-key stages ----
+  // ---- main loop over 32-key sub-tiles of BN-key stages ----
   // The logits of sub-tile j+1 are computed in the same basic block as the
   // softmax of sub-tile j, so the matrix cores work while the VALU exponentiates.
   // Stage st's K sits in ring slot st % 3 and its V^T in slot st % 2.  The
@@ -534,7 +544,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   // K of st+1 and V^T of st (loaded during stage st-1) and frees the slots of
   // K and V^T of st-1, which then receive K of st+2 and V^T of st+1.
   const int nst = (nk + BN - 1) / BN;
-  const int nsub = 2 * nst;
+  const int nsub = C::SUB * nst;
   issue_k(0, 0);
   wait_loads();
   __syncthreads();
@@ -561,7 +571,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   for (;;) {
     const int jend = prefix_due ? nk_split / 32 : nsub;
     for (; j < jend; ++j) {
-      const int u = j & 1, st = j >> 1;
+      const int u = C::SUB == 2 ? (j & 1) : j % C::SUB, st = C::SUB == 2 ? (j >> 1) : j / C::SUB;
       if (outgrown(S)) break;   // rare: raise m_run outside
       if (u == 0) {
         wait_loads();
@@ -574,7 +584,8 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       // them issues ahead of waves busy in their P V products (forward 3 %,
       // JVP 1.7 % faster).
       __builtin_amdgcn_s_setprio(1);
-      compute_s(u == 0 ? st % 3 : (st + 1) % 3, u ^ 1, Sn, Sdn);
+      if constexpr (C::SUB == 2) compute_s(u == 0 ? st % 3 : (st + 1) % 3, u ^ 1, Sn, Sdn);
+      else compute_s(((j + 1) / C::SUB) % 3, (j + 1) % C::SUB, Sn, Sdn);
       softmax(S, Sd, P, PS);
       __builtin_amdgcn_s_setprio(0);
       pv_accum(st & 1, u, P, PS);
@@ -584,7 +595,8 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
         for (int mb = 0; mb < C::MB; ++mb) S[mb][t] = Sn[mb][t];
         if constexpr (TAN) Sd[t] = Sdn[t];
       }
-      if (j + 1 < nsub && ((j + 1) >> 1) == nst - 1) mask_s(32 * (j + 1), S, Sd);
+      if (j + 1 < nsub && (C::SUB == 2 ? ((j + 1) >> 1) : (j + 1) / C::SUB) == nst - 1)
+        mask_s(32 * (j + 1), S, Sd);
     }
     if (j >= jend) {
       if (!prefix_due) break;
@@ -689,6 +701,7 @@ template <int DH, bool TAN>
 __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_combine_kernel(AttnParams p, int nqb,
                                                                    int per_xcd, int total, SplitArgs sp) {
   using C = AttnCfg<DH, TAN>;
+  constexpr int BN = C::BN;
   const int slot = blockIdx.x;
   const int L = split_tile(slot, per_xcd, sp);
   if (L >= total) return;
@@ -839,7 +852,7 @@ hipError_t launch_impl(const AttnParams &p, hipStream_t s) {
   static int slots[kMaxDevices];
   SplitArgs sp =
       cap ? plan_split(per_xcd, xcd_slots(attn_fwd_jvp_kernel<DH, TAN>, C::THREADS, C::LDS_BYTES, slots),
-                       (p.Nk + BN - 1) / BN, cap)
+                       (p.Nk + C::BN - 1) / C::BN, cap, kMinPieceKeys / C::BN)
           : SplitArgs{per_xcd, 0, 1, 0};
   sp.pbank = 8 * sp.rem * sp.k;
   hipLaunchKernelGGL((attn_fwd_jvp_kernel<DH, TAN>), dim3(8 * (sp.n_full + sp.rem * sp.k)),

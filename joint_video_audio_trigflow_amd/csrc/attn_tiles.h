@@ -47,12 +47,13 @@ __device__ __forceinline__ floatx4 mfma16(const bf16x8 &a, const bf16x8 &b, cons
 // each XCD runs its tiles in rounds, and a last round with few tiles leaves
 // most of the XCD idle.  Each XCD therefore runs its first n_full tiles whole
 // and cuts its last `rem` tiles into k pieces over consecutive ranges of
-// 64-token stages of the streamed operand, dispatched after every whole tile.
+// stages (64 or 128 tokens) of the streamed operand, dispatched after every
+// whole tile.
 // Each piece stores a partial result into scratch and a second kernel merges
 // the pieces of every split tile in piece order.
 // ---------------------------------------------------------------------------
 constexpr int kMaxPieces = 4;
-constexpr int kMinPieceStages = 8;   // no piece shorter than 8 stages (at the longest sample)
+constexpr int kMinPieceKeys = 512;   // no piece shorter than 512 keys (at the longest sample)
 constexpr int kMaxDevices = 64;
 struct SplitArgs {
   int n_full, rem, k;
@@ -87,9 +88,9 @@ __host__ __device__ __forceinline__ void piece_stages(int nst, int piece, int k,
 // The split of an XCD's per_xcd tiles when it holds `slots` workgroups at
 // once: the k <= kMaxPieces that minimises the time of the last round(s),
 // ceil(rem k / slots) / k whole-tile times, ties to the smaller k; no split
-// when nothing is gained, a piece would span fewer than kMinPieceStages of the
+// when nothing is gained, a piece would span fewer than min_stages of the
 // nst_max stages, or the scratch holds fewer than 8 rem k pieces.
-inline SplitArgs plan_split(int per_xcd, int slots, int nst_max, size_t cap_pieces) {
+inline SplitArgs plan_split(int per_xcd, int slots, int nst_max, size_t cap_pieces, int min_stages) {
   SplitArgs sp{per_xcd, 0, 1, 0};
   if (slots <= 0) return sp;
   const int rem = per_xcd % slots;
@@ -97,7 +98,7 @@ inline SplitArgs plan_split(int per_xcd, int slots, int nst_max, size_t cap_piec
   int best_k = 1;
   int64_t best_num = 1, best_den = 1;   // cost as the fraction ceil(rem k / slots) / k
   for (int k = 2; k <= kMaxPieces; ++k) {
-    if (nst_max / k < kMinPieceStages || (size_t)8 * rem * k > cap_pieces) break;
+    if (nst_max / k < min_stages || (size_t)8 * rem * k > cap_pieces) break;
     const int64_t num = (rem * k + slots - 1) / slots;
     if (num * best_den < best_num * k) {
       best_k = k;

@@ -6,7 +6,8 @@ would be short, the last tiles of each XCD are cut into k pieces over
 consecutive ranges of 64-key stages and merged by a second kernel (only in the
 entry points that carry a workspace).  The rule: with per_xcd = ceil(tiles / 8)
 and rem = per_xcd mod 32, k in 2..4 minimises ceil(rem k / 32) / k, and a
-piece never spans fewer than 8 stages of the longest possible sample.  The
+piece never spans fewer than 512 keys of the longest possible sample (the JVP
+and backward kernels stage 64 keys at a time, the forward kernel 128).  The
 shapes below are chosen to take each branch of that rule:
 
 - split-empty: 4 tiles (per_xcd 1) and 2,088 key positions of which only the
@@ -44,15 +45,16 @@ SPLIT_K3_64 = inputs.Config("split-k3-64", B=1, Nv=1600, Na=64, Nt=64, Ntv=64, C
 CASES = [SPLIT_EMPTY, SPLIT_K3, SPLIT_K3_64]
 
 
-def planned_pieces(tiles, nst_max, slots=32):
+def planned_pieces(tiles, n_keys, stage, slots=32):
     """The split rule as documented above (k = 1: no split)."""
     per_xcd = (tiles + 7) // 8
     rem = per_xcd % slots
     if rem == 0:
         return 1
+    nst_max = (n_keys + stage - 1) // stage
     best_k, best = 1, 1.0
     for k in range(2, 5):
-        if nst_max // k < 8:
+        if nst_max // k < 512 // stage:
             break
         cost = math.ceil(rem * k / slots) / k
         if cost < best - 1e-12:
@@ -79,8 +81,9 @@ def say(*a):
 def test_split_cases_take_each_branch():
     """Host-side check that the shapes exercise k = 4 with empty pieces and k = 3."""
     def plan(cfg, rows):
+        # JVP kernel: 192 rows, 64-key stages; forward kernel: 384 rows, 128-key stages
         tiles = cfg.B * cfg.H * ((cfg.Nq + rows - 1) // rows)
-        return planned_pieces(tiles, (cfg.N_all + 63) // 64)
+        return planned_pieces(tiles, cfg.N_all, 64 if rows == 192 else 128)
     assert plan(SPLIT_EMPTY, 192) == 4 and (SPLIT_EMPTY.Nq + SPLIT_EMPTY.Ntv + 63) // 64 < 4
     assert plan(SPLIT_K3, 192) == 3 and plan(SPLIT_K3, 384) == 3
     assert plan(SPLIT_K3_64, 192) == 3
