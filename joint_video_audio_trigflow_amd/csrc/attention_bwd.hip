@@ -269,6 +269,9 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kerne
     if (st + 1 < nst) issue(cur ^ 1, (st + 1) * BT);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      // the wave that reaches its logits issues first (raised priority over the
+      // S and dP products and the exponentials, dropped for the dQ products)
+      __builtin_amdgcn_s_setprio(1);
       floatx4 S[MB][2], dP[MB][2];
       // both key halves at each k-step: the accumulation chains alternate
 #pragma unroll
@@ -305,6 +308,7 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kerne
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][t][r], c_log2, -lse2[mb]));
           dS[mb][m] = (bf16)(pv * (dP[mb][t][r] - Dq[mb]));
         }
+      __builtin_amdgcn_s_setprio(0);
       // K^T fragments of d-tile e+1 read ahead of the MFMAs of d-tile e
       bf16x8 kta[2];
       kta[0] = *reinterpret_cast<const bf16x8 *>(sKT(cur) + tr.off(u, 0));
@@ -482,6 +486,9 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
     if (st + 1 < nst) issue(cur ^ 1, (st + 1) * BT);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      // raised priority over the S and dP products and the exponentials, as in
+      // the dQ kernel, dropped for the dK and dV products
+      __builtin_amdgcn_s_setprio(1);
       floatx4 S[MB][2], dP[MB][2];
       // both query halves at each k-step: four accumulation chains alternate
 #pragma unroll
@@ -524,6 +531,7 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
       // d-tile e (held in that order by scheduling barriers; left alone, the
       // scheduler sinks each read next to its use and every MFMA pair waits
       // for an LDS round trip)
+      __builtin_amdgcn_s_setprio(0);
       bf16x8 doa[2], qta[2];
       doa[0] = *reinterpret_cast<const bf16x8 *>(sDOT(cur) + tr.off(u, 0));
       qta[0] = *reinterpret_cast<const bf16x8 *>(sQT(cur) + tr.off(u, 0));
