@@ -228,7 +228,8 @@ size_t t2va_scm_workspace_bytes(const t2va_scm_desc *desc);
  * Errors: T2VA_INVALID_ARG (null required pointers, misalignment, t out of
  * range, gamma outside [0, 1], eps_scm <= 0, bad dtypes),
  * T2VA_UNSUPPORTED_SHAPE (d != H*dh, dh not 64/128, Cv/Ca not multiples of 64,
- * B out of range), T2VA_WORKSPACE_TOO_SMALL.
+ * B out of range, or (Nv + Na + Nt + 128) * 3d * 2 bytes >= 2 GiB: one
+ * sample's rows must fit 32-bit buffer offsets), T2VA_WORKSPACE_TOO_SMALL.
  */
 t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights *teacher,
                             const t2va_block_weights *student, const void *z0_v, const void *z0_a,

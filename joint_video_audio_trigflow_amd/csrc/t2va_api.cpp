@@ -110,6 +110,12 @@ t2va_status check_shape(int B, int Nv, int Na, int Nt, int Cv, int Ca, int d, in
   const int dh = d / H;
   if (dh != 64 && dh != 128)
     return fail(T2VA_UNSUPPORTED_SHAPE, "head dim d/H = %d must be 64 or 128", dh);
+  // The attention kernels address one sample's token rows (up to 3d elements
+  // apart, plus a stage past the last key) with 32-bit buffer offsets.
+  const int64_t tokens = (int64_t)Nv + Na + Nt;
+  if ((tokens + 128) * 3 * d * 2 >= ((int64_t)1 << 31))
+    return fail(T2VA_UNSUPPORTED_SHAPE, "%lld tokens x d = %d: a sample's rows exceed 2 GiB of 32-bit offsets",
+                (long long)tokens, d);
   if (!valid_dtype(in_dt) || !valid_dtype(w_dt))
     return fail(T2VA_INVALID_ARG, "in_dtype / weight_dtype must be T2VA_DTYPE_BF16 or _FP32");
   return T2VA_OK;

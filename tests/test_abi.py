@@ -67,6 +67,13 @@ def test_workspace_bytes_validation(lib):
     assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) == 0
     bad = _lib.scm_desc(cfg.replace(Cv=100), _lib.DTYPE_BF16, _lib.DTYPE_BF16)
     assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) == 0
+    # one sample's rows must fit 32-bit offsets: (tokens + 128) * 3d * 2 < 2^31
+    limit = 2**31 // (3 * cfg.d * 2) - 128 - cfg.Na - cfg.Nt   # largest Nv that fits, exclusive
+    ok = _lib.scm_desc(cfg.replace(Nv=limit - 1), _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(ok)) > 0
+    bad = _lib.scm_desc(cfg.replace(Nv=limit + 1), _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) == 0
+    assert "2 GiB" in err(lib)
     bad = _lib.scm_desc(cfg.replace(gamma=1.5), _lib.DTYPE_BF16, _lib.DTYPE_BF16)
     assert lib.t2va_scm_workspace_bytes(ctypes.byref(bad)) == 0
     assert "gamma" in err(lib)
