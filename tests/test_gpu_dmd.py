@@ -158,8 +158,10 @@ ONETOK = inputs.Config("onetoken", B=2, Nv=1, Na=1, Nt=3, Ntv=2, Cv=64, Ca=64, d
                          ids=lambda c: c.name + f"-nq{c.Nq}")
 def test_dmd_target_edge_cases(cfg):
     """All text padded (the null condition equals the condition), one token per
-    modality, and Nq a multiple of 32 but not of 64 (the single guided pass
-    stores its null output in the middle of a 64-key stage)."""
+    modality, and Nq a multiple of 32 but not of 64 (Nq = 1696: the single
+    guided pass stores its null output in the middle of a 128-key stage, and
+    with 40 forward tiles the launch splits each tile's keys in three, the
+    last piece straddling Nq)."""
     say(f"dmd_target edge case {cfg.name} Nq={cfg.Nq}")
     p = inputs.make_dmd_problem(cfg)
     got = run_dmd(p)
