@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define T2VA_ABI_VERSION 2
+#define T2VA_ABI_VERSION 3
 
 typedef int t2va_status;
 #define T2VA_OK 0
@@ -64,6 +64,24 @@ typedef int t2va_status;
  *   passes through the wrapper and the time embedding. */
 #define T2VA_PARAM_X0 0
 #define T2VA_PARAM_RF 1
+
+/* Precision of the primal logit path (the descriptors' `precision` field).
+ * T2VA_PREC_BF16: every activation between kernels is stored in bf16 (fp32
+ *   accumulation inside each kernel).
+ * T2VA_PREC_SPLIT: the primal values that decide the attention logits -- the
+ *   noised latents, the block's token rows X and the projections Q and K -- are
+ *   carried as pairs hi + lo of bf16 values (hi = bf16(x), lo = bf16(x - hi),
+ *   about 16 significant bits).  The projections contract the pairs against
+ *   the bf16 weights on the matrix cores with fp32 accumulation, and the
+ *   attention kernels form the logits as Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T.
+ *   Tangents, V and the attention outputs stay bf16.  This is for inputs whose
+ *   logits are large enough that a bf16 rounding of Q or K (a relative 2^-9)
+ *   moves a logit by a sizeable fraction of one unit, which makes softmax,
+ *   and with it J, sensitive to the storage rounding: scaled latents at small t
+ *   (deep read, section 3.1, the J_theta equation near t -> 0).  It costs two
+ *   to three times the projection and logit work. */
+#define T2VA_PREC_BF16 0
+#define T2VA_PREC_SPLIT 1
 
 /* Largest batch one call accepts (per-sample coefficients travel as kernel
  * arguments). */
@@ -159,6 +177,21 @@ t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, c
                                     const void *vdt, const int32_t *nk_valid, void *o, void *od,
                                     float *lse, t2va_stream stream);
 
+/*
+ * t2va_joint_attn_fwd_jvp_split - as t2va_joint_attn_fwd_jvp, with the logits
+ * taken from split operands (T2VA_PREC_SPLIT): the query is q + q_lo and the key
+ * k + k_lo (q_lo and k_lo bf16 with q's and k's strides), and
+ *   s = scale (q k^T + q k_lo^T + q_lo k^T)
+ * in fp32 (the lo x lo term, 2^-16 of the product, is left out).  The tangent
+ * logits and P V use q, k, vt and their tangents as in t2va_joint_attn_fwd_jvp.
+ * Errors: as t2va_joint_attn_fwd_jvp, plus T2VA_INVALID_ARG for a NULL or
+ * misaligned q_lo or k_lo.
+ */
+t2va_status t2va_joint_attn_fwd_jvp_split(const t2va_attn_desc *desc, const void *q, const void *q_lo,
+                                          const void *k, const void *k_lo, const void *vt, const void *qd,
+                                          const void *kd, const void *vdt, const int32_t *nk_valid, void *o,
+                                          void *od, float *lse, t2va_stream stream);
+
 /* ------------------------------------------------------------------------ */
 /* The joint sCM target                                                      */
 /* ------------------------------------------------------------------------ */
@@ -176,6 +209,7 @@ typedef struct {
   double eps_scm; /* > 0, added to the L2 norm */
   double w_v, w_a; /* modality weights of the joint loss */
   int param;       /* T2VA_PARAM_X0 or T2VA_PARAM_RF (the block's parameterisation) */
+  int precision;   /* T2VA_PREC_BF16 or T2VA_PREC_SPLIT (zero-initialised: bf16) */
 } t2va_scm_desc;
 
 /* One copy of the joint block (teacher or student); device pointers. */
@@ -226,7 +260,7 @@ size_t t2va_scm_workspace_bytes(const t2va_scm_desc *desc);
  * workspace: device buffer of at least t2va_scm_workspace_bytes(desc) bytes,
  * 256-byte aligned; its contents on entry are irrelevant.
  * Errors: T2VA_INVALID_ARG (null required pointers, misalignment, t out of
- * range, gamma outside [0, 1], eps_scm <= 0, bad dtypes),
+ * range, gamma outside [0, 1], eps_scm <= 0, bad dtypes, unknown precision),
  * T2VA_UNSUPPORTED_SHAPE (d != H*dh, dh not 64/128, Cv/Ca not multiples of 64,
  * B out of range, or (Nv + Na + Nt + 128) * 3d * 2 bytes >= 2 GiB: one
  * sample's rows must fit 32-bit buffer offsets), T2VA_WORKSPACE_TOO_SMALL.
@@ -272,7 +306,10 @@ size_t t2va_scm_grad_workspace_bytes(const t2va_scm_desc *desc);
  * Inputs and the target's outputs as in t2va_scm_target (J and r are not
  * produced); grads: all six pointers required.
  * workspace: at least t2va_scm_grad_workspace_bytes(desc) bytes, 256-byte aligned.
- * Errors: as t2va_scm_target, plus T2VA_INVALID_ARG for NULL gradient pointers.
+ * The backward is built for desc->precision == T2VA_PREC_BF16 only (it
+ * recomputes the softmax from bf16 Q and K): T2VA_PREC_SPLIT is rejected.
+ * Errors: as t2va_scm_target, plus T2VA_INVALID_ARG for NULL gradient pointers
+ * and for T2VA_PREC_SPLIT.
  * Deterministic: no atomics; every reduction runs in a fixed order.
  */
 t2va_status t2va_scm_grad(const t2va_scm_desc *desc, const t2va_block_weights *teacher,
@@ -299,6 +336,7 @@ typedef struct {
   double eps_dmd;      /* > 0, added to the residual scale */
   double w_v, w_a;     /* modality weights of the joint loss */
   int param;           /* T2VA_PARAM_X0 or T2VA_PARAM_RF, as in t2va_scm_desc */
+  int precision;       /* T2VA_PREC_BF16 or T2VA_PREC_SPLIT, as in t2va_scm_desc */
 } t2va_dmd_desc;
 
 /* Exact workspace size in bytes for t2va_dmd_target (0 if the descriptor is invalid). */

@@ -22,7 +22,8 @@ T2VA_OK = 0
 DTYPE_BF16, DTYPE_FP32 = 0, 1
 NOISE, FIELD = 0, 1
 PARAM_X0, PARAM_RF = 0, 1
-ABI_VERSION = 2
+PREC_BF16, PREC_SPLIT = 0, 1
+ABI_VERSION = 3
 MAX_BATCH = 64
 NUM_PHASES = 6
 PHASES = ("total", "teacher_attn", "student_attn", "gemm", "other", "bwd_attn")
@@ -50,7 +51,8 @@ class ScmDesc(ctypes.Structure):
                 ("Cv", ctypes.c_int), ("Ca", ctypes.c_int), ("d", ctypes.c_int), ("H", ctypes.c_int),
                 ("in_dtype", ctypes.c_int), ("weight_dtype", ctypes.c_int),
                 ("beta", ctypes.c_double), ("gamma", ctypes.c_double), ("eps_scm", ctypes.c_double),
-                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double), ("param", ctypes.c_int)]
+                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double), ("param", ctypes.c_int),
+                ("precision", ctypes.c_int)]
 
 
 class DmdDesc(ctypes.Structure):
@@ -58,7 +60,8 @@ class DmdDesc(ctypes.Structure):
                 ("Cv", ctypes.c_int), ("Ca", ctypes.c_int), ("d", ctypes.c_int), ("H", ctypes.c_int),
                 ("in_dtype", ctypes.c_int), ("weight_dtype", ctypes.c_int),
                 ("cfg_v", ctypes.c_double), ("cfg_a", ctypes.c_double), ("eps_dmd", ctypes.c_double),
-                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double), ("param", ctypes.c_int)]
+                ("w_v", ctypes.c_double), ("w_a", ctypes.c_double), ("param", ctypes.c_int),
+                ("precision", ctypes.c_int)]
 
 
 class BlockWeights(ctypes.Structure):
@@ -94,6 +97,8 @@ def load() -> ctypes.CDLL:
     lib.t2va_trigflow_field.argtypes = [i32, i32, i64, i32, i32, i32, dp, vp, vp, vp, vp]
     lib.t2va_joint_attn_fwd_jvp.restype = i32
     lib.t2va_joint_attn_fwd_jvp.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 10 + [vp]
+    lib.t2va_joint_attn_fwd_jvp_split.restype = i32
+    lib.t2va_joint_attn_fwd_jvp_split.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 12 + [vp]
     lib.t2va_scm_workspace_bytes.restype = ctypes.c_size_t
     lib.t2va_scm_workspace_bytes.argtypes = [ctypes.POINTER(ScmDesc)]
     lib.t2va_scm_target.restype = i32
@@ -207,8 +212,31 @@ def joint_attn_fwd_jvp(q, k, vt, nk, qd=None, kd=None, vdt=None, out_dtype=torch
     return o, od, lse
 
 
+def joint_attn_fwd_jvp_split(q, q_lo, k, k_lo, vt, nk, qd=None, kd=None, vdt=None, out_dtype=torch.float32,
+                             want_lse=False, scale: float = 0.0):
+    """As joint_attn_fwd_jvp, with the logits taken from q + q_lo and k + k_lo
+    (q_lo, k_lo bf16 with q's and k's strides).  Returns (o, od, lse)."""
+    lib = load()
+    tan = qd is not None
+    B, Nq, H, dh = q.shape
+    assert q_lo.stride() == q.stride() and k_lo.stride() == k.stride()
+    odt = torch.bfloat16 if out_dtype == torch.bfloat16 else torch.float32
+    desc = attn_desc(q, k, vt, tan, _dt(torch.empty(0, dtype=odt)), scale)
+    o = torch.empty((B, Nq, H, dh), dtype=odt, device=q.device)
+    od = torch.empty_like(o) if tan else None
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if want_lse else None
+    _check(lib.t2va_joint_attn_fwd_jvp_split(ctypes.byref(desc), _ptr(q), _ptr(q_lo), _ptr(k), _ptr(k_lo),
+                                             _ptr(vt), _ptr(qd), _ptr(kd), _ptr(vdt), _ptr(nk), _ptr(o),
+                                             _ptr(od), _ptr(lse), _stream(q.device)))
+    return o, od, lse
+
+
 def _param(cfg) -> int:
     return {"x0": PARAM_X0, "rf": PARAM_RF}[getattr(cfg, "param", "x0")]
+
+
+def _precision(cfg) -> int:
+    return {"bf16": PREC_BF16, "split": PREC_SPLIT}[getattr(cfg, "precision", "bf16")]
 
 
 def scm_desc(cfg, in_dtype: int, weight_dtype: int) -> ScmDesc:
@@ -218,6 +246,7 @@ def scm_desc(cfg, in_dtype: int, weight_dtype: int) -> ScmDesc:
     d.in_dtype, d.weight_dtype = in_dtype, weight_dtype
     d.beta, d.gamma, d.eps_scm, d.w_v, d.w_a = cfg.beta, cfg.gamma, cfg.eps_scm, cfg.w_v, cfg.w_a
     d.param = _param(cfg)
+    d.precision = _precision(cfg)
     return d
 
 
@@ -330,6 +359,7 @@ def dmd_desc(cfg, in_dtype: int, weight_dtype: int, cfg_v=None, cfg_a=None) -> D
     d.cfg_a = cfg.cfg_a if cfg_a is None else cfg_a
     d.eps_dmd, d.w_v, d.w_a = cfg.eps_dmd, cfg.w_v, cfg.w_a
     d.param = _param(cfg)
+    d.precision = _precision(cfg)
     return d
 
 

@@ -60,21 +60,29 @@ constexpr int kLoadWaves = 8;         // waves that issue the LDS loads
 // 16-byte slot of key chunk kc of V^T row e for rows of VCPR chunks: 8 chunks
 // (64 keys): the shared swizzle; 16 chunks (128 keys, rows 256 B apart, i.e.
 // on the same banks): XOR with the row's low four bits, so the 16 rows a
-// 16-lane group reads at one chunk index fall on 16 distinct slots.
+// 16-lane group reads at one chunk index fall on 16 distinct slots; 4 chunks
+// (32 keys, rows 64 B apart: rows e and e + 4 share banks): XOR with row bits
+// 2-3, so the 16 rows again cover all 16 bank groups.
 template <int VCPR>
 __device__ __forceinline__ int vslot_n(int e, int kc) {
-  if constexpr (VCPR == 8) return vslot(e, kc);
+  if constexpr (VCPR == 4) return kc ^ ((e >> 2) & 3);   // 32 keys: rows 64 B apart
+  else if constexpr (VCPR == 8) return vslot(e, kc);
   else return kc ^ (e & 15);
 }
 
-template <int DH, bool TAN>
+// SPLIT: the split-precision kernels (logits from q + q_lo and k + k_lo).  They
+// hold Q_lo in registers and stage K_lo beside K, so they use one row block
+// per wave, 64-key stages in the forward kernel and 4096-element K tiles in
+// the JVP kernel (32 keys at dh 128), and the JVP kernel runs 8 waves (two per
+// SIMD, with room for the extra registers).
+template <int DH, bool TAN, bool SPLIT = false>
 struct AttnCfg {
   // waves per workgroup: 12 (three per SIMD) by default; MB blocks of 16
   // query rows per wave.  In the forward kernel every K / V^T fragment a wave
   // reads from LDS feeds MB MFMAs; in the JVP kernel each pair of fragments
   // (K and dK, or V^T and dV^T) feeds three (S, dS twice; O, dO twice).
-  static constexpr int NW = TAN ? T2VA_ATTN_WAVES_JVP : T2VA_ATTN_WAVES_FWD;
-  static constexpr int MB = TAN ? 1 : T2VA_ATTN_MB_FWD;
+  static constexpr int NW = SPLIT ? (TAN ? 8 : 12) : (TAN ? T2VA_ATTN_WAVES_JVP : T2VA_ATTN_WAVES_FWD);
+  static constexpr int MB = (TAN || SPLIT) ? 1 : T2VA_ATTN_MB_FWD;
   // row sums on the matrix cores (forward); the JVP kernel keeps them on the
   // VALU, where its register budget has room and the matrix cores do not
   static constexpr bool MFMA_SUMS = !TAN;
@@ -82,7 +90,7 @@ struct AttnCfg {
   // keys per LDS stage (one barrier each): 64 for the JVP kernel, whose
   // tangent tiles double its LDS; 128 for the forward, which then also fills
   // the 160 KB and needs half as many barriers
-  static constexpr int BN = TAN ? 64 : 128;
+  static constexpr int BN = SPLIT ? (TAN ? 4096 / DH : 64) : (TAN ? 64 : 128);
   static constexpr int SUB = BN / 32;      // 32-key sub-tiles per stage
   static constexpr int VCPR = BN / 8;      // 16-byte chunks per V^T row
   static constexpr int BM = 16 * MB * NW;  // query rows per workgroup
@@ -92,9 +100,11 @@ struct AttnCfg {
   static constexpr int K_ELEMS = BN * DH;  // K tile [BN][DH], swizzled slots
   static constexpr int V_ELEMS = DH * BN;  // V^T tile [DH][BN], swizzled slots
   static constexpr int NSTREAM = TAN ? 2 : 1;
-  // rings of three K stages ([K | dK] each) and two V^T stages ([V^T | dV^T])
-  static constexpr int KBUF_ELEMS = NSTREAM * K_ELEMS;
+  // rings of three K stages ([K | dK | K_lo] each, as present) and two V^T
+  // stages ([V^T | dV^T])
+  static constexpr int KBUF_ELEMS = (NSTREAM + (SPLIT ? 1 : 0)) * K_ELEMS;
   static constexpr int VBUF_ELEMS = NSTREAM * V_ELEMS;
+  static constexpr int KLO_AT = NSTREAM * K_ELEMS;   // K_lo's offset in a K stage
   static constexpr size_t LDS_BYTES = (size_t)(3 * KBUF_ELEMS + 2 * VBUF_ELEMS) * sizeof(bf16);
   // one direct load instruction moves 64 lanes x 16 B = 1 KB = 512 elements
   static constexpr int KCH = K_ELEMS / 512 / kLoadWaves;   // per loading wave, per operand tile
@@ -107,6 +117,8 @@ struct AttnCfg {
   static constexpr int PIECE_STATS = 2 * MB * THREADS;
   static constexpr int PIECE_O = 4 * MB * DT * THREADS;
   static constexpr int PIECE_FLOATS = PIECE_STATS + PIECE_O + (TAN ? 4 * DT * THREADS : 0);
+  static_assert(KCH >= 1 && VCH >= 1, "every loading wave moves at least one 1 KB chunk per tile");
+  static_assert(BN % 32 == 0 && (VCPR == 4 || VCPR == 8 || VCPR == 16), "32-key sub-tiles, known V^T swizzle");
 };
 
 
@@ -133,16 +145,17 @@ __device__ __forceinline__ void store_out4(const AttnParams &p, int64_t at, cons
   }
 }
 
-template <int DH, bool TAN>
-__global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_kernel(AttnParams p, int nqb,
-                                                                   int per_xcd, int total, SplitArgs sp) {
-  using C = AttnCfg<DH, TAN>;
+template <int DH, bool TAN, bool SPLIT>
+__global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_fwd_jvp_kernel(
+    AttnParams p, int nqb, int per_xcd, int total, SplitArgs sp) {
+  using C = AttnCfg<DH, TAN, SPLIT>;
   constexpr int BN = C::BN;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16 *const lds = reinterpret_cast<bf16 *>(smem_raw);
-  // LDS: K ring [3][K | dK], then V^T ring [2][V^T | dV^T]
+  // LDS: K ring [3][K | dK | K_lo], then V^T ring [2][V^T | dV^T]
   auto sK = [&](int kb) { return lds + kb * C::KBUF_ELEMS; };
   auto sKd = [&](int kb) { return lds + kb * C::KBUF_ELEMS + C::K_ELEMS; };
+  auto sKlo = [&](int kb) { return lds + kb * C::KBUF_ELEMS + C::KLO_AT; };
   auto sVT = [&](int vb) { return lds + 3 * C::KBUF_ELEMS + vb * C::VBUF_ELEMS; };
   auto sVdT = [&](int vb) { return lds + 3 * C::KBUF_ELEMS + vb * C::VBUF_ELEMS + C::V_ELEMS; };
 
@@ -206,14 +219,19 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   const float scale = p.scale;
   const float c_log2 = scale * 1.4426950408889634f;
 
-  // Q^T (and dQ^T) as B operands: lane holds Q[q_row][32 s + 8 g .. +7].
-  bf16x8 qf[C::MB][C::KSTEPS], qdf[TAN ? C::KSTEPS : 1];
+  // Q^T (and dQ^T, Q_lo^T) as B operands: lane holds Q[q_row][32 s + 8 g .. +7].
+  bf16x8 qf[C::MB][C::KSTEPS], qdf[TAN ? C::KSTEPS : 1], qlf[SPLIT ? C::MB : 1][SPLIT ? C::KSTEPS : 1];
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
     const int q_ld = min(q_row0 + 16 * mb, p.Nq - 1);
-    const bf16 *qp = p.q + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * g;
+    const int64_t q_at = (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * g;
+    const bf16 *qp = p.q + q_at;
 #pragma unroll
     for (int s = 0; s < C::KSTEPS; ++s) qf[mb][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) qlf[mb][s] = *reinterpret_cast<const bf16x8 *>(p.q_lo + q_at + 32 * s);
+    }
     if constexpr (TAN) {
       const bf16 *qdp = p.qd + (int64_t)b * p.q_bs + (int64_t)q_ld * p.q_rs + h * DH + 8 * g;
 #pragma unroll
@@ -232,11 +250,12 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
   const int64_t v_at = (int64_t)b * p.vt_bs + (int64_t)h * p.vt_hs + key0;
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.k + k_at, k_bytes);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.vt + v_at, v_bytes);
-  __amdgpu_buffer_rsrc_t rKd = rK, rVd = rV;
+  __amdgpu_buffer_rsrc_t rKd = rK, rVd = rV, rKlo = rK;
   if constexpr (TAN) {
     rKd = make_rsrc(p.kd + k_at, k_bytes);
     rVd = make_rsrc(p.vdt + v_at, v_bytes);
   }
+  if constexpr (SPLIT) rKlo = make_rsrc(p.k_lo + k_at, k_bytes);
   const int lw = wave % kLoadWaves;
   const bool loader = wave < kLoadWaves;
   // Per-lane byte offsets of this lane's 16-byte chunks (at key 0).  Chunk r
@@ -274,6 +293,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
       const int chunk = lw + kLoadWaves * r;
       load_lds16(rK, k_off(r, k0), sK(kb) + chunk * 512);
       if constexpr (TAN) load_lds16(rKd, k_off(r, k0), sKd(kb) + chunk * 512);
+      if constexpr (SPLIT) load_lds16(rKlo, k_off(r, k0), sKlo(kb) + chunk * 512);
     }
   };
   auto issue_v = [&](int vb, int k0) {
@@ -306,9 +326,11 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
 
   // ---- logits of one 32-key sub-tile u of a stage buffer ----
   // S[mb][t][r] holds key 32 u + 8 g + 4 t + r of row block mb.
+  // Split kernels add K_lo Q^T and K Q_lo^T to each logit chain.
   auto compute_s = [&](int buf, int u, floatx4 (&S)[C::MB][2], floatx4 (&Sd)[2]) {
     const bf16 *kt = sK(buf) + 32 * u * DH;
     const bf16 *kdt = sKd(buf) + 32 * u * DH;
+    const bf16 *klt = sKlo(buf) + 32 * u * DH;
     // the first k-step starts from a zero accumulator operand (no VALU clears)
     const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
     // Both key halves at each k-step: the accumulation chains of the two
@@ -329,6 +351,15 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
         for (int t = 0; t < 2; ++t) S[0][t] = mfma16(ka[t], qf[0][s], s == 0 ? zero4 : S[0][t]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) Sd[t] = mfma16(ka[t], qdf[s], Sd[t]);
+        if constexpr (SPLIT) {
+          bf16x8 kla[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) kla[t] = *reinterpret_cast<const bf16x8 *>(klt + koff(t, s));
+#pragma unroll
+          for (int t = 0; t < 2; ++t) S[0][t] = mfma16(kla[t], qf[0][s], S[0][t]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) S[0][t] = mfma16(ka[t], qlf[0][s], S[0][t]);
+        }
       }
     } else {
 #pragma unroll
@@ -340,6 +371,18 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int mb = 0; mb < C::MB; ++mb) S[mb][t] = mfma16(ka[t], qf[mb][s], s == 0 ? zero4 : S[mb][t]);
+        if constexpr (SPLIT) {
+          bf16x8 kla[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) kla[t] = *reinterpret_cast<const bf16x8 *>(klt + koff(t, s));
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb) {
+              S[mb][t] = mfma16(kla[t], qf[mb][s], S[mb][t]);
+              S[mb][t] = mfma16(ka[t], qlf[mb][s], S[mb][t]);
+            }
+        }
       }
     }
   };
@@ -697,10 +740,10 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_fwd_jvp_k
 // o = sum w_i o_i, mu = sum w_i mu_i and do = sum w_i (do_i + (mu_i - mu) o_i)
 // (each do_i is centred on its own mu_i).  Pieces are taken in key order, so
 // the result does not depend on which finished first.
-template <int DH, bool TAN>
-__global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_combine_kernel(AttnParams p, int nqb,
-                                                                   int per_xcd, int total, SplitArgs sp) {
-  using C = AttnCfg<DH, TAN>;
+template <int DH, bool TAN, bool SPLIT>
+__global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_combine_kernel(
+    AttnParams p, int nqb, int per_xcd, int total, SplitArgs sp) {
+  using C = AttnCfg<DH, TAN, SPLIT>;
   constexpr int BN = C::BN;
   const int slot = blockIdx.x;
   const int L = split_tile(slot, per_xcd, sp);
@@ -822,20 +865,20 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN>::THREADS), 1) void attn_combine_k
 
 constexpr size_t kCapPieces = 768;   // scratch for at most this many pieces
 
-template <int DH, bool TAN>
+template <int DH, bool TAN, bool SPLIT>
 size_t split_bytes(int B, int H, int Nq, bool prefix) {
-  using C = AttnCfg<DH, TAN>;
+  using C = AttnCfg<DH, TAN, SPLIT>;
   const int64_t total = (int64_t)B * H * ((Nq + C::BM - 1) / C::BM);
   const size_t pieces = std::min<size_t>(kCapPieces, (size_t)kMaxPieces * 8 * ((total + 7) / 8));
   return pieces * C::PIECE_FLOATS * sizeof(float) * (prefix && !TAN ? 2 : 1);
 }
 
-template <int DH, bool TAN>
+template <int DH, bool TAN, bool SPLIT>
 hipError_t launch_impl(const AttnParams &p, hipStream_t s) {
-  using C = AttnCfg<DH, TAN>;
+  using C = AttnCfg<DH, TAN, SPLIT>;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_jvp_kernel<DH, TAN>,
+    hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_jvp_kernel<DH, TAN, SPLIT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)C::LDS_BYTES);
     if (e != hipSuccess) return e;
@@ -851,33 +894,45 @@ hipError_t launch_impl(const AttnParams &p, hipStream_t s) {
       p.part ? p.part_bytes / (sizeof(float) * C::PIECE_FLOATS) / (two_banks ? 2 : 1) : 0;
   static int slots[kMaxDevices];
   SplitArgs sp =
-      cap ? plan_split(per_xcd, xcd_slots(attn_fwd_jvp_kernel<DH, TAN>, C::THREADS, C::LDS_BYTES, slots),
+      cap ? plan_split(per_xcd,
+                       xcd_slots(attn_fwd_jvp_kernel<DH, TAN, SPLIT>, C::THREADS, C::LDS_BYTES, slots),
                        (p.Nk + C::BN - 1) / C::BN, cap, kMinPieceKeys / C::BN)
           : SplitArgs{per_xcd, 0, 1, 0};
   sp.pbank = 8 * sp.rem * sp.k;
-  hipLaunchKernelGGL((attn_fwd_jvp_kernel<DH, TAN>), dim3(8 * (sp.n_full + sp.rem * sp.k)),
+  hipLaunchKernelGGL((attn_fwd_jvp_kernel<DH, TAN, SPLIT>), dim3(8 * (sp.n_full + sp.rem * sp.k)),
                      dim3(C::THREADS), C::LDS_BYTES, s, p, nqb, per_xcd, total, sp);
   if (sp.rem > 0) {
     if (hipError_t e = hipGetLastError()) return e;
-    hipLaunchKernelGGL((attn_combine_kernel<DH, TAN>), dim3(8 * sp.rem), dim3(C::THREADS), 0, s, p, nqb,
+    hipLaunchKernelGGL((attn_combine_kernel<DH, TAN, SPLIT>), dim3(8 * sp.rem), dim3(C::THREADS), 0, s, p, nqb,
                        per_xcd, total, sp);
   }
   return hipGetLastError();
 }
 
+template <int DH, bool SPLIT>
+hipError_t launch_dh(bool tangent, const AttnParams &p, hipStream_t s) {
+  return tangent ? launch_impl<DH, true, SPLIT>(p, s) : launch_impl<DH, false, SPLIT>(p, s);
+}
+
+template <int DH>
+size_t split_bytes_dh(int B, int H, int Nq, bool prefix) {
+  return std::max({split_bytes<DH, true, false>(B, H, Nq, prefix), split_bytes<DH, false, false>(B, H, Nq, prefix),
+                   split_bytes<DH, true, true>(B, H, Nq, prefix), split_bytes<DH, false, true>(B, H, Nq, prefix)});
+}
+
 }  // namespace
 
 hipError_t launch_attention(int dh, bool tangent, const AttnParams &p, hipStream_t s) {
-  if (dh == 128) return tangent ? launch_impl<128, true>(p, s) : launch_impl<128, false>(p, s);
-  if (dh == 64) return tangent ? launch_impl<64, true>(p, s) : launch_impl<64, false>(p, s);
+  const bool split = p.q_lo != nullptr;
+  if (split != (p.k_lo != nullptr)) return hipErrorInvalidValue;
+  if (dh == 128) return split ? launch_dh<128, true>(tangent, p, s) : launch_dh<128, false>(tangent, p, s);
+  if (dh == 64) return split ? launch_dh<64, true>(tangent, p, s) : launch_dh<64, false>(tangent, p, s);
   return hipErrorInvalidValue;
 }
 
 size_t attention_split_bytes(int dh, int B, int H, int Nq, bool prefix) {
-  if (dh == 128)
-    return std::max(split_bytes<128, true>(B, H, Nq, prefix), split_bytes<128, false>(B, H, Nq, prefix));
-  if (dh == 64)
-    return std::max(split_bytes<64, true>(B, H, Nq, prefix), split_bytes<64, false>(B, H, Nq, prefix));
+  if (dh == 128) return split_bytes_dh<128>(B, H, Nq, prefix);
+  if (dh == 64) return split_bytes_dh<64>(B, H, Nq, prefix);
   return 0;
 }
 

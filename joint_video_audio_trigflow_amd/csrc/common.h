@@ -98,10 +98,22 @@ hipError_t launch_time_linear(const float *E, int rows, int d, const bf16 *w_t, 
 // Text rows of X: for each sample, the valid text positions (mask != 0) in
 // order, converted to bf16, at rows [Nq, Nq + count); rows up to Nq + Nt are
 // zero.  With zero_only, every text row is zero (tangent of the text).
-// nk[b] = Nq + count (written when nk != nullptr).
+// nk[b] = Nq + count (written when nk != nullptr).  Rows are x_row_stride
+// elements apart; with split, columns [d, 2d) of a row receive the low half
+// bf16(x - bf16(x)) of each value (zero for bf16 text).
 hipError_t launch_text_rows(int B, int Nq, int Nt, int d, const void *text, int text_dt,
-                            const uint8_t *mask, bf16 *X, int64_t x_batch_stride, int zero_only,
-                            int32_t *nk, hipStream_t s);
+                            const uint8_t *mask, bf16 *X, int64_t x_batch_stride, int64_t x_row_stride,
+                            int split, int zero_only, int32_t *nk, hipStream_t s);
+
+// Split rows: fp32 src [nb][rows][w] (strides s_bs, s_rs) -> bf16 dst rows
+// [hi | lo] of 2w elements (strides d_bs, d_rs): hi = bf16(x), lo = bf16(x - hi).
+// w a multiple of 8; strides multiples of 8.
+hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 *dst, int64_t d_bs,
+                             int64_t d_rs, int nb, int rows, int w, hipStream_t s);
+
+// W2 [n][2k] = [W | W] for bf16 W [n][k] (k a multiple of 8): the weight of a
+// product whose operand rows are [hi | lo] pairs.
+hipError_t launch_dup_cols(const bf16 *W, bf16 *W2, int n, int k, hipStream_t s);
 
 // nk[b] = value for every sample (used when there is no text).
 hipError_t launch_fill_nk(int32_t *nk, int B, int value, hipStream_t s);
@@ -167,6 +179,8 @@ hipError_t launch_mix(int B, float a, const float *x, float c, const float *y, f
                       hipStream_t s);
 
 // C = A W^T (+ bias) for `batch` independent problems.
+// c_dt: 0 bf16, 1 fp32, 2 split bf16: column c < n_split of a row receives
+// hi = bf16(x) and column c + n_split lo = bf16(x - hi).
 struct GemmParams {
   const bf16 *A; int64_t lda, a_bs;
   const bf16 *W; int64_t ldw, w_bs;       // W [N, K]; w_bs = 0 shares it across batches
@@ -182,9 +196,11 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t s);
 // other): a small one then runs beside the other instead of after it.
 hipError_t launch_gemm_pair(const GemmParams &a, const GemmParams &b, hipStream_t s);
 
-// Attention forward (+JVP).
+// Attention forward (+JVP).  With q_lo and k_lo (q's and k's strides) the
+// logits are scale (q k^T + q k_lo^T + q_lo k^T): the split-precision kernels.
 struct AttnParams {
   const bf16 *q, *k, *vt, *qd, *kd, *vdt;
+  const bf16 *q_lo = nullptr, *k_lo = nullptr;
   const int32_t *nk;
   void *o, *od;
   // forward only (nullable): o2 receives the output over the first nk_split

@@ -155,13 +155,15 @@ __global__ __launch_bounds__(kThreads) void time_linear_kernel(const float *E, i
 
 // ---------------------------------------------------------------------------
 // Text rows: block (j, b) writes row Nq + j of sample b: the j-th valid text
-// position if there is one, else zeros.
+// position if there is one, else zeros.  With split, the row holds the value
+// rounded to bf16 in columns [0, d) and the rounding remainder, rounded to
+// bf16, in columns [d, 2d).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void text_rows_kernel(int Nq, int Nt, int d, const T *text,
                                                              const uint8_t *mask, bf16 *X,
-                                                             int64_t x_bs, int zero_only,
-                                                             int32_t *nk) {
+                                                             int64_t x_bs, int64_t x_rs, int split,
+                                                             int zero_only, int32_t *nk) {
   const int j = blockIdx.x, bi = blockIdx.y;
   __shared__ int src;
   __shared__ int count;
@@ -181,20 +183,46 @@ __global__ __launch_bounds__(kThreads) void text_rows_kernel(int Nq, int Nt, int
   }
   __syncthreads();
   if (j == 0 && threadIdx.x == 0 && nk != nullptr) nk[bi] = Nq + count;
-  bf16 *dst = X + (int64_t)bi * x_bs + (int64_t)(Nq + j) * d;
-  if (src < 0) {
-    for (int c0 = threadIdx.x * 8; c0 < d; c0 += kThreads * 8) {
-      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      store8(dst + c0, z);
-    }
-  } else {
-    const T *row = text + ((int64_t)bi * Nt + src) * d;
-    for (int c0 = threadIdx.x * 8; c0 < d; c0 += kThreads * 8) {
-      float f[8];
-      load8(row + c0, f);
-      store8(dst + c0, f);
+  bf16 *dst = X + (int64_t)bi * x_bs + (int64_t)(Nq + j) * x_rs;
+  const T *row = src < 0 ? nullptr : text + ((int64_t)bi * Nt + src) * d;
+  for (int c0 = threadIdx.x * 8; c0 < d; c0 += kThreads * 8) {
+    float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (row) load8(row + c0, f);
+    store8(dst + c0, f);
+    if (split) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] -= (float)(bf16)f[i];
+      store8(dst + d + c0, f);
     }
   }
+}
+
+// Rows of w fp32 values -> rows [hi | lo] of 2w bf16 values.
+__global__ __launch_bounds__(kThreads) void split_rows_kernel(const float *src, int64_t s_bs, int64_t s_rs,
+                                                              bf16 *dst, int64_t d_bs, int64_t d_rs,
+                                                              int rows, int w) {
+  const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  const int64_t per = (int64_t)rows * w;
+  if (i0 >= per) return;
+  const int bi = blockIdx.y;
+  const int64_t r = i0 / w, c = i0 - r * w;   // w is a multiple of 8: one row per group
+  float f[8], lo[8];
+  load8(src + bi * s_bs + r * s_rs + c, f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lo[i] = f[i] - (float)(bf16)f[i];
+  bf16 *o = dst + bi * d_bs + r * d_rs + c;
+  store8(o, f);
+  store8(o + w, lo);
+}
+
+// [W | W]: row i of W2 holds row i of W twice.
+__global__ __launch_bounds__(kThreads) void dup_cols_kernel(const bf16 *W, bf16 *W2, int n, int k) {
+  const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (i0 >= (int64_t)n * k) return;
+  const int64_t r = i0 / k, c = i0 - r * k;
+  const uint4 v = *reinterpret_cast<const uint4 *>(W + i0);
+  *reinterpret_cast<uint4 *>(W2 + r * 2 * k + c) = v;
+  *reinterpret_cast<uint4 *>(W2 + r * 2 * k + k + c) = v;
 }
 
 __global__ __launch_bounds__(kThreads) void cast_kernel(const float *src, bf16 *dst, int64_t n) {
@@ -400,16 +428,33 @@ hipError_t launch_time_linear(const float *E, int rows, int d, const bf16 *w_t, 
 }
 
 hipError_t launch_text_rows(int B, int Nq, int Nt, int d, const void *text, int text_dt,
-                            const uint8_t *mask, bf16 *X, int64_t x_batch_stride, int zero_only,
-                            int32_t *nk, hipStream_t s) {
+                            const uint8_t *mask, bf16 *X, int64_t x_batch_stride, int64_t x_row_stride,
+                            int split, int zero_only, int32_t *nk, hipStream_t s) {
   if (Nt == 0) return hipSuccess;  // no text rows; the host sets nk = Nq itself
   dim3 grid(Nt, B);
   if (text_dt == 0)
     hipLaunchKernelGGL(text_rows_kernel<bf16>, grid, dim3(kThreads), 0, s, Nq, Nt, d,
-                       (const bf16 *)text, mask, X, x_batch_stride, zero_only, nk);
+                       (const bf16 *)text, mask, X, x_batch_stride, x_row_stride, split, zero_only, nk);
   else
     hipLaunchKernelGGL(text_rows_kernel<float>, grid, dim3(kThreads), 0, s, Nq, Nt, d,
-                       (const float *)text, mask, X, x_batch_stride, zero_only, nk);
+                       (const float *)text, mask, X, x_batch_stride, x_row_stride, split, zero_only, nk);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 *dst, int64_t d_bs,
+                             int64_t d_rs, int nb, int rows, int w, hipStream_t s) {
+  const int64_t per = (int64_t)rows * w;
+  if (per <= 0 || nb <= 0) return hipSuccess;
+  dim3 grid((unsigned)((per + kChunk - 1) / kChunk), nb);
+  hipLaunchKernelGGL(split_rows_kernel, grid, dim3(kThreads), 0, s, src, s_bs, s_rs, dst, d_bs, d_rs, rows, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_dup_cols(const bf16 *W, bf16 *W2, int n, int k, hipStream_t s) {
+  const int64_t total = (int64_t)n * k;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dup_cols_kernel, dim3((unsigned)((total + kChunk - 1) / kChunk)), dim3(kThreads), 0, s, W,
+                     W2, n, k);
   return hipGetLastError();
 }
 

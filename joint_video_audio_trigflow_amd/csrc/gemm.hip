@@ -22,6 +22,20 @@ namespace t2va {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 64;
+
+// One element of C at offset `off`: bf16, fp32, or a split pair (bf16(x) at
+// off, bf16(x - bf16(x)) at off + n_split).
+__device__ __forceinline__ void store_c(const GemmParams &p, int64_t off, float val) {
+  if (p.c_dt == 0) {
+    reinterpret_cast<bf16 *>(p.C)[off] = (bf16)val;
+  } else if (p.c_dt == 1) {
+    reinterpret_cast<float *>(p.C)[off] = val;
+  } else {
+    const bf16 hi = (bf16)val;
+    reinterpret_cast<bf16 *>(p.C)[off] = hi;
+    reinterpret_cast<bf16 *>(p.C)[off + p.n_split] = (bf16)(val - (float)hi);
+  }
+}
 constexpr int LROW = BK + 8;  // padded LDS row (elements): 144 B, conflict-free 16-B reads
 constexpr int kThreads = 256;
 constexpr int kStageElems = (BM + BN) * LROW;
@@ -130,10 +144,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p1, Gemm
           if (row < p.M) {
             const float val = acc[i][j][v] + bcol;
             const int64_t off = (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col;
-            if (p.c_dt == 0)
-              reinterpret_cast<bf16 *>(p.C)[off] = (bf16)val;
-            else
-              reinterpret_cast<float *>(p.C)[off] = val;
+            store_c(p, off, val);
           }
         }
       }
@@ -473,10 +484,7 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
           if (row < p.M) {
             const float val = acc[i][j][v] + bcol;
             const int64_t off = (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col;
-            if (p.c_dt == 0)
-              reinterpret_cast<bf16 *>(p.C)[off] = (bf16)val;
-            else
-              reinterpret_cast<float *>(p.C)[off] = val;
+            store_c(p, off, val);
           }
         }
       }

@@ -152,12 +152,43 @@ hipError_t prepare_weights(const t2va_block_weights *const *wb, int count, int w
   return hipSuccess;
 }
 
+// Split precision: the input and QKV projections contract [hi | lo] operand
+// rows, so their weights are used as [W | W] (w_in_v [d, 2Cv], w_in_a
+// [d, 2Ca], w_qkv [3d, 2d]), built into the workspace per call.
+void dup_weight_elems(int Cv, int Ca, int d, size_t *n) {
+  const size_t D = d;
+  n[0] = D * 2 * Cv;
+  n[1] = D * 2 * Ca;
+  n[2] = 3 * D * 2 * D;
+}
+size_t dup_weight_bytes(int Cv, int Ca, int d, int blocks) {
+  size_t n[3];
+  dup_weight_elems(Cv, Ca, d, n);
+  size_t c = 0;
+  for (int i = 0; i < 3; ++i) c += align_up(n[i], 128);
+  return (size_t)blocks * c * sizeof(bf16);
+}
+hipError_t prepare_dup(const bf16 *W[][6], int count, int Cv, int Ca, int d, bf16 *dst, const bf16 *Wd[][3],
+                       hipStream_t s) {
+  size_t n[3];
+  dup_weight_elems(Cv, Ca, d, n);
+  const int rows[3] = {d, d, 3 * d}, cols[3] = {Cv, Ca, d}, src[3] = {0, 1, 3};
+  for (int i = 0; i < count; ++i)
+    for (int j = 0; j < 3; ++j) {
+      if (hipError_t e = launch_dup_cols(W[i][src[j]], dst, rows[j], cols[j], s)) return e;
+      Wd[i][j] = dst;
+      dst += align_up(n[j], 128);
+    }
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------------------------
 // Workspace layout of t2va_scm_target.
 // ---------------------------------------------------------------------------
 struct Layout {
   int Nq, N_all, dh, ldv, nblk_v, nblk_a;
-  size_t wts, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v, x0S_a, part_v, part_a, apart;
+  bool split;   // T2VA_PREC_SPLIT: [hi | lo] rows for z, X and Q|K
+  size_t wts, wdup, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v, x0S_a, part_v, part_a, apart;
   size_t total, apart_bytes;
   size_t w_elems[6];  // per-block weight element counts
 };
@@ -180,13 +211,18 @@ Layout make_layout(const t2va_scm_desc &d) {
     off = align_up(off + bytes, 256);
     return o;
   };
+  L.split = d.precision == T2VA_PREC_SPLIT;
+  const size_t sp = L.split ? 2 : 1;   // [hi | lo] rows are twice as wide
   L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
-  L.zv = take(2 * B * d.Nv * d.Cv * sizeof(bf16));
-  L.za = take(2 * B * d.Na * d.Ca * sizeof(bf16));
+  L.wdup = take(L.split ? dup_weight_bytes(d.Cv, d.Ca, d.d, 2) : 0);
+  L.zf_v = take(L.split ? 2 * B * d.Nv * d.Cv * sizeof(float) : 0);
+  L.zf_a = take(L.split ? 2 * B * d.Na * d.Ca * sizeof(float) : 0);
+  L.zv = take(2 * B * d.Nv * d.Cv * sp * sizeof(bf16));
+  L.za = take(2 * B * d.Na * d.Ca * sp * sizeof(bf16));
   L.E = take(2 * B * D * sizeof(float));
   L.tau = take(2 * B * D * sizeof(float));
-  L.X = take(2 * B * L.N_all * D * sizeof(bf16));
-  L.QK = take(2 * B * L.N_all * 2 * D * sizeof(bf16));
+  L.X = take(2 * B * L.N_all * D * sp * sizeof(bf16));
+  L.QK = take(2 * B * L.N_all * 2 * D * sp * sizeof(bf16));
   L.VT = take(2 * B * D * (size_t)L.ldv * sizeof(bf16));
   L.nk = take(B * sizeof(int32_t));
   L.O = take(2 * B * L.Nq * D * sizeof(bf16));
@@ -288,6 +324,8 @@ t2va_status check_desc(const t2va_scm_desc *d) {
     return st;
   if (d->param != T2VA_PARAM_X0 && d->param != T2VA_PARAM_RF)
     return fail(T2VA_INVALID_ARG, "param = %d must be T2VA_PARAM_X0 or T2VA_PARAM_RF", d->param);
+  if (d->precision != T2VA_PREC_BF16 && d->precision != T2VA_PREC_SPLIT)
+    return fail(T2VA_INVALID_ARG, "precision = %d must be T2VA_PREC_BF16 or T2VA_PREC_SPLIT", d->precision);
   if (!(d->gamma >= 0.0 && d->gamma <= 1.0))
     return fail(T2VA_INVALID_ARG, "gamma = %g outside [0, 1]", d->gamma);
   if (!(d->eps_scm > 0.0) || !isfinite(d->eps_scm))
@@ -314,7 +352,9 @@ t2va_status check_weights(const t2va_block_weights *const *wb, int n, const char
 // Workspace layout of t2va_dmd_target.
 struct DmdLayout {
   int ldv, nblk_v, nblk_a;
-  size_t wts, zv, za, E, tau, X, QK, VT, nk, nk_null, O, xT_v, xT_a, xF_v, xF_a, pa_v, pa_a, ps_v, ps_a, apart;
+  bool split;
+  size_t wts, wdup, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, nk_null, O, xT_v, xT_a, xF_v, xF_a, pa_v, pa_a, ps_v,
+      ps_a, apart;
   size_t total, apart_bytes;
   size_t w_elems[6];
 };
@@ -336,13 +376,18 @@ DmdLayout make_dmd_layout(const t2va_dmd_desc &d) {
     off = align_up(off + bytes, 256);
     return o;
   };
+  L.split = d.precision == T2VA_PREC_SPLIT;
+  const size_t sp = L.split ? 2 : 1;
   L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
-  L.zv = take(B * nv * sizeof(bf16));
-  L.za = take(B * na * sizeof(bf16));
+  L.wdup = take(L.split ? dup_weight_bytes(d.Cv, d.Ca, d.d, 2) : 0);
+  L.zf_v = take(L.split ? B * nv * sizeof(float) : 0);
+  L.zf_a = take(L.split ? B * na * sizeof(float) : 0);
+  L.zv = take(B * nv * sp * sizeof(bf16));
+  L.za = take(B * na * sp * sizeof(bf16));
   L.E = take(2 * B * D * sizeof(float));
   L.tau = take(B * D * sizeof(float));
-  L.X = take(B * N_all * D * sizeof(bf16));
-  L.QK = take(B * N_all * 2 * D * sizeof(bf16));
+  L.X = take(B * N_all * D * sp * sizeof(bf16));
+  L.QK = take(B * N_all * 2 * D * sp * sizeof(bf16));
   L.VT = take(B * D * (size_t)L.ldv * sizeof(bf16));
   L.nk = take(B * sizeof(int32_t));
   L.nk_null = take(B * sizeof(int32_t));
@@ -368,6 +413,8 @@ t2va_status check_dmd_desc(const t2va_dmd_desc *d) {
     return st;
   if (d->param != T2VA_PARAM_X0 && d->param != T2VA_PARAM_RF)
     return fail(T2VA_INVALID_ARG, "param = %d must be T2VA_PARAM_X0 or T2VA_PARAM_RF", d->param);
+  if (d->precision != T2VA_PREC_BF16 && d->precision != T2VA_PREC_SPLIT)
+    return fail(T2VA_INVALID_ARG, "precision = %d must be T2VA_PREC_BF16 or T2VA_PREC_SPLIT", d->precision);
   if (!isfinite(d->cfg_v) || !isfinite(d->cfg_a))
     return fail(T2VA_INVALID_ARG, "guidance scales must be finite");
   if (!(d->eps_dmd > 0.0) || !isfinite(d->eps_dmd))
@@ -417,6 +464,8 @@ struct PhaseScope {
 // unconditional outputs).
 struct Block {
   int B, Nv, Na, Cv, Ca, D, H, dh, Nq, NA, ldv;
+  bool split;        // T2VA_PREC_SPLIT: z, X and Q|K rows are [hi | lo] pairs
+  int64_t xs, qks;   // row strides of X (d, or 2d split) and QK (2d, or 4d split)
   int64_t nv, na, x_bs, qk_bs, vt_hs, vt_bs, o_bs;
   hipStream_t s;
   bool prof;
@@ -424,13 +473,15 @@ struct Block {
   size_t apart_bytes = 0;
 
   Block(int B_, int Nv_, int Na_, int Nt, int Cv_, int Ca_, int d, int H_, int ldv_, hipStream_t s_,
-        bool prof_)
+        bool prof_, bool split_ = false)
       : B(B_), Nv(Nv_), Na(Na_), Cv(Cv_), Ca(Ca_), D(d), H(H_), dh(d / H_), Nq(Nv_ + Na_),
-        NA(Nv_ + Na_ + Nt), ldv(ldv_), s(s_), prof(prof_) {
+        NA(Nv_ + Na_ + Nt), ldv(ldv_), split(split_), s(s_), prof(prof_) {
     nv = (int64_t)Nv * Cv;
     na = (int64_t)Na * Ca;
-    x_bs = (int64_t)NA * D;
-    qk_bs = (int64_t)NA * 2 * D;
+    xs = split ? 2 * D : D;
+    qks = split ? 4 * D : 2 * D;
+    x_bs = (int64_t)NA * xs;
+    qk_bs = (int64_t)NA * qks;
     vt_hs = (int64_t)dh * ldv;
     vt_bs = (int64_t)H * vt_hs;
     o_bs = (int64_t)Nq * D;
@@ -461,9 +512,20 @@ struct Block {
   }
 
   // X rows [0, Nq) = [z^v W_in_v^T; z^a W_in_a^T] + tau[b]; then Q|K row-major
-  // into QK and V dh-major into VT, for `batch` problems.
-  t2va_status project_in(const bf16 *const *W, const bf16 *zv, const bf16 *za, const float *tau,
-                         bf16 *X, bf16 *QK, bf16 *VT, int batch) const {
+  // into QK and V dh-major into VT, for `batch` problems.  Split: z rows are
+  // [hi | lo] (2 C_m wide) against Wd = [W | W], X and Q|K are written as
+  // [hi | lo] pairs (X rows [X_hi | X_lo], QK rows [Q_hi | K_hi | Q_lo | K_lo]).
+  t2va_status project_in(const bf16 *const *W, const bf16 *const *Wd, const bf16 *zv, const bf16 *za,
+                         const float *tau, bf16 *X, bf16 *QK, bf16 *VT, int batch) const {
+    if (split) {
+      if (t2va_status st = gemm(zv, 2 * Cv, 2 * nv, Wd[0], 2 * Cv, X, xs, x_bs, 2, tau, D, Nv, D, 2 * Cv, batch,
+                                nullptr, D))
+        return st;
+      if (t2va_status st = gemm(za, 2 * Ca, 2 * na, Wd[1], 2 * Ca, X + (int64_t)Nv * xs, xs, x_bs, 2, tau, D, Na,
+                                D, 2 * Ca, batch, nullptr, D))
+        return st;
+      return gemm(X, xs, x_bs, Wd[2], 2 * D, QK, qks, qk_bs, 2, nullptr, 0, NA, 3 * D, 2 * D, batch, VT, 2 * D);
+    }
     if (t2va_status st = gemm(zv, Cv, nv, W[0], Cv, X, D, x_bs, 0, tau, D, Nv, D, Cv, batch, nullptr, D))
       return st;
     if (t2va_status st = gemm(za, Ca, na, W[1], Ca, X + (int64_t)Nv * D, D, x_bs, 0, tau, D, Na, D,
@@ -490,12 +552,14 @@ struct Block {
                         int phase, float *lse = nullptr, bf16 *O_prefix = nullptr, int nk_split = 0) const {
     AttnParams p;
     p.q = QK; p.k = QK + D; p.vt = VT;
+    p.q_lo = split ? QK + 2 * D : nullptr;
+    p.k_lo = split ? QK + 3 * D : nullptr;
     p.qd = tan ? QK + (int64_t)B * qk_bs : nullptr;
     p.kd = tan ? QK + (int64_t)B * qk_bs + D : nullptr;
     p.vdt = tan ? VT + (int64_t)B * vt_bs : nullptr;
     p.nk = nk; p.o = O; p.od = tan ? O + (int64_t)B * o_bs : nullptr; p.lse = lse;
     p.o2 = O_prefix; p.nk_split = nk_split;
-    p.q_bs = qk_bs; p.q_rs = 2 * D; p.k_bs = qk_bs; p.k_rs = 2 * D;
+    p.q_bs = qk_bs; p.q_rs = qks; p.k_bs = qk_bs; p.k_rs = qks;
     p.vt_bs = vt_bs; p.vt_hs = vt_hs; p.vt_rs = ldv;
     p.o_bs = o_bs; p.o_rs = D;
     p.B = B; p.H = H; p.Nq = Nq; p.Nk = NA;
@@ -545,7 +609,7 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
                     float *loss, void *workspace, float *lse_student, const bf16 *(&W)[2][6],
                     hipStream_t s, bool prof) {
   char *ws = (char *)workspace;
-  Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
+  Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof, L.split);
   blk.apart = (float *)(ws + L.apart);
   blk.apart_bytes = L.apart_bytes;
   const int B = d.B, D = d.d, Nq = L.Nq;
@@ -553,8 +617,11 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   const CoefTable coef = make_coef(B, t_host, d.beta, d.gamma, d.param);
 
   HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
+  const bf16 *Wd[2][3] = {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}};
+  if (L.split) HIP_TRY(prepare_dup(W, 2, d.Cv, d.Ca, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
+  float *zf_v = (float *)(ws + L.zf_v), *zf_a = (float *)(ws + L.zf_a);
   float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
   bf16 *X = (bf16 *)(ws + L.X), *QK = (bf16 *)(ws + L.QK), *VT = (bf16 *)(ws + L.VT);
   bf16 *O = (bf16 *)(ws + L.O);
@@ -563,38 +630,55 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   float *x0S_v = (float *)(ws + L.x0S_v), *x0S_a = (float *)(ws + L.x0S_a);
   float *part_v = (float *)(ws + L.part_v), *part_a = (float *)(ws + L.part_a);
 
-  // z_t = cos t z0 + sin t eps (bf16 GEMM input), half 0 of zv / za.
-  HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v,
-                          nullptr, zv, nv, nv, 0, nv, s), "noise");
-  HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a,
-                          nullptr, za, na, na, 0, na, s), "noise");
+  // The block's latent token rows of batch half `half` (0: z_t, 1: F_T) from
+  // the trigflow op: bf16, or in split precision fp32 split into [hi | lo].
+  auto token_rows = [&](int op, int half, const float *x0_v, const float *x0_a) -> t2va_status {
+    const int64_t xs_v = op == 2 ? nv : 0, xs_a = op == 2 ? na : 0;
+    if (!L.split) {
+      HIP_TRY(launch_trigflow(op, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v, x0_v,
+                              zv + (int64_t)half * B * nv, nv, nv, xs_v, nv, s), "token rows");
+      HIP_TRY(launch_trigflow(op, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a, x0_a,
+                              za + (int64_t)half * B * na, na, na, xs_a, na, s), "token rows");
+      return T2VA_OK;
+    }
+    float *fv = zf_v + (int64_t)half * B * nv, *fa = zf_a + (int64_t)half * B * na;
+    HIP_TRY(launch_trigflow(op, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, z0_v, eps_v, x0_v, fv, nv, nv,
+                            xs_v, nv, s), "token rows");
+    HIP_TRY(launch_trigflow(op, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, z0_a, eps_a, x0_a, fa, na, na,
+                            xs_a, na, s), "token rows");
+    HIP_TRY(launch_split_rows(fv, nv, d.Cv, zv + (int64_t)half * B * 2 * nv, 2 * nv, 2 * d.Cv, B, d.Nv, d.Cv, s),
+            "split rows");
+    HIP_TRY(launch_split_rows(fa, na, d.Ca, za + (int64_t)half * B * 2 * na, 2 * na, 2 * d.Ca, B, d.Na, d.Ca, s),
+            "split rows");
+    return T2VA_OK;
+  };
+
+#define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
+  // z_t = cos t z0 + sin t eps (the GEMM input), half 0 of zv / za.
+  T2VA_CALL(token_rows(0, 0, nullptr, nullptr));
   HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
   HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
   if (d.Nt > 0)
-    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, 0, nk, s), "text rows");
+    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, blk.xs, L.split, 0, nk, s),
+            "text rows");
   else
     HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
 
-#define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
-
   // ---------------- teacher: x0_T = G_T(z_t, t, c) ----------------
-  T2VA_CALL(blk.project_in(W[0], zv, za, tau, X, QK, VT, B));
+  T2VA_CALL(blk.project_in(W[0], Wd[0], zv, za, tau, X, QK, VT, B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
   T2VA_CALL(blk.project_out(W[0], O, x0T_v, x0T_a, B));
 
-  // ---------------- F_T (tangent of the student's latent inputs) ----------------
-  HIP_TRY(launch_trigflow(2, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v, x0T_v,
-                          zv + (int64_t)B * nv, nv, nv, nv, nv, s), "teacher field");
-  HIP_TRY(launch_trigflow(2, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a, x0T_a,
-                          za + (int64_t)B * na, na, na, na, na, s), "teacher field");
+  // ---------------- F_T (tangent of the student's latent inputs), half 1 ----------------
+  T2VA_CALL(token_rows(2, 1, x0T_v, x0T_a));
 
   // ---------------- student: G_S and its JVP ----------------
   // Batches [0, B) carry the primal rows, [B, 2B) their tangents.
   HIP_TRY(launch_time_linear(E, 2 * B, D, W[1][2], tau, s), "student time linear");
   if (d.Nt > 0)
     HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X + (int64_t)B * blk.x_bs,
-                             blk.x_bs, 1, nullptr, s), "tangent text rows");
-  T2VA_CALL(blk.project_in(W[1], zv, za, tau, X, QK, VT, 2 * B));
+                             blk.x_bs, blk.xs, L.split, 1, nullptr, s), "tangent text rows");
+  T2VA_CALL(blk.project_in(W[1], Wd[1], zv, za, tau, X, QK, VT, 2 * B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, true, T2VA_PHASE_STUDENT_ATTN, lse_student));
   T2VA_CALL(blk.project_out(W[1], O, x0S_v, x0S_a, 2 * B));
 #undef T2VA_CALL
@@ -623,6 +707,62 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   np.norms = norms; np.loss = loss;
   np.eps = d.eps_scm; np.w[0] = d.w_v; np.w[1] = d.w_a;
   HIP_TRY(launch_normalise(B, np, s), "normalise");
+  return T2VA_OK;
+}
+
+// The standalone attention entry points (validated here; no workspace, so
+// every tile runs whole).  split: the logits also take q_lo and k_lo.
+t2va_status attn_entry(const t2va_attn_desc *desc, const void *q, const void *q_lo, const void *k,
+                       const void *k_lo, const void *vt, const void *qd, const void *kd, const void *vdt,
+                       const int32_t *nk_valid, void *o, void *od, float *lse, t2va_stream stream, bool split) {
+  if (!desc) return fail(T2VA_INVALID_ARG, "desc is NULL");
+  const t2va_attn_desc &d = *desc;
+  if (d.dh != 64 && d.dh != 128) return fail(T2VA_UNSUPPORTED_SHAPE, "dh = %d must be 64 or 128", d.dh);
+  if (d.B < 1 || d.H < 1 || d.Nq < 1 || d.Nk < 1)
+    return fail(T2VA_UNSUPPORTED_SHAPE, "B, H, Nq and Nk must be >= 1");
+  if (!q || !k || !vt || !nk_valid || !o) return fail(T2VA_INVALID_ARG, "q, k, vt, nk_valid and o are required");
+  if (split && (!q_lo || !k_lo)) return fail(T2VA_INVALID_ARG, "q_lo and k_lo are required");
+  const bool tan = d.has_tangent != 0;
+  if (tan && (!qd || !kd || !vdt || !od))
+    return fail(T2VA_INVALID_ARG, "has_tangent needs qd, kd, vdt and od");
+  if (!tan && (qd || kd || vdt || od))
+    return fail(T2VA_INVALID_ARG, "tangent pointers given with has_tangent = 0");
+  if (!valid_dtype(d.out_dtype)) return fail(T2VA_INVALID_ARG, "bad out_dtype");
+  if (!(d.scale >= 0.f) || !isfinite(d.scale))
+    return fail(T2VA_INVALID_ARG, "scale = %g must be finite and >= 0 (0: 1/sqrt(dh))", (double)d.scale);
+  const void *ptrs[] = {q, q_lo, k, k_lo, vt, qd, kd, vdt, nk_valid, o, od};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(T2VA_INVALID_ARG, "operands must be 16-byte aligned");
+  const int64_t strides[] = {d.q_batch_stride, d.q_row_stride, d.k_batch_stride, d.k_row_stride,
+                             d.vt_batch_stride, d.vt_head_stride, d.vt_row_stride,
+                             d.o_batch_stride, d.o_row_stride};
+  for (int64_t st : strides)
+    if (st < 0 || st % 8) return fail(T2VA_INVALID_ARG, "strides must be non-negative multiples of 8");
+  if (d.vt_row_stride < ((d.Nk + 63) / 64) * 64)
+    return fail(T2VA_INVALID_ARG, "vt_row_stride %lld < round_up(Nk, 64)", (long long)d.vt_row_stride);
+  // Per-(sample, head) byte offsets must fit the 32-bit buffer addressing: the
+  // kernels address K rows up to one 128-key stage past the last key, and
+  // every V^T row of a head.
+  if ((int64_t)(d.Nk + 128) * d.k_row_stride * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)d.dh * d.vt_row_stride * 2 >= ((int64_t)1 << 31))
+    return fail(T2VA_UNSUPPORTED_SHAPE, "K or V^T extent per (sample, head) exceeds 2 GiB");
+  if (d.q_row_stride < (int64_t)d.H * d.dh || d.k_row_stride < (int64_t)d.H * d.dh ||
+      d.o_row_stride < (int64_t)d.H * d.dh)
+    return fail(T2VA_INVALID_ARG, "row strides must cover H*dh elements");
+  AttnParams p;
+  p.q = (const bf16 *)q; p.k = (const bf16 *)k; p.vt = (const bf16 *)vt;
+  p.q_lo = (const bf16 *)q_lo; p.k_lo = (const bf16 *)k_lo;
+  p.qd = (const bf16 *)qd; p.kd = (const bf16 *)kd; p.vdt = (const bf16 *)vdt;
+  p.nk = nk_valid; p.o = o; p.od = od; p.lse = lse;
+  p.o2 = nullptr; p.nk_split = 0;
+  p.q_bs = d.q_batch_stride; p.q_rs = d.q_row_stride;
+  p.k_bs = d.k_batch_stride; p.k_rs = d.k_row_stride;
+  p.vt_bs = d.vt_batch_stride; p.vt_hs = d.vt_head_stride; p.vt_rs = d.vt_row_stride;
+  p.o_bs = d.o_batch_stride; p.o_rs = d.o_row_stride;
+  p.B = d.B; p.H = d.H; p.Nq = d.Nq; p.Nk = d.Nk;
+  p.out_dt = d.out_dtype;
+  p.scale = d.scale != 0.f ? d.scale : (float)(1.0 / sqrt((double)d.dh));
+  HIP_TRY(launch_attention(d.dh, tan, p, (hipStream_t)stream), "attention kernel launch");
   return T2VA_OK;
 }
 
@@ -661,51 +801,15 @@ t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, c
                                     const void *vdt, const int32_t *nk_valid, void *o, void *od,
                                     float *lse, t2va_stream stream) {
   g_err.clear();
-  if (!desc) return fail(T2VA_INVALID_ARG, "desc is NULL");
-  const t2va_attn_desc &d = *desc;
-  if (d.dh != 64 && d.dh != 128) return fail(T2VA_UNSUPPORTED_SHAPE, "dh = %d must be 64 or 128", d.dh);
-  if (d.B < 1 || d.H < 1 || d.Nq < 1 || d.Nk < 1)
-    return fail(T2VA_UNSUPPORTED_SHAPE, "B, H, Nq and Nk must be >= 1");
-  if (!q || !k || !vt || !nk_valid || !o) return fail(T2VA_INVALID_ARG, "q, k, vt, nk_valid and o are required");
-  const bool tan = d.has_tangent != 0;
-  if (tan && (!qd || !kd || !vdt || !od))
-    return fail(T2VA_INVALID_ARG, "has_tangent needs qd, kd, vdt and od");
-  if (!tan && (qd || kd || vdt || od))
-    return fail(T2VA_INVALID_ARG, "tangent pointers given with has_tangent = 0");
-  if (!valid_dtype(d.out_dtype)) return fail(T2VA_INVALID_ARG, "bad out_dtype");
-  if (!(d.scale >= 0.f) || !isfinite(d.scale))
-    return fail(T2VA_INVALID_ARG, "scale = %g must be finite and >= 0 (0: 1/sqrt(dh))", (double)d.scale);
-  const void *ptrs[] = {q, k, vt, qd, kd, vdt, nk_valid, o, od};
-  for (const void *p : ptrs)
-    if (p && !aligned16(p)) return fail(T2VA_INVALID_ARG, "operands must be 16-byte aligned");
-  const int64_t strides[] = {d.q_batch_stride, d.q_row_stride, d.k_batch_stride, d.k_row_stride,
-                             d.vt_batch_stride, d.vt_head_stride, d.vt_row_stride,
-                             d.o_batch_stride, d.o_row_stride};
-  for (int64_t s : strides)
-    if (s < 0 || s % 8) return fail(T2VA_INVALID_ARG, "strides must be non-negative multiples of 8");
-  if (d.vt_row_stride < ((d.Nk + 63) / 64) * 64)
-    return fail(T2VA_INVALID_ARG, "vt_row_stride %lld < round_up(Nk, 64)", (long long)d.vt_row_stride);
-  // per-(sample, head) byte offsets must fit the 32-bit buffer addressing
-  if ((int64_t)(d.Nk + 64) * d.k_row_stride * 2 >= ((int64_t)1 << 31) ||
-      (int64_t)d.dh * d.vt_row_stride * 2 >= ((int64_t)1 << 31))
-    return fail(T2VA_UNSUPPORTED_SHAPE, "K or V^T extent per (sample, head) exceeds 2 GiB");
-  if (d.q_row_stride < (int64_t)d.H * d.dh || d.k_row_stride < (int64_t)d.H * d.dh ||
-      d.o_row_stride < (int64_t)d.H * d.dh)
-    return fail(T2VA_INVALID_ARG, "row strides must cover H*dh elements");
-  AttnParams p;
-  p.q = (const bf16 *)q; p.k = (const bf16 *)k; p.vt = (const bf16 *)vt;
-  p.qd = (const bf16 *)qd; p.kd = (const bf16 *)kd; p.vdt = (const bf16 *)vdt;
-  p.nk = nk_valid; p.o = o; p.od = od; p.lse = lse;
-  p.o2 = nullptr; p.nk_split = 0;
-  p.q_bs = d.q_batch_stride; p.q_rs = d.q_row_stride;
-  p.k_bs = d.k_batch_stride; p.k_rs = d.k_row_stride;
-  p.vt_bs = d.vt_batch_stride; p.vt_hs = d.vt_head_stride; p.vt_rs = d.vt_row_stride;
-  p.o_bs = d.o_batch_stride; p.o_rs = d.o_row_stride;
-  p.B = d.B; p.H = d.H; p.Nq = d.Nq; p.Nk = d.Nk;
-  p.out_dt = d.out_dtype;
-  p.scale = d.scale != 0.f ? d.scale : (float)(1.0 / sqrt((double)d.dh));
-  HIP_TRY(launch_attention(d.dh, tan, p, (hipStream_t)stream), "attention kernel launch");
-  return T2VA_OK;
+  return attn_entry(desc, q, nullptr, k, nullptr, vt, qd, kd, vdt, nk_valid, o, od, lse, stream, false);
+}
+
+t2va_status t2va_joint_attn_fwd_jvp_split(const t2va_attn_desc *desc, const void *q, const void *q_lo,
+                                          const void *k, const void *k_lo, const void *vt, const void *qd,
+                                          const void *kd, const void *vdt, const int32_t *nk_valid, void *o,
+                                          void *od, float *lse, t2va_stream stream) {
+  g_err.clear();
+  return attn_entry(desc, q, q_lo, k, k_lo, vt, qd, kd, vdt, nk_valid, o, od, lse, stream, true);
 }
 
 size_t t2va_scm_workspace_bytes(const t2va_scm_desc *desc) {
@@ -777,6 +881,10 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
 size_t t2va_scm_grad_workspace_bytes(const t2va_scm_desc *desc) {
   g_err.clear();
   if (check_desc(desc) != T2VA_OK) return 0;
+  if (desc->precision != T2VA_PREC_BF16) {
+    fail(T2VA_INVALID_ARG, "t2va_scm_grad supports precision T2VA_PREC_BF16 only");
+    return 0;
+  }
   return make_grad_layout(*desc).total;
 }
 
@@ -794,6 +902,8 @@ t2va_status t2va_scm_grad(const t2va_scm_desc *desc, const t2va_block_weights *t
                                     nullptr, gbar_v, gbar_a, nullptr, nullptr, loss, workspace,
                                     workspace_bytes, needed))
     return st;
+  if (desc->precision != T2VA_PREC_BF16)
+    return fail(T2VA_INVALID_ARG, "t2va_scm_grad supports precision T2VA_PREC_BF16 only");
   if (!grads) return fail(T2VA_INVALID_ARG, "grads is NULL");
   float *gout[6] = {grads->w_in_v, grads->w_in_a, grads->w_t, grads->w_qkv, grads->w_out_v, grads->w_out_a};
   for (float *g : gout)
@@ -980,7 +1090,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   PhaseScope total(s, T2VA_PHASE_TOTAL, prof);
 
   char *ws = (char *)workspace;
-  Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof);
+  Block blk(d.B, d.Nv, d.Na, d.Nt, d.Cv, d.Ca, d.d, d.H, L.ldv, s, prof, L.split);
   blk.apart = (float *)(ws + L.apart);
   blk.apart_bytes = L.apart_bytes;
   const int B = d.B, D = d.d, Nq = d.Nv + d.Na;
@@ -990,6 +1100,8 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
 
   const bf16 *W[2][6];
   HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
+  const bf16 *Wd[2][3] = {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}};
+  if (L.split) HIP_TRY(prepare_dup(W, 2, d.Cv, d.Ca, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
   float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
@@ -999,14 +1111,26 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   float *xT_v = (float *)(ws + L.xT_v), *xT_a = (float *)(ws + L.xT_a);
   float *xF_v = (float *)(ws + L.xF_v), *xF_a = (float *)(ws + L.xF_a);
 
-  // z_t = cos t x0 + sin t eps of the student's sample (bf16 GEMM input).
-  HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, x0_v, eps_v,
-                          nullptr, zv, nv, nv, 0, nv, s), "noise");
-  HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, x0_a, eps_a,
-                          nullptr, za, na, na, 0, na, s), "noise");
+  // z_t = cos t x0 + sin t eps of the student's sample (the GEMM input: bf16,
+  // or in split precision fp32 split into [hi | lo] rows).
+  if (!L.split) {
+    HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, x0_v, eps_v,
+                            nullptr, zv, nv, nv, 0, nv, s), "noise");
+    HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, x0_a, eps_a,
+                            nullptr, za, na, na, 0, na, s), "noise");
+  } else {
+    float *zf_v = (float *)(ws + L.zf_v), *zf_a = (float *)(ws + L.zf_a);
+    HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, x0_v, eps_v,
+                            nullptr, zf_v, nv, nv, 0, nv, s), "noise");
+    HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, x0_a, eps_a,
+                            nullptr, zf_a, na, na, 0, na, s), "noise");
+    HIP_TRY(launch_split_rows(zf_v, nv, d.Cv, zv, 2 * nv, 2 * d.Cv, B, d.Nv, d.Cv, s), "split rows");
+    HIP_TRY(launch_split_rows(zf_a, na, d.Ca, za, 2 * na, 2 * d.Ca, B, d.Na, d.Ca, s), "split rows");
+  }
   HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
   if (d.Nt > 0)
-    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, 0, nk, s), "text rows");
+    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, blk.xs, L.split, 0, nk, s),
+            "text rows");
   else
     HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
   if (guided && Nq % 32 != 0) HIP_TRY(launch_fill_nk(nk_null, B, Nq, s), "fill nk");
@@ -1017,7 +1141,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   // its attention runs over the video and audio keys only.  Outputs: batches
   // [0, B) conditional, [B, 2B) unconditional.
   HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
-  T2VA_CALL(blk.project_in(W[0], zv, za, tau, X, QK, VT, B));
+  T2VA_CALL(blk.project_in(W[0], Wd[0], zv, za, tau, X, QK, VT, B));
   if (guided && Nq % 32 == 0) {
     // the text keys follow the video and audio keys, so the null-condition
     // output is the running state after the first Nq keys: one pass stores both
@@ -1032,7 +1156,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
 
   // ---------------- fake-score block ----------------
   HIP_TRY(launch_time_linear(E, B, D, W[1][2], tau, s), "fake time linear");
-  T2VA_CALL(blk.project_in(W[1], zv, za, tau, X, QK, VT, B));
+  T2VA_CALL(blk.project_in(W[1], Wd[1], zv, za, tau, X, QK, VT, B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
   T2VA_CALL(blk.project_out(W[1], O, xF_v, xF_a, B));
 #undef T2VA_CALL

@@ -57,6 +57,11 @@ class Config:
     # Parameterisation of the block: "x0" (it predicts x0 at TrigFlow inputs)
     # or "rf" (a rectified-flow velocity model behind the TrigFlow wrapper).
     param: str = "x0"
+    # Precision of the primal logit path on the GPU: "bf16" (bf16 storage
+    # between kernels) or "split" (hi + lo bf16 pairs for the noised latents,
+    # token rows, Q and K; for inputs whose large logits make attention
+    # sensitive to bf16 rounding).  The oracle is exact fp64 either way.
+    precision: str = "bf16"
     cfg_v: float = 3.0
     cfg_a: float = 5.0
     eps_dmd: float = 1e-6
@@ -93,7 +98,7 @@ CONFIGS = {
                        H=16, in_dtype="bf16", beta=1.0, gamma=1.0, index=3),
     "stress": Config("stress", B=8, Nv=1536, Na=1024, Nt=128, Ntv=128, Cv=128, Ca=64, d=1024, H=8,
                      in_dtype="bf16", beta=2.0, gamma=0.25, w_v=1.0, w_a=4.0, t_mode="edges",
-                     z0_scale_v=10.0, z0_scale_a=0.1, index=4),
+                     z0_scale_v=10.0, z0_scale_a=0.1, index=4, precision="split"),
 }
 
 

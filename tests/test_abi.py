@@ -28,20 +28,22 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"t2va_scm_target", "t2va_joint_attn_fwd_jvp", "t2va_trigflow_field",
-            "t2va_scm_workspace_bytes", "t2va_last_error", "t2va_dmd_target",
+    assert {"t2va_scm_target", "t2va_joint_attn_fwd_jvp", "t2va_joint_attn_fwd_jvp_split",
+            "t2va_trigflow_field", "t2va_scm_workspace_bytes", "t2va_last_error", "t2va_dmd_target",
             "t2va_dmd_workspace_bytes", "t2va_stage3_mix"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.t2va_abi_version() == 2
+    assert lib.t2va_abi_version() == 3
 
 
 def test_struct_sizes_match_header(lib):
     # the binding's structs mirror the header: field counts and natural packing
     assert ctypes.sizeof(_lib.AttnDesc) == 5 * 4 + 4 + 9 * 8 + 3 * 4 + 4
-    assert ctypes.sizeof(_lib.ScmDesc) == 10 * 4 + 5 * 8 + 8   # + int param, padded
+    assert ctypes.sizeof(_lib.ScmDesc) == 10 * 4 + 5 * 8 + 2 * 4   # + int param, int precision
     assert ctypes.sizeof(_lib.BlockWeights) == 6 * 8
-    assert ctypes.sizeof(_lib.DmdDesc) == 10 * 4 + 5 * 8 + 8
+    assert ctypes.sizeof(_lib.DmdDesc) == 10 * 4 + 5 * 8 + 2 * 4
+    assert _lib.ScmDesc.precision.offset == 10 * 4 + 5 * 8 + 4
+    assert _lib.DmdDesc.precision.offset == 10 * 4 + 5 * 8 + 4
 
 
 def err(lib):
@@ -200,3 +202,67 @@ def test_param_validation(lib):
     dd = _lib.dmd_desc(cfg, _lib.DTYPE_BF16, _lib.DTYPE_BF16)
     dd.param = -1
     assert lib.t2va_dmd_workspace_bytes(ctypes.byref(dd)) == 0 and "param" in err(lib)
+
+
+def test_precision_validation(lib):
+    cfg = inputs.CONFIGS["stress"]
+    assert cfg.precision == "split"
+    d = _lib.scm_desc(cfg, _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    assert d.precision == _lib.PREC_SPLIT
+    n_split = lib.t2va_scm_workspace_bytes(ctypes.byref(d))
+    d.precision = _lib.PREC_BF16
+    n_bf16 = lib.t2va_scm_workspace_bytes(ctypes.byref(d))
+    # split rows double the latent, token-row and Q|K buffers and add the fp32 latents and weight pairs
+    assert n_split > n_bf16 > 0
+    d.precision = 2
+    assert lib.t2va_scm_workspace_bytes(ctypes.byref(d)) == 0 and "precision" in err(lib)
+    # the training backward runs in bf16 precision only
+    d.precision = _lib.PREC_SPLIT
+    assert lib.t2va_scm_grad_workspace_bytes(ctypes.byref(d)) == 0 and "precision" in err(lib)
+    d.precision = _lib.PREC_BF16
+    assert lib.t2va_scm_grad_workspace_bytes(ctypes.byref(d)) > 0
+    dd = _lib.dmd_desc(cfg, _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    assert dd.precision == _lib.PREC_SPLIT and lib.t2va_dmd_workspace_bytes(ctypes.byref(dd)) > 0
+    dd.precision = -1
+    assert lib.t2va_dmd_workspace_bytes(ctypes.byref(dd)) == 0 and "precision" in err(lib)
+
+
+def test_split_attention_rejects_before_launch(lib):
+    d = _lib.AttnDesc()
+    d.B, d.H, d.dh, d.Nq, d.Nk = 1, 2, 128, 10, 20
+    d.q_batch_stride = d.k_batch_stride = 20 * 256
+    d.q_row_stride = d.k_row_stride = d.o_row_stride = 256
+    d.o_batch_stride = 10 * 256
+    d.vt_row_stride, d.vt_head_stride, d.vt_batch_stride = 64, 64 * 128, 2 * 64 * 128
+    d.has_tangent, d.out_dtype = 0, 1
+    p = [fake_ptr(i + 1) for i in range(12)]
+
+    def call(q_lo=p[1], k_lo=p[3]):
+        return lib.t2va_joint_attn_fwd_jvp_split(ctypes.byref(d), p[0], q_lo, p[2], k_lo, p[4], None, None, None,
+                                                 p[8], p[9], None, None, None)
+
+    assert call(q_lo=None) == 1 and "q_lo" in err(lib)
+    assert call(k_lo=None) == 1
+    assert call(k_lo=ctypes.c_void_p(0x30008)) == 1 and "aligned" in err(lib)
+    d.dh = 96
+    assert call() == 2
+
+
+def test_attention_offset_bound_covers_a_stage_past_the_keys(lib):
+    """The kernels address K rows up to one 128-key stage past the last key
+    with 32-bit offsets: the host bound uses (Nk + 128) rows."""
+    d = _lib.AttnDesc()
+    d.B, d.H, d.dh = 1, 1, 128
+    d.Nq = 16
+    d.q_row_stride = d.o_row_stride = 128
+    d.q_batch_stride = d.o_batch_stride = 16 * 128
+    d.k_row_stride = 3 * 2048   # the fused QKV row stride of a 2048-wide block
+    d.k_batch_stride = 0
+    d.has_tangent, d.out_dtype = 0, 1
+    p = [fake_ptr(i + 1) for i in range(10)]
+    limit = 2**31 // (d.k_row_stride * 2)   # rows whose byte offsets stay below 2^31
+    d.Nk = limit - 127                      # Nk + 128 rows pass it (Nk + 64 would not): rejected
+    ldv = (d.Nk + 63) // 64 * 64
+    d.vt_row_stride, d.vt_head_stride, d.vt_batch_stride = ldv, 128 * ldv, 128 * ldv
+    assert lib.t2va_joint_attn_fwd_jvp(ctypes.byref(d), p[0], p[1], p[2], None, None, None, p[6], p[7],
+                                       None, None, None) == 2 and "2 GiB" in err(lib)

@@ -7,14 +7,12 @@ and the seeded input generator): per-sample norms and losses, and J and gbar
 on a fixed random sample of rows.  The GPU run recomputes the same seeded
 inputs.  Properties that hold at any size are checked on all elements.
 
-Where stored, the oracle was also run with bf16 rounding at the points where
-the GPU path stores bf16; the gap between the two oracle runs measures how
-sensitive a sample is to that storage precision.  Wherever it is below half
-the tolerance, the GPU must match both oracle runs within the tolerance.  For
-more sensitive samples (the stress workload's small-t samples, whose
-attention is nearly one-hot because the block has no normalisation and the
-latents are scaled by 10) the GPU's gaps to both runs must stay within that
-sensitivity plus the tolerance, and are reported.
+Every sample is held to the exact oracle at the target's tolerances.  The
+stress workload (latents scaled by 10, half of its samples at t < 0.1, no
+normalisation in the block) has logits of order 100, where one bf16 rounding
+of Q or K changes J^v by 23-41 %; it runs in split precision
+(T2VA_PREC_SPLIT, the workload's "precision" field), which carries the primal
+logit path in hi + lo bf16 pairs.
 """
 import os
 
@@ -57,31 +55,11 @@ def test_full_size_target_against_stored_oracle(name):
         for m, i in (("v", 0), ("a", 1)):
             rows = exp[f"rows_{m}"][b]
             for key in ("J", "gbar"):
-                g = got[f"{key}_{m}"][b, rows]
-                e = rel_l2(g, exp[f"{key}_{m}"][b])
-                cond, e_st = 0.0, None
-                if f"st_{key}_{m}" in exp:
-                    # the oracle run with bf16 storage where the GPU stores bf16:
-                    # how far bf16 storage alone moves the exact result
-                    e_st = rel_l2(g, exp[f"st_{key}_{m}"][b])
-                    cond = rel_l2(exp[f"st_{key}_{m}"][b], exp[f"{key}_{m}"][b])
-                if cond <= 0.5 * TOL_FIELD:
-                    # well conditioned: bf16 storage moves the exact result by < 1e-2
-                    assert e <= TOL_FIELD, (name, b, m, key, e)
-                    if e_st is not None:
-                        assert e_st <= TOL_FIELD, (name, b, m, key, "storage oracle", e_st)
-                    worst[f"{key}_{m}"] = max(worst.get(f"{key}_{m}", 0.0), e)
-                else:
-                    # ill conditioned (near one-hot attention): one bf16 ulp can flip
-                    # the dominant key of a row, so neither oracle is reproducible to
-                    # the tolerance; the GPU must stay within the measured sensitivity
-                    assert e <= cond + TOL_FIELD, (name, b, m, key, e, cond)
-                    assert e_st <= cond + TOL_FIELD, (name, b, m, key, "storage oracle", e_st, cond)
-                    print(f"  {name} b={b} {key}_{m}: ill-conditioned: gap to exact oracle {e:.3f}, "
-                          f"to bf16-storage oracle {e_st:.3f}; storage sensitivity {cond:.3f}", flush=True)
+                e = rel_l2(got[f"{key}_{m}"][b, rows], exp[f"{key}_{m}"][b])
+                assert e <= TOL_FIELD, (name, b, m, key, e)
+                worst[f"{key}_{m}"] = max(worst.get(f"{key}_{m}", 0.0), e)
             n = got["norms"][b, i]
-            n_cond = abs(exp["st_norms"][b, i] / exp["norms"][b, i] - 1) if "st_norms" in exp else 0.0
-            assert abs(n - exp["norms"][b, i]) <= (TOL_FIELD + n_cond) * exp["norms"][b, i]
+            assert abs(n - exp["norms"][b, i]) <= TOL_FIELD * exp["norms"][b, i]
             # at any size: ||gbar|| = n/(n + eps), r = -gbar, everything finite
             gb = got[f"gbar_{m}"][b].astype(np.float64)
             assert np.all(np.isfinite(gb)) and np.all(np.isfinite(got[f"J_{m}"][b]))
@@ -130,10 +108,9 @@ def test_attention_full_high_res_shape_sampled_queries():
 TOL_DMD_LOSS = 2 * TOL_FIELD + TOL_FIELD ** 2   # |dL|/L <= 2e + e^2 for a relative L2 error e in Delta
 
 
-@pytest.mark.parametrize("name", ["standard", "stress"])
+@pytest.mark.parametrize("name", ["standard", "stress", "high-res"])
 def test_full_size_dmd_against_stored_oracle(name):
-    """The joint DMD term at full size against the stored oracle run, with the
-    same conditioning protocol as the sCM target."""
+    """The joint DMD term at full size against the stored exact oracle run."""
     from joint_video_audio_trigflow_amd import _lib
     path = os.path.join(GOLDEN, f"expected_dmd_{name}.npz")
     print(f"full-size dmd_target {name}", flush=True)
@@ -151,22 +128,12 @@ def test_full_size_dmd_against_stored_oracle(name):
     for b in range(cfg.B):
         for m, i in (("v", 0), ("a", 1)):
             rows = exp[f"rows_{m}"][b]
-            g = got[f"delta_{m}"][b, rows]
-            e = rel_l2(g, exp[f"delta_{m}"][b])
-            e_st = rel_l2(g, exp[f"st_delta_{m}"][b])
-            cond = rel_l2(exp[f"st_delta_{m}"][b], exp[f"delta_{m}"][b])
-            if cond <= 0.5 * TOL_FIELD:
-                assert e <= TOL_FIELD and e_st <= TOL_FIELD, (name, b, m, e, e_st)
-                worst[m] = max(worst.get(m, 0.0), e)
-            else:
-                assert e <= cond + TOL_FIELD and e_st <= cond + TOL_FIELD, (name, b, m, e, e_st, cond)
-                print(f"  {name} b={b} delta_{m}: ill-conditioned: gap to exact oracle {e:.3f}, "
-                      f"to bf16-storage oracle {e_st:.3f}; storage sensitivity {cond:.3f}", flush=True)
-            c_cond = abs(exp["st_scales"][b, i] / exp["scales"][b, i] - 1)
-            assert abs(got["scales"][b, i] / exp["scales"][b, i] - 1) <= TOL_FIELD + c_cond
+            e = rel_l2(got[f"delta_{m}"][b, rows], exp[f"delta_{m}"][b])
+            assert e <= TOL_FIELD, (name, b, m, e)
+            worst[m] = max(worst.get(m, 0.0), e)
+            assert abs(got["scales"][b, i] / exp["scales"][b, i] - 1) <= TOL_FIELD
             assert np.all(np.isfinite(got[f"delta_{m}"][b]))
-        l_cond = abs(exp["st_loss"][b] / exp["loss"][b] - 1)
-        assert abs(got["loss"][b] / exp["loss"][b] - 1) <= TOL_DMD_LOSS + l_cond, (b, got["loss"][b], exp["loss"][b])
+        assert abs(got["loss"][b] / exp["loss"][b] - 1) <= TOL_DMD_LOSS, (b, got["loss"][b], exp["loss"][b])
     print(name, "DMD worst sampled rel-L2:", {k: f"{v:.2e}" for k, v in worst.items()}, flush=True)
 
 
