@@ -273,6 +273,33 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
                             float *loss, void *workspace, size_t workspace_bytes,
                             t2va_stream stream);
 
+/*
+ * t2va_scm_target_noalloc - t2va_scm_target for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It allocates nothing: its workspace is a static
+ * device array of T2VA_NOALLOC_SCRATCH_BYTES bytes in the library, one per GPU
+ * the library runs on, held until the process ends.  Arguments and outputs are
+ * those of t2va_scm_target without the workspace; the stream must belong to
+ * the current device.  Every attention tile runs whole (no split tails), so
+ * results may differ from t2va_scm_target's in the last bits.
+ * Shapes whose workspace exceeds the scratch (for one sample at d = 1024,
+ * roughly 3,000 tokens; the small workload fits, the standard one does not)
+ * are rejected with T2VA_WORKSPACE_TOO_SMALL before any launch.
+ * All calls on one GPU share its scratch: calls that overlap on one GPU (two
+ * streams, or two host threads) race and must be ordered by the caller.  Its
+ * contents on entry are irrelevant (every buffer is written before it is
+ * read).  The first call on a device looks up the scratch's device address.
+ * Errors: as t2va_scm_target, plus T2VA_WORKSPACE_TOO_SMALL for shapes beyond
+ * the scratch and T2VA_HIP_ERROR if the address lookup fails.
+ */
+#define T2VA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+t2va_status t2va_scm_target_noalloc(const t2va_scm_desc *desc, const t2va_block_weights *teacher,
+                                    const t2va_block_weights *student, const void *z0_v, const void *z0_a,
+                                    const void *eps_v, const void *eps_a, const void *text,
+                                    const uint8_t *text_mask, const double *t_host, float *J_v, float *J_a,
+                                    float *gbar_v, float *gbar_a, float *r_v, float *r_a, float *norms,
+                                    float *loss, t2va_stream stream);
+
 /* ------------------------------------------------------------------------ */
 /* Training backward of the joint sCM loss                                   */
 /* ------------------------------------------------------------------------ */

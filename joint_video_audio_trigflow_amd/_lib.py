@@ -105,6 +105,10 @@ def load() -> ctypes.CDLL:
     lib.t2va_scm_target.argtypes = ([ctypes.POINTER(ScmDesc), ctypes.POINTER(BlockWeights),
                                      ctypes.POINTER(BlockWeights)] + [vp] * 5 + [vp, dp]
                                     + [f32p] * 8 + [vp, ctypes.c_size_t, vp])
+    lib.t2va_scm_target_noalloc.restype = i32
+    lib.t2va_scm_target_noalloc.argtypes = ([ctypes.POINTER(ScmDesc), ctypes.POINTER(BlockWeights),
+                                             ctypes.POINTER(BlockWeights)] + [vp] * 5 + [vp, dp]
+                                            + [f32p] * 8 + [vp])
     lib.t2va_scm_grad_workspace_bytes.restype = ctypes.c_size_t
     lib.t2va_scm_grad_workspace_bytes.argtypes = [ctypes.POINTER(ScmDesc)]
     lib.t2va_scm_grad.restype = i32
@@ -301,6 +305,23 @@ class ScmTarget:
             _ptr(o["r_a"]), _ptr(o["norms"]), _ptr(o["loss"]), self.ws_ptr, self.ws_bytes,
             _stream(self.device)))
         return o
+
+
+def scm_target_noalloc(cfg, teacher: dict, student: dict, z0_v, z0_a, eps_v, eps_a, text, text_mask, t,
+                       out: dict, in_dtype=DTYPE_BF16, weight_dtype=DTYPE_BF16) -> dict:
+    """t2va_scm_target_noalloc into the caller's output tensors (the dict keys of
+    ScmTarget.out; J and r may be None).  The library takes its workspace from
+    its static scratch."""
+    lib = load()
+    desc = scm_desc(cfg, in_dtype, weight_dtype)
+    tw, sw = ScmTarget.weights_struct(teacher), ScmTarget.weights_struct(student)
+    dev = out["loss"].device
+    _check(lib.t2va_scm_target_noalloc(
+        ctypes.byref(desc), ctypes.byref(tw), ctypes.byref(sw), _ptr(z0_v), _ptr(z0_a), _ptr(eps_v), _ptr(eps_a),
+        _ptr(text), _ptr(text_mask), _t_host(t), _ptr(out.get("J_v")), _ptr(out.get("J_a")), _ptr(out["gbar_v"]),
+        _ptr(out["gbar_a"]), _ptr(out.get("r_v")), _ptr(out.get("r_a")), _ptr(out.get("norms")), _ptr(out["loss"]),
+        _stream(dev)))
+    return out
 
 
 def grad_workspace_bytes(desc: ScmDesc) -> int:

@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -193,7 +194,8 @@ struct Layout {
   size_t w_elems[6];  // per-block weight element counts
 };
 
-Layout make_layout(const t2va_scm_desc &d) {
+// whole_tiles: no scratch for split attention tails (every tile runs whole).
+Layout make_layout(const t2va_scm_desc &d, bool whole_tiles = false) {
   Layout L;
   L.Nq = d.Nv + d.Na;
   L.N_all = L.Nq + d.Nt;
@@ -232,7 +234,7 @@ Layout make_layout(const t2va_scm_desc &d) {
   L.x0S_a = take(2 * B * d.Na * d.Ca * sizeof(float));
   L.part_v = take(B * L.nblk_v * sizeof(float));
   L.part_a = take(B * L.nblk_a * sizeof(float));
-  L.apart_bytes = attention_split_bytes(L.dh, d.B, d.H, L.Nq);
+  L.apart_bytes = whole_tiles ? 0 : attention_split_bytes(L.dh, d.B, d.H, L.Nq);
   L.apart = take(L.apart_bytes);
   L.total = off;
   return L;
@@ -766,6 +768,48 @@ t2va_status attn_entry(const t2va_attn_desc *desc, const void *q, const void *q_
   return T2VA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free entry point's workspace: one file-scope device array per
+// GPU, held from the library's load until the process ends.  Host code never
+// uses the array's name as an address: it takes the device address from
+// hipGetSymbolAddress, once per device, with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;   // T2VA_NOALLOC_SCRATCH_BYTES
+static_assert(kNoAllocScratchBytes == (size_t)T2VA_NOALLOC_SCRATCH_BYTES, "header and library agree");
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+void *g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array (nullptr and a message on failure).
+void *device_scratch(t2va_status *st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    *st = fail(T2VA_UNSUPPORTED_SHAPE, "device %d is beyond the %d devices the scratch table holds", dev,
+               kMaxScratchDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *st = e != hipSuccess ? hip_fail(e, "hipGetSymbolAddress(scratch)")
+                            : fail(T2VA_HIP_ERROR, "hipGetSymbolAddress(scratch) returned NULL");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *st = T2VA_OK;
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -873,6 +917,37 @@ t2va_status t2va_scm_target(const t2va_scm_desc *desc, const t2va_block_weights 
   const bf16 *W[2][6];
   return run_scm(*desc, make_layout(*desc), wb, z0_v, z0_a, eps_v, eps_a, text, text_mask, t_host, J_v, J_a,
                  gbar_v, gbar_a, r_v, r_a, norms, loss, workspace, nullptr, W, s, prof);
+}
+
+t2va_status t2va_scm_target_noalloc(const t2va_scm_desc *desc, const t2va_block_weights *teacher,
+                                    const t2va_block_weights *student, const void *z0_v, const void *z0_a,
+                                    const void *eps_v, const void *eps_a, const void *text,
+                                    const uint8_t *text_mask, const double *t_host, float *J_v, float *J_a,
+                                    float *gbar_v, float *gbar_a, float *r_v, float *r_a, float *norms,
+                                    float *loss, t2va_stream stream) {
+  g_err.clear();
+  const t2va_block_weights *wb[2] = {teacher, student};
+  if (t2va_status st = check_desc(desc)) return st;
+  const Layout L = make_layout(*desc, true);
+  if (L.total > kNoAllocScratchBytes)
+    return fail(T2VA_WORKSPACE_TOO_SMALL,
+                "t2va_scm_target_noalloc: this shape needs %zu bytes of workspace; its static scratch holds %zu "
+                "(use t2va_scm_target with a caller workspace)",
+                L.total, kNoAllocScratchBytes);
+  // validation with a stand-in address (the scratch is 256-byte aligned and large enough)
+  if (t2va_status st = validate_scm(desc, wb, z0_v, z0_a, eps_v, eps_a, text, text_mask, t_host, J_v, J_a,
+                                    gbar_v, gbar_a, r_v, r_a, loss, (void *)(uintptr_t)256, L.total, L.total))
+    return st;
+  t2va_status st = T2VA_OK;
+  void *ws = device_scratch(&st);
+  if (!ws) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const bool prof = g_prof.active();
+  if (prof) g_prof.calls++;
+  PhaseScope total(s, T2VA_PHASE_TOTAL, prof);
+  const bf16 *W[2][6];
+  return run_scm(*desc, L, wb, z0_v, z0_a, eps_v, eps_a, text, text_mask, t_host, J_v, J_a, gbar_v, gbar_a, r_v,
+                 r_a, norms, loss, ws, nullptr, W, s, prof);
 }
 
 // ---------------------------------------------------------------------------

@@ -266,3 +266,21 @@ def test_attention_offset_bound_covers_a_stage_past_the_keys(lib):
     d.vt_row_stride, d.vt_head_stride, d.vt_batch_stride = ldv, 128 * ldv, 128 * ldv
     assert lib.t2va_joint_attn_fwd_jvp(ctypes.byref(d), p[0], p[1], p[2], None, None, None, p[6], p[7],
                                        None, None, None) == 2 and "2 GiB" in err(lib)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """The allocation-free entry point refuses, before touching the GPU, any
+    shape whose workspace (without split attention tails) exceeds its static
+    scratch."""
+    assert hasattr(lib, "t2va_scm_target_noalloc")
+    cfg = inputs.CONFIGS["standard"]
+    d = _lib.scm_desc(cfg, _lib.DTYPE_BF16, _lib.DTYPE_BF16)
+    w = _lib.BlockWeights(*[0x10000 * (i + 1) for i in range(6)])
+    t = (ctypes.c_double * 1)(0.5)
+    ptrs = [fake_ptr(i + 10) for i in range(6)]
+    outs = [fake_ptr(i + 20) for i in range(8)]
+    st = lib.t2va_scm_target_noalloc(ctypes.byref(d), ctypes.byref(w), ctypes.byref(w), *ptrs, t, *outs, None)
+    assert st == 3 and "static scratch" in err(lib)
+    d.gamma = 2.0   # descriptor errors come first
+    st = lib.t2va_scm_target_noalloc(ctypes.byref(d), ctypes.byref(w), ctypes.byref(w), *ptrs, t, *outs, None)
+    assert st == 1 and "gamma" in err(lib)
