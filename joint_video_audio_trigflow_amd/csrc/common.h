@@ -105,6 +105,12 @@ hipError_t launch_text_rows(int B, int Nq, int Nt, int d, const void *text, int 
                             const uint8_t *mask, bf16 *X, int64_t x_batch_stride, int64_t x_row_stride,
                             int split, int zero_only, int32_t *nk, hipStream_t s);
 
+// Guided attention output of B samples [Nq][D] (fp32 conditional c and
+// unconditional u, batch stride Nq D): out = bf16(u + s (c - u)) with s = s_v
+// for rows < Nv, s_a for the rest.
+hipError_t launch_guide(const float *c, const float *u, bf16 *out, int B, int Nq, int Nv, int D, float s_v,
+                        float s_a, hipStream_t s);
+
 // Split rows: fp32 src [nb][rows][w] (strides s_bs, s_rs) -> bf16 dst rows
 // [hi | lo] of 2w elements (strides d_bs, d_rs): hi = bf16(x), lo = bf16(x - hi).
 // w a multiple of 8; strides multiples of 8.

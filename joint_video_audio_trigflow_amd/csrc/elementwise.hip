@@ -215,6 +215,21 @@ __global__ __launch_bounds__(kThreads) void split_rows_kernel(const float *src, 
   store8(o + w, lo);
 }
 
+// Guided attention output: u + s (c - u) per element, s by the row's modality.
+__global__ __launch_bounds__(kThreads) void guide_kernel(const float *c, const float *u, bf16 *out, int64_t per,
+                                                         int D, int Nv, float s_v, float s_a) {
+  const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (i0 >= per) return;
+  const int64_t at = (int64_t)blockIdx.y * per + i0;
+  const float sc = (i0 / D) < Nv ? s_v : s_a;   // D is a multiple of 8: one row per group
+  float fc[8], fu[8];
+  load8(c + at, fc);
+  load8(u + at, fu);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fc[i] = fu[i] + sc * (fc[i] - fu[i]);
+  store8(out + at, fc);
+}
+
 // [W | W]: row i of W2 holds row i of W twice.
 __global__ __launch_bounds__(kThreads) void dup_cols_kernel(const bf16 *W, bf16 *W2, int n, int k) {
   const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
@@ -447,6 +462,15 @@ hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 
   if (per <= 0 || nb <= 0) return hipSuccess;
   dim3 grid((unsigned)((per + kChunk - 1) / kChunk), nb);
   hipLaunchKernelGGL(split_rows_kernel, grid, dim3(kThreads), 0, s, src, s_bs, s_rs, dst, d_bs, d_rs, rows, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_guide(const float *c, const float *u, bf16 *out, int B, int Nq, int Nv, int D, float s_v,
+                        float s_a, hipStream_t s) {
+  const int64_t per = (int64_t)Nq * D;
+  if (per <= 0 || B <= 0) return hipSuccess;
+  dim3 grid((unsigned)((per + kChunk - 1) / kChunk), B);
+  hipLaunchKernelGGL(guide_kernel, grid, dim3(kThreads), 0, s, c, u, out, per, D, Nv, s_v, s_a);
   return hipGetLastError();
 }
 

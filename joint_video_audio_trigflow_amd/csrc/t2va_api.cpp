@@ -355,8 +355,8 @@ t2va_status check_weights(const t2va_block_weights *const *wb, int n, const char
 struct DmdLayout {
   int ldv, nblk_v, nblk_a;
   bool split;
-  size_t wts, wdup, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, nk_null, O, xT_v, xT_a, xF_v, xF_a, pa_v, pa_a, ps_v,
-      ps_a, apart;
+  size_t wts, wdup, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, nk_null, O, Of, xT_v, xT_a, xF_v, xF_a, pa_v, pa_a,
+      ps_v, ps_a, apart;
   size_t total, apart_bytes;
   size_t w_elems[6];
 };
@@ -393,9 +393,10 @@ DmdLayout make_dmd_layout(const t2va_dmd_desc &d) {
   L.VT = take(B * D * (size_t)L.ldv * sizeof(bf16));
   L.nk = take(B * sizeof(int32_t));
   L.nk_null = take(B * sizeof(int32_t));
-  L.O = take(2 * B * Nq * D * sizeof(bf16));
-  L.xT_v = take(2 * B * nv * sizeof(float));
-  L.xT_a = take(2 * B * na * sizeof(float));
+  L.O = take(B * Nq * D * sizeof(bf16));
+  L.Of = take(2 * B * Nq * D * sizeof(float));   // guided teacher: conditional and null outputs, fp32
+  L.xT_v = take(B * nv * sizeof(float));
+  L.xT_a = take(B * na * sizeof(float));
   L.xF_v = take(B * nv * sizeof(float));
   L.xF_a = take(B * na * sizeof(float));
   L.pa_v = take(B * L.nblk_v * sizeof(float));
@@ -550,8 +551,10 @@ struct Block {
   // Attention of the B problems in QK/VT over nk[b] keys into O; with `tan`,
   // the tangent operands are the batches that follow (QK + B qk_bs, VT + B
   // vt_bs) and the tangent output goes to O + B o_bs.
-  t2va_status attention(const bf16 *QK, const bf16 *VT, const int32_t *nk, bf16 *O, bool tan,
-                        int phase, float *lse = nullptr, bf16 *O_prefix = nullptr, int nk_split = 0) const {
+  // out_dt: the dtype of O (and O_prefix); elements at the same strides either way.
+  t2va_status attention(const bf16 *QK, const bf16 *VT, const int32_t *nk, void *O, bool tan,
+                        int phase, float *lse = nullptr, void *O_prefix = nullptr, int nk_split = 0,
+                        int out_dt = T2VA_DTYPE_BF16) const {
     AttnParams p;
     p.q = QK; p.k = QK + D; p.vt = VT;
     p.q_lo = split ? QK + 2 * D : nullptr;
@@ -559,13 +562,13 @@ struct Block {
     p.qd = tan ? QK + (int64_t)B * qk_bs : nullptr;
     p.kd = tan ? QK + (int64_t)B * qk_bs + D : nullptr;
     p.vdt = tan ? VT + (int64_t)B * vt_bs : nullptr;
-    p.nk = nk; p.o = O; p.od = tan ? O + (int64_t)B * o_bs : nullptr; p.lse = lse;
+    p.nk = nk; p.o = O; p.od = tan ? (bf16 *)O + (int64_t)B * o_bs : nullptr; p.lse = lse;
     p.o2 = O_prefix; p.nk_split = nk_split;
     p.q_bs = qk_bs; p.q_rs = qks; p.k_bs = qk_bs; p.k_rs = qks;
     p.vt_bs = vt_bs; p.vt_hs = vt_hs; p.vt_rs = ldv;
     p.o_bs = o_bs; p.o_rs = D;
     p.B = B; p.H = H; p.Nq = Nq; p.Nk = NA;
-    p.out_dt = T2VA_DTYPE_BF16;
+    p.out_dt = out_dt;
     p.scale = (float)(1.0 / sqrt((double)dh));
     p.part = apart;
     p.part_bytes = apart_bytes;
@@ -1213,21 +1216,33 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
 #define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
   // ---------------- teacher: conditional and null-condition passes ----------------
   // Both passes share Q, K and V; the null condition masks every text key, so
-  // its attention runs over the video and audio keys only.  Outputs: batches
-  // [0, B) conditional, [B, 2B) unconditional.
+  // its attention runs over the video and audio keys only.  Guided, both
+  // outputs stay fp32 (Of: batches [0, B) conditional, [B, 2B) unconditional)
+  // and are combined, O = O_u + s_m (O_c - O_u), before the one bf16 rounding
+  // of the output projection's input: the output projection is linear, so
+  // this is the guided prediction, and the large scales (5 for audio) no
+  // longer amplify two separate roundings.
   HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
   T2VA_CALL(blk.project_in(W[0], Wd[0], zv, za, tau, X, QK, VT, B));
-  if (guided && Nq % 32 == 0) {
-    // the text keys follow the video and audio keys, so the null-condition
-    // output is the running state after the first Nq keys: one pass stores both
-    T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN, nullptr,
-                            O + (int64_t)B * blk.o_bs, Nq));
+  if (guided) {
+    float *Of = (float *)(ws + L.Of);
+    if (Nq % 32 == 0) {
+      // the text keys follow the video and audio keys, so the null-condition
+      // output is the running state after the first Nq keys: one pass stores both
+      T2VA_CALL(blk.attention(QK, VT, nk, Of, false, T2VA_PHASE_TEACHER_ATTN, nullptr, Of + (int64_t)B * blk.o_bs,
+                              Nq, T2VA_DTYPE_FP32));
+    } else {
+      T2VA_CALL(blk.attention(QK, VT, nk, Of, false, T2VA_PHASE_TEACHER_ATTN, nullptr, nullptr, 0,
+                              T2VA_DTYPE_FP32));
+      T2VA_CALL(blk.attention(QK, VT, nk_null, Of + (int64_t)B * blk.o_bs, false, T2VA_PHASE_TEACHER_ATTN, nullptr,
+                              nullptr, 0, T2VA_DTYPE_FP32));
+    }
+    HIP_TRY(launch_guide(Of, Of + (int64_t)B * blk.o_bs, O, B, Nq, d.Nv, D, (float)d.cfg_v, (float)d.cfg_a, s),
+            "guidance");
   } else {
     T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
-    if (guided)
-      T2VA_CALL(blk.attention(QK, VT, nk_null, O + (int64_t)B * blk.o_bs, false, T2VA_PHASE_TEACHER_ATTN));
   }
-  T2VA_CALL(blk.project_out(W[0], O, xT_v, xT_a, guided ? 2 * B : B));
+  T2VA_CALL(blk.project_out(W[0], O, xT_v, xT_a, B));
 
   // ---------------- fake-score block ----------------
   HIP_TRY(launch_time_linear(E, B, D, W[1][2], tau, s), "fake time linear");
@@ -1241,8 +1256,8 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   dp.x0[0] = x0_v; dp.x0[1] = x0_a;
   dp.eps[0] = eps_v; dp.eps[1] = eps_a;
   dp.tc[0] = xT_v; dp.tc[1] = xT_a;
-  dp.tu[0] = guided ? xT_v + (int64_t)B * nv : nullptr;
-  dp.tu[1] = guided ? xT_a + (int64_t)B * na : nullptr;
+  dp.tu[0] = nullptr;   // the teacher's prediction is already guided
+  dp.tu[1] = nullptr;
   dp.fk[0] = xF_v; dp.fk[1] = xF_a;
   dp.x_bs[0] = nv; dp.x_bs[1] = na;
   dp.scale[0] = (float)d.cfg_v; dp.scale[1] = (float)d.cfg_a;
