@@ -124,6 +124,15 @@ struct AttnCfg {
 
 // Four consecutive output columns of one row (and of its tangent): bf16 or
 // fp32 as p.out_dt says, at element offset `at` of o (od).
+// The value x, opaque to the optimiser: address arithmetic that starts from
+// it stays where it is used instead of being hoisted above the key loop, where
+// the forward kernel has no registers to hold it (it then spilled ~40 output
+// addresses per lane, 344 bytes of scratch, on every launch).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 template <bool TAN>
 __device__ __forceinline__ void store_out4(const AttnParams &p, int64_t at, const float (&o4)[4],
                                            const float (&od4)[4]) {
@@ -547,7 +556,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_fw
     if constexpr (!TAN) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
-        const int q_row = q_row0 + 16 * mb;
+        const int q_row = opaque(q_row0 + 16 * mb);
         if (ppart) {
           const float inv_l = 1.f / Lacc[mb][0];
           const int pi = 4 * (q_row - qb * C::BM) + g;
@@ -680,7 +689,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_fw
   // ---- epilogue: combine the four lanes of a row, normalise, store ----
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
-  const int q_row = q_row0 + 16 * mb;
+  const int q_row = opaque(q_row0 + 16 * mb);
   float l_tot;
   if constexpr (C::MFMA_SUMS) {
     l_tot = Lacc[mb][0];
