@@ -33,8 +33,9 @@ PEAK_HBM_GBS = 8000.0
 
 
 def workload_name(cfg) -> str:
+    storage = "bf16 storage" if cfg.precision == "bf16" else "bf16 storage, split-bf16 logit path"
     return (f"{cfg.name} joint sCM target: B={cfg.B}, video {cfg.Nv}x{cfg.Cv}, audio {cfg.Na}x{cfg.Ca}, "
-            f"text {cfg.Nt} ({cfg.Ntv} valid), d={cfg.d}, {cfg.H}x{cfg.dh} heads, bf16 storage, "
+            f"text {cfg.Nt} ({cfg.Ntv} valid), d={cfg.d}, {cfg.H}x{cfg.dh} heads, {storage}, "
             f"teacher + student fwd+JVP")
 
 
@@ -163,7 +164,8 @@ def time_grad(cfg, problem, dev, steps, nk) -> dict:
     import torch
     from joint_video_audio_trigflow_amd import _lib
     dt = _lib.DTYPE_BF16 if cfg.in_dtype == "bf16" else _lib.DTYPE_FP32
-    op = _lib.ScmGrad(cfg, in_dtype=dt, weight_dtype=dt)
+    # the backward is built for bf16 precision (it recomputes the softmax from bf16 Q and K)
+    op = _lib.ScmGrad(cfg.replace(precision="bf16"), in_dtype=dt, weight_dtype=dt)
     call = lambda: op(dev["teacher"], dev["student"], dev["z0_v"], dev["z0_a"], dev["eps_v"],
                       dev["eps_a"], dev["text"], dev["text_mask"], dev["t"])
     call()
@@ -181,7 +183,7 @@ def time_grad(cfg, problem, dev, steps, nk) -> dict:
     # algorithmic attention-backward work: 2.5x the forward's 4 d Nq nk (dP, dV, dQ, dK and
     # recomputing S); the two kernels also recompute dP, 14 d Nq nk in all
     flops = sum(10.0 * cfg.d * cfg.Nq * k for k in nk)
-    return {"steps": steps, "ms_per_call": ms, "samples_per_s": cfg.B / (ms * 1e-3),
+    return {"steps": steps, "ms_per_call": ms, "samples_per_s": cfg.B / (ms * 1e-3), "precision": "bf16",
             "phases_ms_per_call": {k: v / n for k, v in phases.items()},
             "attn_bwd_tflops": flops / (bwd_ms * 1e-3) / 1e12,
             "attn_bwd_flops_per_launch": flops}
@@ -236,12 +238,19 @@ def main() -> int:
     print(f"[bench] {cfg.name}: warmup done", file=sys.stderr, flush=True)
 
     _lib.profile_enable(args.steps)
+    # one event between steps on the launch stream (torch's current stream,
+    # which the binding passes to the library): per-step times for the median
+    # and min
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         call()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     phases, ncalls = _lib.profile_read()
     _lib.profile_enable(0)
     assert ncalls == args.steps, (ncalls, args.steps)
@@ -264,13 +273,17 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": step_ms[len(step_ms) // 2] if len(step_ms) % 2 else
+        0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2]),
+        "ms_per_step_min": step_ms[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) latents/noise/text, N(0,1/fan_in) weights)",
         "config": {"workload": workload_name(cfg), "global_batch": cfg.B,
-                   "tokens": cfg.N_all, "valid_keys": nk, "parallelism": "none (1 GPU)"},
+                   "tokens": cfg.N_all, "valid_keys": nk, "precision": cfg.precision,
+                   "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": counted_traffic(cfg),
                      "kernel": f"attn_fwd_jvp_kernel<{cfg.dh},true> + attn_combine_kernel<{cfg.dh},true>",

@@ -8,6 +8,12 @@ dispatch, the calibration factors, the resulting HBM traffic per launch and
 the achieved HBM bandwidth (traffic over the traced average duration).
 Usage: python -m joint_video_audio_trigflow_amd.profile_summary <rocprof output dir>
 
+With --per-config <file>..., it reads bench.py's JSON lines (one per
+workload) and prints one row per workload: samples/s, the step's mean,
+median and min, the student attention's time and rate against the dense bf16
+peak, the teacher attention's rate, and the DMD term's and the backward's
+times when present.
+
 With --clock <dir>, it reads one --pmc --kernel-trace run per subdirectory of
 <dir> instead and prints, per attention and GEMM kernel, the average of each
 counter per dispatch and these derived figures (MI355X: 8 XCDs, 256 CUs,
@@ -130,7 +136,34 @@ def clock_table(d):
     return out
 
 
+def per_config(paths):
+    """One row per bench.py JSON line (the last line of each file)."""
+    rows = []
+    for path in paths:
+        lines = [ln for ln in open(path).read().splitlines() if ln.startswith("{")]
+        rows.append(json.loads(lines[-1]))
+    print("| workload | B | precision | samples/s | ms/step mean / median / min | student attn ms | "
+          "student attn TFLOP/s (% of 2.5 PF) | teacher attn TFLOP/s | DMD ms/call | target + backward ms | "
+          "attn backward TFLOP/s |\n|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        c, rf = r["config"], r["roofline"]
+        name = c["workload"].split(" ")[0]
+        dmd = r.get("dmd_target", {}).get("ms_per_call")
+        grad = r.get("scm_grad", {})
+        fmt = lambda x, f: "-" if x is None else f.format(x)
+        print(f"| {name} | {c['global_batch']} | {c.get('precision', 'bf16')} | {r['value']:.1f} | "
+              f"{r['ms_per_step']:.3f} / {r.get('ms_per_step_median', float('nan')):.3f} / "
+              f"{r.get('ms_per_step_min', float('nan')):.3f} | {rf['avg_launch_ms']:.3f} | "
+              f"{rf['achieved']:.0f} ({100 * rf['frac']:.1f} %) | {r.get('teacher_attn_tflops', float('nan')):.0f} | "
+              f"{fmt(dmd, '{:.3f}')} | {fmt(grad.get('ms_per_call'), '{:.3f}')} | "
+              f"{fmt(grad.get('attn_bwd_tflops'), '{:.0f}')} |")
+    return rows
+
+
 if __name__ == "__main__":
+    if sys.argv[1] == "--per-config":
+        per_config(sys.argv[2:])
+        sys.exit(0)
     if sys.argv[1] == "--clock":
         res = clock_table(sys.argv[2])
         if len(sys.argv) > 3:

@@ -40,9 +40,22 @@ def _torch():
     return torch
 
 
-def student_x0_torch(zv, za, t, text, mask, W, H, param="x0"):
+def _attention_rows(q, k, v, dh):
+    """softmax(q k^T / sqrt(dh)) v for a block of query rows (one head)."""
+    torch = _torch()
+    s = (q @ k.T) / math.sqrt(dh)
+    return torch.softmax(s, dim=1) @ v
+
+
+def student_x0_torch(zv, za, t, text, mask, W, H, param="x0", query_chunk=None):
     """The student's x0-predictions as a torch float64 graph of the weights
-    ``W`` (dict of tensors); zv, za, text are float64 tensors, t a float."""
+    ``W`` (dict of tensors); zv, za, text are float64 tensors, t a float.
+
+    ``query_chunk``: evaluate each head's attention over blocks of that many
+    query rows and let autograd recompute a block's logits and softmax in the
+    backward pass instead of keeping them (torch.utils.checkpoint): the same
+    arithmetic, with memory for one block of logits at a time, which the
+    high-resolution workload needs (29k x 29k logits per head)."""
     torch = _torch()
     d = W["w_t"].shape[0]
     dh = d // H
@@ -67,9 +80,14 @@ def student_x0_torch(zv, za, t, text, mask, W, H, param="x0"):
     outs = []
     for h in range(H):
         sl = slice(h * dh, (h + 1) * dh)
-        s = (Q[:, sl] @ K[:, sl].T) / math.sqrt(dh)
-        p = torch.softmax(s, dim=1)
-        outs.append(p @ V[:, sl])
+        if query_chunk is None:
+            outs.append(_attention_rows(Q[:, sl], K[:, sl], V[:, sl], dh))
+        else:
+            from torch.utils.checkpoint import checkpoint
+            blocks = [checkpoint(_attention_rows, Q[r0:r0 + query_chunk, sl], K[:, sl], V[:, sl], dh,
+                                 use_reentrant=False)
+                      for r0 in range(0, Nq, query_chunk)]
+            outs.append(torch.cat(blocks, dim=0))
     Y = torch.cat(outs, dim=1)
     Nv = hv.shape[0]
     yv = Y[:Nv] @ W["w_out_v"].T
@@ -79,11 +97,12 @@ def student_x0_torch(zv, za, t, text, mask, W, H, param="x0"):
     return yv, ya
 
 
-def scm_loss_and_grads(problem: dict, scm_result: dict | None = None) -> dict:
+def scm_loss_and_grads(problem: dict, scm_result: dict | None = None, query_chunk=None) -> dict:
     """sum_b L_b of the joint sCM loss with gbar held constant, and its
     gradient with respect to every student weight (float64 arrays shaped like
     the weights).  ``scm_result`` is the sCM oracle's output for the same
-    problem (computed here when absent)."""
+    problem (computed here when absent); ``query_chunk`` as in
+    student_x0_torch."""
     torch = _torch()
     cfg, data = problem["cfg"], problem["data"]
     param = getattr(cfg, "param", "x0")
@@ -95,7 +114,8 @@ def scm_loss_and_grads(problem: dict, scm_result: dict | None = None) -> dict:
         t = float(data["t"][b])
         zt = {m: torch.tensor(res[f"z_t_{m}"][b]) for m in "va"}
         text = torch.tensor(np.asarray(data["text"][b], np.float64))
-        xv, xa = student_x0_torch(zt["v"], zt["a"], t, text, data["text_mask"][b], W, cfg.H, param)
+        xv, xa = student_x0_torch(zt["v"], zt["a"], t, text, data["text_mask"][b], W, cfg.H, param,
+                                  query_chunk=query_chunk)
         Lb = torch.zeros((), dtype=torch.float64)
         for m, x0, w in (("v", xv, cfg.w_v), ("a", xa, cfg.w_a)):
             F = (math.cos(t) * zt[m] - x0) / math.sin(t)

@@ -1,11 +1,13 @@
 """Write oracle expectations for the training backward at full size (calls only
 oracle/ and the seeded inputs).
 
-For the standard workload this runs the fp64 sCM oracle (for gbar) and the fp64
-autograd backward, and stores per student weight: the gradient's norm, its
-inner products with four seeded random directions, and 2048 seeded sampled
-entries; plus the per-sample loss.  The GPU test draws the same directions and
-indices from the same seeds.
+For the standard and high-resolution workloads this runs the fp64 sCM oracle
+(for gbar) and the fp64 autograd backward, and stores per student weight: the
+gradient's norm, its inner products with four seeded random directions, and
+2048 seeded sampled entries; plus the per-sample loss.  The GPU test draws the
+same directions and indices from the same seeds.  At high resolution the
+attention is evaluated in blocks of query rows recomputed in the backward
+(the oracle's query_chunk), since 29k x 29k logits per head do not fit.
 Usage: python tests/golden/make_grad_expected.py [names...]
 """
 import os
@@ -39,7 +41,7 @@ def main(names):
         cfg = inputs.CONFIGS[name]
         t0 = time.time()
         p = inputs.make_problem(cfg)
-        g = oracle.scm_loss_and_grads(p)
+        g = oracle.scm_loss_and_grads(p, query_chunk=4096 if cfg.Nv > 10000 else None)
         out = {"t": p["data"]["t"], "loss": g["loss"]}
         for k in WEIGHTS:
             dirs, idx = probes(g[k].shape, k)

@@ -92,3 +92,17 @@ def test_batch_gradient_is_the_sum_over_samples():
     for k in WEIGHTS:
         assert rel_l2(g[k], parts[0][k] + parts[1][k]) < 1e-12, k
     assert abs(g["loss_sum"] - parts[0]["loss_sum"] - parts[1]["loss_sum"]) < 1e-12
+
+
+def test_query_chunked_backward_matches_the_plain_one():
+    """The chunked, recomputed attention (used at high resolution, where the
+    logits do not fit in memory) gives the plain autograd's loss and
+    gradients: the same arithmetic, evaluated block by block.  Query blocks of
+    17 rows do not divide the 80 queries of the tiny workload."""
+    p = inputs.make_problem(inputs.CONFIGS["tiny"])
+    ref = oracle.scm_target(p)
+    a = oracle.scm_loss_and_grads(p, ref)
+    b = oracle.scm_loss_and_grads(p, ref, query_chunk=17)
+    assert np.allclose(a["loss"], b["loss"], rtol=1e-13, atol=0)
+    for k in oracle.grad_oracle.WEIGHTS:
+        assert np.allclose(a[k], b[k], rtol=1e-10, atol=1e-14 * np.max(np.abs(a[k]))), k
