@@ -114,6 +114,8 @@ def test_full_size_dmd_against_stored_oracle(name):
     from joint_video_audio_trigflow_amd import _lib
     path = os.path.join(GOLDEN, f"expected_dmd_{name}.npz")
     print(f"full-size dmd_target {name}", flush=True)
+    if not os.path.exists(path):
+        pytest.skip(f"{os.path.basename(path)} not written yet (tests/golden/make_full_size_expected.py --dmd {name})")
     exp = np.load(path)
     cfg = inputs.CONFIGS[name]
     p = inputs.make_dmd_problem(cfg)
