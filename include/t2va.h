@@ -129,7 +129,8 @@ t2va_status t2va_trigflow_field(int mode, int B, int64_t n_per_sample, int a_dty
  *   q, qd   element (b, i, h, c) at  b*q_batch_stride + i*q_row_stride + h*dh + c
  *           (sequence-major; the projection's [B, N, H*dh] output works as is)
  *   k, kd   element (b, j, h, c) at  b*k_batch_stride + j*k_row_stride + h*dh + c
- *   vt, vdt V stored dh-major per head ("V transposed"):
+ *   vt, vdt V stored dh-major per head ("V transposed"; t2va_v_transpose
+ *           converts a sequence-major V):
  *           element (b, j, h, c) at  b*vt_batch_stride + h*vt_head_stride + c*vt_row_stride + j
  *           vt_row_stride must be a multiple of 8 and >= round_up(Nk, 64).  Keys
  *           are read in blocks of 64: columns j in [nk_valid[b], round_up(nk_valid[b], 64))
@@ -176,6 +177,25 @@ t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, c
                                     const void *vt, const void *qd, const void *kd,
                                     const void *vdt, const int32_t *nk_valid, void *o, void *od,
                                     float *lse, t2va_stream stream);
+
+/*
+ * t2va_v_transpose - V (or dV) from the sequence-major layout of q and k to
+ * the dh-major layout the attention entry points take for V:
+ *   vt[b*vt_batch_stride + h*vt_head_stride + c*vt_row_stride + j]
+ *       = v[b*v_batch_stride + j*v_row_stride + h*dh + c]        for j < N,
+ * and columns j in [N, round_up(N, 64)) are written as zeros.  The joint
+ * block's own QKV projection writes V in the dh-major layout directly; this is
+ * for callers holding V sequence-major, e.g. in place in a fused [B, N, 3 H dh]
+ * projection output (v then points at its V columns).
+ *   B, N, H >= 1; dh in {64, 128}; all strides in elements, non-negative
+ *   multiples of 8; v_row_stride >= H*dh; vt_row_stride >= round_up(N, 64);
+ *   v and vt 16-byte aligned device buffers that do not overlap.
+ * Errors: T2VA_INVALID_ARG (null/misaligned pointers, strides),
+ * T2VA_UNSUPPORTED_SHAPE (B, N, H < 1 or dh not 64/128).
+ */
+t2va_status t2va_v_transpose(int B, int N, int H, int dh, const void *v, int64_t v_batch_stride,
+                             int64_t v_row_stride, void *vt, int64_t vt_batch_stride, int64_t vt_head_stride,
+                             int64_t vt_row_stride, t2va_stream stream);
 
 /*
  * t2va_joint_attn_fwd_jvp_split - as t2va_joint_attn_fwd_jvp, with the logits

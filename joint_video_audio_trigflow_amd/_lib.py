@@ -97,6 +97,8 @@ def load() -> ctypes.CDLL:
     lib.t2va_trigflow_field.argtypes = [i32, i32, i64, i32, i32, i32, dp, vp, vp, vp, vp]
     lib.t2va_joint_attn_fwd_jvp.restype = i32
     lib.t2va_joint_attn_fwd_jvp.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 10 + [vp]
+    lib.t2va_v_transpose.restype = i32
+    lib.t2va_v_transpose.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i64, vp]
     lib.t2va_joint_attn_fwd_jvp_split.restype = i32
     lib.t2va_joint_attn_fwd_jvp_split.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 12 + [vp]
     lib.t2va_scm_workspace_bytes.restype = ctypes.c_size_t
@@ -214,6 +216,18 @@ def joint_attn_fwd_jvp(q, k, vt, nk, qd=None, kd=None, vdt=None, out_dtype=torch
                                        _ptr(kd), _ptr(vdt), _ptr(nk), _ptr(o), _ptr(od), _ptr(lse),
                                        _stream(q.device)))
     return o, od, lse
+
+
+def v_transpose(v: torch.Tensor) -> torch.Tensor:
+    """Sequence-major V [B, N, H, dh] (last two dims dense) -> dh-major V^T
+    [B, H, dh, round_up(N, 64)] with zero padding, on the device."""
+    B, N, H, dh = v.shape
+    assert v.stride(3) == 1 and v.stride(2) == dh
+    ldv = (N + 63) // 64 * 64
+    vt = torch.empty((B, H, dh, ldv), dtype=v.dtype, device=v.device)
+    _check(load().t2va_v_transpose(B, N, H, dh, _ptr(v), v.stride(0), v.stride(1), _ptr(vt), vt.stride(0),
+                                   vt.stride(1), vt.stride(2), _stream(v.device)))
+    return vt
 
 
 def joint_attn_fwd_jvp_split(q, q_lo, k, k_lo, vt, nk, qd=None, kd=None, vdt=None, out_dtype=torch.float32,

@@ -851,6 +851,29 @@ t2va_status t2va_joint_attn_fwd_jvp(const t2va_attn_desc *desc, const void *q, c
   return attn_entry(desc, q, nullptr, k, nullptr, vt, qd, kd, vdt, nk_valid, o, od, lse, stream, false);
 }
 
+t2va_status t2va_v_transpose(int B, int N, int H, int dh, const void *v, int64_t v_batch_stride,
+                             int64_t v_row_stride, void *vt, int64_t vt_batch_stride, int64_t vt_head_stride,
+                             int64_t vt_row_stride, t2va_stream stream) {
+  g_err.clear();
+  if (B < 1 || N < 1 || H < 1) return fail(T2VA_UNSUPPORTED_SHAPE, "B, N and H must be >= 1");
+  if (dh != 64 && dh != 128) return fail(T2VA_UNSUPPORTED_SHAPE, "dh = %d must be 64 or 128", dh);
+  if (!v || !vt) return fail(T2VA_INVALID_ARG, "v and vt are required");
+  if (!aligned16(v) || !aligned16(vt)) return fail(T2VA_INVALID_ARG, "v and vt must be 16-byte aligned");
+  const int64_t strides[] = {v_batch_stride, v_row_stride, vt_batch_stride, vt_head_stride, vt_row_stride};
+  for (int64_t st : strides)
+    if (st < 0 || st % 8) return fail(T2VA_INVALID_ARG, "strides must be non-negative multiples of 8");
+  if (v_row_stride < (int64_t)H * dh) return fail(T2VA_INVALID_ARG, "v_row_stride must cover H*dh elements");
+  const int npad = (N + 63) / 64 * 64;
+  if (vt_row_stride < npad)
+    return fail(T2VA_INVALID_ARG, "vt_row_stride %lld < round_up(N, 64)", (long long)vt_row_stride);
+  TransposeParams tp;
+  tp.src = v; tp.s_bs = v_batch_stride; tp.s_hs = dh; tp.s_rs = v_row_stride;
+  tp.dst = (bf16 *)vt; tp.d_bs = vt_batch_stride; tp.d_hs = vt_head_stride; tp.d_rs = vt_row_stride;
+  tp.B = B; tp.H = H; tp.R = N; tp.C = dh; tp.Rpad = npad;
+  HIP_TRY(launch_transpose(tp, 0, (hipStream_t)stream), "transpose kernel launch");
+  return T2VA_OK;
+}
+
 t2va_status t2va_joint_attn_fwd_jvp_split(const t2va_attn_desc *desc, const void *q, const void *q_lo,
                                           const void *k, const void *k_lo, const void *vt, const void *qd,
                                           const void *kd, const void *vdt, const int32_t *nk_valid, void *o,

@@ -284,3 +284,18 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     d.gamma = 2.0   # descriptor errors come first
     st = lib.t2va_scm_target_noalloc(ctypes.byref(d), ctypes.byref(w), ctypes.byref(w), *ptrs, t, *outs, None)
     assert st == 1 and "gamma" in err(lib)
+
+
+def test_v_transpose_rejects_before_launch(lib):
+    """The dh-major V layout of the attention entry points: t2va_v_transpose
+    converts a sequence-major V and rejects what it cannot convert."""
+    v, vt = fake_ptr(1), fake_ptr(2)
+    call = lambda B=1, N=100, H=2, dh=128, vrs=256, vtrs=128, vp=v: lib.t2va_v_transpose(
+        B, N, H, dh, vp, N * vrs, vrs, vt, 2 * 128 * vtrs, 128 * vtrs, vtrs, None)
+    assert call(dh=96) == 2
+    assert call(N=0) == 2
+    assert call(vtrs=64) == 1 and "round_up" in err(lib)      # 100 keys need 128 columns
+    assert call(vrs=200) == 1                                  # below H * dh
+    assert call(vrs=260) == 1                                  # not a multiple of 8
+    assert call(vp=ctypes.c_void_p(0x10008)) == 1 and "aligned" in err(lib)
+    assert call(vp=None) == 1

@@ -151,6 +151,32 @@ def test_attention_bf16_output_and_padding_garbage():
     assert rel_l2(o, eo) < 1e-2 and rel_l2(od, eod) < 1e-2
 
 
+def test_attention_with_sequence_major_v_through_v_transpose():
+    """A caller holding V (and dV) sequence-major, in place in a fused
+    [B, N, 3 H dh] projection output, converts them with t2va_v_transpose:
+    the result equals the dh-major path's bit for bit."""
+    L = lib()
+    B, H, dh, Nq, Nk = 2, 3, 64, 90, 131
+    say("attention with sequence-major V via t2va_v_transpose")
+    ops = inputs.make_attention_operands(B, H, dh, Nq, Nk, seed=17, nk_valid=[131, 100])
+    fused = np.zeros((B, Nk, 3, H, dh), np.float32)
+    fused[:, :, 2] = ops["v"]
+    fz = torch.from_numpy(fused.reshape(B, Nk, 3 * H * dh)).to("cuda", torch.bfloat16)
+    v_view = fz[:, :, 2 * H * dh:].view(B, Nk, H, dh)       # strided: row stride 3 H dh
+    vt = L.v_transpose(v_view)
+    vdt = L.v_transpose(torch.from_numpy(ops["vd"].astype(np.float32)).to("cuda", torch.bfloat16).contiguous())
+    torch.cuda.synchronize()
+    assert vt.shape == (B, H, dh, 192) and torch.all(vt[..., Nk:] == 0)
+
+    def dev(x):
+        return torch.from_numpy(x.astype(np.float32)).to("cuda", torch.bfloat16).contiguous()
+
+    nk = torch.from_numpy(ops["nk"]).to("cuda")
+    o1, od1, _ = L.joint_attn_fwd_jvp(dev(ops["q"]), dev(ops["k"]), vt, nk, dev(ops["qd"]), dev(ops["kd"]), vdt)
+    o2, od2, _ = run_attention(ops, H, dh, True)
+    assert np.array_equal(o1.cpu().numpy(), o2) and np.array_equal(od1.cpu().numpy(), od2)
+
+
 def test_attention_softmax_tangent_with_constant_values():
     """V = 1, dV = 0 gives O = 1 and dO = 0 (rows of dP sum to zero)."""
     B, H, dh, Nq, Nk = 1, 1, 128, 64, 200
