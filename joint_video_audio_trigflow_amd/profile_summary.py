@@ -14,6 +14,12 @@ median and min, the student attention's time and rate against the dense bf16
 peak, the teacher attention's rate, and the DMD term's and the backward's
 times when present.
 
+With --counters-record <dir> <out.json>, after the summary above it writes the
+record bench.py reads for the roofline's "traffic" field: the student
+attention's counted bytes per launch (its kernel and its split-tail merge),
+the calibration factors, the commands, and the digest of the attention
+sources the counters were taken on.
+
 With --clock <dir>, it reads one --pmc --kernel-trace run per subdirectory of
 <dir> instead and prints, per attention and GEMM kernel, the average of each
 counter per dispatch and these derived figures (MI355X: 8 XCDs, 256 CUs,
@@ -33,10 +39,12 @@ import sys
 
 
 def short(name: str) -> str:
-    for key, label in (("attn_fwd_jvp_kernel<128, true>", "attn_fwd_jvp<128,true> (student fwd+JVP)"),
-                       ("attn_fwd_jvp_kernel<128, false>", "attn_fwd_jvp<128,false> (forward: teacher, fake)"),
-                       ("attn_combine_kernel<128, true>", "attn_combine<128,true> (JVP split-tail merge)"),
-                       ("attn_combine_kernel<128, false>", "attn_combine<128,false> (forward split-tail merge)"),
+    for key, label in (("attn_fwd_jvp_kernel<128, true, false>", "attn_fwd_jvp<128,true> (student fwd+JVP)"),
+                       ("attn_fwd_jvp_kernel<128, false, false>", "attn_fwd_jvp<128,false> (forward: teacher, fake)"),
+                       ("attn_fwd_jvp_kernel<128, true, true>", "attn_fwd_jvp<128,true,split> (student, split)"),
+                       ("attn_fwd_jvp_kernel<128, false, true>", "attn_fwd_jvp<128,false,split> (forward, split)"),
+                       ("attn_combine_kernel<128, true, false>", "attn_combine<128,true> (JVP split-tail merge)"),
+                       ("attn_combine_kernel<128, false, false>", "attn_combine<128,false> (forward split-tail merge)"),
                        ("attn_bwd_dkv_kernel<128>", "attn_bwd_dkv<128> (backward dK, dV)"),
                        ("attn_bwd_dq_kernel<128>", "attn_bwd_dq<128> (backward dQ)"),
                        ("attn_bwd_dkv_merge_kernel<128>", "attn_bwd_dkv_merge<128> (split-tail sum)"),
@@ -50,7 +58,8 @@ def short(name: str) -> str:
     for key in ("trigflow_kernel", "text_rows_kernel", "scm_direction_kernel", "normalise_kernel",
                 "time_linear_kernel", "time_embedding_kernel", "cast_kernel", "dmd_direction_kernel",
                 "transpose16_kernel", "transpose_kernel", "rowterm_kernel", "seed_kernel", "colsum_kernel", "time_grad_kernel",
-                "reduce_splits_kernel", "zero_rows_kernel", "fill_nk_kernel", "mix_kernel"):
+                "reduce_splits_kernel", "zero_rows_kernel", "fill_nk_kernel", "mix_kernel", "guide_kernel",
+                "split_rows_kernel", "dup_cols_kernel"):
         if key in name:
             return key
     return name[:60]
@@ -160,7 +169,50 @@ def per_config(paths):
     return rows
 
 
+COUNTER_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <dir>/FETCH_SIZE -o run -- python3 bench.py "
+    "--steps 2 --warmup 1 --no-cpu-baseline --dmd-steps 1 --grad-steps 1",
+    "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d <dir>/WRITE_SIZE -o run -- python3 bench.py "
+    "--steps 2 --warmup 1 --no-cpu-baseline --dmd-steps 1 --grad-steps 1",
+    "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <dir>/copy_FETCH_SIZE -o run -- python3 "
+    "bench.py --copy-calibration 1024 --steps 3",
+    "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d <dir>/copy_WRITE_SIZE -o run -- python3 "
+    "bench.py --copy-calibration 1024 --steps 3",
+    "python -m joint_video_audio_trigflow_amd.profile_summary --counters-record <dir> "
+    "profiles/attn_fwd_jvp_high_res_counters.json",
+]
+
+
+def counters_record(d, out_path):
+    """The student attention's counted traffic per launch, for bench.py."""
+    res = main(d)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    k, c = "attn_fwd_jvp<128,true> (student fwd+JVP)", "attn_combine<128,true> (JVP split-tail merge)"
+    rec = {
+        "kernel": "attn_fwd_jvp_kernel<128,true>",
+        "workload": "high-res joint sCM target (bench.py defaults)",
+        "kernel_source_digest": bench.attention_kernel_digest(),
+        "kernel_source_digest_of": "bench.attention_kernel_digest(): attention.hip + attn_tiles.h + common.h up "
+                                   "to the per-sample coefficient table + struct AttnParams",
+        "fetch_kib_per_dispatch": res["fetch"][k],
+        "write_kib_per_dispatch": res["write"][k],
+        "fetch_factor": res["fetch_factor"],
+        "write_factor": res["write_factor"],
+        "traffic_bytes_per_launch": res["bytes"][k] + res["bytes"].get(c, 0.0),
+        "commands": COUNTER_COMMANDS,
+        "combine_fetch_kib_per_dispatch": res["fetch"].get(c, 0.0),
+        "combine_write_kib_per_dispatch": res["write"].get(c, 0.0),
+    }
+    json.dump(rec, open(out_path, "w"), indent=1)
+    return rec
+
+
 if __name__ == "__main__":
+    if sys.argv[1] == "--counters-record":
+        counters_record(sys.argv[2], sys.argv[3])
+        sys.exit(0)
     if sys.argv[1] == "--per-config":
         per_config(sys.argv[2:])
         sys.exit(0)
