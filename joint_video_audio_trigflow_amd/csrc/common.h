@@ -94,6 +94,9 @@ hipError_t launch_time_embedding(const CoefTable &coef, int d, float *E, hipStre
 // tau[r] = W_t e_r for r in [0, rows): fp32 [rows, d] from bf16 W_t [d, d].
 hipError_t launch_time_linear(const float *E, int rows, int d, const bf16 *w_t, float *tau,
                               hipStream_t s);
+// out[r] = W e_r for r in [0, rows): fp32 [rows, n_out] from bf16 W [n_out, d] and fp32 E [rows, d].
+hipError_t launch_row_linear(const float *E, int rows, int d, int n_out, const bf16 *W, float *out,
+                             hipStream_t s);
 
 // Text rows of X: for each sample, the valid text positions (mask != 0) in
 // order, converted to bf16, at rows [Nq, Nq + count); rows up to Nq + Nt are

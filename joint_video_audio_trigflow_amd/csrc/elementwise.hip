@@ -130,12 +130,12 @@ __global__ __launch_bounds__(kThreads) void time_embedding_kernel(CoefTable coef
   de[half + k] = wd * cs;
 }
 
-// One wave per output feature i: tau[r][i] = sum_k W_t[i][k] E[r][k].
-__global__ __launch_bounds__(kThreads) void time_linear_kernel(const float *E, int rows, int d,
+// One wave per output feature i: out[r][i] = sum_k W[i][k] E[r][k] (W [n_out][d]).
+__global__ __launch_bounds__(kThreads) void time_linear_kernel(const float *E, int rows, int d, int n_out,
                                                                const bf16 *w_t, float *tau) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (i >= d) return;
+  if (i >= n_out) return;
   const bf16 *wr = w_t + (int64_t)i * d;
   for (int r = 0; r < rows; ++r) {
     const float *er = E + (int64_t)r * d;
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void time_linear_kernel(const float *E, i
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) tau[(int64_t)r * d + i] = acc;
+    if (lane == 0) tau[(int64_t)r * n_out + i] = acc;
   }
 }
 
@@ -438,7 +438,12 @@ hipError_t launch_time_embedding(const CoefTable &coef, int d, float *E, hipStre
 
 hipError_t launch_time_linear(const float *E, int rows, int d, const bf16 *w_t, float *tau,
                               hipStream_t s) {
-  hipLaunchKernelGGL(time_linear_kernel, dim3((d + 3) / 4), dim3(kThreads), 0, s, E, rows, d, w_t, tau);
+  return launch_row_linear(E, rows, d, d, w_t, tau, s);
+}
+
+hipError_t launch_row_linear(const float *E, int rows, int d, int n_out, const bf16 *W, float *out,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(time_linear_kernel, dim3((n_out + 3) / 4), dim3(kThreads), 0, s, E, rows, d, n_out, W, out);
   return hipGetLastError();
 }
 

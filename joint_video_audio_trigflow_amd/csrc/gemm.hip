@@ -158,7 +158,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p1, Gemm
         for (int g = 0; g < 4; ++g) {
           const int row = m0 + wm * 64 + i * 32 + 8 * g + 4 * hi;
           // rows in [M, vt_rows) read zero A rows: they store the zero padding
-          if (row + 3 < p.vt_rows) {
+          // (V^T may start at any token: a vector store needs an aligned address)
+          if (row + 3 < p.vt_rows && (((uintptr_t)(vt + row)) & 7) == 0) {
             bf16x4 pk;
 #pragma unroll
             for (int u = 0; u < 4; ++u) pk[u] = (bf16)(acc[i][j][4 * g + u] + bcol);
@@ -460,7 +461,7 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
         const bf16x8 v = read_chunk(st + c * 128, rc, ekey_col(c));
         const int cc = col - p.n_split;
         bf16 *vt = p.VT + (int64_t)bz * p.vt_bs + (int64_t)(cc / p.dh) * p.vt_hs + (int64_t)(cc % p.dh) * p.vt_rs;
-        if (row + 8 <= p.vt_rows) {
+        if (row + 8 <= p.vt_rows && (((uintptr_t)(vt + row)) & 15) == 0) {
           *reinterpret_cast<bf16x8 *>(vt + row) = v;
         } else {
           for (int u = 0; u < 8; ++u)
@@ -498,7 +499,8 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
         for (int g = 0; g < 4; ++g) {
           const int row = m0 + wm * 128 + i * 32 + 8 * g + 4 * hi;
           // rows in [M, vt_rows) read zero A rows: they store the zero padding
-          if (row + 3 < p.vt_rows) {
+          // (V^T may start at any token: a vector store needs an aligned address)
+          if (row + 3 < p.vt_rows && (((uintptr_t)(vt + row)) & 7) == 0) {
             bf16x4 pk;
 #pragma unroll
             for (int u = 0; u < 4; ++u) pk[u] = (bf16)(acc[i][j][4 * g + u] + bcol);
@@ -541,7 +543,8 @@ hipError_t set_small_attr() {
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
-  if (p.M <= 0 || p.batch <= 0) return hipSuccess;
+  // M = 0 still writes the V^T padding rows [0, vt_rows) as zeros
+  if ((p.M <= 0 && !(p.VT && p.vt_rows > 0)) || p.batch <= 0) return hipSuccess;
   const int rows = max(p.M, p.VT ? p.vt_rows : 0);
   if (use_large(p)) {
     if (!g_lattr_set) {

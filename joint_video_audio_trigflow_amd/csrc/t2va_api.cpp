@@ -189,10 +189,15 @@ hipError_t prepare_dup(const bf16 *W[][6], int count, int Cv, int Ca, int d, bf1
 struct Layout {
   int Nq, N_all, dh, ldv, nblk_v, nblk_a;
   bool split;   // T2VA_PREC_SPLIT: [hi | lo] rows for z, X and Q|K
-  size_t wts, wdup, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v, x0S_a, part_v, part_a, apart;
+  size_t wts, wdup, wfold, wint, bqkv, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v, x0S_a,
+      part_v, part_a, apart;
   size_t total, apart_bytes;
   size_t w_elems[6];  // per-block weight element counts
 };
+
+// bf16 precision: the folded weights of two blocks (W_qkv W_in_m, [3d, C_m] per
+// modality), the W_in^T scratch they are made from, and the QKV bias rows.
+size_t fold_elems(int Cv, int Ca, int d) { return align_up((size_t)3 * d * (Cv + Ca), 128); }
 
 // whole_tiles: no scratch for split attention tails (every tile runs whole).
 Layout make_layout(const t2va_scm_desc &d, bool whole_tiles = false) {
@@ -217,6 +222,9 @@ Layout make_layout(const t2va_scm_desc &d, bool whole_tiles = false) {
   const size_t sp = L.split ? 2 : 1;   // [hi | lo] rows are twice as wide
   L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
   L.wdup = take(L.split ? dup_weight_bytes(d.Cv, d.Ca, d.d, 2) : 0);
+  L.wfold = take(L.split ? 0 : 2 * fold_elems(d.Cv, d.Ca, d.d) * sizeof(bf16));
+  L.wint = take(L.split ? 0 : (size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
+  L.bqkv = take(L.split ? 0 : 2 * B * 3 * D * sizeof(float));
   L.zf_v = take(L.split ? 2 * B * d.Nv * d.Cv * sizeof(float) : 0);
   L.zf_a = take(L.split ? 2 * B * d.Na * d.Ca * sizeof(float) : 0);
   L.zv = take(2 * B * d.Nv * d.Cv * sp * sizeof(bf16));
@@ -355,8 +363,8 @@ t2va_status check_weights(const t2va_block_weights *const *wb, int n, const char
 struct DmdLayout {
   int ldv, nblk_v, nblk_a;
   bool split;
-  size_t wts, wdup, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, nk_null, O, Of, xT_v, xT_a, xF_v, xF_a, pa_v, pa_a,
-      ps_v, ps_a, apart;
+  size_t wts, wdup, wfold, wint, bqkv, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, nk_null, O, Of, xT_v, xT_a, xF_v,
+      xF_a, pa_v, pa_a, ps_v, ps_a, apart;
   size_t total, apart_bytes;
   size_t w_elems[6];
 };
@@ -382,6 +390,9 @@ DmdLayout make_dmd_layout(const t2va_dmd_desc &d) {
   const size_t sp = L.split ? 2 : 1;
   L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
   L.wdup = take(L.split ? dup_weight_bytes(d.Cv, d.Ca, d.d, 2) : 0);
+  L.wfold = take(L.split ? 0 : 2 * fold_elems(d.Cv, d.Ca, d.d) * sizeof(bf16));
+  L.wint = take(L.split ? 0 : (size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
+  L.bqkv = take(L.split ? 0 : B * 3 * D * sizeof(float));
   L.zf_v = take(L.split ? B * nv * sizeof(float) : 0);
   L.zf_a = take(L.split ? B * na * sizeof(float) : 0);
   L.zv = take(B * nv * sp * sizeof(bf16));
@@ -492,23 +503,24 @@ struct Block {
 
   GemmParams params(const bf16 *A, int64_t lda, int64_t a_bs, const bf16 *Wt, int64_t ldw, void *Cp,
                     int64_t ldc, int64_t c_bs, int c_dt, const float *bias, int64_t bias_bs, int M, int N,
-                    int K, int batch, bf16 *vt, int n_split, int64_t w_bs = 0) const {
+                    int K, int batch, bf16 *vt, int n_split, int64_t w_bs = 0, int vt_rows = -1) const {
     GemmParams g;
     g.A = A; g.lda = lda; g.a_bs = a_bs;
     g.W = Wt; g.ldw = ldw; g.w_bs = w_bs;
     g.C = Cp; g.ldc = ldc; g.c_bs = c_bs; g.c_dt = c_dt;
     g.bias = bias; g.bias_bs = bias_bs;
-    g.VT = vt; g.vt_bs = vt_bs; g.vt_hs = vt_hs; g.vt_rs = ldv; g.vt_rows = ldv;
+    g.VT = vt; g.vt_bs = vt_bs; g.vt_hs = vt_hs; g.vt_rs = ldv; g.vt_rows = vt_rows < 0 ? ldv : vt_rows;
     g.n_split = n_split; g.dh = dh;
     g.M = M; g.N = N; g.K = K; g.batch = batch;
     return g;
   }
 
+  // vt_rows: V^T token columns [0, vt_rows) from vt are written (rows past M as zeros); -1: up to ldv
   t2va_status gemm(const bf16 *A, int64_t lda, int64_t a_bs, const bf16 *Wt, int64_t ldw, void *Cp,
                    int64_t ldc, int64_t c_bs, int c_dt, const float *bias, int64_t bias_bs, int M,
-                   int N, int K, int batch, bf16 *vt, int n_split, int64_t w_bs = 0) const {
+                   int N, int K, int batch, bf16 *vt, int n_split, int64_t w_bs = 0, int vt_rows = -1) const {
     const GemmParams g = params(A, lda, a_bs, Wt, ldw, Cp, ldc, c_bs, c_dt, bias, bias_bs, M, N, K, batch, vt,
-                                n_split, w_bs);
+                                n_split, w_bs, vt_rows);
     PhaseScope ps(s, T2VA_PHASE_GEMM, prof);
     HIP_TRY(launch_gemm(g, s), "gemm");
     return T2VA_OK;
@@ -518,6 +530,54 @@ struct Block {
   // into QK and V dh-major into VT, for `batch` problems.  Split: z rows are
   // [hi | lo] (2 C_m wide) against Wd = [W | W], X and Q|K are written as
   // [hi | lo] pairs (X rows [X_hi | X_lo], QK rows [Q_hi | K_hi | Q_lo | K_lo]).
+  // Folded weights of one block (bf16 precision): Wf = W_qkv [W_in_v | W_in_a],
+  // [3d, Cv + Ca] (row stride Cv + Ca; the video part is its first Cv
+  // columns).  Before attention the block is linear, so for video and audio
+  // rows Q|K|V = (z W_in^T + tau) W_qkv^T = z (W_qkv W_in)^T + tau W_qkv^T:
+  // a product with K = C_m instead of the input projection and a K = d
+  // product.  wint: scratch for [W_in_v^T; W_in_a^T], [Cv + Ca, d].
+  t2va_status fold_weights(const bf16 *const *W, bf16 *Wf, bf16 *wint) const {
+    const bf16 *win[2] = {W[0], W[1]};
+    const int C[2] = {Cv, Ca};
+    for (int m = 0; m < 2; ++m) {
+      TransposeParams tp;
+      tp.src = win[m]; tp.s_bs = 0; tp.s_hs = 0; tp.s_rs = C[m];
+      tp.dst = wint + (m ? (int64_t)Cv * D : 0); tp.d_bs = 0; tp.d_hs = 0; tp.d_rs = D;
+      tp.B = 1; tp.H = 1; tp.R = D; tp.C = C[m]; tp.Rpad = D;
+      HIP_TRY(launch_transpose(tp, 0, s), "transpose");
+    }
+    return gemm(W[3], D, 0, wint, D, Wf, Cv + Ca, 0, 0, nullptr, 0, 3 * D, Cv + Ca, D, 1, nullptr, Cv + Ca);
+  }
+
+  // X rows [0, Nq) = [z^v W_in_v^T; z^a W_in_a^T] + tau[b] for `batch` problems.
+  t2va_status in_proj(const bf16 *const *W, const bf16 *zv, const bf16 *za, const float *tau, bf16 *X,
+                      int batch) const {
+    if (t2va_status st = gemm(zv, Cv, nv, W[0], Cv, X, D, x_bs, 0, tau, D, Nv, D, Cv, batch, nullptr, D))
+      return st;
+    return gemm(za, Ca, na, W[1], Ca, X + (int64_t)Nv * D, D, x_bs, 0, tau, D, Na, D, Ca, batch, nullptr, D);
+  }
+
+  // bf16 precision with folded weights Wf [3d, Cv + Ca] (fold_weights): Q|K and
+  // V^T of the video and audio rows straight from z (bias W_qkv tau per batch,
+  // into bqkv [batch][3d]); the text rows [Nq, NA) from X with W_qkv (no bias;
+  // their V^T columns and the zero padding up to ldv).  The audio and text
+  // products are small and run as one two-problem launch.
+  t2va_status project_in_folded(const bf16 *const *W, const bf16 *Wf, const bf16 *zv, const bf16 *za,
+                                const float *tau, float *bqkv, const bf16 *X, bf16 *QK, bf16 *VT, int batch) const {
+    const int CC = Cv + Ca;
+    HIP_TRY(launch_row_linear(tau, batch, D, 3 * D, W[3], bqkv, s), "QKV bias");
+    if (t2va_status st = gemm(zv, Cv, nv, Wf, CC, QK, 2 * D, qk_bs, 0, bqkv, 3 * D, Nv, 3 * D, Cv, batch, VT,
+                              2 * D, 0, Nv))
+      return st;
+    const GemmParams ga = params(za, Ca, na, Wf + Cv, CC, QK + (int64_t)Nv * 2 * D, 2 * D, qk_bs, 0, bqkv, 3 * D,
+                                 Na, 3 * D, Ca, batch, VT + Nv, 2 * D, 0, Na);
+    const GemmParams gt = params(X + (int64_t)Nq * D, D, x_bs, W[3], D, QK + (int64_t)Nq * 2 * D, 2 * D, qk_bs, 0,
+                                 nullptr, 0, NA - Nq, 3 * D, D, batch, VT + Nq, 2 * D, 0, ldv - Nq);
+    PhaseScope ps(s, T2VA_PHASE_GEMM, prof);
+    HIP_TRY(launch_gemm_pair(ga, gt, s), "gemm");
+    return T2VA_OK;
+  }
+
   t2va_status project_in(const bf16 *const *W, const bf16 *const *Wd, const bf16 *zv, const bf16 *za,
                          const float *tau, bf16 *X, bf16 *QK, bf16 *VT, int batch) const {
     if (split) {
@@ -624,6 +684,16 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
   const bf16 *Wd[2][3] = {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}};
   if (L.split) HIP_TRY(prepare_dup(W, 2, d.Cv, d.Ca, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
+  // bf16 precision: fold W_qkv W_in_m for both blocks
+  const bf16 *Wf[2] = {nullptr, nullptr};
+  float *bqkv = (float *)(ws + L.bqkv);
+  if (!L.split) {
+    for (int i = 0; i < 2; ++i) {
+      bf16 *f = (bf16 *)(ws + L.wfold) + i * fold_elems(d.Cv, d.Ca, D);
+      if (t2va_status st = blk.fold_weights(W[i], f, (bf16 *)(ws + L.wint))) return st;
+      Wf[i] = f;
+    }
+  }
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
   float *zf_v = (float *)(ws + L.zf_v), *zf_a = (float *)(ws + L.zf_a);
@@ -670,7 +740,8 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
     HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
 
   // ---------------- teacher: x0_T = G_T(z_t, t, c) ----------------
-  T2VA_CALL(blk.project_in(W[0], Wd[0], zv, za, tau, X, QK, VT, B));
+  if (L.split) T2VA_CALL(blk.project_in(W[0], Wd[0], zv, za, tau, X, QK, VT, B));
+  else T2VA_CALL(blk.project_in_folded(W[0], Wf[0], zv, za, tau, bqkv, X, QK, VT, B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
   T2VA_CALL(blk.project_out(W[0], O, x0T_v, x0T_a, B));
 
@@ -683,7 +754,8 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   if (d.Nt > 0)
     HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X + (int64_t)B * blk.x_bs,
                              blk.x_bs, blk.xs, L.split, 1, nullptr, s), "tangent text rows");
-  T2VA_CALL(blk.project_in(W[1], Wd[1], zv, za, tau, X, QK, VT, 2 * B));
+  if (L.split) T2VA_CALL(blk.project_in(W[1], Wd[1], zv, za, tau, X, QK, VT, 2 * B));
+  else T2VA_CALL(blk.project_in_folded(W[1], Wf[1], zv, za, tau, bqkv, X, QK, VT, 2 * B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, true, T2VA_PHASE_STUDENT_ATTN, lse_student));
   T2VA_CALL(blk.project_out(W[1], O, x0S_v, x0S_a, 2 * B));
 #undef T2VA_CALL
@@ -1078,6 +1150,11 @@ t2va_status t2va_scm_grad(const t2va_scm_desc *desc, const t2va_block_weights *t
   };
 #define T2VA_CALL(x) do { t2va_status _st = (x); if (_st) return _st; } while (0)
 
+  // The token rows X of the student's primal batch (the folded forward never
+  // forms them): the weight gradients contract over them.  tau holds the
+  // student's [tau; dtau] rows.
+  T2VA_CALL(blk.in_proj(Ws, zv, za, (const float *)(ws + L.tau), X, B));
+
   // ---- dL/dy at the block's outputs, and dO = dy W_out ----
   HIP_TRY(launch_seed(coef, (float)d.w_v, gbar_v, dy_v, nv, s), "seed");
   HIP_TRY(launch_seed(coef, (float)d.w_a, gbar_a, dy_a, na, s), "seed");
@@ -1203,6 +1280,15 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
   const bf16 *Wd[2][3] = {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}};
   if (L.split) HIP_TRY(prepare_dup(W, 2, d.Cv, d.Ca, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
+  const bf16 *Wf[2] = {nullptr, nullptr};
+  float *bqkv = (float *)(ws + L.bqkv);
+  if (!L.split) {
+    for (int i = 0; i < 2; ++i) {
+      bf16 *f = (bf16 *)(ws + L.wfold) + i * fold_elems(d.Cv, d.Ca, D);
+      if (t2va_status st = blk.fold_weights(W[i], f, (bf16 *)(ws + L.wint))) return st;
+      Wf[i] = f;
+    }
+  }
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
   float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
@@ -1246,7 +1332,8 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   // this is the guided prediction, and the large scales (5 for audio) no
   // longer amplify two separate roundings.
   HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
-  T2VA_CALL(blk.project_in(W[0], Wd[0], zv, za, tau, X, QK, VT, B));
+  if (L.split) T2VA_CALL(blk.project_in(W[0], Wd[0], zv, za, tau, X, QK, VT, B));
+  else T2VA_CALL(blk.project_in_folded(W[0], Wf[0], zv, za, tau, bqkv, X, QK, VT, B));
   if (guided) {
     float *Of = (float *)(ws + L.Of);
     if (Nq % 32 == 0) {
@@ -1269,7 +1356,8 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
 
   // ---------------- fake-score block ----------------
   HIP_TRY(launch_time_linear(E, B, D, W[1][2], tau, s), "fake time linear");
-  T2VA_CALL(blk.project_in(W[1], Wd[1], zv, za, tau, X, QK, VT, B));
+  if (L.split) T2VA_CALL(blk.project_in(W[1], Wd[1], zv, za, tau, X, QK, VT, B));
+  else T2VA_CALL(blk.project_in_folded(W[1], Wf[1], zv, za, tau, bqkv, X, QK, VT, B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
   T2VA_CALL(blk.project_out(W[1], O, xF_v, xF_a, B));
 #undef T2VA_CALL
