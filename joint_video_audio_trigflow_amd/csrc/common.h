@@ -115,10 +115,18 @@ hipError_t launch_guide(const float *c, const float *u, bf16 *out, int B, int Nq
                         float s_a, hipStream_t s);
 
 // Split rows: fp32 src [nb][rows][w] (strides s_bs, s_rs) -> bf16 dst rows
-// [hi | lo] of 2w elements (strides d_bs, d_rs): hi = bf16(x), lo = bf16(x - hi).
-// w a multiple of 8; strides multiples of 8.
+// [hi | lo] of 2w elements, or with repeat_hi [hi | lo | hi] of 3w (strides
+// d_bs, d_rs): hi = bf16(x), lo = bf16(x - hi).  w a multiple of 8; strides
+// multiples of 8.
 hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 *dst, int64_t d_bs,
-                             int64_t d_rs, int nb, int rows, int w, hipStream_t s);
+                             int64_t d_rs, int nb, int rows, int w, bool repeat_hi, hipStream_t s);
+
+// Folded weights from split-K partials part [splits][rows][Cv + Ca] (fp32,
+// summed in split order): bf16 Wf [rows][Cv + Ca], or with split per modality
+// [rows][3 C_m] = [hi | hi | lo] (hi = bf16(x), lo = bf16(x - hi); video
+// first, audio at 3 rows Cv).  Cv, Ca multiples of 8.
+hipError_t launch_fold_finish(const float *part, int splits, int rows, int Cv, int Ca, bool split, bf16 *Wf,
+                              hipStream_t s);
 
 // W2 [n][2k] = [W | W] for bf16 W [n][k] (k a multiple of 8): the weight of a
 // product whose operand rows are [hi | lo] pairs.

@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void text_rows_kernel(int Nq, int Nt, int
 // Rows of w fp32 values -> rows [hi | lo] of 2w bf16 values.
 __global__ __launch_bounds__(kThreads) void split_rows_kernel(const float *src, int64_t s_bs, int64_t s_rs,
                                                               bf16 *dst, int64_t d_bs, int64_t d_rs,
-                                                              int rows, int w) {
+                                                              int rows, int w, bool repeat_hi) {
   const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
   const int64_t per = (int64_t)rows * w;
   if (i0 >= per) return;
@@ -213,6 +213,7 @@ __global__ __launch_bounds__(kThreads) void split_rows_kernel(const float *src, 
   bf16 *o = dst + bi * d_bs + r * d_rs + c;
   store8(o, f);
   store8(o + w, lo);
+  if (repeat_hi) store8(o + 2 * w, f);
 }
 
 // Guided attention output: u + s (c - u) per element, s by the row's modality.
@@ -238,6 +239,39 @@ __global__ __launch_bounds__(kThreads) void dup_cols_kernel(const bf16 *W, bf16 
   const uint4 v = *reinterpret_cast<const uint4 *>(W + i0);
   *reinterpret_cast<uint4 *>(W2 + r * 2 * k + c) = v;
   *reinterpret_cast<uint4 *>(W2 + r * 2 * k + k + c) = v;
+}
+
+// Folded weights from split-K partials: part [splits][rows][Cv + Ca] fp32,
+// summed over the splits in order.  bf16: Wf [rows][Cv + Ca].  split: per
+// modality [rows][3 C_m] = [hi | hi | lo] (video first, audio at 3 rows Cv).
+__global__ __launch_bounds__(kThreads) void fold_finish_kernel(const float *part, int splits, int rows, int Cv,
+                                                               int Ca, bool split, bf16 *Wf) {
+  const int CC = Cv + Ca;
+  const int64_t n = (int64_t)rows * CC;
+  const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (i0 >= n) return;
+  float f[8], g[8];
+  load8(part + i0, f);
+  for (int k = 1; k < splits; ++k) {
+    load8(part + (int64_t)k * n + i0, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] += g[i];
+  }
+  if (!split) {
+    store8(Wf + i0, f);
+    return;
+  }
+  const int64_t r = i0 / CC;
+  const int c = (int)(i0 - r * CC);   // Cv, Ca multiples of 8: the group stays in one modality
+  const bool vid = c < Cv;
+  const int cm = vid ? Cv : Ca, j = vid ? c : c - Cv;
+  bf16 *o = Wf + (vid ? 0 : (int64_t)3 * rows * Cv) + r * 3 * cm + j;
+  float lo[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lo[i] = f[i] - (float)(bf16)f[i];
+  store8(o, f);
+  store8(o + cm, f);
+  store8(o + 2 * cm, lo);
 }
 
 __global__ __launch_bounds__(kThreads) void cast_kernel(const float *src, bf16 *dst, int64_t n) {
@@ -462,11 +496,21 @@ hipError_t launch_text_rows(int B, int Nq, int Nt, int d, const void *text, int 
 }
 
 hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 *dst, int64_t d_bs,
-                             int64_t d_rs, int nb, int rows, int w, hipStream_t s) {
+                             int64_t d_rs, int nb, int rows, int w, bool repeat_hi, hipStream_t s) {
   const int64_t per = (int64_t)rows * w;
   if (per <= 0 || nb <= 0) return hipSuccess;
   dim3 grid((unsigned)((per + kChunk - 1) / kChunk), nb);
-  hipLaunchKernelGGL(split_rows_kernel, grid, dim3(kThreads), 0, s, src, s_bs, s_rs, dst, d_bs, d_rs, rows, w);
+  hipLaunchKernelGGL(split_rows_kernel, grid, dim3(kThreads), 0, s, src, s_bs, s_rs, dst, d_bs, d_rs, rows, w,
+                     repeat_hi);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_finish(const float *part, int splits, int rows, int Cv, int Ca, bool split, bf16 *Wf,
+                              hipStream_t s) {
+  const int64_t total = (int64_t)rows * (Cv + Ca);
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fold_finish_kernel, dim3((unsigned)((total + kChunk - 1) / kChunk)), dim3(kThreads), 0, s,
+                     part, splits, rows, Cv, Ca, split, Wf);
   return hipGetLastError();
 }
 

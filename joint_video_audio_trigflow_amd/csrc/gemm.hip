@@ -331,7 +331,8 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
   // holds one output row and four consecutive columns per register group;
   // V^T outputs keep the plain order (a lane holds one column, runs of rows).
   const int wcol0 = n0 + wn * 32 * kLJ, wrow0 = m0 + wm * 128;
-  const bool staged = kLWaves == 8 && p.c_dt == 0 && (p.n_split % 64 == 0 || p.n_split >= p.N);
+  // (split outputs c_dt = 2 stage their hi and lo parts one after the other)
+  const bool staged = kLWaves == 8 && (p.c_dt == 0 || p.c_dt == 2) && (p.n_split % 64 == 0 || p.n_split >= p.N);
   const bool rowmajor = staged && wcol0 < p.n_split;
 
   const int KT = p.K / BK;
@@ -399,6 +400,12 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
     // 128x64 tile and writes it out in 16-byte chunks
     bf16 *st = smem + wave * kEpiElems;
     if (rowmajor) {
+      // pass 0: the values (split: their bf16 hi parts); pass 1 (split only):
+      // the lo parts bf16(x - hi), n_split columns further along the row
+      for (int pass = 0; pass < (p.c_dt == 2 ? 2 : 1); ++pass) {
+      // the wave's lanes exchange values through its own LDS tile: keep the
+      // compiler from moving one lane's stores across another lane's loads
+      __builtin_amdgcn_wave_barrier();
       // [128 rows][64 columns]: row m = 32 i + l32; unit 8 j + 2 k + hi holds
       // columns 32 j + 8 k + 4 hi .. + 3
 #pragma unroll
@@ -413,11 +420,13 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const float bc = (bias && wcol0 + c0 + u < p.N) ? bias[wcol0 + c0 + u] : 0.f;
-              pk[u] = (bf16)(acc[i][j][4 * k + u] + bc);
+              const float x = acc[i][j][4 * k + u] + bc;
+              pk[u] = pass == 0 ? (bf16)x : (bf16)(x - (float)(bf16)x);
             }
             *reinterpret_cast<bf16x4 *>(st + m * 64 + 4 * ((8 * j + 2 * k + hi) ^ key)) = pk;
           }
       }
+      __builtin_amdgcn_wave_barrier();
       // chunk q = row q / 8, columns 8 (q % 8) .. + 7
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
@@ -426,13 +435,15 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
         const int row = wrow0 + r, col = wcol0 + 8 * c;
         if (row >= p.M || col >= p.N) continue;
         const bf16x8 v = read_chunk(st + r * 64, c, ekey_row(r));
-        bf16 *dst = reinterpret_cast<bf16 *>(p.C) + (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col;
-        if (col + 8 <= p.N && ((p.ldc | col) & 7) == 0) {
+        bf16 *dst = reinterpret_cast<bf16 *>(p.C) + (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col +
+                    (pass ? p.n_split : 0);
+        if (col + 8 <= p.N && ((p.ldc | col | (pass ? p.n_split : 0)) & 7) == 0) {
           *reinterpret_cast<bf16x8 *>(dst) = v;
         } else {
           for (int u = 0; u < 8; ++u)
             if (col + u < p.N) dst[u] = v[u];
         }
+      }
       }
     } else {
       // V^T, [64 columns][128 rows]: column n = 32 j + l32; unit 8 i + 2 g + hi
@@ -523,9 +534,13 @@ bool g_attr_set = false, g_lattr_set = false;
 namespace {
 // the large tile for wide outputs with many rows; per-(batch, tile) byte
 // extents must fit the 32-bit buffer descriptors
+// The 256x256 tiles for wide outputs with many rows: 2048 rows per problem, or
+// a batch of at least 4096 rows in all whose row tiles are at least 80 % full.
 bool use_large(const GemmParams &p) {
   const int rows = max(p.M, p.VT ? p.vt_rows : 0);
-  return p.N >= 1024 && rows >= 2048 && (int64_t)LBM * p.lda * 2 < ((int64_t)1 << 31) &&
+  const int64_t padded = (int64_t)(rows + LBM - 1) / LBM * LBM;
+  const bool many = rows >= 2048 || ((int64_t)rows * p.batch >= 4096 && 5 * (int64_t)rows >= 4 * padded);
+  return p.N >= 1024 && many && (int64_t)LBM * p.lda * 2 < ((int64_t)1 << 31) &&
          (int64_t)LBN * p.ldw * 2 < ((int64_t)1 << 31);
 }
 int small_tiles(const GemmParams &p) {

@@ -153,33 +153,16 @@ hipError_t prepare_weights(const t2va_block_weights *const *wb, int count, int w
   return hipSuccess;
 }
 
-// Split precision: the input and QKV projections contract [hi | lo] operand
-// rows, so their weights are used as [W | W] (w_in_v [d, 2Cv], w_in_a
-// [d, 2Ca], w_qkv [3d, 2d]), built into the workspace per call.
-void dup_weight_elems(int Cv, int Ca, int d, size_t *n) {
-  const size_t D = d;
-  n[0] = D * 2 * Cv;
-  n[1] = D * 2 * Ca;
-  n[2] = 3 * D * 2 * D;
-}
-size_t dup_weight_bytes(int Cv, int Ca, int d, int blocks) {
-  size_t n[3];
-  dup_weight_elems(Cv, Ca, d, n);
-  size_t c = 0;
-  for (int i = 0; i < 3; ++i) c += align_up(n[i], 128);
-  return (size_t)blocks * c * sizeof(bf16);
-}
-hipError_t prepare_dup(const bf16 *W[][6], int count, int Cv, int Ca, int d, bf16 *dst, const bf16 *Wd[][3],
-                       hipStream_t s) {
-  size_t n[3];
-  dup_weight_elems(Cv, Ca, d, n);
-  const int rows[3] = {d, d, 3 * d}, cols[3] = {Cv, Ca, d}, src[3] = {0, 1, 3};
-  for (int i = 0; i < count; ++i)
-    for (int j = 0; j < 3; ++j) {
-      if (hipError_t e = launch_dup_cols(W[i][src[j]], dst, rows[j], cols[j], s)) return e;
-      Wd[i][j] = dst;
-      dst += align_up(n[j], 128);
-    }
+// Split precision: the text rows' QKV product contracts [X_hi | X_lo] rows, so
+// its weight is used as [W_qkv | W_qkv] ([3d, 2d]), built into the workspace
+// per call for each block.
+size_t dup_qkv_elems(int d) { return align_up((size_t)3 * d * 2 * d, 128); }
+hipError_t prepare_dup(const bf16 *W[][6], int count, int d, bf16 *dst, const bf16 *Wd[], hipStream_t s) {
+  for (int i = 0; i < count; ++i) {
+    if (hipError_t e = launch_dup_cols(W[i][3], dst, 3 * d, d, s)) return e;
+    Wd[i] = dst;
+    dst += dup_qkv_elems(d);
+  }
   return hipSuccess;
 }
 
@@ -188,16 +171,29 @@ hipError_t prepare_dup(const bf16 *W[][6], int count, int Cv, int Ca, int d, bf1
 // ---------------------------------------------------------------------------
 struct Layout {
   int Nq, N_all, dh, ldv, nblk_v, nblk_a;
-  bool split;   // T2VA_PREC_SPLIT: [hi | lo] rows for z, X and Q|K
-  size_t wts, wdup, wfold, wint, bqkv, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v, x0S_a,
+  bool split;   // T2VA_PREC_SPLIT: [hi | lo | hi] z rows, [hi | lo] rows for X and Q|K
+  size_t wts, wdup, wfold, wint, fpart, bqkv, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v,
+      x0S_a,
       part_v, part_a, apart;
   size_t total, apart_bytes;
   size_t w_elems[6];  // per-block weight element counts
 };
 
-// bf16 precision: the folded weights of two blocks (W_qkv W_in_m, [3d, C_m] per
-// modality), the W_in^T scratch they are made from, and the QKV bias rows.
-size_t fold_elems(int Cv, int Ca, int d) { return align_up((size_t)3 * d * (Cv + Ca), 128); }
+// The folded weights of one block (W_qkv W_in_m, [3d, C_m] per modality; in
+// split precision [3d, 3 C_m] per modality, see Block::fold_weights).
+size_t fold_elems(int Cv, int Ca, int d, bool split) {
+  return align_up((size_t)3 * d * (Cv + Ca) * (split ? 3 : 1), 128);
+}
+// The fold's product (3d rows, Cv + Ca columns, K = d) has few output tiles:
+// it runs split-K over up to 8 chunks of d (multiples of 64) into fp32 partials.
+int fold_splits(int d) {
+  int s = 8;
+  while (s > 1 && d % (64 * s)) s /= 2;
+  return s;
+}
+size_t fold_part_bytes(int Cv, int Ca, int d) {
+  return (size_t)fold_splits(d) * 3 * d * (Cv + Ca) * sizeof(float);
+}
 
 // whole_tiles: no scratch for split attention tails (every tile runs whole).
 Layout make_layout(const t2va_scm_desc &d, bool whole_tiles = false) {
@@ -220,15 +216,17 @@ Layout make_layout(const t2va_scm_desc &d, bool whole_tiles = false) {
   };
   L.split = d.precision == T2VA_PREC_SPLIT;
   const size_t sp = L.split ? 2 : 1;   // [hi | lo] rows are twice as wide
+  const size_t spz = L.split ? 3 : 1;  // z rows [hi | lo | hi]
   L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
-  L.wdup = take(L.split ? dup_weight_bytes(d.Cv, d.Ca, d.d, 2) : 0);
-  L.wfold = take(L.split ? 0 : 2 * fold_elems(d.Cv, d.Ca, d.d) * sizeof(bf16));
-  L.wint = take(L.split ? 0 : (size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
-  L.bqkv = take(L.split ? 0 : 2 * B * 3 * D * sizeof(float));
+  L.wdup = take(L.split ? 2 * dup_qkv_elems(d.d) * sizeof(bf16) : 0);
+  L.wfold = take(2 * fold_elems(d.Cv, d.Ca, d.d, L.split) * sizeof(bf16));
+  L.wint = take((size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
+  L.fpart = take(fold_part_bytes(d.Cv, d.Ca, d.d));
+  L.bqkv = take(2 * B * 3 * D * sizeof(float));
   L.zf_v = take(L.split ? 2 * B * d.Nv * d.Cv * sizeof(float) : 0);
   L.zf_a = take(L.split ? 2 * B * d.Na * d.Ca * sizeof(float) : 0);
-  L.zv = take(2 * B * d.Nv * d.Cv * sp * sizeof(bf16));
-  L.za = take(2 * B * d.Na * d.Ca * sp * sizeof(bf16));
+  L.zv = take(2 * B * d.Nv * d.Cv * spz * sizeof(bf16));
+  L.za = take(2 * B * d.Na * d.Ca * spz * sizeof(bf16));
   L.E = take(2 * B * D * sizeof(float));
   L.tau = take(2 * B * D * sizeof(float));
   L.X = take(2 * B * L.N_all * D * sp * sizeof(bf16));
@@ -363,7 +361,8 @@ t2va_status check_weights(const t2va_block_weights *const *wb, int n, const char
 struct DmdLayout {
   int ldv, nblk_v, nblk_a;
   bool split;
-  size_t wts, wdup, wfold, wint, bqkv, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, nk_null, O, Of, xT_v, xT_a, xF_v,
+  size_t wts, wdup, wfold, wint, fpart, bqkv, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, nk_null, O, Of, xT_v,
+      xT_a, xF_v,
       xF_a, pa_v, pa_a, ps_v, ps_a, apart;
   size_t total, apart_bytes;
   size_t w_elems[6];
@@ -388,15 +387,17 @@ DmdLayout make_dmd_layout(const t2va_dmd_desc &d) {
   };
   L.split = d.precision == T2VA_PREC_SPLIT;
   const size_t sp = L.split ? 2 : 1;
+  const size_t spz = L.split ? 3 : 1;
   L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
-  L.wdup = take(L.split ? dup_weight_bytes(d.Cv, d.Ca, d.d, 2) : 0);
-  L.wfold = take(L.split ? 0 : 2 * fold_elems(d.Cv, d.Ca, d.d) * sizeof(bf16));
-  L.wint = take(L.split ? 0 : (size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
-  L.bqkv = take(L.split ? 0 : B * 3 * D * sizeof(float));
+  L.wdup = take(L.split ? 2 * dup_qkv_elems(d.d) * sizeof(bf16) : 0);
+  L.wfold = take(2 * fold_elems(d.Cv, d.Ca, d.d, L.split) * sizeof(bf16));
+  L.wint = take((size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
+  L.fpart = take(fold_part_bytes(d.Cv, d.Ca, d.d));
+  L.bqkv = take(B * 3 * D * sizeof(float));
   L.zf_v = take(L.split ? B * nv * sizeof(float) : 0);
   L.zf_a = take(L.split ? B * na * sizeof(float) : 0);
-  L.zv = take(B * nv * sp * sizeof(bf16));
-  L.za = take(B * na * sp * sizeof(bf16));
+  L.zv = take(B * nv * spz * sizeof(bf16));
+  L.za = take(B * na * spz * sizeof(bf16));
   L.E = take(2 * B * D * sizeof(float));
   L.tau = take(B * D * sizeof(float));
   L.X = take(B * N_all * D * sp * sizeof(bf16));
@@ -478,7 +479,7 @@ struct PhaseScope {
 // unconditional outputs).
 struct Block {
   int B, Nv, Na, Cv, Ca, D, H, dh, Nq, NA, ldv;
-  bool split;        // T2VA_PREC_SPLIT: z, X and Q|K rows are [hi | lo] pairs
+  bool split;        // T2VA_PREC_SPLIT: z rows [hi | lo | hi], X and Q|K rows [hi | lo]
   int64_t xs, qks;   // row strides of X (d, or 2d split) and QK (2d, or 4d split)
   int64_t nv, na, x_bs, qk_bs, vt_hs, vt_bs, o_bs;
   hipStream_t s;
@@ -526,17 +527,19 @@ struct Block {
     return T2VA_OK;
   }
 
-  // X rows [0, Nq) = [z^v W_in_v^T; z^a W_in_a^T] + tau[b]; then Q|K row-major
-  // into QK and V dh-major into VT, for `batch` problems.  Split: z rows are
-  // [hi | lo] (2 C_m wide) against Wd = [W | W], X and Q|K are written as
-  // [hi | lo] pairs (X rows [X_hi | X_lo], QK rows [Q_hi | K_hi | Q_lo | K_lo]).
-  // Folded weights of one block (bf16 precision): Wf = W_qkv [W_in_v | W_in_a],
-  // [3d, Cv + Ca] (row stride Cv + Ca; the video part is its first Cv
-  // columns).  Before attention the block is linear, so for video and audio
-  // rows Q|K|V = (z W_in^T + tau) W_qkv^T = z (W_qkv W_in)^T + tau W_qkv^T:
-  // a product with K = C_m instead of the input projection and a K = d
-  // product.  wint: scratch for [W_in_v^T; W_in_a^T], [Cv + Ca, d].
-  t2va_status fold_weights(const bf16 *const *W, bf16 *Wf, bf16 *wint) const {
+  // Folded weights of one block: Wf = W_qkv [W_in_v | W_in_a].  Before
+  // attention the block is linear, so for video and audio rows Q|K|V =
+  // (z W_in^T + tau) W_qkv^T = z (W_qkv W_in)^T + tau W_qkv^T: a product with
+  // K = C_m instead of the input projection and a K = d product.  wint:
+  // scratch for [W_in_v^T; W_in_a^T], [Cv + Ca, d].
+  //   bf16: Wf [3d, Cv + Ca] (row stride Cv + Ca; the video part is its first
+  //     Cv columns).
+  //   split: per modality Wf_m [3d, 3 C_m] = [Wf_hi | Wf_hi | Wf_lo] (video,
+  //     then audio at 9 d Cv), the hi/lo pair of the fp32 product; against z
+  //     rows [z_hi | z_lo | z_hi] one K = 3 C_m product then sums
+  //     z_hi Wf_hi + z_lo Wf_hi + z_hi Wf_lo, the pair product less its
+  //     lo x lo term (relative 2^-18).
+  t2va_status fold_weights(const bf16 *const *W, bf16 *Wf, bf16 *wint, float *fpart) const {
     const bf16 *win[2] = {W[0], W[1]};
     const int C[2] = {Cv, Ca};
     for (int m = 0; m < 2; ++m) {
@@ -546,7 +549,13 @@ struct Block {
       tp.B = 1; tp.H = 1; tp.R = D; tp.C = C[m]; tp.Rpad = D;
       HIP_TRY(launch_transpose(tp, 0, s), "transpose");
     }
-    return gemm(W[3], D, 0, wint, D, Wf, Cv + Ca, 0, 0, nullptr, 0, 3 * D, Cv + Ca, D, 1, nullptr, Cv + Ca);
+    // split-K: chunk k of W_qkv's columns against the same chunk of W_in^T's
+    const int splits = fold_splits(D), kc = D / splits, CC = Cv + Ca;
+    if (t2va_status st = gemm(W[3], D, kc, wint, D, fpart, CC, (int64_t)3 * D * CC, 1, nullptr, 0, 3 * D, CC, kc,
+                              splits, nullptr, CC, kc))
+      return st;
+    HIP_TRY(launch_fold_finish(fpart, splits, 3 * D, Cv, Ca, split, Wf, s), "fold");
+    return T2VA_OK;
   }
 
   // X rows [0, Nq) = [z^v W_in_v^T; z^a W_in_a^T] + tau[b] for `batch` problems.
@@ -554,47 +563,37 @@ struct Block {
                       int batch) const {
     if (t2va_status st = gemm(zv, Cv, nv, W[0], Cv, X, D, x_bs, 0, tau, D, Nv, D, Cv, batch, nullptr, D))
       return st;
-    return gemm(za, Ca, na, W[1], Ca, X + (int64_t)Nv * D, D, x_bs, 0, tau, D, Na, D, Ca, batch, nullptr, D);
+    return gemm(za, Ca, na, W[1], Ca, X + (int64_t)Nv * D, D, x_bs, 0, tau, D, Na, D, Ca,
+                batch, nullptr, D);
   }
 
-  // bf16 precision with folded weights Wf [3d, Cv + Ca] (fold_weights): Q|K and
-  // V^T of the video and audio rows straight from z (bias W_qkv tau per batch,
-  // into bqkv [batch][3d]); the text rows [Nq, NA) from X with W_qkv (no bias;
-  // their V^T columns and the zero padding up to ldv).  The audio and text
+  // Q|K (row-major into QK) and V^T (dh-major into VT) of `batch` problems:
+  // the video and audio rows straight from z with the folded weights Wf
+  // (fold_weights; bias W_qkv tau per batch, into bqkv [batch][3d]), the text
+  // rows [Nq, NA) from X with W_qkv (no bias; their V^T columns and the zero
+  // padding up to ldv).  Split precision: z rows are [hi | lo | hi] (3 C_m
+  // wide), the text rows of X [hi | lo] against Wd_qkv = [W_qkv | W_qkv], and
+  // Q|K rows are written [Q_hi | K_hi | Q_lo | K_lo].  The audio and text
   // products are small and run as one two-problem launch.
-  t2va_status project_in_folded(const bf16 *const *W, const bf16 *Wf, const bf16 *zv, const bf16 *za,
-                                const float *tau, float *bqkv, const bf16 *X, bf16 *QK, bf16 *VT, int batch) const {
-    const int CC = Cv + Ca;
+  t2va_status project_in_folded(const bf16 *const *W, const bf16 *Wd_qkv, const bf16 *Wf, const bf16 *zv,
+                                const bf16 *za, const float *tau, float *bqkv, const bf16 *X, bf16 *QK,
+                                bf16 *VT, int batch) const {
+    const int kz = split ? 3 : 1, cdt = split ? 2 : 0;
+    const bf16 *Wv = Wf, *Wa = split ? Wf + (int64_t)9 * D * Cv : Wf + Cv;
+    const int64_t ldwv = split ? 3 * Cv : Cv + Ca, ldwa = split ? 3 * Ca : Cv + Ca;
+    const bf16 *Wt = split ? Wd_qkv : W[3];
+    const int kt = split ? 2 * D : D;
     HIP_TRY(launch_row_linear(tau, batch, D, 3 * D, W[3], bqkv, s), "QKV bias");
-    if (t2va_status st = gemm(zv, Cv, nv, Wf, CC, QK, 2 * D, qk_bs, 0, bqkv, 3 * D, Nv, 3 * D, Cv, batch, VT,
-                              2 * D, 0, Nv))
+    if (t2va_status st = gemm(zv, kz * Cv, kz * nv, Wv, ldwv, QK, qks, qk_bs, cdt, bqkv, 3 * D, Nv, 3 * D, kz * Cv,
+                              batch, VT, 2 * D, 0, Nv))
       return st;
-    const GemmParams ga = params(za, Ca, na, Wf + Cv, CC, QK + (int64_t)Nv * 2 * D, 2 * D, qk_bs, 0, bqkv, 3 * D,
-                                 Na, 3 * D, Ca, batch, VT + Nv, 2 * D, 0, Na);
-    const GemmParams gt = params(X + (int64_t)Nq * D, D, x_bs, W[3], D, QK + (int64_t)Nq * 2 * D, 2 * D, qk_bs, 0,
-                                 nullptr, 0, NA - Nq, 3 * D, D, batch, VT + Nq, 2 * D, 0, ldv - Nq);
+    const GemmParams ga = params(za, kz * Ca, kz * na, Wa, ldwa, QK + (int64_t)Nv * qks, qks, qk_bs, cdt, bqkv,
+                                 3 * D, Na, 3 * D, kz * Ca, batch, VT + Nv, 2 * D, 0, Na);
+    const GemmParams gt = params(X + (int64_t)Nq * xs, xs, x_bs, Wt, kt, QK + (int64_t)Nq * qks, qks, qk_bs, cdt,
+                                 nullptr, 0, NA - Nq, 3 * D, kt, batch, VT + Nq, 2 * D, 0, ldv - Nq);
     PhaseScope ps(s, T2VA_PHASE_GEMM, prof);
     HIP_TRY(launch_gemm_pair(ga, gt, s), "gemm");
     return T2VA_OK;
-  }
-
-  t2va_status project_in(const bf16 *const *W, const bf16 *const *Wd, const bf16 *zv, const bf16 *za,
-                         const float *tau, bf16 *X, bf16 *QK, bf16 *VT, int batch) const {
-    if (split) {
-      if (t2va_status st = gemm(zv, 2 * Cv, 2 * nv, Wd[0], 2 * Cv, X, xs, x_bs, 2, tau, D, Nv, D, 2 * Cv, batch,
-                                nullptr, D))
-        return st;
-      if (t2va_status st = gemm(za, 2 * Ca, 2 * na, Wd[1], 2 * Ca, X + (int64_t)Nv * xs, xs, x_bs, 2, tau, D, Na,
-                                D, 2 * Ca, batch, nullptr, D))
-        return st;
-      return gemm(X, xs, x_bs, Wd[2], 2 * D, QK, qks, qk_bs, 2, nullptr, 0, NA, 3 * D, 2 * D, batch, VT, 2 * D);
-    }
-    if (t2va_status st = gemm(zv, Cv, nv, W[0], Cv, X, D, x_bs, 0, tau, D, Nv, D, Cv, batch, nullptr, D))
-      return st;
-    if (t2va_status st = gemm(za, Ca, na, W[1], Ca, X + (int64_t)Nv * D, D, x_bs, 0, tau, D, Na, D,
-                              Ca, batch, nullptr, D))
-      return st;
-    return gemm(X, D, x_bs, W[3], D, QK, 2 * D, qk_bs, 0, nullptr, 0, NA, 3 * D, D, batch, VT, 2 * D);
   }
 
   // O [batch, Nq, D] -> fp32 x0^v [batch, Nv, Cv] and x0^a [batch, Na, Ca], in one launch: the
@@ -682,17 +681,15 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   const CoefTable coef = make_coef(B, t_host, d.beta, d.gamma, d.param);
 
   HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
-  const bf16 *Wd[2][3] = {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}};
-  if (L.split) HIP_TRY(prepare_dup(W, 2, d.Cv, d.Ca, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
-  // bf16 precision: fold W_qkv W_in_m for both blocks
+  const bf16 *Wd[2] = {nullptr, nullptr};
+  if (L.split) HIP_TRY(prepare_dup(W, 2, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
+  // fold W_qkv W_in_m for both blocks
   const bf16 *Wf[2] = {nullptr, nullptr};
   float *bqkv = (float *)(ws + L.bqkv);
-  if (!L.split) {
-    for (int i = 0; i < 2; ++i) {
-      bf16 *f = (bf16 *)(ws + L.wfold) + i * fold_elems(d.Cv, d.Ca, D);
-      if (t2va_status st = blk.fold_weights(W[i], f, (bf16 *)(ws + L.wint))) return st;
-      Wf[i] = f;
-    }
+  for (int i = 0; i < 2; ++i) {
+    bf16 *f = (bf16 *)(ws + L.wfold) + i * fold_elems(d.Cv, d.Ca, D, L.split);
+    if (t2va_status st = blk.fold_weights(W[i], f, (bf16 *)(ws + L.wint), (float *)(ws + L.fpart))) return st;
+    Wf[i] = f;
   }
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
@@ -706,7 +703,7 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   float *part_v = (float *)(ws + L.part_v), *part_a = (float *)(ws + L.part_a);
 
   // The block's latent token rows of batch half `half` (0: z_t, 1: F_T) from
-  // the trigflow op: bf16, or in split precision fp32 split into [hi | lo].
+  // the trigflow op: bf16, or in split precision fp32 split into [hi | lo | hi].
   auto token_rows = [&](int op, int half, const float *x0_v, const float *x0_a) -> t2va_status {
     const int64_t xs_v = op == 2 ? nv : 0, xs_a = op == 2 ? na : 0;
     if (!L.split) {
@@ -721,10 +718,10 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
                             xs_v, nv, s), "token rows");
     HIP_TRY(launch_trigflow(op, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, z0_a, eps_a, x0_a, fa, na, na,
                             xs_a, na, s), "token rows");
-    HIP_TRY(launch_split_rows(fv, nv, d.Cv, zv + (int64_t)half * B * 2 * nv, 2 * nv, 2 * d.Cv, B, d.Nv, d.Cv, s),
-            "split rows");
-    HIP_TRY(launch_split_rows(fa, na, d.Ca, za + (int64_t)half * B * 2 * na, 2 * na, 2 * d.Ca, B, d.Na, d.Ca, s),
-            "split rows");
+    HIP_TRY(launch_split_rows(fv, nv, d.Cv, zv + (int64_t)half * B * 3 * nv, 3 * nv, 3 * d.Cv, B, d.Nv, d.Cv, true,
+                              s), "split rows");
+    HIP_TRY(launch_split_rows(fa, na, d.Ca, za + (int64_t)half * B * 3 * na, 3 * na, 3 * d.Ca, B, d.Na, d.Ca, true,
+                              s), "split rows");
     return T2VA_OK;
   };
 
@@ -740,8 +737,7 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
     HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
 
   // ---------------- teacher: x0_T = G_T(z_t, t, c) ----------------
-  if (L.split) T2VA_CALL(blk.project_in(W[0], Wd[0], zv, za, tau, X, QK, VT, B));
-  else T2VA_CALL(blk.project_in_folded(W[0], Wf[0], zv, za, tau, bqkv, X, QK, VT, B));
+  T2VA_CALL(blk.project_in_folded(W[0], Wd[0], Wf[0], zv, za, tau, bqkv, X, QK, VT, B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
   T2VA_CALL(blk.project_out(W[0], O, x0T_v, x0T_a, B));
 
@@ -754,8 +750,7 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   if (d.Nt > 0)
     HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X + (int64_t)B * blk.x_bs,
                              blk.x_bs, blk.xs, L.split, 1, nullptr, s), "tangent text rows");
-  if (L.split) T2VA_CALL(blk.project_in(W[1], Wd[1], zv, za, tau, X, QK, VT, 2 * B));
-  else T2VA_CALL(blk.project_in_folded(W[1], Wf[1], zv, za, tau, bqkv, X, QK, VT, 2 * B));
+  T2VA_CALL(blk.project_in_folded(W[1], Wd[1], Wf[1], zv, za, tau, bqkv, X, QK, VT, 2 * B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, true, T2VA_PHASE_STUDENT_ATTN, lse_student));
   T2VA_CALL(blk.project_out(W[1], O, x0S_v, x0S_a, 2 * B));
 #undef T2VA_CALL
@@ -1278,16 +1273,14 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
 
   const bf16 *W[2][6];
   HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
-  const bf16 *Wd[2][3] = {{nullptr, nullptr, nullptr}, {nullptr, nullptr, nullptr}};
-  if (L.split) HIP_TRY(prepare_dup(W, 2, d.Cv, d.Ca, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
+  const bf16 *Wd[2] = {nullptr, nullptr};
+  if (L.split) HIP_TRY(prepare_dup(W, 2, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
   const bf16 *Wf[2] = {nullptr, nullptr};
   float *bqkv = (float *)(ws + L.bqkv);
-  if (!L.split) {
-    for (int i = 0; i < 2; ++i) {
-      bf16 *f = (bf16 *)(ws + L.wfold) + i * fold_elems(d.Cv, d.Ca, D);
-      if (t2va_status st = blk.fold_weights(W[i], f, (bf16 *)(ws + L.wint))) return st;
-      Wf[i] = f;
-    }
+  for (int i = 0; i < 2; ++i) {
+    bf16 *f = (bf16 *)(ws + L.wfold) + i * fold_elems(d.Cv, d.Ca, D, L.split);
+    if (t2va_status st = blk.fold_weights(W[i], f, (bf16 *)(ws + L.wint), (float *)(ws + L.fpart))) return st;
+    Wf[i] = f;
   }
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
@@ -1299,7 +1292,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   float *xF_v = (float *)(ws + L.xF_v), *xF_a = (float *)(ws + L.xF_a);
 
   // z_t = cos t x0 + sin t eps of the student's sample (the GEMM input: bf16,
-  // or in split precision fp32 split into [hi | lo] rows).
+  // or in split precision fp32 split into [hi | lo | hi] rows).
   if (!L.split) {
     HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, x0_v, eps_v,
                             nullptr, zv, nv, nv, 0, nv, s), "noise");
@@ -1311,8 +1304,8 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
                             nullptr, zf_v, nv, nv, 0, nv, s), "noise");
     HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, x0_a, eps_a,
                             nullptr, zf_a, na, na, 0, na, s), "noise");
-    HIP_TRY(launch_split_rows(zf_v, nv, d.Cv, zv, 2 * nv, 2 * d.Cv, B, d.Nv, d.Cv, s), "split rows");
-    HIP_TRY(launch_split_rows(zf_a, na, d.Ca, za, 2 * na, 2 * d.Ca, B, d.Na, d.Ca, s), "split rows");
+    HIP_TRY(launch_split_rows(zf_v, nv, d.Cv, zv, 3 * nv, 3 * d.Cv, B, d.Nv, d.Cv, true, s), "split rows");
+    HIP_TRY(launch_split_rows(zf_a, na, d.Ca, za, 3 * na, 3 * d.Ca, B, d.Na, d.Ca, true, s), "split rows");
   }
   HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
   if (d.Nt > 0)
@@ -1332,8 +1325,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   // this is the guided prediction, and the large scales (5 for audio) no
   // longer amplify two separate roundings.
   HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
-  if (L.split) T2VA_CALL(blk.project_in(W[0], Wd[0], zv, za, tau, X, QK, VT, B));
-  else T2VA_CALL(blk.project_in_folded(W[0], Wf[0], zv, za, tau, bqkv, X, QK, VT, B));
+  T2VA_CALL(blk.project_in_folded(W[0], Wd[0], Wf[0], zv, za, tau, bqkv, X, QK, VT, B));
   if (guided) {
     float *Of = (float *)(ws + L.Of);
     if (Nq % 32 == 0) {
@@ -1356,8 +1348,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
 
   // ---------------- fake-score block ----------------
   HIP_TRY(launch_time_linear(E, B, D, W[1][2], tau, s), "fake time linear");
-  if (L.split) T2VA_CALL(blk.project_in(W[1], Wd[1], zv, za, tau, X, QK, VT, B));
-  else T2VA_CALL(blk.project_in_folded(W[1], Wf[1], zv, za, tau, bqkv, X, QK, VT, B));
+  T2VA_CALL(blk.project_in_folded(W[1], Wd[1], Wf[1], zv, za, tau, bqkv, X, QK, VT, B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
   T2VA_CALL(blk.project_out(W[1], O, xF_v, xF_a, B));
 #undef T2VA_CALL
