@@ -45,6 +45,8 @@ def short(name: str) -> str:
                        ("attn_fwd_jvp_kernel<128, false, true>", "attn_fwd_jvp<128,false,split> (forward, split)"),
                        ("attn_combine_kernel<128, true, false>", "attn_combine<128,true> (JVP split-tail merge)"),
                        ("attn_combine_kernel<128, false, false>", "attn_combine<128,false> (forward split-tail merge)"),
+                       ("attn_combine_kernel<128, true, true>", "attn_combine<128,true,split> (JVP merge, split)"),
+                       ("attn_combine_kernel<128, false, true>", "attn_combine<128,false,split> (forward merge, split)"),
                        ("attn_bwd_dkv_kernel<128>", "attn_bwd_dkv<128> (backward dK, dV)"),
                        ("attn_bwd_dq_kernel<128>", "attn_bwd_dq<128> (backward dQ)"),
                        ("attn_bwd_dkv_merge_kernel<128>", "attn_bwd_dkv_merge<128> (split-tail sum)"),
@@ -59,7 +61,7 @@ def short(name: str) -> str:
                 "time_linear_kernel", "time_embedding_kernel", "cast_kernel", "dmd_direction_kernel",
                 "transpose16_kernel", "transpose_kernel", "rowterm_kernel", "seed_kernel", "colsum_kernel", "time_grad_kernel",
                 "reduce_splits_kernel", "zero_rows_kernel", "fill_nk_kernel", "mix_kernel", "guide_kernel",
-                "split_rows_kernel", "dup_cols_kernel"):
+                "split_rows_kernel", "dup_cols_kernel", "fold_finish_kernel"):
         if key in name:
             return key
     return name[:60]
