@@ -69,17 +69,19 @@ typedef int t2va_status;
  * T2VA_PREC_BF16: every activation between kernels is stored in bf16 (fp32
  *   accumulation inside each kernel).
  * T2VA_PREC_SPLIT: the primal values that decide the attention logits -- the
- *   noised latents, the block's token rows X and the projections Q and K -- are
- *   carried as pairs hi + lo of bf16 values (hi = bf16(x), lo = bf16(x - hi),
- *   about 16 significant bits).  The projections contract the pairs against
- *   the bf16 weights on the matrix cores with fp32 accumulation, and the
- *   attention kernels form the logits as Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T.
+ *   noised latents, the folded weights W_qkv W_in (and the token rows X of the
+ *   text) and the projections Q and K -- are carried as pairs hi + lo of bf16
+ *   values (hi = bf16(x), lo = bf16(x - hi), about 16 significant bits).  The
+ *   projections contract the pairs on the matrix cores with fp32 accumulation
+ *   (dropping only the lo x lo product), and the attention kernels form the
+ *   logits as Q_hi K_hi^T + Q_hi K_lo^T + Q_lo K_hi^T.
  *   Tangents, V and the attention outputs stay bf16.  This is for inputs whose
  *   logits are large enough that a bf16 rounding of Q or K (a relative 2^-9)
  *   moves a logit by a sizeable fraction of one unit, which makes softmax,
  *   and with it J, sensitive to the storage rounding: scaled latents at small t
- *   (deep read, section 3.1, the J_theta equation near t -> 0).  It costs two
- *   to three times the projection and logit work. */
+ *   (deep read, section 3.1, the J_theta equation near t -> 0).  It costs three
+ *   times the latent-row projection work, twice the text rows', and 1.5 to 2
+ *   times the logit work. */
 #define T2VA_PREC_BF16 0
 #define T2VA_PREC_SPLIT 1
 
