@@ -47,8 +47,7 @@ namespace {
 #ifndef T2VA_BWD_MB_DKV
 #define T2VA_BWD_MB_DKV 1
 #endif
-constexpr int BT = 64;          // streamed tokens per LDS stage
-constexpr int kBwdLoaders = 8;  // waves that issue the LDS loads
+constexpr int BT = 64;   // streamed tokens per LDS stage
 
 template <int DH>
 struct BwdCfg {
@@ -64,8 +63,8 @@ struct BwdCfg {
   static constexpr int CPR = DH / 8;
   static constexpr int ROW_ELEMS = BT * DH;   // row tile [BT][DH]
   static constexpr int T_ELEMS = DH * BT;     // transposed tile [DH][BT]
-  static constexpr int RCH = ROW_ELEMS / 512 / kBwdLoaders;
-  static constexpr int TCH = T_ELEMS / 512 / kBwdLoaders;
+  // waves that issue a stage's LDS loads (at most 8)
+  static constexpr int LD_DQ = NW_DQ < 8 ? NW_DQ : 8, LD_DKV = NW_DKV < 8 ? NW_DKV : 8;
   static constexpr int ROWS_PER_CHUNK = 512 / DH;
   // dQ stage: K rows, V rows, K^T; dK/dV stage: Q rows, dO rows, Q^T, dO^T, lse2, D
   static constexpr int DQ_STAGE = 2 * ROW_ELEMS + T_ELEMS;
@@ -80,23 +79,25 @@ struct BwdCfg {
   static constexpr int PIECE_DKV = 2 * PIECE_DKV_HALF;
 };
 
-// Per-lane byte offsets (at token 0) of the chunks a loading wave moves into a
-// row tile / a transposed tile; chunk j of the tile holds 512 elements.
-template <int DH>
+// Per-lane byte offsets (at token 0) of the chunks loading wave lw of LD moves
+// into a row tile / a transposed tile; chunk j of the tile holds 512 elements.
+template <int DH, int LD>
 struct TileOffsets {
   using C = BwdCfg<DH>;
-  uint32_t row[C::RCH], tr[C::TCH];
+  static constexpr int RCH = C::ROW_ELEMS / 512 / LD, TCH = C::T_ELEMS / 512 / LD;
+  static_assert(RCH * LD * 512 == C::ROW_ELEMS && TCH * LD * 512 == C::T_ELEMS, "whole chunks per loader");
+  uint32_t row[RCH], tr[TCH];
   __device__ void init(int lw, int lane, int64_t rs, int64_t trs) {
 #pragma unroll
-    for (int r = 0; r < C::RCH; ++r) {
-      const int chunk = lw + kBwdLoaders * r;
+    for (int r = 0; r < RCH; ++r) {
+      const int chunk = lw + LD * r;
       const int rr = chunk * C::ROWS_PER_CHUNK + lane / C::CPR;
       const int c = kslot<C::CPR>(rr, lane % C::CPR);
       row[r] = (uint32_t)((rr * rs + 8 * c) * 2);
     }
 #pragma unroll
-    for (int r = 0; r < C::TCH; ++r) {
-      const int chunk = lw + kBwdLoaders * r;
+    for (int r = 0; r < TCH; ++r) {
+      const int chunk = lw + LD * r;
       const int e = chunk * 8 + lane / 8;
       tr[r] = (uint32_t)((e * trs + 8 * vslot(e, lane % 8)) * 2);
     }
@@ -225,23 +226,25 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_kerne
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.v + (int64_t)b * p.v_bs + (int64_t)key0 * p.v_rs + h * DH, v_bytes);
   const __amdgpu_buffer_rsrc_t rKT =
       make_rsrc(p.kt + (int64_t)b * p.kt_bs + (int64_t)h * p.kt_hs + key0, kt_bytes);
-  const int lw = wave % kBwdLoaders;
-  const bool loader = wave < kBwdLoaders;
-  TileOffsets<DH> ko, vo;
+  constexpr int LD = C::LD_DQ;
+  using TO = TileOffsets<DH, LD>;
+  const int lw = wave % LD;
+  const bool loader = wave < LD;
+  TO ko, vo;
   ko.init(lw, lane, p.k_rs, p.kt_rs);
   vo.init(lw, lane, p.v_rs, p.kt_rs);
   auto issue = [&](int buf, int k0) {
     if (!loader) return;
     const uint32_t kst = (uint32_t)(k0 * p.k_rs * 2), vst = (uint32_t)(k0 * p.v_rs * 2), tst = (uint32_t)(k0 * 2);
 #pragma unroll
-    for (int r = 0; r < C::RCH; ++r) {
-      const int chunk = lw + kBwdLoaders * r;
+    for (int r = 0; r < TO::RCH; ++r) {
+      const int chunk = lw + LD * r;
       load_lds16(rK, ko.row[r] + kst, sK(buf) + chunk * 512);
       load_lds16(rV, vo.row[r] + vst, sV(buf) + chunk * 512);
     }
 #pragma unroll
-    for (int r = 0; r < C::TCH; ++r) {
-      const int chunk = lw + kBwdLoaders * r;
+    for (int r = 0; r < TO::TCH; ++r) {
+      const int chunk = lw + LD * r;
       load_lds16(rKT, ko.tr[r] + tst, sKT(buf) + chunk * 512);
     }
   };
@@ -434,23 +437,25 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
   const int64_t srow = ((int64_t)b * p.H + h) * p.Nq + q0;
   const __amdgpu_buffer_rsrc_t rL = make_rsrc(p.lse2 + srow, s_bytes);
   const __amdgpu_buffer_rsrc_t rD = make_rsrc(p.D + srow, s_bytes);
-  const int lw = wave % kBwdLoaders;
-  const bool loader = wave < kBwdLoaders;
-  TileOffsets<DH> qo, doo;
+  constexpr int LD = C::LD_DKV;
+  using TO = TileOffsets<DH, LD>;
+  const int lw = wave % LD;
+  const bool loader = wave < LD;
+  TO qo, doo;
   qo.init(lw, lane, p.q_rs, p.qt_rs);
   doo.init(lw, lane, p.do_rs, p.qt_rs);
   auto issue = [&](int buf, int q0) {
     if (!loader) return;
     const uint32_t qst = (uint32_t)(q0 * p.q_rs * 2), dst = (uint32_t)(q0 * p.do_rs * 2), tst = (uint32_t)(q0 * 2);
 #pragma unroll
-    for (int r = 0; r < C::RCH; ++r) {
-      const int chunk = lw + kBwdLoaders * r;
+    for (int r = 0; r < TO::RCH; ++r) {
+      const int chunk = lw + LD * r;
       load_lds16(rQ, qo.row[r] + qst, sQ(buf) + chunk * 512);
       load_lds16(rDO, doo.row[r] + dst, sDO(buf) + chunk * 512);
     }
 #pragma unroll
-    for (int r = 0; r < C::TCH; ++r) {
-      const int chunk = lw + kBwdLoaders * r;
+    for (int r = 0; r < TO::TCH; ++r) {
+      const int chunk = lw + LD * r;
       load_lds16(rQT, qo.tr[r] + tst, sQT(buf) + chunk * 512);
       load_lds16(rDOT, qo.tr[r] + tst, sDOT(buf) + chunk * 512);
     }
