@@ -167,19 +167,29 @@ __global__ __launch_bounds__(kThreads) void text_rows_kernel(int Nq, int Nt, int
   const int j = blockIdx.x, bi = blockIdx.y;
   __shared__ int src;
   __shared__ int count;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    // the first wave ranks the valid positions 64 at a time: position i of
+    // this chunk is valid row c + (valid lanes below it)
+    const int lane = threadIdx.x;
+    const uint64_t below = (1ull << lane) - 1;
     int c = 0, found = -1;
     if (!zero_only) {
       const uint8_t *m = mask + (int64_t)bi * Nt;
-      for (int i = 0; i < Nt; ++i) {
-        if (m[i]) {
-          if (c == j) found = i;
-          ++c;
-        }
+      for (int base = 0; base < Nt; base += 64) {
+        const int i = base + lane;
+        const bool v = i < Nt && m[i] != 0;
+        const uint64_t bal = __ballot(v);
+        if (v && c + __popcll(bal & below) == j) found = i;
+        c += __popcll(bal);
       }
     }
-    src = found;
-    count = c;
+    const uint64_t hit = __ballot(found >= 0);   // at most one lane
+    const int from = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+    const int f = __shfl(found, from);             // every lane takes part
+    if (lane == 0) {
+      src = hit ? f : -1;
+      count = c;
+    }
   }
   __syncthreads();
   if (j == 0 && threadIdx.x == 0 && nk != nullptr) nk[bi] = Nq + count;
