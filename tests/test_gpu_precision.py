@@ -123,8 +123,13 @@ ONETOK = inputs.Config("onetoken", B=2, Nv=1, Na=1, Nt=3, Ntv=2, Cv=64, Ca=64, d
                        in_dtype="bf16", index=16)
 ALLPAD = inputs.Config("allpad", B=2, Nv=96, Na=40, Nt=16, Ntv=0, Cv=64, Ca=64, d=256, H=2,
                        in_dtype="bf16", index=13)
+# no text rows at all: the text rows' QKV product has M = 0 and only writes the
+# V^T padding; head dimension 64
+NOTEXT = inputs.Config("notext", B=2, Nv=130, Na=70, Nt=0, Ntv=0, Cv=64, Ca=64, d=256, H=4,
+                       in_dtype="bf16", beta=1.2, gamma=0.4, index=17)
+# tiny is an fp32 workload: fp32 latents, text and weights, cast on the device
 SPLIT_CFGS = [c.replace(precision="split") for c in
-              (inputs.CONFIGS["tiny"], RAGGED, PEAKED, ONETOK, ALLPAD, inputs.CONFIGS["small"],
+              (inputs.CONFIGS["tiny"], RAGGED, PEAKED, ONETOK, ALLPAD, NOTEXT, inputs.CONFIGS["small"],
                RAGGED.replace(name="ragged-rf", param="rf"), PEAKED.replace(name="peaked-rf", param="rf"))]
 
 
@@ -172,7 +177,7 @@ def test_scm_target_split_matches_oracle(cfg):
 
 
 @pytest.mark.parametrize("cfg", [c for c in SPLIT_CFGS if c.name in ("tiny", "ragged", "peaked", "allpad",
-                                                                     "peaked-rf")],
+                                                                     "notext", "peaked-rf")],
                          ids=lambda c: c.name)
 def test_dmd_target_split_matches_oracle(cfg):
     say(f"dmd_target split {cfg.name}")
