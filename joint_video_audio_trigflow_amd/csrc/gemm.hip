@@ -41,6 +41,58 @@ constexpr int kThreads = 256;
 constexpr int kStageElems = (BM + BN) * LROW;
 constexpr size_t kLdsBytes = 2 * kStageElems * sizeof(bf16);
 
+// Output of a 128x128 tile held as 2x2 v_mfma_f32_32x32x16_bf16 results per
+// wave (wave (wm, wn) owns rows wm*64.., columns wn*64..): bias, then the
+// element stores of store_c, or columns past n_split dh-major into V^T.
+__device__ __forceinline__ void small_epilogue(const GemmParams &p, int bz, int m0, int n0, int wm, int wn,
+                                               int l32, int hi, const floatx16 (&acc)[2][2]) {
+  // MFMA 32x32 output: lane holds column l32 and rows 8*(v/4) + 4*hi + v%4.
+  const float *bias = p.bias ? p.bias + (int64_t)bz * p.bias_bs : nullptr;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + wn * 64 + j * 32 + l32;
+    if (col >= p.N) continue;
+    const float bcol = bias ? bias[col] : 0.f;
+    if (col < p.n_split) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+          if (row < p.M) {
+            const float val = acc[i][j][v] + bcol;
+            const int64_t off = (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col;
+            store_c(p, off, val);
+          }
+        }
+      }
+    } else {
+      const int cc = col - p.n_split;
+      const int h = cc / p.dh, e = cc % p.dh;
+      bf16 *vt = p.VT + (int64_t)bz * p.vt_bs + (int64_t)h * p.vt_hs + (int64_t)e * p.vt_rs;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row = m0 + wm * 64 + i * 32 + 8 * g + 4 * hi;
+          // rows in [M, vt_rows) read zero A rows: they store the zero padding
+          // (V^T may start at any token: a vector store needs an aligned address)
+          if (row + 3 < p.vt_rows && (((uintptr_t)(vt + row)) & 7) == 0) {
+            bf16x4 pk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pk[u] = (bf16)(acc[i][j][4 * g + u] + bcol);
+            *reinterpret_cast<bf16x4 *>(vt + row) = pk;
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (row + u < p.vt_rows) vt[row + u] = (bf16)(acc[i][j][4 * g + u] + bcol);
+          }
+        }
+      }
+    }
+  }
+}
+
 // Two independent problems can share one launch (the first tiles1 workgroups
 // of each batch row run p1, the rest p2): a problem with few tiles then runs
 // beside a larger one instead of after it.
@@ -128,51 +180,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p1, Gemm
     __syncthreads();
   }
 
-  // Epilogue.  MFMA 32x32 output: lane holds column l32 and rows 8*(v/4) + 4*hi + v%4.
-  const float *bias = p.bias ? p.bias + (int64_t)bz * p.bias_bs : nullptr;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + wn * 64 + j * 32 + l32;
-    if (col >= p.N) continue;
-    const float bcol = bias ? bias[col] : 0.f;
-    if (col < p.n_split) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (row < p.M) {
-            const float val = acc[i][j][v] + bcol;
-            const int64_t off = (int64_t)bz * p.c_bs + (int64_t)row * p.ldc + col;
-            store_c(p, off, val);
-          }
-        }
-      }
-    } else {
-      const int cc = col - p.n_split;
-      const int h = cc / p.dh, e = cc % p.dh;
-      bf16 *vt = p.VT + (int64_t)bz * p.vt_bs + (int64_t)h * p.vt_hs + (int64_t)e * p.vt_rs;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int row = m0 + wm * 64 + i * 32 + 8 * g + 4 * hi;
-          // rows in [M, vt_rows) read zero A rows: they store the zero padding
-          // (V^T may start at any token: a vector store needs an aligned address)
-          if (row + 3 < p.vt_rows && (((uintptr_t)(vt + row)) & 7) == 0) {
-            bf16x4 pk;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) pk[u] = (bf16)(acc[i][j][4 * g + u] + bcol);
-            *reinterpret_cast<bf16x4 *>(vt + row) = pk;
-          } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (row + u < p.vt_rows) vt[row + u] = (bf16)(acc[i][j][4 * g + u] + bcol);
-          }
-        }
-      }
-    }
-  }
+  small_epilogue(p, bz, m0, n0, wm, wn, l32, hi, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -529,6 +537,145 @@ void gemm_bf16_large_kernel(GemmParams p, int tiles_n,
 
 bool g_attr_set = false, g_lattr_set = false;
 
+
+// ---------------------------------------------------------------------------
+// 128x128 tiles with a deep direct-to-LDS ring, for products with long K and
+// few tiles (the output projections, K = d; the text rows' QKV; the weight
+// fold).  With the tile held one k-step ahead in registers (the kernel above)
+// such launches wait on memory most of the time: a workgroup's loads of the
+// next k-tile take longer than its MFMAs on the current one.  Here the operand
+// tiles go straight into a ring of kRing LDS stages, kRing - 1 k-tiles in
+// flight, in the 256x256 kernel's layout (unpadded 128-byte rows, 16-byte
+// chunks XOR-swizzled by lslot; rows past M or N lie past the descriptor's end
+// and read zeros).  4 waves of 64x64 as 2x2 v_mfma_f32_32x32x16_bf16 tiles;
+// output through small_epilogue.
+// ---------------------------------------------------------------------------
+// Workgroup barrier for the ring: a fence (as in __syncthreads()) would wait
+// for every load in flight, since the ring's loads write LDS; each wave has
+// already waited for its own loads of the tile it is about to read, so only
+// the compiler must keep memory accesses on their side of the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kRing = 4;
+constexpr int kRStageElems = (BM + BN) * BK;                                  // 32 KB
+constexpr size_t kRLdsBytes = (size_t)kRing * kRStageElems * sizeof(bf16);   // 128 KB
+constexpr int kRGroups = BM / 8 / (kThreads / 64);   // 8-row chunks per wave and operand: 4
+
+// s_waitcnt with the vector-memory count n (0..63) and the other counters
+// left alone (expcnt 7, lgkmcnt 15)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__global__ __launch_bounds__(kThreads) void gemm_bf16_ring_kernel(GemmParams p1, GemmParams p2, int tiles_n1,
+                                                                  int tiles_n2, int tiles1) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16 *smem = reinterpret_cast<bf16 *>(smem_raw);
+
+  const bool second = (int)blockIdx.x >= tiles1;
+  const GemmParams &p = second ? p2 : p1;
+  const int tiles_n = second ? tiles_n2 : tiles_n1;
+  const int bx = second ? (int)blockIdx.x - tiles1 : (int)blockIdx.x;
+  const int bz = blockIdx.y;
+  if (bz >= p.batch) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tn = bx % tiles_n, tm = bx / tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int m_rows = max(min(p.M - m0, BM), 0), n_rows = max(min(p.N - n0, BN), 0);
+  const bf16 *A = p.A + (int64_t)bz * p.a_bs + (int64_t)m0 * p.lda;
+  const bf16 *W = p.W + (int64_t)bz * p.w_bs + (int64_t)n0 * p.ldw;
+  const __amdgpu_buffer_rsrc_t rA =
+      gemm_rsrc(A, (uint32_t)(m_rows > 0 ? ((int64_t)(m_rows - 1) * p.lda + p.K) * 2 : 0));
+  const __amdgpu_buffer_rsrc_t rW =
+      gemm_rsrc(W, (uint32_t)(n_rows > 0 ? ((int64_t)(n_rows - 1) * p.ldw + p.K) * 2 : 0));
+
+  // wave w moves the 8-row chunks w*kRGroups .. of A and of W of each stage
+  uint32_t aoff[kRGroups], woff[kRGroups];
+#pragma unroll
+  for (int r = 0; r < kRGroups; ++r) {
+    const int row = (wave * kRGroups + r) * 8 + (lane >> 3);
+    const int c = lslot(row, lane & 7);   // the slot map is an involution
+    aoff[r] = (uint32_t)((row * p.lda + 8 * c) * 2);
+    woff[r] = (uint32_t)((row * p.ldw + 8 * c) * 2);
+  }
+  auto issue = [&](int stage, int k0) {
+    bf16 *sA = smem + stage * kRStageElems;
+    bf16 *sW = sA + BM * BK;
+    const uint32_t kb = (uint32_t)(k0 * 2);
+#pragma unroll
+    for (int r = 0; r < kRGroups; ++r) {
+      const int grp = wave * kRGroups + r;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(sA + grp * 512), 16, aoff[r] + kb, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_void *)(sW + grp * 512), 16, woff[r] + kb, 0, 0, 0);
+    }
+  };
+  // fragment rows and their swizzle keys
+  int abase[2], wbase[2], ax[2], wx[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ra = wm * 64 + i * 32 + l32, rw = wn * 64 + i * 32 + l32;
+    abase[i] = ra * BK;
+    ax[i] = lxor(ra);
+    wbase[i] = rw * BK;
+    wx[i] = lxor(rw);
+  }
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int KT = p.K / BK;
+#pragma unroll
+  for (int t = 0; t < kRing - 1; ++t)
+    if (t < KT) issue(t, t * BK);
+  for (int kt = 0; kt < KT; ++kt) {
+    // this wave's loads of tile kt have landed once at most the loads of the
+    // tiles issued after it (up to kRing - 2 of them, 2 kRGroups each) remain
+    const int newer = min(KT - 1 - kt, kRing - 2);
+    static_assert(kRing == 4, "the waits below count up to two newer tiles");
+    if (newer >= 2) wait_vm<4 * kRGroups>();
+    else if (newer == 1) wait_vm<2 * kRGroups>();
+    else wait_vm<0>();
+    // every wave's tile kt is in LDS, and every wave is done reading tile
+    // kt - 1, whose stage the tile kRing - 1 ahead now takes
+    ring_barrier();
+    if (kt + kRing - 1 < KT) issue((kt + kRing - 1) % kRing, (kt + kRing - 1) * BK);
+    const bf16 *sA = smem + (kt % kRing) * kRStageElems;
+    const bf16 *sW = sA + BM * BK;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int c = 2 * s + hi;
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8 *>(sA + abase[i] + 8 * (c ^ ax[i]));
+        b[i] = *reinterpret_cast<const bf16x8 *>(sW + wbase[i] + 8 * (c ^ wx[i]));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  small_epilogue(p, bz, m0, n0, wm, wn, l32, hi, acc);
+}
+
 }  // namespace
 
 namespace {
@@ -542,6 +689,25 @@ bool use_large(const GemmParams &p) {
   const bool many = rows >= 2048 || ((int64_t)rows * p.batch >= 4096 && 5 * (int64_t)rows >= 4 * padded);
   return p.N >= 1024 && many && (int64_t)LBM * p.lda * 2 < ((int64_t)1 << 31) &&
          (int64_t)LBN * p.ldw * 2 < ((int64_t)1 << 31);
+}
+// The ring kernel for long K (at least 8 k-tiles) when the launch has few
+// workgroups (its 128 KB of LDS allow one per CU); 32-bit tile offsets.
+bool use_ring(const GemmParams &p) {
+  const int64_t tiles = (int64_t)((p.N + BN - 1) / BN) * ((max(p.M, p.VT ? p.vt_rows : 0) + BM - 1) / BM);
+  return p.K >= 8 * BK && tiles * p.batch <= 1024;
+}
+bool tile_offsets_fit(const GemmParams &p) {
+  return (int64_t)BM * max(p.lda, p.ldw) * 2 < ((int64_t)1 << 31);
+}
+hipError_t set_ring_attr() {
+  static bool done = false;
+  if (!done) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_ring_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRLdsBytes);
+    if (e != hipSuccess) return e;
+    done = true;
+  }
+  return hipSuccess;
 }
 int small_tiles(const GemmParams &p) {
   return ((p.N + BN - 1) / BN) * ((max(p.M, p.VT ? p.vt_rows : 0) + BM - 1) / BM);
@@ -575,9 +741,15 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
                        s, p, tiles_n, tiles_m);
     return hipGetLastError();
   }
-  if (hipError_t e = set_small_attr()) return e;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles = small_tiles(p);
+  if (use_ring(p) && tile_offsets_fit(p)) {
+    if (hipError_t e = set_ring_attr()) return e;
+    hipLaunchKernelGGL(gemm_bf16_ring_kernel, dim3(tiles, p.batch), dim3(kThreads), kRLdsBytes, s, p, p, tiles_n,
+                       tiles_n, tiles);
+    return hipGetLastError();
+  }
+  if (hipError_t e = set_small_attr()) return e;
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3(tiles, p.batch), dim3(kThreads), kLdsBytes, s, p, p, tiles_n, tiles_n,
                      tiles);
   return hipGetLastError();
@@ -589,8 +761,14 @@ hipError_t launch_gemm_pair(const GemmParams &a, const GemmParams &b, hipStream_
     if (hipError_t e = launch_gemm(a, s)) return e;
     return launch_gemm(b, s);
   }
-  if (hipError_t e = set_small_attr()) return e;
   const int ta = small_tiles(a);
+  if ((use_ring(a) || use_ring(b)) && tile_offsets_fit(a) && tile_offsets_fit(b)) {
+    if (hipError_t e = set_ring_attr()) return e;
+    hipLaunchKernelGGL(gemm_bf16_ring_kernel, dim3(ta + small_tiles(b), max(a.batch, b.batch)), dim3(kThreads),
+                       kRLdsBytes, s, a, b, (a.N + BN - 1) / BN, (b.N + BN - 1) / BN, ta);
+    return hipGetLastError();
+  }
+  if (hipError_t e = set_small_attr()) return e;
   hipLaunchKernelGGL(gemm_bf16_kernel, dim3(ta + small_tiles(b), max(a.batch, b.batch)), dim3(kThreads),
                      kLdsBytes, s, a, b, (a.N + BN - 1) / BN, (b.N + BN - 1) / BN, ta);
   return hipGetLastError();

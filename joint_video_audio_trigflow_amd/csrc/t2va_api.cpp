@@ -185,10 +185,11 @@ size_t fold_elems(int Cv, int Ca, int d, bool split) {
   return align_up((size_t)3 * d * (Cv + Ca) * (split ? 3 : 1), 128);
 }
 // The fold's product (3d rows, Cv + Ca columns, K = d) has few output tiles:
-// it runs split-K over up to 8 chunks of d (multiples of 64) into fp32 partials.
+// it runs split-K into fp32 partials, in chunks of d of at least 512 (the
+// deep-ring GEMM's long-K case) and multiples of 64, at most 8 of them.
 int fold_splits(int d) {
   int s = 8;
-  while (s > 1 && d % (64 * s)) s /= 2;
+  while (s > 1 && (d % (64 * s) || d / s < 512)) s /= 2;
   return s;
 }
 size_t fold_part_bytes(int Cv, int Ca, int d) {
