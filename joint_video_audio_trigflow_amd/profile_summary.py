@@ -53,6 +53,7 @@ def short(name: str) -> str:
                        ("attn_bwd_dq_merge_kernel<128>", "attn_bwd_dq_merge<128> (split-tail sum)"),
                        ("gemm_bf16_large_kernel", "gemm_bf16_large (256x256 tiles)"),
                        ("gemm_bf16_kernel", "gemm_bf16 (128x128 tiles)"),
+                       ("gemm_bf16_ring_kernel", "gemm_bf16_ring (128x128 tiles, long K)"),
                        ("copyBuffer", "copyBuffer"),
                        ("elementwise_kernel", "torch copy")):
         if key in name:
