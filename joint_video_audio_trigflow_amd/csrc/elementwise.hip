@@ -137,19 +137,35 @@ __global__ __launch_bounds__(kThreads) void time_linear_kernel(const float *E, i
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= n_out) return;
   const bf16 *wr = w_t + (int64_t)i * d;
-  for (int r = 0; r < rows; ++r) {
-    const float *er = E + (int64_t)r * d;
-    float acc = 0.f;
-    for (int k0 = lane * 8; k0 < d; k0 += 64 * 8) {
-      float w8[8], e8[8];
-      load8(wr + k0, w8);
-      load8(er + k0, e8);
+  // rows in groups of kR: each weight chunk is read once per group, and the
+  // group's kR sums are reduced together (independent shuffle chains)
+  constexpr int kR = 8;
+  for (int r0 = 0; r0 < rows; r0 += kR) {
+    float acc[kR];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc += w8[j] * e8[j];
+    for (int q = 0; q < kR; ++q) acc[q] = 0.f;
+    for (int k0 = lane * 8; k0 < d; k0 += 64 * 8) {
+      float w8[8];
+      load8(wr + k0, w8);
+#pragma unroll
+      for (int q = 0; q < kR; ++q) {
+        if (r0 + q < rows) {
+          float e8[8];
+          load8(E + (int64_t)(r0 + q) * d + k0, e8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[q] += w8[j] * e8[j];
+        }
+      }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) tau[(int64_t)r * n_out + i] = acc;
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int q = 0; q < kR; ++q) acc[q] += __shfl_xor(acc[q], off);
+    if (lane == 0) {
+#pragma unroll
+      for (int q = 0; q < kR; ++q)
+        if (r0 + q < rows) tau[(int64_t)(r0 + q) * n_out + i] = acc[q];
+    }
   }
 }
 
