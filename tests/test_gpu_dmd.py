@@ -152,16 +152,19 @@ ALLPAD = inputs.Config("allpad", B=2, Nv=96, Na=40, Nt=16, Ntv=0, Cv=64, Ca=64, 
                        in_dtype="bf16", index=13)
 ONETOK = inputs.Config("onetoken", B=2, Nv=1, Na=1, Nt=3, Ntv=2, Cv=64, Ca=64, d=128, H=1,
                        in_dtype="bf16", index=16)
+MAXB = inputs.Config("maxbatch", B=64, Nv=64, Na=32, Nt=8, Ntv=5, Cv=64, Ca=64, d=128, H=2,
+                     in_dtype="bf16", mask_mode="scatter", index=14)
 
 
-@pytest.mark.parametrize("cfg", [ALLPAD, ONETOK, inputs.CONFIGS["small"].replace(B=1, Nv=1568)],
+@pytest.mark.parametrize("cfg", [ALLPAD, ONETOK, MAXB, inputs.CONFIGS["small"].replace(B=1, Nv=1568)],
                          ids=lambda c: c.name + f"-nq{c.Nq}")
 def test_dmd_target_edge_cases(cfg):
     """All text padded (the null condition equals the condition), one token per
-    modality, and Nq a multiple of 32 but not of 64 (Nq = 1696: the single
-    guided pass stores its null output in the middle of a 128-key stage, and
-    with 40 forward tiles the launch splits each tile's keys in three, the
-    last piece straddling Nq)."""
+    modality, the largest batch the coefficient table holds (64 samples,
+    scattered valid text), and Nq a multiple of 32 but not of 64 (Nq = 1696:
+    the single guided pass stores its null output in the middle of a 128-key
+    stage, and with 40 forward tiles the launch splits each tile's keys in
+    three, the last piece straddling Nq)."""
     say(f"dmd_target edge case {cfg.name} Nq={cfg.Nq}")
     p = inputs.make_dmd_problem(cfg)
     got = run_dmd(p)

@@ -127,9 +127,12 @@ ALLPAD = inputs.Config("allpad", B=2, Nv=96, Na=40, Nt=16, Ntv=0, Cv=64, Ca=64, 
 # V^T padding; head dimension 64
 NOTEXT = inputs.Config("notext", B=2, Nv=130, Na=70, Nt=0, Ntv=0, Cv=64, Ca=64, d=256, H=4,
                        in_dtype="bf16", beta=1.2, gamma=0.4, index=17)
+# the largest batch the coefficient table holds
+MAXB = inputs.Config("maxbatch", B=64, Nv=64, Na=32, Nt=8, Ntv=5, Cv=64, Ca=64, d=128, H=2,
+                     in_dtype="bf16", mask_mode="scatter", index=14)
 # tiny is an fp32 workload: fp32 latents, text and weights, cast on the device
 SPLIT_CFGS = [c.replace(precision="split") for c in
-              (inputs.CONFIGS["tiny"], RAGGED, PEAKED, ONETOK, ALLPAD, NOTEXT, inputs.CONFIGS["small"],
+              (inputs.CONFIGS["tiny"], RAGGED, PEAKED, ONETOK, ALLPAD, NOTEXT, MAXB, inputs.CONFIGS["small"],
                RAGGED.replace(name="ragged-rf", param="rf"), PEAKED.replace(name="peaked-rf", param="rf"))]
 
 
@@ -177,7 +180,7 @@ def test_scm_target_split_matches_oracle(cfg):
 
 
 @pytest.mark.parametrize("cfg", [c for c in SPLIT_CFGS if c.name in ("tiny", "ragged", "peaked", "allpad",
-                                                                     "notext", "peaked-rf")],
+                                                                     "notext", "maxbatch", "peaked-rf")],
                          ids=lambda c: c.name)
 def test_dmd_target_split_matches_oracle(cfg):
     say(f"dmd_target split {cfg.name}")
