@@ -682,11 +682,11 @@ namespace {
 // the large tile for wide outputs with many rows; per-(batch, tile) byte
 // extents must fit the 32-bit buffer descriptors
 // The 256x256 tiles for wide outputs with many rows: 2048 rows per problem, or
-// a batch of at least 4096 rows in all whose row tiles are at least 80 % full.
+// a batch of at least 2048 rows in all whose row tiles are at least 80 % full.
 bool use_large(const GemmParams &p) {
   const int rows = max(p.M, p.VT ? p.vt_rows : 0);
   const int64_t padded = (int64_t)(rows + LBM - 1) / LBM * LBM;
-  const bool many = rows >= 2048 || ((int64_t)rows * p.batch >= 4096 && 5 * (int64_t)rows >= 4 * padded);
+  const bool many = rows >= 2048 || ((int64_t)rows * p.batch >= 2048 && 5 * (int64_t)rows >= 4 * padded);
   return p.N >= 1024 && many && (int64_t)LBM * p.lda * 2 < ((int64_t)1 << 31) &&
          (int64_t)LBN * p.ldw * 2 < ((int64_t)1 << 31);
 }
