@@ -87,6 +87,19 @@ hipError_t launch_trigflow(int op, const CoefTable &coef, int64_t n, int a_dt, i
                            const void *a, const void *b, const float *x, void *out,
                            int64_t a_bs, int64_t b_bs, int64_t x_bs, int64_t out_bs,
                            hipStream_t s);
+// Two such maps in one launch (the video and the audio rows): per sample,
+// n elements from a, b (and x for op 2) into out, each with its own batch
+// strides; vec is set by the launcher (16-byte accesses when n and the strides
+// allow them).
+struct TrigSeg {
+  const void *a, *b;
+  const float *x;
+  void *out;
+  int64_t n, a_bs, b_bs, x_bs, o_bs;
+  int vec;
+};
+hipError_t launch_trigflow_pair(int op, const CoefTable &coef, int a_dt, int b_dt, int out_dt, const TrigSeg &s1,
+                                const TrigSeg &s2, hipStream_t s);
 
 // Sinusoidal time embedding e(t_b) (rows 0..B-1) and de/dt (rows B..2B-1), fp32 [2B, d].
 hipError_t launch_time_embedding(const CoefTable &coef, int d, float *E, hipStream_t s);
@@ -98,15 +111,16 @@ hipError_t launch_time_linear(const float *E, int rows, int d, const bf16 *w_t, 
 hipError_t launch_row_linear(const float *E, int rows, int d, int n_out, const bf16 *W, float *out,
                              hipStream_t s);
 
-// Text rows of X: for each sample, the valid text positions (mask != 0) in
-// order, converted to bf16, at rows [Nq, Nq + count); rows up to Nq + Nt are
-// zero.  With zero_only, every text row is zero (tangent of the text).
-// nk[b] = Nq + count (written when nk != nullptr).  Rows are x_row_stride
-// elements apart; with split, columns [d, 2d) of a row receive the low half
-// bf16(x - bf16(x)) of each value (zero for bf16 text).
+// Text rows of X for B problems: for each sample b < copy_b, the valid text
+// positions (mask != 0) in order, converted to bf16, at rows [Nq, Nq + count);
+// rows up to Nq + Nt are zero.  Problems b >= copy_b get zero text rows (the
+// tangent of the text, for the stacked primal and tangent batches).
+// nk[b] = Nq + count for b < copy_b (written when nk != nullptr).  Rows are
+// x_row_stride elements apart; with split, columns [d, 2d) of a row receive
+// the low half bf16(x - bf16(x)) of each value (zero for bf16 text).
 hipError_t launch_text_rows(int B, int Nq, int Nt, int d, const void *text, int text_dt,
                             const uint8_t *mask, bf16 *X, int64_t x_batch_stride, int64_t x_row_stride,
-                            int split, int zero_only, int32_t *nk, hipStream_t s);
+                            int split, int copy_b, int32_t *nk, hipStream_t s);
 
 // Guided attention output of B samples [Nq][D] (fp32 conditional c and
 // unconditional u, batch stride Nq D): out = bf16(u + s (c - u)) with s = s_v

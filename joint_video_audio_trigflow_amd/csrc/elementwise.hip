@@ -44,22 +44,24 @@ __device__ __forceinline__ void store_n(T *p, int64_t i0, int64_t n, bool vec, c
 // the teacher's x0-prediction x0 = rf ? r z - t_emb x : x, F_T = (cos z - x0)/sin
 // and out = r F_T + rdot z (the tangent of the student's token input).
 template <typename TA, typename TB, typename TO>
-__global__ __launch_bounds__(kThreads) void trigflow_kernel(int op, CoefTable coef, int64_t n,
-                                                            const TA *a, const TB *b,
-                                                            const float *x, TO *out, int64_t a_bs,
-                                                            int64_t b_bs, int64_t x_bs,
-                                                            int64_t o_bs, int vec) {
+__global__ __launch_bounds__(kThreads) void trigflow_kernel(int op, CoefTable coef, TrigSeg s1, TrigSeg s2,
+                                                            int blocks1) {
+  // the first blocks1 blocks of each sample's row take segment 1, the rest segment 2
+  const bool second = (int)blockIdx.x >= blocks1;
+  const TrigSeg &sg = second ? s2 : s1;
   const int bi = blockIdx.y;
   const Coef c = coef.c[bi];
-  const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPerThread;
+  const int64_t n = sg.n;
+  const int64_t i0 = ((int64_t)((int)blockIdx.x - (second ? blocks1 : 0)) * kThreads + threadIdx.x) * kPerThread;
   if (i0 >= n) return;
-  a += bi * a_bs;
-  b += bi * b_bs;
-  out += bi * o_bs;
+  const TA *a = (const TA *)sg.a + bi * sg.a_bs;
+  const TB *b = (const TB *)sg.b + bi * sg.b_bs;
+  TO *out = (TO *)sg.out + bi * sg.o_bs;
+  const int vec = sg.vec;
   float fa[8], fb[8], fx[8], fo[8];
   load_n(a, i0, n, vec, fa);
   load_n(b, i0, n, vec, fb);
-  if (op == 2) load_n(x + bi * x_bs, i0, n, vec, fx);
+  if (op == 2) load_n(sg.x + bi * sg.x_bs, i0, n, vec, fx);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (op == 0) {
@@ -77,34 +79,30 @@ __global__ __launch_bounds__(kThreads) void trigflow_kernel(int op, CoefTable co
 }
 
 template <typename TA, typename TB, typename TO>
-hipError_t trigflow_launch3(int op, const CoefTable &coef, int64_t n, const void *a, const void *b,
-                            const float *x, void *out, int64_t a_bs, int64_t b_bs, int64_t x_bs,
-                            int64_t o_bs, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const bool vec = (n % 8 == 0) && (a_bs % 8 == 0) && (b_bs % 8 == 0) && (o_bs % 8 == 0) &&
-                   (x == nullptr || x_bs % 8 == 0);
-  dim3 grid((unsigned)((n + kChunk - 1) / kChunk), coef.B);
-  hipLaunchKernelGGL((trigflow_kernel<TA, TB, TO>), grid, dim3(kThreads), 0, s, op, coef, n,
-                     (const TA *)a, (const TB *)b, x, (TO *)out, a_bs, b_bs, x_bs, o_bs, (int)vec);
+hipError_t trigflow_launch3(int op, const CoefTable &coef, TrigSeg s1, TrigSeg s2, hipStream_t s) {
+  for (TrigSeg *g : {&s1, &s2})
+    g->vec = (g->n % 8 == 0) && (g->a_bs % 8 == 0) && (g->b_bs % 8 == 0) && (g->o_bs % 8 == 0) &&
+             (g->x == nullptr || g->x_bs % 8 == 0);
+  const int b1 = (int)((max(s1.n, (int64_t)0) + kChunk - 1) / kChunk);
+  const int b2 = (int)((max(s2.n, (int64_t)0) + kChunk - 1) / kChunk);
+  if (b1 + b2 == 0) return hipSuccess;
+  hipLaunchKernelGGL((trigflow_kernel<TA, TB, TO>), dim3(b1 + b2, coef.B), dim3(kThreads), 0, s, op, coef, s1, s2,
+                     b1);
   return hipGetLastError();
 }
 
 template <typename TA, typename TB>
-hipError_t trigflow_launch2(int op, const CoefTable &coef, int64_t n, int out_dt, const void *a,
-                            const void *b, const float *x, void *out, int64_t a_bs, int64_t b_bs,
-                            int64_t x_bs, int64_t o_bs, hipStream_t s) {
-  if (out_dt == 0)
-    return trigflow_launch3<TA, TB, bf16>(op, coef, n, a, b, x, out, a_bs, b_bs, x_bs, o_bs, s);
-  return trigflow_launch3<TA, TB, float>(op, coef, n, a, b, x, out, a_bs, b_bs, x_bs, o_bs, s);
+hipError_t trigflow_launch2(int op, const CoefTable &coef, int out_dt, const TrigSeg &s1, const TrigSeg &s2,
+                            hipStream_t s) {
+  if (out_dt == 0) return trigflow_launch3<TA, TB, bf16>(op, coef, s1, s2, s);
+  return trigflow_launch3<TA, TB, float>(op, coef, s1, s2, s);
 }
 
 template <typename TA>
-hipError_t trigflow_launch1(int op, const CoefTable &coef, int64_t n, int b_dt, int out_dt,
-                            const void *a, const void *b, const float *x, void *out, int64_t a_bs,
-                            int64_t b_bs, int64_t x_bs, int64_t o_bs, hipStream_t s) {
-  if (b_dt == 0)
-    return trigflow_launch2<TA, bf16>(op, coef, n, out_dt, a, b, x, out, a_bs, b_bs, x_bs, o_bs, s);
-  return trigflow_launch2<TA, float>(op, coef, n, out_dt, a, b, x, out, a_bs, b_bs, x_bs, o_bs, s);
+hipError_t trigflow_launch1(int op, const CoefTable &coef, int b_dt, int out_dt, const TrigSeg &s1,
+                            const TrigSeg &s2, hipStream_t s) {
+  if (b_dt == 0) return trigflow_launch2<TA, bf16>(op, coef, out_dt, s1, s2, s);
+  return trigflow_launch2<TA, float>(op, coef, out_dt, s1, s2, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -179,8 +177,9 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void text_rows_kernel(int Nq, int Nt, int d, const T *text,
                                                              const uint8_t *mask, bf16 *X,
                                                              int64_t x_bs, int64_t x_rs, int split,
-                                                             int zero_only, int32_t *nk) {
+                                                             int copy_b, int32_t *nk) {
   const int j = blockIdx.x, bi = blockIdx.y;
+  const bool zero_only = bi >= copy_b;   // a tangent problem: zero text rows
   __shared__ int src;
   __shared__ int count;
   if (threadIdx.x < 64) {
@@ -208,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void text_rows_kernel(int Nq, int Nt, int
     }
   }
   __syncthreads();
-  if (j == 0 && threadIdx.x == 0 && nk != nullptr) nk[bi] = Nq + count;
+  if (j == 0 && threadIdx.x == 0 && nk != nullptr && !zero_only) nk[bi] = Nq + count;
   bf16 *dst = X + (int64_t)bi * x_bs + (int64_t)(Nq + j) * x_rs;
   const T *row = src < 0 ? nullptr : text + ((int64_t)bi * Nt + src) * d;
   for (int c0 = threadIdx.x * 8; c0 < d; c0 += kThreads * 8) {
@@ -481,13 +480,19 @@ __global__ __launch_bounds__(kThreads) void normalise_kernel(int B, NormParams p
 
 int elementwise_blocks(int64_t n) { return (int)((n + kChunk - 1) / kChunk); }
 
+hipError_t launch_trigflow_pair(int op, const CoefTable &coef, int a_dt, int b_dt, int out_dt, const TrigSeg &s1,
+                                const TrigSeg &s2, hipStream_t s) {
+  if (a_dt == 0) return trigflow_launch1<bf16>(op, coef, b_dt, out_dt, s1, s2, s);
+  return trigflow_launch1<float>(op, coef, b_dt, out_dt, s1, s2, s);
+}
+
 hipError_t launch_trigflow(int op, const CoefTable &coef, int64_t n, int a_dt, int b_dt,
                            int out_dt, const void *a, const void *b, const float *x, void *out,
                            int64_t a_bs, int64_t b_bs, int64_t x_bs, int64_t out_bs,
                            hipStream_t s) {
-  if (a_dt == 0)
-    return trigflow_launch1<bf16>(op, coef, n, b_dt, out_dt, a, b, x, out, a_bs, b_bs, x_bs, out_bs, s);
-  return trigflow_launch1<float>(op, coef, n, b_dt, out_dt, a, b, x, out, a_bs, b_bs, x_bs, out_bs, s);
+  const TrigSeg s1{a, b, x, out, n, a_bs, b_bs, x_bs, out_bs, 0};
+  const TrigSeg none{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, 0};
+  return launch_trigflow_pair(op, coef, a_dt, b_dt, out_dt, s1, none, s);
 }
 
 hipError_t launch_time_embedding(const CoefTable &coef, int d, float *E, hipStream_t s) {
@@ -509,15 +514,15 @@ hipError_t launch_row_linear(const float *E, int rows, int d, int n_out, const b
 
 hipError_t launch_text_rows(int B, int Nq, int Nt, int d, const void *text, int text_dt,
                             const uint8_t *mask, bf16 *X, int64_t x_batch_stride, int64_t x_row_stride,
-                            int split, int zero_only, int32_t *nk, hipStream_t s) {
+                            int split, int copy_b, int32_t *nk, hipStream_t s) {
   if (Nt == 0) return hipSuccess;  // no text rows; the host sets nk = Nq itself
   dim3 grid(Nt, B);
   if (text_dt == 0)
     hipLaunchKernelGGL(text_rows_kernel<bf16>, grid, dim3(kThreads), 0, s, Nq, Nt, d,
-                       (const bf16 *)text, mask, X, x_batch_stride, x_row_stride, split, zero_only, nk);
+                       (const bf16 *)text, mask, X, x_batch_stride, x_row_stride, split, copy_b, nk);
   else
     hipLaunchKernelGGL(text_rows_kernel<float>, grid, dim3(kThreads), 0, s, Nq, Nt, d,
-                       (const float *)text, mask, X, x_batch_stride, x_row_stride, split, zero_only, nk);
+                       (const float *)text, mask, X, x_batch_stride, x_row_stride, split, copy_b, nk);
   return hipGetLastError();
 }
 

@@ -707,18 +707,17 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   // the trigflow op: bf16, or in split precision fp32 split into [hi | lo | hi].
   auto token_rows = [&](int op, int half, const float *x0_v, const float *x0_a) -> t2va_status {
     const int64_t xs_v = op == 2 ? nv : 0, xs_a = op == 2 ? na : 0;
+    // video and audio rows in one launch
     if (!L.split) {
-      HIP_TRY(launch_trigflow(op, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_v, eps_v, x0_v,
-                              zv + (int64_t)half * B * nv, nv, nv, xs_v, nv, s), "token rows");
-      HIP_TRY(launch_trigflow(op, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, z0_a, eps_a, x0_a,
-                              za + (int64_t)half * B * na, na, na, xs_a, na, s), "token rows");
+      const TrigSeg sv{z0_v, eps_v, x0_v, zv + (int64_t)half * B * nv, nv, nv, nv, xs_v, nv, 0};
+      const TrigSeg sa{z0_a, eps_a, x0_a, za + (int64_t)half * B * na, na, na, na, xs_a, na, 0};
+      HIP_TRY(launch_trigflow_pair(op, coef, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, sv, sa, s), "token rows");
       return T2VA_OK;
     }
     float *fv = zf_v + (int64_t)half * B * nv, *fa = zf_a + (int64_t)half * B * na;
-    HIP_TRY(launch_trigflow(op, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, z0_v, eps_v, x0_v, fv, nv, nv,
-                            xs_v, nv, s), "token rows");
-    HIP_TRY(launch_trigflow(op, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, z0_a, eps_a, x0_a, fa, na, na,
-                            xs_a, na, s), "token rows");
+    const TrigSeg sv{z0_v, eps_v, x0_v, fv, nv, nv, nv, xs_v, nv, 0};
+    const TrigSeg sa{z0_a, eps_a, x0_a, fa, na, na, na, xs_a, na, 0};
+    HIP_TRY(launch_trigflow_pair(op, coef, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, sv, sa, s), "token rows");
     HIP_TRY(launch_split_rows(fv, nv, d.Cv, zv + (int64_t)half * B * 3 * nv, 3 * nv, 3 * d.Cv, B, d.Nv, d.Cv, true,
                               s), "split rows");
     HIP_TRY(launch_split_rows(fa, na, d.Ca, za + (int64_t)half * B * 3 * na, 3 * na, 3 * d.Ca, B, d.Na, d.Ca, true,
@@ -732,8 +731,10 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
   HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
   if (d.Nt > 0)
-    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, blk.xs, L.split, 0, nk, s),
-            "text rows");
+    // the primal text rows of both blocks' batches [0, B) and the zero tangent
+    // rows [B, 2B) of the student's, in one launch
+    HIP_TRY(launch_text_rows(2 * B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, blk.xs, L.split, B, nk,
+                             s), "text rows");
   else
     HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
 
@@ -748,9 +749,6 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   // ---------------- student: G_S and its JVP ----------------
   // Batches [0, B) carry the primal rows, [B, 2B) their tangents.
   HIP_TRY(launch_time_linear(E, 2 * B, D, W[1][2], tau, s), "student time linear");
-  if (d.Nt > 0)
-    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X + (int64_t)B * blk.x_bs,
-                             blk.x_bs, blk.xs, L.split, 1, nullptr, s), "tangent text rows");
   T2VA_CALL(blk.project_in_folded(W[1], Wd[1], Wf[1], zv, za, tau, bqkv, X, QK, VT, 2 * B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, true, T2VA_PHASE_STUDENT_ATTN, lse_student));
   T2VA_CALL(blk.project_out(W[1], O, x0S_v, x0S_a, 2 * B));
@@ -1295,22 +1293,20 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   // z_t = cos t x0 + sin t eps of the student's sample (the GEMM input: bf16,
   // or in split precision fp32 split into [hi | lo | hi] rows).
   if (!L.split) {
-    HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, x0_v, eps_v,
-                            nullptr, zv, nv, nv, 0, nv, s), "noise");
-    HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, x0_a, eps_a,
-                            nullptr, za, na, na, 0, na, s), "noise");
+    const TrigSeg sv{x0_v, eps_v, nullptr, zv, nv, nv, nv, 0, nv, 0};
+    const TrigSeg sa{x0_a, eps_a, nullptr, za, na, na, na, 0, na, 0};
+    HIP_TRY(launch_trigflow_pair(0, coef, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, sv, sa, s), "noise");
   } else {
     float *zf_v = (float *)(ws + L.zf_v), *zf_a = (float *)(ws + L.zf_a);
-    HIP_TRY(launch_trigflow(0, coef, nv, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, x0_v, eps_v,
-                            nullptr, zf_v, nv, nv, 0, nv, s), "noise");
-    HIP_TRY(launch_trigflow(0, coef, na, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, x0_a, eps_a,
-                            nullptr, zf_a, na, na, 0, na, s), "noise");
+    const TrigSeg sv{x0_v, eps_v, nullptr, zf_v, nv, nv, nv, 0, nv, 0};
+    const TrigSeg sa{x0_a, eps_a, nullptr, zf_a, na, na, na, 0, na, 0};
+    HIP_TRY(launch_trigflow_pair(0, coef, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, sv, sa, s), "noise");
     HIP_TRY(launch_split_rows(zf_v, nv, d.Cv, zv, 3 * nv, 3 * d.Cv, B, d.Nv, d.Cv, true, s), "split rows");
     HIP_TRY(launch_split_rows(zf_a, na, d.Ca, za, 3 * na, 3 * d.Ca, B, d.Na, d.Ca, true, s), "split rows");
   }
   HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
   if (d.Nt > 0)
-    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, blk.xs, L.split, 0, nk, s),
+    HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, blk.xs, L.split, B, nk, s),
             "text rows");
   else
     HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
