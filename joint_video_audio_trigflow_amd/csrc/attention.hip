@@ -133,6 +133,14 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// max(a, b, c) in one v_max3_f32 (written out: fmaxf's NaN rules make the
+// compiler quieten every operand of an MFMA result first)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 template <bool TAN>
 __device__ __forceinline__ void store_out4(const AttnParams &p, int64_t at, const float (&o4)[4],
                                            const float (&od4)[4]) {
@@ -538,14 +546,19 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_fw
       }
     }
   };
-  // any lane's own logits past its row's threshold (no lane exchange); plain
-  // compares, which compile to fewer operations than fmaxf's NaN rules allow
+  // any lane's own logits past its row's threshold (no lane exchange): the
+  // lane's largest logit per row block from four three-way maxima, then one
+  // compare (v_max3 ignores a quiet NaN operand, as the compare does).  Eight
+  // compares per row block cost more VALU issue slots, which the forward
+  // kernel is short of (teacher attention 2.5 % slower).
   auto outgrown = [&](const floatx4 (&S)[C::MB][2]) {
     bool any = false;
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) any |= S[mb][m >> 2][m & 3] > thr[mb];
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const float m = max3f(max3f(S[mb][0][0], S[mb][0][1], S[mb][0][2]), max3f(S[mb][0][3], S[mb][1][0], S[mb][1][1]),
+                            max3f(S[mb][1][2], S[mb][1][3], S[mb][1][3]));
+      any |= m > thr[mb];
+    }
     return __any(any);
   };
 
@@ -742,8 +755,9 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_fw
   }
 }
 
-// Merges the pieces of the split tiles (one workgroup per split tile, each
-// thread the rows and columns it held in the attention kernel).  A piece holds
+// Merges the pieces of the split tiles (one workgroup per split tile and
+// 16-column d-tile, each thread the rows and columns of that d-tile it held in
+// the attention kernel).  A piece holds
 // its own normalised result o_i, do_i, log-sum-exp and mean tangent logit
 // mu_i; with w_i the softmax of the log-sum-exps over the pieces,
 // o = sum w_i o_i, mu = sum w_i mu_i and do = sum w_i (do_i + (mu_i - mu) o_i)
@@ -762,6 +776,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_co
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  const int e = blockIdx.y;   // the d-tile this workgroup merges
   const float *part = p.part + (size_t)slot * sp.k * C::PIECE_FLOATS;
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb) {
@@ -795,10 +810,9 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_co
       wgt[i] *= inv;
       mu_all += wgt[i] * mu[i];
     }
-    if (p.lse && g == 0) p.lse[((int64_t)b * p.H + h) * p.Nq + q_row] = mx + logf(wsum);
+    if (p.lse && g == 0 && e == 0) p.lse[((int64_t)b * p.H + h) * p.Nq + q_row] = mx + logf(wsum);
     const int64_t obase = (int64_t)b * p.o_bs + (int64_t)q_row * p.o_rs + h * DH + 4 * g;
-#pragma unroll
-    for (int e = 0; e < C::DT; ++e) {
+    {
       float o4[4] = {0.f, 0.f, 0.f, 0.f}, od4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < kMaxPieces; ++i) {
@@ -850,8 +864,7 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_co
           psum += pw[i];
         }
         const float pinv = 1.f / psum;
-#pragma unroll
-        for (int e = 0; e < C::DT; ++e) {
+        {
           float o4[4] = {0.f, 0.f, 0.f, 0.f}, unused[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int i = 0; i < kMaxPieces; ++i) {
@@ -912,8 +925,10 @@ hipError_t launch_impl(const AttnParams &p, hipStream_t s) {
                      dim3(C::THREADS), C::LDS_BYTES, s, p, nqb, per_xcd, total, sp);
   if (sp.rem > 0) {
     if (hipError_t e = hipGetLastError()) return e;
-    hipLaunchKernelGGL((attn_combine_kernel<DH, TAN, SPLIT>), dim3(8 * sp.rem), dim3(C::THREADS), 0, s, p, nqb,
-                       per_xcd, total, sp);
+    // one workgroup per (split tile, d-tile): a tile's pieces hold up to a few
+    // MB of partials, which one workgroup alone would stream slowly
+    hipLaunchKernelGGL((attn_combine_kernel<DH, TAN, SPLIT>), dim3(8 * sp.rem, C::DT), dim3(C::THREADS), 0, s, p,
+                       nqb, per_xcd, total, sp);
   }
   return hipGetLastError();
 }

@@ -589,8 +589,9 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
   }
 }
 
-// Sum of the pieces of each split dQ tile (one workgroup per split tile, each
-// thread the rows and columns it held in the dQ kernel), in piece order.
+// Sum of the pieces of each split dQ tile (one workgroup per split tile and
+// 16-column d-tile, each thread the rows and columns of that d-tile it held in
+// the dQ kernel), in piece order.
 template <int DH>
 __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_merge_kernel(AttnBwdParams p, int nqb,
                                                                                     int per_xcd, int total,
@@ -604,6 +605,7 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_merge
   const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  const int e = blockIdx.y;   // the d-tile this workgroup sums
   const float *part = p.part + (size_t)slot * sp.k * C::PIECE_DQ;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -612,8 +614,7 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DQ), 1) void attn_bwd_dq_merge
     if (q_row >= p.Nq) continue;
     const int pi = 4 * row + g;
     bf16 *dst = p.dq + (int64_t)b * p.dq_bs + (int64_t)q_row * p.dq_rs + h * DH + 4 * g;
-#pragma unroll
-    for (int e = 0; e < C::DT; ++e) {
+    {
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int i = 0; i < sp.k; ++i) {
         const float4 v = *reinterpret_cast<const float4 *>(part + (size_t)i * C::PIECE_DQ +
@@ -641,6 +642,7 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_mer
   const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
+  const int e = blockIdx.y;   // the d-tile this workgroup sums
   const float *part = p.part + (size_t)slot * sp.k * C::PIECE_DKV;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -649,8 +651,7 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_mer
     if (k_row >= p.Nk) continue;
     const int pi = 4 * row + g;
     const int64_t o = (int64_t)b * p.dk_bs + (int64_t)k_row * p.dk_rs + h * DH + 4 * g;
-#pragma unroll
-    for (int e = 0; e < C::DT; ++e) {
+    {
       float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak;
       for (int i = 0; i < sp.k; ++i) {
         const float *pk = part + (size_t)i * C::PIECE_DKV + 4 * (e * MB * C::THREADS_DKV + pi);
@@ -709,7 +710,7 @@ hipError_t launch_bwd_impl(const AttnBwdParams &p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (sp.rem > 0) {
-    hipLaunchKernelGGL((attn_bwd_dq_merge_kernel<DH>), dim3(8 * sp.rem), dim3(C::THREADS_DQ), 0, s, p, nqb,
+    hipLaunchKernelGGL((attn_bwd_dq_merge_kernel<DH>), dim3(8 * sp.rem, C::DT), dim3(C::THREADS_DQ), 0, s, p, nqb,
                        per_xcd, total, sp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -726,7 +727,7 @@ hipError_t launch_bwd_impl(const AttnBwdParams &p, hipStream_t s) {
                      C::DKV_LDS, s, p, nkb, per_xcd, total, sp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (sp.rem > 0)
-    hipLaunchKernelGGL((attn_bwd_dkv_merge_kernel<DH>), dim3(8 * sp.rem), dim3(C::THREADS_DKV), 0, s, p, nkb,
+    hipLaunchKernelGGL((attn_bwd_dkv_merge_kernel<DH>), dim3(8 * sp.rem, C::DT), dim3(C::THREADS_DKV), 0, s, p, nkb,
                        per_xcd, total, sp);
   return hipGetLastError();
 }

@@ -35,9 +35,8 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(CoefTable coef, float w,
 // dst[c][r] = src[r][c] for one (b, h) slice per blockIdx.z; rows r in
 // [R, Rpad) of dst are written as zeros.  64x64 tiles through LDS; bf16
 // sources with 8-aligned rows move 16 bytes per lane on both sides.
-__global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeParams p) {
+__device__ __forceinline__ void transpose16_tile(const TransposeParams &p, int bh) {
   __shared__ __attribute__((aligned(16))) bf16 tile[64][64 + 8];
-  const int bh = blockIdx.z;
   const int b = bh / p.H, h = bh % p.H;
   const bf16 *src = reinterpret_cast<const bf16 *>(p.src) + (int64_t)b * p.s_bs + (int64_t)h * p.s_hs;
   bf16 *dst = p.dst + (int64_t)b * p.d_bs + (int64_t)h * p.d_hs;
@@ -75,6 +74,19 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeParams p
         if (r + u < p.Rpad) d[u] = v[u];
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeParams p) { transpose16_tile(p, blockIdx.z); }
+
+// Up to four independent transposes: blockIdx.z = problem (B = H = 1 each);
+// blocks past a problem's extent return.
+struct TransposeSet {
+  TransposeParams p[4];
+};
+__global__ __launch_bounds__(kThreads) void transpose16_set_kernel(TransposeSet set) {
+  const TransposeParams &p = set.p[blockIdx.z];
+  if ((int)blockIdx.x * 64 >= p.Rpad || (int)blockIdx.y * 64 >= p.C) return;
+  transpose16_tile(p, 0);
 }
 
 template <typename TS>
@@ -205,6 +217,27 @@ hipError_t launch_transpose(const TransposeParams &p, int src_fp32, hipStream_t 
     hipLaunchKernelGGL(transpose16_kernel, grid, dim3(kThreads), 0, s, p);
   else
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_set(const TransposeParams *ps, int n, hipStream_t s) {
+  bool vec = n >= 1 && n <= 4;
+  int gx = 0, gy = 0;
+  for (int i = 0; i < n && vec; ++i) {
+    const TransposeParams &p = ps[i];
+    vec = p.B == 1 && p.H == 1 && p.s_rs % 8 == 0 && ((uintptr_t)p.src & 15) == 0;
+    gx = std::max(gx, (p.Rpad + 63) / 64);
+    gy = std::max(gy, (p.C + 63) / 64);
+  }
+  if (!vec) {
+    for (int i = 0; i < n; ++i)
+      if (hipError_t e = launch_transpose(ps[i], 0, s)) return e;
+    return hipSuccess;
+  }
+  if (gx == 0 || gy == 0) return hipSuccess;
+  TransposeSet set = {};
+  for (int i = 0; i < n; ++i) set.p[i] = ps[i];
+  hipLaunchKernelGGL(transpose16_set_kernel, dim3(gx, gy, n), dim3(kThreads), 0, s, set);
   return hipGetLastError();
 }
 

@@ -104,12 +104,16 @@ hipError_t launch_trigflow_pair(int op, const CoefTable &coef, int a_dt, int b_d
 // Sinusoidal time embedding e(t_b) (rows 0..B-1) and de/dt (rows B..2B-1), fp32 [2B, d].
 hipError_t launch_time_embedding(const CoefTable &coef, int d, float *E, hipStream_t s);
 
-// tau[r] = W_t e_r for r in [0, rows): fp32 [rows, d] from bf16 W_t [d, d].
-hipError_t launch_time_linear(const float *E, int rows, int d, const bf16 *w_t, float *tau,
-                              hipStream_t s);
-// out[r] = W e_r for r in [0, rows): fp32 [rows, n_out] from bf16 W [n_out, d] and fp32 E [rows, d].
-hipError_t launch_row_linear(const float *E, int rows, int d, int n_out, const bf16 *W, float *out,
-                             hipStream_t s);
+// out[r] = W e_r for r in [0, rows): fp32 [rows, n_out] from bf16 W [n_out, d] and fp32 E [rows, d]
+// (tau = W_t e(t), and the QKV bias W_qkv tau).
+// Two such products (same d and n_out) per launch; a problem with rows = 0 is skipped.
+struct RowLinSeg {
+  const float *E;
+  const bf16 *W;
+  float *out;
+  int rows;
+};
+hipError_t launch_row_linear_pair(int d, int n_out, const RowLinSeg &s1, const RowLinSeg &s2, hipStream_t s);
 
 // Text rows of X for B problems: for each sample b < copy_b, the valid text
 // positions (mask != 0) in order, converted to bf16, at rows [Nq, Nq + count);
@@ -138,9 +142,10 @@ hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 
 // Folded weights from split-K partials part [splits][rows][Cv + Ca] (fp32,
 // summed in split order): bf16 Wf [rows][Cv + Ca], or with split per modality
 // [rows][3 C_m] = [hi | hi | lo] (hi = bf16(x), lo = bf16(x - hi); video
-// first, audio at 3 rows Cv).  Cv, Ca multiples of 8.
+// first, audio at 3 rows Cv).  Cv, Ca multiples of 8.  nblk blocks' folds
+// in one launch: block i reads part + i part_bs and writes Wf + i wf_bs.
 hipError_t launch_fold_finish(const float *part, int splits, int rows, int Cv, int Ca, bool split, bf16 *Wf,
-                              hipStream_t s);
+                              int nblk, int64_t part_bs, int64_t wf_bs, hipStream_t s);
 
 // W2 [n][2k] = [W | W] for bf16 W [n][k] (k a multiple of 8): the weight of a
 // product whose operand rows are [hi | lo] pairs.
@@ -290,6 +295,9 @@ struct TransposeParams {
   int B, H, R, C, Rpad;
 };
 hipError_t launch_transpose(const TransposeParams &p, int src_fp32, hipStream_t s);
+// n (at most 4) bf16 transposes in one launch when each is eligible for the
+// vectorised kernel (16-byte aligned source rows), else one launch each.
+hipError_t launch_transpose_set(const TransposeParams *ps, int n, hipStream_t s);
 // D = rowsum(dO * O) per (b, h, q) and lse2 = lse * log2(e).
 hipError_t launch_rowterms(const bf16 *dO, const bf16 *O, int64_t bs, int64_t rs, int B, int H, int dh, int Nq,
                            const float *lse, float *lse2, float *D, hipStream_t s);

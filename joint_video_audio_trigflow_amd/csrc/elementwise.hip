@@ -128,11 +128,18 @@ __global__ __launch_bounds__(kThreads) void time_embedding_kernel(CoefTable coef
   de[half + k] = wd * cs;
 }
 
-// One wave per output feature i: out[r][i] = sum_k W[i][k] E[r][k] (W [n_out][d]).
-__global__ __launch_bounds__(kThreads) void time_linear_kernel(const float *E, int rows, int d, int n_out,
-                                                               const bf16 *w_t, float *tau) {
+// One wave per output feature i: out[r][i] = sum_k W[i][k] E[r][k] (W [n_out][d]),
+// for two independent problems in one launch: blocks [0, blocks1) compute
+// problem 1, the rest problem 2 (same d and n_out).
+__global__ __launch_bounds__(kThreads) void time_linear_kernel(int d, int n_out, RowLinSeg s1, RowLinSeg s2,
+                                                               int blocks1) {
+  const bool second = (int)blockIdx.x >= blocks1;
+  const float *E = second ? s2.E : s1.E;
+  const bf16 *w_t = second ? s2.W : s1.W;
+  float *tau = second ? s2.out : s1.out;
+  const int rows = second ? s2.rows : s1.rows;
   const int lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int i = ((int)blockIdx.x - (second ? blocks1 : 0)) * 4 + (threadIdx.x >> 6);
   if (i >= n_out) return;
   const bf16 *wr = w_t + (int64_t)i * d;
   // rows in groups of kR: each weight chunk is read once per group, and the
@@ -270,7 +277,10 @@ __global__ __launch_bounds__(kThreads) void dup_cols_kernel(const bf16 *W, bf16 
 // summed over the splits in order.  bf16: Wf [rows][Cv + Ca].  split: per
 // modality [rows][3 C_m] = [hi | hi | lo] (video first, audio at 3 rows Cv).
 __global__ __launch_bounds__(kThreads) void fold_finish_kernel(const float *part, int splits, int rows, int Cv,
-                                                               int Ca, bool split, bf16 *Wf) {
+                                                               int Ca, bool split, bf16 *Wf, int64_t part_bs,
+                                                               int64_t wf_bs) {
+  part += blockIdx.y * part_bs;   // block blockIdx.y of the launch
+  Wf += blockIdx.y * wf_bs;
   const int CC = Cv + Ca;
   const int64_t n = (int64_t)rows * CC;
   const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
@@ -501,14 +511,11 @@ hipError_t launch_time_embedding(const CoefTable &coef, int d, float *E, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_time_linear(const float *E, int rows, int d, const bf16 *w_t, float *tau,
-                              hipStream_t s) {
-  return launch_row_linear(E, rows, d, d, w_t, tau, s);
-}
-
-hipError_t launch_row_linear(const float *E, int rows, int d, int n_out, const bf16 *W, float *out,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(time_linear_kernel, dim3((n_out + 3) / 4), dim3(kThreads), 0, s, E, rows, d, n_out, W, out);
+hipError_t launch_row_linear_pair(int d, int n_out, const RowLinSeg &s1, const RowLinSeg &s2, hipStream_t s) {
+  const int per = (n_out + 3) / 4;
+  const int blocks1 = s1.rows > 0 ? per : 0, blocks2 = s2.rows > 0 ? per : 0;
+  if (blocks1 + blocks2 == 0) return hipSuccess;
+  hipLaunchKernelGGL(time_linear_kernel, dim3(blocks1 + blocks2), dim3(kThreads), 0, s, d, n_out, s1, s2, blocks1);
   return hipGetLastError();
 }
 
@@ -537,11 +544,11 @@ hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 
 }
 
 hipError_t launch_fold_finish(const float *part, int splits, int rows, int Cv, int Ca, bool split, bf16 *Wf,
-                              hipStream_t s) {
+                              int nblk, int64_t part_bs, int64_t wf_bs, hipStream_t s) {
   const int64_t total = (int64_t)rows * (Cv + Ca);
-  if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fold_finish_kernel, dim3((unsigned)((total + kChunk - 1) / kChunk)), dim3(kThreads), 0, s,
-                     part, splits, rows, Cv, Ca, split, Wf);
+  if (total <= 0 || nblk <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fold_finish_kernel, dim3((unsigned)((total + kChunk - 1) / kChunk), nblk), dim3(kThreads), 0,
+                     s, part, splits, rows, Cv, Ca, split, Wf, part_bs, wf_bs);
   return hipGetLastError();
 }
 

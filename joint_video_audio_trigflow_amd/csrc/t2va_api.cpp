@@ -221,15 +221,15 @@ Layout make_layout(const t2va_scm_desc &d, bool whole_tiles = false) {
   L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
   L.wdup = take(L.split ? 2 * dup_qkv_elems(d.d) * sizeof(bf16) : 0);
   L.wfold = take(2 * fold_elems(d.Cv, d.Ca, d.d, L.split) * sizeof(bf16));
-  L.wint = take((size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
-  L.fpart = take(fold_part_bytes(d.Cv, d.Ca, d.d));
-  L.bqkv = take(2 * B * 3 * D * sizeof(float));
+  L.wint = take(2 * (size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
+  L.fpart = take(2 * fold_part_bytes(d.Cv, d.Ca, d.d));
+  L.bqkv = take(3 * B * 3 * D * sizeof(float));   // student [0, 2B), teacher [2B, 3B)
   L.zf_v = take(L.split ? 2 * B * d.Nv * d.Cv * sizeof(float) : 0);
   L.zf_a = take(L.split ? 2 * B * d.Na * d.Ca * sizeof(float) : 0);
   L.zv = take(2 * B * d.Nv * d.Cv * spz * sizeof(bf16));
   L.za = take(2 * B * d.Na * d.Ca * spz * sizeof(bf16));
   L.E = take(2 * B * D * sizeof(float));
-  L.tau = take(2 * B * D * sizeof(float));
+  L.tau = take(3 * B * D * sizeof(float));   // student [tau; dtau] [0, 2B), teacher [2B, 3B)
   L.X = take(2 * B * L.N_all * D * sp * sizeof(bf16));
   L.QK = take(2 * B * L.N_all * 2 * D * sp * sizeof(bf16));
   L.VT = take(2 * B * D * (size_t)L.ldv * sizeof(bf16));
@@ -392,15 +392,15 @@ DmdLayout make_dmd_layout(const t2va_dmd_desc &d) {
   L.wts = take(d.weight_dtype == T2VA_DTYPE_FP32 ? 2 * wcount * sizeof(bf16) : 0);
   L.wdup = take(L.split ? 2 * dup_qkv_elems(d.d) * sizeof(bf16) : 0);
   L.wfold = take(2 * fold_elems(d.Cv, d.Ca, d.d, L.split) * sizeof(bf16));
-  L.wint = take((size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
-  L.fpart = take(fold_part_bytes(d.Cv, d.Ca, d.d));
-  L.bqkv = take(B * 3 * D * sizeof(float));
+  L.wint = take(2 * (size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
+  L.fpart = take(2 * fold_part_bytes(d.Cv, d.Ca, d.d));
+  L.bqkv = take(2 * B * 3 * D * sizeof(float));   // teacher [0, B), fake [B, 2B)
   L.zf_v = take(L.split ? B * nv * sizeof(float) : 0);
   L.zf_a = take(L.split ? B * na * sizeof(float) : 0);
   L.zv = take(B * nv * spz * sizeof(bf16));
   L.za = take(B * na * spz * sizeof(bf16));
   L.E = take(2 * B * D * sizeof(float));
-  L.tau = take(B * D * sizeof(float));
+  L.tau = take(2 * B * D * sizeof(float));   // teacher [0, B), fake [B, 2B)
   L.X = take(B * N_all * D * sp * sizeof(bf16));
   L.QK = take(B * N_all * 2 * D * sp * sizeof(bf16));
   L.VT = take(B * D * (size_t)L.ldv * sizeof(bf16));
@@ -528,11 +528,13 @@ struct Block {
     return T2VA_OK;
   }
 
-  // Folded weights of one block: Wf = W_qkv [W_in_v | W_in_a].  Before
+  // Folded weights of both blocks: Wf = W_qkv [W_in_v | W_in_a].  Before
   // attention the block is linear, so for video and audio rows Q|K|V =
   // (z W_in^T + tau) W_qkv^T = z (W_qkv W_in)^T + tau W_qkv^T: a product with
-  // K = C_m instead of the input projection and a K = d product.  wint:
-  // scratch for [W_in_v^T; W_in_a^T], [Cv + Ca, d].
+  // K = C_m instead of the input projection and a K = d product.  Block i
+  // (weights W[i]) writes Wf + i fold_elems; wint: scratch for
+  // [W_in_v^T; W_in_a^T] of each block, 2 [Cv + Ca, d]; fpart: 2
+  // fold_part_bytes of split-K partials.
   //   bf16: Wf [3d, Cv + Ca] (row stride Cv + Ca; the video part is its first
   //     Cv columns).
   //   split: per modality Wf_m [3d, 3 C_m] = [Wf_hi | Wf_hi | Wf_lo] (video,
@@ -540,22 +542,34 @@ struct Block {
   //     rows [z_hi | z_lo | z_hi] one K = 3 C_m product then sums
   //     z_hi Wf_hi + z_lo Wf_hi + z_hi Wf_lo, the pair product less its
   //     lo x lo term (relative 2^-18).
-  t2va_status fold_weights(const bf16 *const *W, bf16 *Wf, bf16 *wint, float *fpart) const {
-    const bf16 *win[2] = {W[0], W[1]};
-    const int C[2] = {Cv, Ca};
-    for (int m = 0; m < 2; ++m) {
-      TransposeParams tp;
-      tp.src = win[m]; tp.s_bs = 0; tp.s_hs = 0; tp.s_rs = C[m];
-      tp.dst = wint + (m ? (int64_t)Cv * D : 0); tp.d_bs = 0; tp.d_hs = 0; tp.d_rs = D;
-      tp.B = 1; tp.H = 1; tp.R = D; tp.C = C[m]; tp.Rpad = D;
-      HIP_TRY(launch_transpose(tp, 0, s), "transpose");
-    }
+  // Three launches for both blocks: the four transposes, the two split-K
+  // products, the two sums.
+  t2va_status fold_weights(const bf16 *const (&W)[2][6], bf16 *Wf, bf16 *wint, float *fpart) const {
+    const int C[2] = {Cv, Ca}, CC = Cv + Ca;
+    const int64_t wint_bs = (int64_t)CC * D;
+    TransposeParams tp[4];
+    for (int i = 0; i < 2; ++i)
+      for (int m = 0; m < 2; ++m) {
+        TransposeParams &t = tp[2 * i + m];
+        t.src = W[i][m]; t.s_bs = 0; t.s_hs = 0; t.s_rs = C[m];
+        t.dst = wint + i * wint_bs + (m ? (int64_t)Cv * D : 0); t.d_bs = 0; t.d_hs = 0; t.d_rs = D;
+        t.B = 1; t.H = 1; t.R = D; t.C = C[m]; t.Rpad = D;
+      }
+    HIP_TRY(launch_transpose_set(tp, 4, s), "transpose");
     // split-K: chunk k of W_qkv's columns against the same chunk of W_in^T's
-    const int splits = fold_splits(D), kc = D / splits, CC = Cv + Ca;
-    if (t2va_status st = gemm(W[3], D, kc, wint, D, fpart, CC, (int64_t)3 * D * CC, 1, nullptr, 0, 3 * D, CC, kc,
-                              splits, nullptr, CC, kc))
-      return st;
-    HIP_TRY(launch_fold_finish(fpart, splits, 3 * D, Cv, Ca, split, Wf, s), "fold");
+    const int splits = fold_splits(D), kc = D / splits;
+    const int64_t part_bs = (int64_t)fold_part_bytes(Cv, Ca, D) / sizeof(float);
+    GemmParams g[2];
+    for (int i = 0; i < 2; ++i)
+      g[i] = params(W[i][3], D, kc, wint + i * wint_bs, D, fpart + i * part_bs, CC, (int64_t)3 * D * CC, 1,
+                    nullptr, 0, 3 * D, CC, kc, splits, nullptr, CC, kc);
+    {
+      PhaseScope ps(s, T2VA_PHASE_GEMM, prof);
+      HIP_TRY(launch_gemm_pair(g[0], g[1], s), "gemm");
+    }
+    HIP_TRY(launch_fold_finish(fpart, splits, 3 * D, Cv, Ca, split, Wf, 2, part_bs,
+                               (int64_t)fold_elems(Cv, Ca, D, split), s),
+            "fold");
     return T2VA_OK;
   }
 
@@ -570,21 +584,20 @@ struct Block {
 
   // Q|K (row-major into QK) and V^T (dh-major into VT) of `batch` problems:
   // the video and audio rows straight from z with the folded weights Wf
-  // (fold_weights; bias W_qkv tau per batch, into bqkv [batch][3d]), the text
+  // (fold_weights; bias bqkv [batch][3d] = W_qkv tau per batch), the text
   // rows [Nq, NA) from X with W_qkv (no bias; their V^T columns and the zero
   // padding up to ldv).  Split precision: z rows are [hi | lo | hi] (3 C_m
   // wide), the text rows of X [hi | lo] against Wd_qkv = [W_qkv | W_qkv], and
   // Q|K rows are written [Q_hi | K_hi | Q_lo | K_lo].  The audio and text
   // products are small and run as one two-problem launch.
   t2va_status project_in_folded(const bf16 *const *W, const bf16 *Wd_qkv, const bf16 *Wf, const bf16 *zv,
-                                const bf16 *za, const float *tau, float *bqkv, const bf16 *X, bf16 *QK,
-                                bf16 *VT, int batch) const {
+                                const bf16 *za, const float *bqkv, const bf16 *X, bf16 *QK, bf16 *VT,
+                                int batch) const {
     const int kz = split ? 3 : 1, cdt = split ? 2 : 0;
     const bf16 *Wv = Wf, *Wa = split ? Wf + (int64_t)9 * D * Cv : Wf + Cv;
     const int64_t ldwv = split ? 3 * Cv : Cv + Ca, ldwa = split ? 3 * Ca : Cv + Ca;
     const bf16 *Wt = split ? Wd_qkv : W[3];
     const int kt = split ? 2 * D : D;
-    HIP_TRY(launch_row_linear(tau, batch, D, 3 * D, W[3], bqkv, s), "QKV bias");
     if (t2va_status st = gemm(zv, kz * Cv, kz * nv, Wv, ldwv, QK, qks, qk_bs, cdt, bqkv, 3 * D, Nv, 3 * D, kz * Cv,
                               batch, VT, 2 * D, 0, Nv))
       return st;
@@ -685,13 +698,10 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   const bf16 *Wd[2] = {nullptr, nullptr};
   if (L.split) HIP_TRY(prepare_dup(W, 2, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
   // fold W_qkv W_in_m for both blocks
-  const bf16 *Wf[2] = {nullptr, nullptr};
   float *bqkv = (float *)(ws + L.bqkv);
-  for (int i = 0; i < 2; ++i) {
-    bf16 *f = (bf16 *)(ws + L.wfold) + i * fold_elems(d.Cv, d.Ca, D, L.split);
-    if (t2va_status st = blk.fold_weights(W[i], f, (bf16 *)(ws + L.wint), (float *)(ws + L.fpart))) return st;
-    Wf[i] = f;
-  }
+  bf16 *const wfold = (bf16 *)(ws + L.wfold);
+  if (t2va_status st = blk.fold_weights(W, wfold, (bf16 *)(ws + L.wint), (float *)(ws + L.fpart))) return st;
+  const bf16 *Wf[2] = {wfold, wfold + fold_elems(d.Cv, d.Ca, D, L.split)};
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
   float *zf_v = (float *)(ws + L.zf_v), *zf_a = (float *)(ws + L.zf_a);
@@ -729,7 +739,14 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   // z_t = cos t z0 + sin t eps (the GEMM input), half 0 of zv / za.
   T2VA_CALL(token_rows(0, 0, nullptr, nullptr));
   HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
-  HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
+  // tau = W_t e(t) and the QKV bias W_qkv tau of both blocks, two launches:
+  // the student's rows [tau; dtau] (its batches [0, 2B)), then the teacher's
+  float *tau_T = tau + (int64_t)2 * B * D, *bqkv_T = bqkv + (int64_t)2 * B * 3 * D;
+  HIP_TRY(launch_row_linear_pair(D, D, RowLinSeg{E, W[0][2], tau_T, B}, RowLinSeg{E, W[1][2], tau, 2 * B}, s),
+          "time linear");
+  HIP_TRY(launch_row_linear_pair(D, 3 * D, RowLinSeg{tau_T, W[0][3], bqkv_T, B},
+                                 RowLinSeg{tau, W[1][3], bqkv, 2 * B}, s),
+          "QKV bias");
   if (d.Nt > 0)
     // the primal text rows of both blocks' batches [0, B) and the zero tangent
     // rows [B, 2B) of the student's, in one launch
@@ -739,7 +756,7 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
     HIP_TRY(launch_fill_nk(nk, B, Nq, s), "fill nk");
 
   // ---------------- teacher: x0_T = G_T(z_t, t, c) ----------------
-  T2VA_CALL(blk.project_in_folded(W[0], Wd[0], Wf[0], zv, za, tau, bqkv, X, QK, VT, B));
+  T2VA_CALL(blk.project_in_folded(W[0], Wd[0], Wf[0], zv, za, bqkv_T, X, QK, VT, B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
   T2VA_CALL(blk.project_out(W[0], O, x0T_v, x0T_a, B));
 
@@ -748,8 +765,7 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
 
   // ---------------- student: G_S and its JVP ----------------
   // Batches [0, B) carry the primal rows, [B, 2B) their tangents.
-  HIP_TRY(launch_time_linear(E, 2 * B, D, W[1][2], tau, s), "student time linear");
-  T2VA_CALL(blk.project_in_folded(W[1], Wd[1], Wf[1], zv, za, tau, bqkv, X, QK, VT, 2 * B));
+  T2VA_CALL(blk.project_in_folded(W[1], Wd[1], Wf[1], zv, za, bqkv, X, QK, VT, 2 * B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, true, T2VA_PHASE_STUDENT_ATTN, lse_student));
   T2VA_CALL(blk.project_out(W[1], O, x0S_v, x0S_a, 2 * B));
 #undef T2VA_CALL
@@ -1274,13 +1290,10 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   HIP_TRY(prepare_weights(wb, 2, d.weight_dtype, L.w_elems, (bf16 *)(ws + L.wts), W, s), "cast");
   const bf16 *Wd[2] = {nullptr, nullptr};
   if (L.split) HIP_TRY(prepare_dup(W, 2, D, (bf16 *)(ws + L.wdup), Wd, s), "weight pairs");
-  const bf16 *Wf[2] = {nullptr, nullptr};
   float *bqkv = (float *)(ws + L.bqkv);
-  for (int i = 0; i < 2; ++i) {
-    bf16 *f = (bf16 *)(ws + L.wfold) + i * fold_elems(d.Cv, d.Ca, D, L.split);
-    if (t2va_status st = blk.fold_weights(W[i], f, (bf16 *)(ws + L.wint), (float *)(ws + L.fpart))) return st;
-    Wf[i] = f;
-  }
+  bf16 *const wfold = (bf16 *)(ws + L.wfold);
+  if (t2va_status st = blk.fold_weights(W, wfold, (bf16 *)(ws + L.wint), (float *)(ws + L.fpart))) return st;
+  const bf16 *Wf[2] = {wfold, wfold + fold_elems(d.Cv, d.Ca, D, L.split)};
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
   float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
@@ -1305,6 +1318,13 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
     HIP_TRY(launch_split_rows(zf_a, na, d.Ca, za, 3 * na, 3 * d.Ca, B, d.Na, d.Ca, true, s), "split rows");
   }
   HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
+  // tau and the QKV bias of the teacher (rows [0, B)) and the fake-score block ([B, 2B))
+  float *tau_F = tau + (int64_t)B * D, *bqkv_F = bqkv + (int64_t)B * 3 * D;
+  HIP_TRY(launch_row_linear_pair(D, D, RowLinSeg{E, W[0][2], tau, B}, RowLinSeg{E, W[1][2], tau_F, B}, s),
+          "time linear");
+  HIP_TRY(launch_row_linear_pair(D, 3 * D, RowLinSeg{tau, W[0][3], bqkv, B}, RowLinSeg{tau_F, W[1][3], bqkv_F, B},
+                                 s),
+          "QKV bias");
   if (d.Nt > 0)
     HIP_TRY(launch_text_rows(B, Nq, d.Nt, D, text, d.in_dtype, text_mask, X, blk.x_bs, blk.xs, L.split, B, nk, s),
             "text rows");
@@ -1321,8 +1341,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   // of the output projection's input: the output projection is linear, so
   // this is the guided prediction, and the large scales (5 for audio) no
   // longer amplify two separate roundings.
-  HIP_TRY(launch_time_linear(E, B, D, W[0][2], tau, s), "teacher time linear");
-  T2VA_CALL(blk.project_in_folded(W[0], Wd[0], Wf[0], zv, za, tau, bqkv, X, QK, VT, B));
+  T2VA_CALL(blk.project_in_folded(W[0], Wd[0], Wf[0], zv, za, bqkv, X, QK, VT, B));
   if (guided) {
     float *Of = (float *)(ws + L.Of);
     if (Nq % 32 == 0) {
@@ -1344,8 +1363,7 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
   T2VA_CALL(blk.project_out(W[0], O, xT_v, xT_a, B));
 
   // ---------------- fake-score block ----------------
-  HIP_TRY(launch_time_linear(E, B, D, W[1][2], tau, s), "fake time linear");
-  T2VA_CALL(blk.project_in_folded(W[1], Wd[1], Wf[1], zv, za, tau, bqkv, X, QK, VT, B));
+  T2VA_CALL(blk.project_in_folded(W[1], Wd[1], Wf[1], zv, za, bqkv_F, X, QK, VT, B));
   T2VA_CALL(blk.attention(QK, VT, nk, O, false, T2VA_PHASE_TEACHER_ATTN));
   T2VA_CALL(blk.project_out(W[1], O, xF_v, xF_a, B));
 #undef T2VA_CALL
