@@ -97,7 +97,12 @@ struct TrigSeg {
   void *out;
   int64_t n, a_bs, b_bs, x_bs, o_bs;
   int vec;
+  int w;   // out_dt kTrigSplitRows only: the row width (a multiple of 8)
 };
+// out_dt of launch_trigflow_pair for split-precision GEMM rows: each row of w
+// values becomes the bf16 row [hi | lo | hi] (3 w wide; hi = bf16(x),
+// lo = bf16(x - hi)); o_bs counts output elements.
+constexpr int kTrigSplitRows = 2;
 hipError_t launch_trigflow_pair(int op, const CoefTable &coef, int a_dt, int b_dt, int out_dt, const TrigSeg &s1,
                                 const TrigSeg &s2, hipStream_t s);
 
@@ -132,13 +137,6 @@ hipError_t launch_text_rows(int B, int Nq, int Nt, int d, const void *text, int 
 hipError_t launch_guide(const float *c, const float *u, bf16 *out, int B, int Nq, int Nv, int D, float s_v,
                         float s_a, hipStream_t s);
 
-// Split rows: fp32 src [nb][rows][w] (strides s_bs, s_rs) -> bf16 dst rows
-// [hi | lo] of 2w elements, or with repeat_hi [hi | lo | hi] of 3w (strides
-// d_bs, d_rs): hi = bf16(x), lo = bf16(x - hi).  w a multiple of 8; strides
-// multiples of 8.
-hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 *dst, int64_t d_bs,
-                             int64_t d_rs, int nb, int rows, int w, bool repeat_hi, hipStream_t s);
-
 // Folded weights from split-K partials part [splits][rows][Cv + Ca] (fp32,
 // summed in split order): bf16 Wf [rows][Cv + Ca], or with split per modality
 // [rows][3 C_m] = [hi | hi | lo] (hi = bf16(x), lo = bf16(x - hi); video
@@ -147,9 +145,10 @@ hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 
 hipError_t launch_fold_finish(const float *part, int splits, int rows, int Cv, int Ca, bool split, bf16 *Wf,
                               int nblk, int64_t part_bs, int64_t wf_bs, hipStream_t s);
 
-// W2 [n][2k] = [W | W] for bf16 W [n][k] (k a multiple of 8): the weight of a
-// product whose operand rows are [hi | lo] pairs.
-hipError_t launch_dup_cols(const bf16 *W, bf16 *W2, int n, int k, hipStream_t s);
+// D [n][2k] = [W | W] for bf16 W [n][k] (k a multiple of 8): the weight of a
+// product whose operand rows are [hi | lo] pairs; W0 -> D0 and, unless W1 is
+// null, W1 -> D1 in the same launch.
+hipError_t launch_dup_cols(const bf16 *W0, const bf16 *W1, bf16 *D0, bf16 *D1, int n, int k, hipStream_t s);
 
 // nk[b] = value for every sample (used when there is no text).
 hipError_t launch_fill_nk(int32_t *nk, int B, int value, hipStream_t s);
@@ -157,8 +156,17 @@ hipError_t launch_fill_nk(int32_t *nk, int B, int value, hipStream_t s);
 // Blocks the per-sample elementwise kernels use for n elements.
 int elementwise_blocks(int64_t n);
 
-// fp32 -> bf16 copy.
-hipError_t launch_cast_bf16(const float *src, bf16 *dst, int64_t n, hipStream_t s);
+// fp32 -> bf16 copies of count (at most kMaxCasts) arrays src[k] -> dst[k] of
+// n[k] elements, in one launch.
+constexpr int kMaxCasts = 12;
+struct CastSet {
+  const float *src[kMaxCasts];
+  bf16 *dst[kMaxCasts];
+  int64_t n[kMaxCasts];
+  int64_t start[kMaxCasts + 1];
+  int count;
+};
+hipError_t launch_cast_set(const float *const *src, bf16 *const *dst, const int64_t *n, int count, hipStream_t s);
 
 // g, J and per-block partial sums of g^2 for both modalities.
 struct GParams {

@@ -43,7 +43,7 @@ __device__ __forceinline__ void store_n(T *p, int64_t i0, int64_t n, bool vec, c
 // op 0: r (cos a + sin b); op 1: (cos a - b)/sin; op 2: with z = cos a + sin b and
 // the teacher's x0-prediction x0 = rf ? r z - t_emb x : x, F_T = (cos z - x0)/sin
 // and out = r F_T + rdot z (the tangent of the student's token input).
-template <typename TA, typename TB, typename TO>
+template <typename TA, typename TB, typename TO, bool SPLIT_ROWS = false>
 __global__ __launch_bounds__(kThreads) void trigflow_kernel(int op, CoefTable coef, TrigSeg s1, TrigSeg s2,
                                                             int blocks1) {
   // the first blocks1 blocks of each sample's row take segment 1, the rest segment 2
@@ -75,19 +75,33 @@ __global__ __launch_bounds__(kThreads) void trigflow_kernel(int op, CoefTable co
       fo[j] = coef.rf ? c.r * F + c.rdot * z : F;
     }
   }
-  store_n(out, i0, n, vec, fo);
+  if constexpr (SPLIT_ROWS) {
+    // the 8 values lie in one row (w and i0 multiples of 8)
+    const int64_t r = i0 / sg.w, col = i0 - r * sg.w;
+    bf16 *o = reinterpret_cast<bf16 *>(out) + r * 3 * sg.w + col;
+    float lo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lo[j] = fo[j] - (float)(bf16)fo[j];
+    store8(o, fo);
+    store8(o + sg.w, lo);
+    store8(o + 2 * sg.w, fo);
+  } else {
+    store_n(out, i0, n, vec, fo);
+  }
 }
 
-template <typename TA, typename TB, typename TO>
+template <typename TA, typename TB, typename TO, bool SPLIT_ROWS = false>
 hipError_t trigflow_launch3(int op, const CoefTable &coef, TrigSeg s1, TrigSeg s2, hipStream_t s) {
-  for (TrigSeg *g : {&s1, &s2})
+  for (TrigSeg *g : {&s1, &s2}) {
     g->vec = (g->n % 8 == 0) && (g->a_bs % 8 == 0) && (g->b_bs % 8 == 0) && (g->o_bs % 8 == 0) &&
              (g->x == nullptr || g->x_bs % 8 == 0);
+    if (SPLIT_ROWS && g->n > 0 && (!g->vec || g->w <= 0 || g->w % 8 || g->n % g->w)) return hipErrorInvalidValue;
+  }
   const int b1 = (int)((max(s1.n, (int64_t)0) + kChunk - 1) / kChunk);
   const int b2 = (int)((max(s2.n, (int64_t)0) + kChunk - 1) / kChunk);
   if (b1 + b2 == 0) return hipSuccess;
-  hipLaunchKernelGGL((trigflow_kernel<TA, TB, TO>), dim3(b1 + b2, coef.B), dim3(kThreads), 0, s, op, coef, s1, s2,
-                     b1);
+  hipLaunchKernelGGL((trigflow_kernel<TA, TB, TO, SPLIT_ROWS>), dim3(b1 + b2, coef.B), dim3(kThreads), 0, s, op,
+                     coef, s1, s2, b1);
   return hipGetLastError();
 }
 
@@ -95,6 +109,7 @@ template <typename TA, typename TB>
 hipError_t trigflow_launch2(int op, const CoefTable &coef, int out_dt, const TrigSeg &s1, const TrigSeg &s2,
                             hipStream_t s) {
   if (out_dt == 0) return trigflow_launch3<TA, TB, bf16>(op, coef, s1, s2, s);
+  if (out_dt == kTrigSplitRows) return trigflow_launch3<TA, TB, bf16, true>(op, coef, s1, s2, s);
   return trigflow_launch3<TA, TB, float>(op, coef, s1, s2, s);
 }
 
@@ -229,25 +244,6 @@ __global__ __launch_bounds__(kThreads) void text_rows_kernel(int Nq, int Nt, int
   }
 }
 
-// Rows of w fp32 values -> rows [hi | lo] of 2w bf16 values.
-__global__ __launch_bounds__(kThreads) void split_rows_kernel(const float *src, int64_t s_bs, int64_t s_rs,
-                                                              bf16 *dst, int64_t d_bs, int64_t d_rs,
-                                                              int rows, int w, bool repeat_hi) {
-  const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
-  const int64_t per = (int64_t)rows * w;
-  if (i0 >= per) return;
-  const int bi = blockIdx.y;
-  const int64_t r = i0 / w, c = i0 - r * w;   // w is a multiple of 8: one row per group
-  float f[8], lo[8];
-  load8(src + bi * s_bs + r * s_rs + c, f);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) lo[i] = f[i] - (float)(bf16)f[i];
-  bf16 *o = dst + bi * d_bs + r * d_rs + c;
-  store8(o, f);
-  store8(o + w, lo);
-  if (repeat_hi) store8(o + 2 * w, f);
-}
-
 // Guided attention output: u + s (c - u) per element, s by the row's modality.
 __global__ __launch_bounds__(kThreads) void guide_kernel(const float *c, const float *u, bf16 *out, int64_t per,
                                                          int D, int Nv, float s_v, float s_a) {
@@ -264,7 +260,10 @@ __global__ __launch_bounds__(kThreads) void guide_kernel(const float *c, const f
 }
 
 // [W | W]: row i of W2 holds row i of W twice.
-__global__ __launch_bounds__(kThreads) void dup_cols_kernel(const bf16 *W, bf16 *W2, int n, int k) {
+__global__ __launch_bounds__(kThreads) void dup_cols_kernel(const bf16 *W0, const bf16 *W1, bf16 *D0, bf16 *D1,
+                                                            int n, int k) {
+  const bf16 *W = blockIdx.y ? W1 : W0;   // problem blockIdx.y
+  bf16 *W2 = blockIdx.y ? D1 : D0;
   const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
   if (i0 >= (int64_t)n * k) return;
   const int64_t r = i0 / k, c = i0 - r * k;
@@ -309,12 +308,17 @@ __global__ __launch_bounds__(kThreads) void fold_finish_kernel(const float *part
   store8(o + 2 * cm, lo);
 }
 
-__global__ __launch_bounds__(kThreads) void cast_kernel(const float *src, bf16 *dst, int64_t n) {
-  const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+// Up to kMaxCasts fp32 -> bf16 copies in one launch: segment k owns blocks
+// [start[k], start[k + 1]).
+__global__ __launch_bounds__(kThreads) void cast_set_kernel(CastSet cs) {
+  int k = 0;
+  while (k + 1 < cs.count && (int64_t)blockIdx.x >= cs.start[k + 1]) ++k;
+  const int64_t n = cs.n[k];
+  const int64_t i0 = (((int64_t)blockIdx.x - cs.start[k]) * kThreads + threadIdx.x) * 8;
   if (i0 >= n) return;
   float f[8];
-  load_n(src, i0, n, (n % 8) == 0, f);
-  store_n(dst, i0, n, (n % 8) == 0, f);
+  load_n(cs.src[k], i0, n, (n % 8) == 0, f);
+  store_n(cs.dst[k], i0, n, (n % 8) == 0, f);
 }
 
 // ---------------------------------------------------------------------------
@@ -533,16 +537,6 @@ hipError_t launch_text_rows(int B, int Nq, int Nt, int d, const void *text, int 
   return hipGetLastError();
 }
 
-hipError_t launch_split_rows(const float *src, int64_t s_bs, int64_t s_rs, bf16 *dst, int64_t d_bs,
-                             int64_t d_rs, int nb, int rows, int w, bool repeat_hi, hipStream_t s) {
-  const int64_t per = (int64_t)rows * w;
-  if (per <= 0 || nb <= 0) return hipSuccess;
-  dim3 grid((unsigned)((per + kChunk - 1) / kChunk), nb);
-  hipLaunchKernelGGL(split_rows_kernel, grid, dim3(kThreads), 0, s, src, s_bs, s_rs, dst, d_bs, d_rs, rows, w,
-                     repeat_hi);
-  return hipGetLastError();
-}
-
 hipError_t launch_fold_finish(const float *part, int splits, int rows, int Cv, int Ca, bool split, bf16 *Wf,
                               int nblk, int64_t part_bs, int64_t wf_bs, hipStream_t s) {
   const int64_t total = (int64_t)rows * (Cv + Ca);
@@ -561,11 +555,11 @@ hipError_t launch_guide(const float *c, const float *u, bf16 *out, int B, int Nq
   return hipGetLastError();
 }
 
-hipError_t launch_dup_cols(const bf16 *W, bf16 *W2, int n, int k, hipStream_t s) {
+hipError_t launch_dup_cols(const bf16 *W0, const bf16 *W1, bf16 *D0, bf16 *D1, int n, int k, hipStream_t s) {
   const int64_t total = (int64_t)n * k;
   if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(dup_cols_kernel, dim3((unsigned)((total + kChunk - 1) / kChunk)), dim3(kThreads), 0, s, W,
-                     W2, n, k);
+  hipLaunchKernelGGL(dup_cols_kernel, dim3((unsigned)((total + kChunk - 1) / kChunk), W1 ? 2 : 1), dim3(kThreads), 0,
+                     s, W0, W1, D0, D1, n, k);
   return hipGetLastError();
 }
 
@@ -581,10 +575,22 @@ hipError_t launch_fill_nk(int32_t *nk, int B, int value, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_cast_bf16(const float *src, bf16 *dst, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n + kChunk - 1) / kChunk);
-  hipLaunchKernelGGL(cast_kernel, dim3(blocks), dim3(kThreads), 0, s, src, dst, n);
+hipError_t launch_cast_set(const float *const *src, bf16 *const *dst, const int64_t *n, int count, hipStream_t s) {
+  if (count < 0 || count > kMaxCasts) return hipErrorInvalidValue;
+  CastSet cs = {};
+  int64_t blocks = 0;
+  for (int k = 0; k < count; ++k) {
+    cs.src[cs.count] = src[k];
+    cs.dst[cs.count] = dst[k];
+    cs.n[cs.count] = n[k];
+    cs.start[cs.count] = blocks;
+    if (n[k] <= 0) continue;   // nothing to copy: no segment
+    blocks += (n[k] + kChunk - 1) / kChunk;
+    ++cs.count;
+  }
+  if (blocks == 0) return hipSuccess;
+  cs.start[cs.count] = blocks;
+  hipLaunchKernelGGL(cast_set_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, cs);
   return hipGetLastError();
 }
 

@@ -137,12 +137,19 @@ void block_weight_elems(int Cv, int Ca, int d, size_t *n) {
 // (one after another, 128-element aligned), bf16 weights are used in place.
 hipError_t prepare_weights(const t2va_block_weights *const *wb, int count, int weight_dtype,
                            const size_t *elems, bf16 *dst, const bf16 *W[][6], hipStream_t s) {
+  // fp32 weights: every tensor of every block cast in one launch
+  const float *srcs[kMaxCasts];
+  bf16 *dsts[kMaxCasts];
+  int64_t ns[kMaxCasts];
+  int nc = 0;
   for (int i = 0; i < count; ++i) {
     const void *src[6] = {wb[i]->w_in_v, wb[i]->w_in_a, wb[i]->w_t, wb[i]->w_qkv, wb[i]->w_out_v, wb[i]->w_out_a};
     for (int j = 0; j < 6; ++j) {
       if (weight_dtype == T2VA_DTYPE_FP32) {
-        hipError_t e = launch_cast_bf16((const float *)src[j], dst, (int64_t)elems[j], s);
-        if (e != hipSuccess) return e;
+        if (nc == kMaxCasts) return hipErrorInvalidValue;
+        srcs[nc] = (const float *)src[j];
+        dsts[nc] = dst;
+        ns[nc++] = (int64_t)elems[j];
         W[i][j] = dst;
         dst += align_up(elems[j], 128);
       } else {
@@ -150,20 +157,18 @@ hipError_t prepare_weights(const t2va_block_weights *const *wb, int count, int w
       }
     }
   }
-  return hipSuccess;
+  return nc ? launch_cast_set(srcs, dsts, ns, nc, s) : hipSuccess;
 }
 
 // Split precision: the text rows' QKV product contracts [X_hi | X_lo] rows, so
 // its weight is used as [W_qkv | W_qkv] ([3d, 2d]), built into the workspace
-// per call for each block.
+// per call for each block (both blocks in one launch).
 size_t dup_qkv_elems(int d) { return align_up((size_t)3 * d * 2 * d, 128); }
 hipError_t prepare_dup(const bf16 *W[][6], int count, int d, bf16 *dst, const bf16 *Wd[], hipStream_t s) {
-  for (int i = 0; i < count; ++i) {
-    if (hipError_t e = launch_dup_cols(W[i][3], dst, 3 * d, d, s)) return e;
-    Wd[i] = dst;
-    dst += dup_qkv_elems(d);
-  }
-  return hipSuccess;
+  if (count < 1 || count > 2) return hipErrorInvalidValue;
+  for (int i = 0; i < count; ++i) Wd[i] = dst + i * dup_qkv_elems(d);
+  return launch_dup_cols(W[0][3], count == 2 ? W[1][3] : nullptr, (bf16 *)Wd[0], count == 2 ? (bf16 *)Wd[1] : nullptr,
+                         3 * d, d, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -172,7 +177,7 @@ hipError_t prepare_dup(const bf16 *W[][6], int count, int d, bf16 *dst, const bf
 struct Layout {
   int Nq, N_all, dh, ldv, nblk_v, nblk_a;
   bool split;   // T2VA_PREC_SPLIT: [hi | lo | hi] z rows, [hi | lo] rows for X and Q|K
-  size_t wts, wdup, wfold, wint, fpart, bqkv, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v,
+  size_t wts, wdup, wfold, wint, fpart, bqkv, zv, za, E, tau, X, QK, VT, nk, O, x0T_v, x0T_a, x0S_v,
       x0S_a,
       part_v, part_a, apart;
   size_t total, apart_bytes;
@@ -224,8 +229,6 @@ Layout make_layout(const t2va_scm_desc &d, bool whole_tiles = false) {
   L.wint = take(2 * (size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
   L.fpart = take(2 * fold_part_bytes(d.Cv, d.Ca, d.d));
   L.bqkv = take(3 * B * 3 * D * sizeof(float));   // student [0, 2B), teacher [2B, 3B)
-  L.zf_v = take(L.split ? 2 * B * d.Nv * d.Cv * sizeof(float) : 0);
-  L.zf_a = take(L.split ? 2 * B * d.Na * d.Ca * sizeof(float) : 0);
   L.zv = take(2 * B * d.Nv * d.Cv * spz * sizeof(bf16));
   L.za = take(2 * B * d.Na * d.Ca * spz * sizeof(bf16));
   L.E = take(2 * B * D * sizeof(float));
@@ -362,7 +365,7 @@ t2va_status check_weights(const t2va_block_weights *const *wb, int n, const char
 struct DmdLayout {
   int ldv, nblk_v, nblk_a;
   bool split;
-  size_t wts, wdup, wfold, wint, fpart, bqkv, zf_v, zf_a, zv, za, E, tau, X, QK, VT, nk, nk_null, O, Of, xT_v,
+  size_t wts, wdup, wfold, wint, fpart, bqkv, zv, za, E, tau, X, QK, VT, nk, nk_null, O, Of, xT_v,
       xT_a, xF_v,
       xF_a, pa_v, pa_a, ps_v, ps_a, apart;
   size_t total, apart_bytes;
@@ -395,8 +398,6 @@ DmdLayout make_dmd_layout(const t2va_dmd_desc &d) {
   L.wint = take(2 * (size_t)(d.Cv + d.Ca) * D * sizeof(bf16));
   L.fpart = take(2 * fold_part_bytes(d.Cv, d.Ca, d.d));
   L.bqkv = take(2 * B * 3 * D * sizeof(float));   // teacher [0, B), fake [B, 2B)
-  L.zf_v = take(L.split ? B * nv * sizeof(float) : 0);
-  L.zf_a = take(L.split ? B * na * sizeof(float) : 0);
   L.zv = take(B * nv * spz * sizeof(bf16));
   L.za = take(B * na * spz * sizeof(bf16));
   L.E = take(2 * B * D * sizeof(float));
@@ -704,7 +705,6 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   const bf16 *Wf[2] = {wfold, wfold + fold_elems(d.Cv, d.Ca, D, L.split)};
 
   bf16 *zv = (bf16 *)(ws + L.zv), *za = (bf16 *)(ws + L.za);
-  float *zf_v = (float *)(ws + L.zf_v), *zf_a = (float *)(ws + L.zf_a);
   float *E = (float *)(ws + L.E), *tau = (float *)(ws + L.tau);
   bf16 *X = (bf16 *)(ws + L.X), *QK = (bf16 *)(ws + L.QK), *VT = (bf16 *)(ws + L.VT);
   bf16 *O = (bf16 *)(ws + L.O);
@@ -714,7 +714,8 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   float *part_v = (float *)(ws + L.part_v), *part_a = (float *)(ws + L.part_a);
 
   // The block's latent token rows of batch half `half` (0: z_t, 1: F_T) from
-  // the trigflow op: bf16, or in split precision fp32 split into [hi | lo | hi].
+  // the trigflow op: bf16, or in split precision the fp32 value split into
+  // bf16 rows [hi | lo | hi].
   auto token_rows = [&](int op, int half, const float *x0_v, const float *x0_a) -> t2va_status {
     const int64_t xs_v = op == 2 ? nv : 0, xs_a = op == 2 ? na : 0;
     // video and audio rows in one launch
@@ -724,14 +725,9 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
       HIP_TRY(launch_trigflow_pair(op, coef, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, sv, sa, s), "token rows");
       return T2VA_OK;
     }
-    float *fv = zf_v + (int64_t)half * B * nv, *fa = zf_a + (int64_t)half * B * na;
-    const TrigSeg sv{z0_v, eps_v, x0_v, fv, nv, nv, nv, xs_v, nv, 0};
-    const TrigSeg sa{z0_a, eps_a, x0_a, fa, na, na, na, xs_a, na, 0};
-    HIP_TRY(launch_trigflow_pair(op, coef, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, sv, sa, s), "token rows");
-    HIP_TRY(launch_split_rows(fv, nv, d.Cv, zv + (int64_t)half * B * 3 * nv, 3 * nv, 3 * d.Cv, B, d.Nv, d.Cv, true,
-                              s), "split rows");
-    HIP_TRY(launch_split_rows(fa, na, d.Ca, za + (int64_t)half * B * 3 * na, 3 * na, 3 * d.Ca, B, d.Na, d.Ca, true,
-                              s), "split rows");
+    const TrigSeg sv{z0_v, eps_v, x0_v, zv + (int64_t)half * B * 3 * nv, nv, nv, nv, xs_v, 3 * nv, 0, d.Cv};
+    const TrigSeg sa{z0_a, eps_a, x0_a, za + (int64_t)half * B * 3 * na, na, na, na, xs_a, 3 * na, 0, d.Ca};
+    HIP_TRY(launch_trigflow_pair(op, coef, d.in_dtype, d.in_dtype, kTrigSplitRows, sv, sa, s), "token rows");
     return T2VA_OK;
   };
 
@@ -1310,12 +1306,9 @@ t2va_status t2va_dmd_target(const t2va_dmd_desc *desc, const t2va_block_weights 
     const TrigSeg sa{x0_a, eps_a, nullptr, za, na, na, na, 0, na, 0};
     HIP_TRY(launch_trigflow_pair(0, coef, d.in_dtype, d.in_dtype, T2VA_DTYPE_BF16, sv, sa, s), "noise");
   } else {
-    float *zf_v = (float *)(ws + L.zf_v), *zf_a = (float *)(ws + L.zf_a);
-    const TrigSeg sv{x0_v, eps_v, nullptr, zf_v, nv, nv, nv, 0, nv, 0};
-    const TrigSeg sa{x0_a, eps_a, nullptr, zf_a, na, na, na, 0, na, 0};
-    HIP_TRY(launch_trigflow_pair(0, coef, d.in_dtype, d.in_dtype, T2VA_DTYPE_FP32, sv, sa, s), "noise");
-    HIP_TRY(launch_split_rows(zf_v, nv, d.Cv, zv, 3 * nv, 3 * d.Cv, B, d.Nv, d.Cv, true, s), "split rows");
-    HIP_TRY(launch_split_rows(zf_a, na, d.Ca, za, 3 * na, 3 * d.Ca, B, d.Na, d.Ca, true, s), "split rows");
+    const TrigSeg sv{x0_v, eps_v, nullptr, zv, nv, nv, nv, 0, 3 * nv, 0, d.Cv};
+    const TrigSeg sa{x0_a, eps_a, nullptr, za, na, na, na, 0, 3 * na, 0, d.Ca};
+    HIP_TRY(launch_trigflow_pair(0, coef, d.in_dtype, d.in_dtype, kTrigSplitRows, sv, sa, s), "noise");
   }
   HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
   // tau and the QKV bias of the teacher (rows [0, B)) and the fake-score block ([B, 2B))
