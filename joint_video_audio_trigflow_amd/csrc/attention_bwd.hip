@@ -407,11 +407,13 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
   const float c_log2 = p.scale * 1.4426950408889634f;
 
   bf16x8 kf[MB][C::KSTEPS], vf[MB][C::KSTEPS];
-  float kmask[MB];   // 1 for valid keys, 0 for keys past nk
+  // Keys past nk get dK = dV = 0, applied when they are stored: a lane's
+  // weights P and dS only ever reach its own key's dK and dV columns.
+  bool kvalid[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int k_ld = min(k_row0 + 16 * mb, p.Nk - 1);
-    kmask[mb] = k_row0 + 16 * mb < nk ? 1.f : 0.f;
+    kvalid[mb] = k_row0 + 16 * mb < nk;
     const bf16 *kp = p.k + (int64_t)b * p.k_bs + (int64_t)k_ld * p.k_rs + h * DH + 8 * g;
     const bf16 *vp = p.v + (int64_t)b * p.v_bs + (int64_t)k_ld * p.v_rs + h * DH + 8 * g;
 #pragma unroll
@@ -512,23 +514,23 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
             dP[mb][t] = mfma16(da[t], vf[mb][s], s == 0 ? zero4 : dP[mb][t]);
           }
       }
-      // this lane's queries: 32 u + 8 g + m of the stage, m = 4 t + r
+      // this lane's queries: 32 u + 8 g + m of the stage, m = 4 t + r.
+      // Queries past Nq (in the last stage of the last piece; other pieces end
+      // at a stage boundary) need no mask: their Q and dO rows, lse2 and D lie
+      // past the descriptors' ends and load as zeros, so S = dP = 0, P = 1 and
+      // dS = 0, and their Q^T and dO^T columns are the zeros the transposes
+      // pad with up to a whole stage, so both products add 0.
       float4 l0, l1, d0, d1;
       read_stage_stats(sL(cur) + 32 * u + 8 * g, sD(cur) + 32 * u + 8 * g, l0, l1, d0, d1);
       const float lq[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
       const float dq[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-      // queries past Nq (last stage only) and keys past nk get zero weight
-      float lqm[8];
-      const int qbase = st * BT + 32 * u + 8 * g;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) lqm[m] = (st == nst - 1 && qbase + m >= Nq) ? INFINITY : lq[m];
       bf16x8 P[MB], dS[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const int t = m >> 2, r = m & 3;
-          const float pv = kmask[mb] * __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][t][r], c_log2, -lqm[m]));
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[mb][t][r], c_log2, -lq[m]));
           P[mb][m] = (bf16)pv;
           dS[mb][m] = (bf16)(pv * (dP[mb][t][r] - dq[m]));
         }
@@ -567,10 +569,14 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
 #pragma unroll
       for (int e = 0; e < C::DT; ++e) {
         float *pk = part + 4 * (e * MB * C::THREADS_DKV + pi);
-        *reinterpret_cast<float4 *>(pk) = make_float4(dK[mb][e][0] * p.scale, dK[mb][e][1] * p.scale,
-                                                      dK[mb][e][2] * p.scale, dK[mb][e][3] * p.scale);
-        *reinterpret_cast<float4 *>(pk + C::PIECE_DKV_HALF) =
-            make_float4(dV[mb][e][0], dV[mb][e][1], dV[mb][e][2], dV[mb][e][3]);
+        float k4[4], v4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          k4[r] = kvalid[mb] ? dK[mb][e][r] * p.scale : 0.f;
+          v4[r] = kvalid[mb] ? dV[mb][e][r] : 0.f;
+        }
+        *reinterpret_cast<float4 *>(pk) = make_float4(k4[0], k4[1], k4[2], k4[3]);
+        *reinterpret_cast<float4 *>(pk + C::PIECE_DKV_HALF) = make_float4(v4[0], v4[1], v4[2], v4[3]);
       }
     } else if (k_row < p.Nk) {
       const int64_t o = (int64_t)b * p.dk_bs + (int64_t)k_row * p.dk_rs + h * DH + 4 * g;
@@ -579,8 +585,8 @@ __global__ __launch_bounds__((BwdCfg<DH>::THREADS_DKV), 1) void attn_bwd_dkv_ker
         bf16x4 vk, vv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          vk[r] = (bf16)(dK[mb][e][r] * p.scale);
-          vv[r] = (bf16)dV[mb][e][r];
+          vk[r] = (bf16)(kvalid[mb] ? dK[mb][e][r] * p.scale : 0.f);
+          vv[r] = (bf16)(kvalid[mb] ? dV[mb][e][r] : 0.f);
         }
         *reinterpret_cast<bf16x4 *>(p.dk + o + 16 * e) = vk;
         *reinterpret_cast<bf16x4 *>(p.dv + o + 16 * e) = vv;
