@@ -457,6 +457,16 @@ t2va_status t2va_stage3_mix(int B, double lam_scm, double lam_dmd, const float *
 t2va_status t2va_profile_enable(int max_calls);
 
 /*
+ * t2va_profile_set_phases - which phases the calls record: bit p of
+ * phase_mask for phase T2VA_PHASE_p (all phases until this is called).  A
+ * phase left out issues no events, so a timed loop carries only the events
+ * it reads.  T2VA_PHASE_OTHER (total minus the timed parts) is reported only
+ * when the total and every part are recorded, else 0.  Returns
+ * T2VA_INVALID_ARG while recorded events are unread.
+ */
+t2va_status t2va_profile_set_phases(unsigned phase_mask);
+
+/*
  * t2va_profile_read - waits for the recorded events, writes per-phase sums of
  * milliseconds over the recorded calls into ms_out[T2VA_NUM_PHASES], the
  * number of recorded calls into *n_calls, and starts a new recording window.

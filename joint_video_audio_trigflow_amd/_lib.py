@@ -127,6 +127,8 @@ def load() -> ctypes.CDLL:
     lib.t2va_stage3_mix.argtypes = [i32, ctypes.c_double, ctypes.c_double, f32p, f32p, f32p, vp]
     lib.t2va_profile_enable.restype = i32
     lib.t2va_profile_enable.argtypes = [i32]
+    lib.t2va_profile_set_phases.restype = i32
+    lib.t2va_profile_set_phases.argtypes = [ctypes.c_uint]
     lib.t2va_profile_read.restype = i32
     lib.t2va_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     _lib = lib
@@ -451,6 +453,12 @@ def stage3_mix(loss_scm: torch.Tensor, loss_dmd: torch.Tensor, lam_scm: float, l
 
 def profile_enable(max_calls: int):
     _check(load().t2va_profile_enable(max_calls))
+
+
+def profile_set_phases(names=None):
+    """Record only the named phases (all with None)."""
+    mask = 0xFFFFFFFF if names is None else sum(1 << PHASES.index(n) for n in names)
+    _check(load().t2va_profile_set_phases(mask))
 
 
 def profile_read() -> tuple[dict, int]:

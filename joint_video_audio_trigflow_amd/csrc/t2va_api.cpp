@@ -453,13 +453,14 @@ struct Profiler {
   hipEvent_t next() { return used < pool.size() ? pool[used++] : nullptr; }
 };
 Profiler g_prof;
+unsigned g_prof_phases = ~0u;   // phases whose events are recorded (t2va_profile_set_phases)
 
 struct PhaseScope {
   hipStream_t s;
   int phase;
   hipEvent_t a = nullptr, b = nullptr;
   bool on;
-  PhaseScope(hipStream_t s_, int ph, bool on_) : s(s_), phase(ph), on(on_) {
+  PhaseScope(hipStream_t s_, int ph, bool on_) : s(s_), phase(ph), on(on_ && ((g_prof_phases >> ph) & 1u)) {
     if (on) {
       a = g_prof.next();
       b = g_prof.next();
@@ -979,6 +980,13 @@ t2va_status t2va_profile_enable(int max_calls) {
   return T2VA_OK;
 }
 
+t2va_status t2va_profile_set_phases(unsigned phase_mask) {
+  g_err.clear();
+  if (!g_prof.recs.empty()) return fail(T2VA_INVALID_ARG, "read the recorded events first");
+  g_prof_phases = phase_mask;
+  return T2VA_OK;
+}
+
 t2va_status t2va_profile_read(double *ms_out, int *n_calls) {
   g_err.clear();
   if (!ms_out || !n_calls) return fail(T2VA_INVALID_ARG, "NULL output");
@@ -993,7 +1001,10 @@ t2va_status t2va_profile_read(double *ms_out, int *n_calls) {
   }
   double parts = ms_out[T2VA_PHASE_TEACHER_ATTN] + ms_out[T2VA_PHASE_STUDENT_ATTN] + ms_out[T2VA_PHASE_GEMM] +
                  ms_out[T2VA_PHASE_BWD_ATTN];
-  ms_out[T2VA_PHASE_OTHER] = ms_out[T2VA_PHASE_TOTAL] - parts;
+  // the remainder of the call, when the call and every timed part were recorded
+  const unsigned need = (1u << T2VA_PHASE_TOTAL) | (1u << T2VA_PHASE_TEACHER_ATTN) |
+                        (1u << T2VA_PHASE_STUDENT_ATTN) | (1u << T2VA_PHASE_GEMM) | (1u << T2VA_PHASE_BWD_ATTN);
+  ms_out[T2VA_PHASE_OTHER] = (g_prof_phases & need) == need ? ms_out[T2VA_PHASE_TOTAL] - parts : 0.0;
   *n_calls = g_prof.calls;
   g_prof.recs.clear();
   g_prof.used = 0;

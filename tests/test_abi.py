@@ -299,3 +299,15 @@ def test_v_transpose_rejects_before_launch(lib):
     assert call(vrs=260) == 1                                  # not a multiple of 8
     assert call(vp=ctypes.c_void_p(0x10008)) == 1 and "aligned" in err(lib)
     assert call(vp=None) == 1
+
+
+def test_profile_phase_mask(lib):
+    """t2va_profile_set_phases selects the phases later calls record; with no
+    events recorded (none here: no GPU call runs) it always succeeds, and the
+    binding maps phase names to mask bits in the header's order."""
+    assert lib.t2va_profile_set_phases(1 << 2) == 0          # T2VA_PHASE_STUDENT_ATTN only
+    _lib.profile_set_phases(["student_attn", "bwd_attn"])
+    _lib.profile_set_phases(None)                            # every phase again
+    src = open(HEADER).read()
+    for i, name in enumerate(_lib.PHASES):
+        assert re.search(rf"#define T2VA_PHASE_{name.upper()} {i}\b", src), name
