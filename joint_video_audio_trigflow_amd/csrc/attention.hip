@@ -552,14 +552,16 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_fw
   // compares per row block cost more VALU issue slots, which the forward
   // kernel is short of (teacher attention 2.5 % slower).
   auto outgrown = [&](const floatx4 (&S)[C::MB][2]) {
-    bool any = false;
+    // one ballot per compare: the compares' lane masks OR together in scalar
+    // registers (a vote on an OR-ed bool first copies it to a vector register)
+    uint64_t votes = 0;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
       const float m = max3f(max3f(S[mb][0][0], S[mb][0][1], S[mb][0][2]), max3f(S[mb][0][3], S[mb][1][0], S[mb][1][1]),
                             max3f(S[mb][1][2], S[mb][1][3], S[mb][1][3]));
-      any |= m > thr[mb];
+      votes |= __builtin_amdgcn_ballot_w64(m > thr[mb]);
     }
-    return __any(any);
+    return votes != 0;
   };
 
   // Forward only: the normalised output of the keys seen so far into o2 (o's
