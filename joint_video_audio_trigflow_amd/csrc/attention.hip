@@ -496,7 +496,8 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_fw
                      bf16x8 &PS) {
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
-      float lsum = 0.f, musum = 0.f;
+      // the sums start at -0, the identity of fp addition, so the first add folds away
+      float lsum = -0.f, musum = -0.f;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int t = m >> 2, r = m & 3;
