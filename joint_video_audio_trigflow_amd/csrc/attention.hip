@@ -488,6 +488,16 @@ __global__ __launch_bounds__((AttnCfg<DH, TAN, SPLIT>::THREADS), 1) void attn_fw
   bf16x8 ones;
 #pragma unroll
   for (int m = 0; m < 8; ++m) ones[m] = (bf16)1.f;
+  {
+    // opaque to the compiler, so the forward kernel keeps the operand in four
+    // registers instead of rebuilding it with two moves per sub-tile in the
+    // key loop (its VALU issue slots are the scarce ones; teacher attention
+    // 0.4 % faster, same box)
+    typedef int intx4 __attribute__((ext_vector_type(4)));
+    intx4 bits = *reinterpret_cast<intx4 *>(&ones);
+    asm volatile("" : "+v"(bits));
+    ones = *reinterpret_cast<bf16x8 *>(&bits);
+  }
   // a row needs a raise once a raw logit exceeds (m_run + kLazy)/c_log2
   auto set_thr = [&](int mb) { thr[mb] = (m_run[mb] + kLazy) / c_log2; };
 
