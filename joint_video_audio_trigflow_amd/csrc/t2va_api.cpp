@@ -736,8 +736,9 @@ t2va_status run_scm(const t2va_scm_desc &d, const Layout &L, const t2va_block_we
   // z_t = cos t z0 + sin t eps (the GEMM input), half 0 of zv / za.
   T2VA_CALL(token_rows(0, 0, nullptr, nullptr));
   HIP_TRY(launch_time_embedding(coef, D, E, s), "time embedding");
-  // tau = W_t e(t) and the QKV bias W_qkv tau of both blocks, two launches:
-  // the student's rows [tau; dtau] (its batches [0, 2B)), then the teacher's
+  // tau = W_t e(t) of both blocks in one launch, then both blocks' QKV bias
+  // rows W_qkv tau in a second; the student's [tau; dtau] rows are [0, 2B)
+  // (where the backward reads them), the teacher's [2B, 3B)
   float *tau_T = tau + (int64_t)2 * B * D, *bqkv_T = bqkv + (int64_t)2 * B * 3 * D;
   HIP_TRY(launch_row_linear_pair(D, D, RowLinSeg{E, W[0][2], tau_T, B}, RowLinSeg{E, W[1][2], tau, 2 * B}, s),
           "time linear");
