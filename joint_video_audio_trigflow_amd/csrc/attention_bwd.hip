@@ -681,7 +681,7 @@ template <int DH>
 size_t bwd_split_bytes(int B, int H, int Nq, int Nk) {
   using C = BwdCfg<DH>;
   auto need = [](int64_t tiles, int piece_floats) {
-    return std::min<size_t>(kCapPiecesBwd, (size_t)kMaxPieces * 8 * ((tiles + 7) / 8)) * piece_floats *
+    return std::min<size_t>(kCapPiecesBwd, (size_t)kMaxPiecesBwd * 8 * ((tiles + 7) / 8)) * piece_floats *
            sizeof(float);
   };
   const int64_t tq = (int64_t)B * H * ((Nq + C::BW_DQ - 1) / C::BW_DQ);
@@ -709,7 +709,7 @@ hipError_t launch_bwd_impl(const AttnBwdParams &p, hipStream_t s) {
   int per_xcd = (total + 7) / 8;
   size_t cap = p.part ? p.part_bytes / (sizeof(float) * C::PIECE_DQ) : 0;
   SplitArgs sp = cap ? plan_split(per_xcd, xcd_slots(attn_bwd_dq_kernel<DH>, C::THREADS_DQ, C::DQ_LDS, slots_dq),
-                                  (p.Nk + BT - 1) / BT, cap, kMinPieceKeys / BT)
+                                  (p.Nk + BT - 1) / BT, cap, kMinPieceKeys / BT, kMaxPiecesBwd)
                      : SplitArgs{per_xcd, 0, 1};
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DH>), dim3(8 * (sp.n_full + sp.rem * sp.k)), dim3(C::THREADS_DQ),
                      C::DQ_LDS, s, p, nqb, per_xcd, total, sp);
@@ -727,7 +727,7 @@ hipError_t launch_bwd_impl(const AttnBwdParams &p, hipStream_t s) {
   per_xcd = (total + 7) / 8;
   cap = p.part ? p.part_bytes / (sizeof(float) * C::PIECE_DKV) : 0;
   sp = cap ? plan_split(per_xcd, xcd_slots(attn_bwd_dkv_kernel<DH>, C::THREADS_DKV, C::DKV_LDS, slots_dkv),
-                        (p.Nq + BT - 1) / BT, cap, kMinPieceKeys / BT)
+                        (p.Nq + BT - 1) / BT, cap, kMinPieceKeys / BT, kMaxPiecesBwd)
            : SplitArgs{per_xcd, 0, 1};
   hipLaunchKernelGGL((attn_bwd_dkv_kernel<DH>), dim3(8 * (sp.n_full + sp.rem * sp.k)), dim3(C::THREADS_DKV),
                      C::DKV_LDS, s, p, nkb, per_xcd, total, sp);

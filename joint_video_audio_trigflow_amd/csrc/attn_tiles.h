@@ -52,7 +52,12 @@ __device__ __forceinline__ floatx4 mfma16(const bf16x8 &a, const bf16x8 &b, cons
 // Each piece stores a partial result into scratch and a second kernel merges
 // the pieces of every split tile in piece order.
 // ---------------------------------------------------------------------------
-constexpr int kMaxPieces = 4;
+// The forward kernels cut a tile into at most 8 pieces; the backward kernels,
+// whose pieces each store fp32 partials of a whole tile (dK and dV: 1 KB per
+// key row), at most 4 (8 was 1.7 % slower for the standard workload's
+// backward, 0.6 % faster at high-res).
+constexpr int kMaxPieces = 8;
+constexpr int kMaxPiecesBwd = 4;
 constexpr int kMinPieceKeys = 512;   // no piece shorter than 512 keys (at the longest sample)
 constexpr int kMaxDevices = 64;
 struct SplitArgs {
@@ -86,18 +91,19 @@ __host__ __device__ __forceinline__ void piece_stages(int nst, int piece, int k,
 }
 
 // The split of an XCD's per_xcd tiles when it holds `slots` workgroups at
-// once: the k <= kMaxPieces that minimises the time of the last round(s),
+// once: the k <= max_k (<= kMaxPieces) that minimises the time of the last round(s),
 // ceil(rem k / slots) / k whole-tile times, ties to the smaller k; no split
 // when nothing is gained, a piece would span fewer than min_stages of the
 // nst_max stages, or the scratch holds fewer than 8 rem k pieces.
-inline SplitArgs plan_split(int per_xcd, int slots, int nst_max, size_t cap_pieces, int min_stages) {
+inline SplitArgs plan_split(int per_xcd, int slots, int nst_max, size_t cap_pieces, int min_stages,
+                            int max_k = kMaxPieces) {
   SplitArgs sp{per_xcd, 0, 1, 0};
   if (slots <= 0) return sp;
   const int rem = per_xcd % slots;
   if (rem == 0) return sp;
   int best_k = 1;
   int64_t best_num = 1, best_den = 1;   // cost as the fraction ceil(rem k / slots) / k
-  for (int k = 2; k <= kMaxPieces; ++k) {
+  for (int k = 2; k <= max_k && k <= kMaxPieces; ++k) {
     if (nst_max / k < min_stages || (size_t)8 * rem * k > cap_pieces) break;
     const int64_t num = (rem * k + slots - 1) / slots;
     if (num * best_den < best_num * k) {

@@ -1,7 +1,7 @@
 // Host driver for the tail-split planning and work decomposition of the
 // attention kernels (attn_tiles.h), used by tests/test_split_plan.py.
 // Reads commands from stdin, one per line, and prints one answer line each:
-//   plan PER_XCD SLOTS NST_MAX CAP MIN_STAGES -> n_full rem k
+//   plan PER_XCD SLOTS NST_MAX CAP MIN_STAGES MAX_K -> n_full rem k
 //   items PER_XCD N_FULL REM K       -> for every workgroup w of the launch,
 //                                       "L piece slot" (one line per w, then "end")
 //   tile PER_XCD N_FULL REM K SLOT   -> the logical tile of split slot SLOT
@@ -15,9 +15,9 @@ int main() {
   char cmd[16];
   while (std::scanf("%15s", cmd) == 1) {
     if (!std::strcmp(cmd, "plan")) {
-      int per_xcd, slots, nst, cap, min_stages;
-      if (std::scanf("%d %d %d %d %d", &per_xcd, &slots, &nst, &cap, &min_stages) != 5) return 1;
-      const t2va::SplitArgs sp = t2va::plan_split(per_xcd, slots, nst, (size_t)cap, min_stages);
+      int per_xcd, slots, nst, cap, min_stages, max_k;
+      if (std::scanf("%d %d %d %d %d %d", &per_xcd, &slots, &nst, &cap, &min_stages, &max_k) != 6) return 1;
+      const t2va::SplitArgs sp = t2va::plan_split(per_xcd, slots, nst, (size_t)cap, min_stages, max_k);
       std::printf("%d %d %d\n", sp.n_full, sp.rem, sp.k);
     } else if (!std::strcmp(cmd, "items")) {
       t2va::SplitArgs sp;

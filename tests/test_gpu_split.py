@@ -5,7 +5,8 @@ XCD (32 compute units on MI355X) runs its tiles in rounds.  When the last round
 would be short, the last tiles of each XCD are cut into k pieces over
 consecutive ranges of 64-key stages and merged by a second kernel (only in the
 entry points that carry a workspace).  The rule: with per_xcd = ceil(tiles / 8)
-and rem = per_xcd mod 32, k in 2..4 minimises ceil(rem k / 32) / k, and a
+and rem = per_xcd mod 32, k in 2..8 (2..4 for the backward kernels) minimises
+ceil(rem k / 32) / k, and a
 piece never spans fewer than 512 keys of the longest possible sample (the JVP
 and backward kernels stage 64 keys at a time, the forward kernel 128).  The
 shapes below are chosen to take each branch of that rule:
@@ -15,6 +16,9 @@ shapes below are chosen to take each branch of that rule:
   four pieces of every tile are empty (they must get zero weight);
 - split-k3 (dh 128) and split-k3-64 (dh 64): 1,664 queries over 8 heads give
   72 JVP tiles (per_xcd 9, k = 3) and 40 forward tiles (per_xcd 5, k = 3);
+- split-k8: 1,536 queries over 2 heads and 2,600 valid text keys (4,136 keys)
+  give 16 JVP tiles (per_xcd 2) and 8 forward tiles (per_xcd 1), each cut into
+  k = 8 pieces of at least 512 keys (the dQ kernel's 12 tiles into k = 4);
 - the large sweep shapes and the full-size test take k = 2, the full-size
   teacher forward k = 4.
 
@@ -42,10 +46,12 @@ SPLIT_K3 = inputs.Config("split-k3", B=1, Nv=1600, Na=64, Nt=64, Ntv=40, Cv=128,
                          in_dtype="bf16", beta=1.0, gamma=0.8, mask_mode="scatter", index=81)
 SPLIT_K3_64 = inputs.Config("split-k3-64", B=1, Nv=1600, Na=64, Nt=64, Ntv=64, Cv=64, Ca=128, d=512, H=8,
                             in_dtype="bf16", beta=0.9, gamma=0.4, param="rf", index=82)
-CASES = [SPLIT_EMPTY, SPLIT_K3, SPLIT_K3_64]
+SPLIT_K8 = inputs.Config("split-k8", B=1, Nv=1400, Na=136, Nt=2600, Ntv=2600, Cv=128, Ca=64, d=256, H=2,
+                         in_dtype="bf16", beta=1.1, gamma=0.7, mask_mode="scatter", index=83)
+CASES = [SPLIT_EMPTY, SPLIT_K3, SPLIT_K3_64, SPLIT_K8]
 
 
-def planned_pieces(tiles, n_keys, stage, slots=32):
+def planned_pieces(tiles, n_keys, stage, slots=32, max_k=8):
     """The split rule as documented above (k = 1: no split)."""
     per_xcd = (tiles + 7) // 8
     rem = per_xcd % slots
@@ -53,7 +59,7 @@ def planned_pieces(tiles, n_keys, stage, slots=32):
         return 1
     nst_max = (n_keys + stage - 1) // stage
     best_k, best = 1, 1.0
-    for k in range(2, 5):
+    for k in range(2, max_k + 1):
         if nst_max // k < 512 // stage:
             break
         cost = math.ceil(rem * k / slots) / k
@@ -79,7 +85,7 @@ def say(*a):
 
 
 def test_split_cases_take_each_branch():
-    """Host-side check that the shapes exercise k = 4 with empty pieces and k = 3."""
+    """Host-side check that the shapes exercise k = 4 with empty pieces, k = 3 and k = 8."""
     def plan(cfg, rows):
         # JVP kernel: 192 rows, 64-key stages; forward kernel: 384 rows, 128-key stages
         tiles = cfg.B * cfg.H * ((cfg.Nq + rows - 1) // rows)
@@ -87,6 +93,9 @@ def test_split_cases_take_each_branch():
     assert plan(SPLIT_EMPTY, 192) == 4 and (SPLIT_EMPTY.Nq + SPLIT_EMPTY.Ntv + 63) // 64 < 4
     assert plan(SPLIT_K3, 192) == 3 and plan(SPLIT_K3, 384) == 3
     assert plan(SPLIT_K3_64, 192) == 3
+    assert plan(SPLIT_K8, 192) == 8 and plan(SPLIT_K8, 384) == 8
+    dq_tiles = SPLIT_K8.B * SPLIT_K8.H * ((SPLIT_K8.Nq + 255) // 256)   # dQ kernel: 256 queries per tile
+    assert planned_pieces(dq_tiles, SPLIT_K8.N_all, 64, max_k=4) == 4
     hr = inputs.CONFIGS["high-res"]
     assert plan(hr, 192) == 2 and plan(hr, 384) == 4
 

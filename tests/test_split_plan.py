@@ -8,7 +8,8 @@ planner and the index arithmetic of `csrc/attn_tiles.h` for the host
 (`tests/host/split_plan.cpp`) and check:
 
 - the planner follows its documented rule: rem = per_xcd mod slots, and among
-  k = 2..4 whose pieces still span >= min_stages stages (512 keys: 8 stages of
+  k = 2..max_k (8 for the forward kernels, 4 for the backward ones) whose
+  pieces still span >= min_stages stages (512 keys: 8 stages of
   64 keys, 4 of 128) and whose 8 rem k pieces fit the scratch, the one with the
   fewest tail rounds ceil(rem k / slots) / k, ties to the smaller k; no split
   when that is no better than k = 1;
@@ -49,13 +50,13 @@ def driver(tmp_path_factory):
     return run
 
 
-def rule(per_xcd, slots, nst_max, cap, min_stages=8):
+def rule(per_xcd, slots, nst_max, cap, min_stages=8, max_k=8):
     """The documented planning rule, written out independently."""
     if slots <= 0 or per_xcd % slots == 0:
         return per_xcd, 0, 1
     rem = per_xcd % slots
     best_k, best = 1, Fraction(1)
-    for k in range(2, 5):
+    for k in range(2, max_k + 1):
         if nst_max // k < min_stages or 8 * rem * k > cap:
             break
         cost = Fraction(math.ceil(rem * k / slots), k)
@@ -66,19 +67,20 @@ def rule(per_xcd, slots, nst_max, cap, min_stages=8):
     return per_xcd - rem, rem, best_k
 
 
-PLAN_CASES = [(p, s, n, c, m)
+PLAN_CASES = [(p, s, n, c, m, x)
               for p in list(range(1, 70)) + [151, 152, 226, 302, 304, 342, 684, 1000]
               for s in (32, 38, 64)
               for n in (1, 15, 16, 24, 33, 228, 454)
               for c in (0, 100, 768, 10 ** 6)
-              for m in (4, 8)]
+              for m in (4, 8)
+              for x in (4, 8)]
 
 
 def test_plan_follows_the_rule(driver):
-    out = driver([f"plan {p} {s} {n} {c} {m}" for p, s, n, c, m in PLAN_CASES])
-    for (p, s, n, c, m), line in zip(PLAN_CASES, out):
-        got = tuple(int(x) for x in line.split())
-        assert got == rule(p, s, n, c, m), (p, s, n, c, m, got)
+    out = driver([f"plan {p} {s} {n} {c} {m} {x}" for p, s, n, c, m, x in PLAN_CASES])
+    for (p, s, n, c, m, x), line in zip(PLAN_CASES, out):
+        got = tuple(int(v) for v in line.split())
+        assert got == rule(p, s, n, c, m, x), (p, s, n, c, m, x, got)
         n_full, rem, k = got
         if k > 1:
             assert n_full + rem == p and 0 < rem < s
@@ -91,8 +93,8 @@ def test_high_res_plans(driver):
     """The shapes the profiles quote: 302 JVP tiles (64-key stages) and 152
     forward tiles (128-key stages) per XCD, 226 dQ and 304 dK/dV tiles,
     32 workgroups per XCD."""
-    out = driver(["plan 302 32 454 768 8", "plan 152 32 228 768 4", "plan 226 32 456 768 8",
-                  "plan 304 32 452 768 8"])
+    out = driver(["plan 302 32 454 768 8 8", "plan 152 32 228 768 4 8", "plan 226 32 456 768 8 4",
+                  "plan 304 32 452 768 8 4"])
     assert [tuple(map(int, l.split())) for l in out[:4]] == [(288, 14, 2), (128, 24, 4), (224, 2, 4),
                                                               (288, 16, 2)]
 
