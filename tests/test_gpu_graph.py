@@ -1,4 +1,4 @@
-"""The targets under HIP graph capture.
+"""The targets (and the training backward) under HIP graph capture.
 
 The library allocates nothing, copies nothing between host and device and
 never synchronises inside a call: a call is a fixed sequence of kernel
@@ -105,6 +105,21 @@ def test_dmd_target_graph_replay():
     args = (dev["teacher"], dev["fake"], dev["x0_v"], dev["x0_a"], dev["eps_v"], dev["eps_a"], dev["text"],
             dev["text_mask"], dev["t"])
     check_replays("dmd_target small", lambda: op(*args), op.out)
+
+
+def test_scm_grad_graph_replay():
+    """The training backward is a fixed launch sequence too (the target, the
+    attention backward with its split tails, the weight-gradient GEMMs and
+    their fixed-order split-K sums): a replay reproduces the gradients."""
+    L = lib()
+    print("graph capture: scm_grad small", flush=True)
+    cfg = inputs.CONFIGS["small"]
+    p = inputs.make_problem(cfg)
+    dev = L.to_device_problem(p)
+    op = L.ScmGrad(cfg)
+    args = (dev["teacher"], dev["student"], dev["z0_v"], dev["z0_a"], dev["eps_v"], dev["eps_a"], dev["text"],
+            dev["text_mask"], dev["t"])
+    check_replays("scm_grad small", lambda: op(*args), dict(op.out, **op.grads))
 
 
 def test_noalloc_entry_graph_replay():
